@@ -1,0 +1,185 @@
+/*
+ * tq.h — C ABI of libtq, the TurboQuant KV-cache codec for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (pages: "TurboQuant と RotorQuant を DGX Spark で試してみた",
+ * section "PolarQuant + QJL の 2 段階圧縮"; "TurboQuantとは？仕組み・実測精度
+ * ・2026年7月時点の実装状況", sections 第1段 and 第2段): a key or value vector
+ * keeps its norm, its unit vector is rotated by a random-sign Walsh-Hadamard
+ * transform and each coordinate is Lloyd-Max quantized with no per-block
+ * scale; a key additionally keeps the 1-bit signs of a Gaussian (QJL)
+ * projection of its quantization residual plus the residual norm, which makes
+ * the inner-product estimate q.k unbiased. Attention reads the codes directly.
+ *
+ * Conventions shared by every call
+ *   - All arrays are caller-allocated. "device" arrays live in GPU memory
+ *     (hipMalloc / torch CUDA tensors), "host" arrays in CPU memory.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream). Results are valid after the stream synchronizes.
+ *   - Calls keep no state between invocations and never allocate device
+ *     memory; scratch space comes from the caller's `workspace`.
+ *   - Arguments are validated on the host before anything is launched:
+ *     TQ_EINVAL for a malformed argument (null pointer, negative size,
+ *     workspace too small, inconsistent shapes), TQ_EUNSUPPORTED for a
+ *     well-formed request this build does not implement (a head dimension
+ *     other than 64 or 128, more than 4 Lloyd-Max bits, ...). A failed
+ *     launch returns TQ_EHIP. tq_last_error() then describes the failure.
+ *   - Data values are not inspected: NaN/Inf in inputs propagate, and a norm
+ *     above 65504 is stored as fp16 infinity.
+ *
+ * Codes and scalars (the packed, scale-free cache)
+ *   Let d be the head dimension, w the Lloyd-Max bits, L = 2^w.
+ *   A sequence is one (layer, batch, kv-head) stream of tokens; a cache holds
+ *   n_seq sequences of `cap` token slots each.
+ *   Keys   codes   uint8  [n_seq][cap][(w+1)*d/8]  one record per token: w
+ *                  index planes (plane p holds bit p of each index), then the
+ *                  QJL sign plane; each plane is d/8 bytes, coordinate i at
+ *                  byte i/8, bit i%8 (LSB first).
+ *          scalars fp16   [n_seq][cap][2]  {norm, residual norm}
+ *   Values codes   uint32 [n_seq][cap/32][w][d]  token-major: tokens are
+ *                  grouped in blocks of 32; the word for (block B, plane p,
+ *                  coordinate i) holds bit p of the index of token 32B+j at
+ *                  bit j. `cap` must be a multiple of 32.
+ *          scalars fp16   [n_seq][cap]  {norm}
+ *   Index idx_i of coordinate i is the number of thresholds t_j <= y_i
+ *   (exact ties go to the upper cell); a sign bit is 1 when its projection
+ *   is >= 0.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = -1,
+  TQ_EUNSUPPORTED = -2,
+  TQ_EHIP = -3
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/*
+ * Codec parameters. They depend only on (d, bits, seed): no calibration data
+ * ("TurboQuantとは？…", section キャリブレーション不要が効く場面).
+ *   d           head dimension (a power of two)
+ *   lm_bits     w, Lloyd-Max bits per coordinate: keys use b-1 of their b
+ *               bits (the last bit is the QJL sign), values use all b
+ *   is_key      1: keys (QJL sign plane + residual norm), 0: values
+ *   signs       device float [d], +1/-1: the rotation R = H diag(signs)/sqrt(d),
+ *               H the Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i&j)
+ *   centroids   device float [L], ascending and symmetric (c[L-1-k] = -c[k]),
+ *               e.g. from tq_make_codebook
+ *   thresholds  device float [L-1], t_j between c[j-1] and c[j]
+ *   sketch      device fp16 bit patterns [d][d] (keys only, else NULL): the
+ *               QJL projection S, row j = the j-th projection direction
+ * The arrays are read, never written, and must stay alive while any call
+ * that uses the codec is in flight.
+ */
+typedef struct {
+  int32_t d;
+  int32_t lm_bits;
+  int32_t is_key;
+  int32_t reserved;
+  const float *signs;
+  const float *centroids;
+  const float *thresholds;
+  const uint16_t *sketch;
+} tq_codec;
+
+/*
+ * Lloyd-Max codebook for one coordinate of a uniformly random unit vector in
+ * R^d, whose density is proportional to (1 - x^2)^((d-3)/2) on [-1, 1]; after
+ * the random rotation every coordinate of a unit vector follows it, whatever
+ * the data (stage 1 of the method: rotation, then per-coordinate Lloyd-Max;
+ * "TurboQuantとは？…", section 第1段).
+ *   d        >= 3 (any integer; the GPU calls need 64 or 128)
+ *   lm_bits  1..8
+ *   centroids   host float [2^lm_bits] out, ascending, exactly symmetric
+ *   thresholds  host float [2^lm_bits - 1] out, midpoints (middle one 0)
+ * Host only, synchronous, deterministic. TQ_EINVAL on bad arguments.
+ */
+tq_status tq_make_codebook(int32_t d, int32_t lm_bits, float *centroids, float *thresholds);
+
+/* Bytes of one key record's codes, (w+1)*d/8; 0 if the arguments are invalid. */
+size_t tq_key_record_bytes(int32_t d, int32_t lm_bits);
+/* Bytes of one 32-token value block, 4*w*d; 0 if the arguments are invalid. */
+size_t tq_value_block_bytes(int32_t d, int32_t lm_bits);
+
+/*
+ * Encode n_tok tokens of each of n_seq sequences into cache slots
+ * [t0, t0 + n_tok) (steps: store the norm, rotate, Lloyd-Max quantize; keys
+ * also take the residual, its norm and the QJL sign bits; pack).
+ *   x        device, dtype xt (TQ_F32 / TQ_BF16 / TQ_F16); element i of token
+ *            t of sequence s at x[s*x_seq_stride + t*x_tok_stride + i]
+ *            (strides in elements; rows are contiguous)
+ *   codes    device, key or value layout above (uint32 words for values)
+ *   scalars  device fp16 bit patterns, layout above
+ *   cap      token slots per sequence in codes/scalars (values: multiple of 32)
+ *   t0       first slot written; t0 + n_tok <= cap
+ * Slots outside [t0, t0 + n_tok) are left untouched (value blocks that the
+ * range only partly covers are merged bit by bit), so a decoding loop can
+ * append one token per step. n_seq == 0 or n_tok == 0 is a no-op.
+ */
+tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_t n_seq,
+                       int64_t n_tok, int64_t x_seq_stride, int64_t x_tok_stride, void *codes,
+                       uint16_t *scalars, int64_t cap, int64_t t0, void *stream);
+
+/*
+ * Estimated attention logits q.k for every query head against the first
+ * n_keys keys of its KV head (the attention-logit computation the pages time:
+ * "TurboQuantとは？…", section まとめ; "メモリの壁を砕く圧縮革命…", 検証結果):
+ *   logit = n * ( sum_i q'_i c[idx_i]
+ *                 + sqrt(pi/2)/d * gamma * sum_j p_j (2 sigma_j - 1) ),
+ *   q' = R q, p = S q', n and gamma the stored fp16 norms.
+ *   q        device [batch][n_kv_heads*group][d], dtype qt
+ *   query head h of batch b reads key sequence b*n_kv_heads + h/group
+ *   kcodes, kscalars  key cache (layout above) with `cap` slots per sequence
+ *   logits   device float [batch][n_kv_heads*group][n_keys] out
+ *   workspace  device, >= tq_logits_workspace(...) bytes, 256-byte aligned
+ */
+tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch,
+                    int32_t n_kv_heads, int32_t group, const uint8_t *kcodes,
+                    const uint16_t *kscalars, int64_t cap, int64_t n_keys, float *logits,
+                    void *workspace, size_t ws_bytes, void *stream);
+size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d);
+
+/*
+ * Fused decode attention over the coded cache: logits as tq_logits, exact
+ * softmax of sm_scale*logit over tokens t < ctx_lens[b], and the weighted sum
+ * of the decoded values n_t R_v^T c_v[idx_t] (accumulated in the rotated
+ * domain, rotated back once per output row).
+ *   q        device [batch][n_kv_heads*group][d], dtype qt
+ *   kcodes, kscalars, vcodes, vscalars  key and value caches, `cap` slots
+ *   ctx_lens device int32 [batch]; values are clamped to [0, max_ctx]; a
+ *            row with no tokens gets zeros
+ *   max_ctx  upper bound of ctx_lens (<= cap); sizes the context splits
+ *   out      device [batch][n_kv_heads*group][d], dtype out_t (TQ_F32 or
+ *            TQ_BF16, round to nearest even)
+ *   workspace  device, >= tq_decode_attend_workspace(...) bytes, 256-byte
+ *            aligned
+ */
+tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt,
+                           int32_t batch, int32_t n_kv_heads, int32_t group,
+                           const uint8_t *kcodes, const uint16_t *kscalars,
+                           const uint32_t *vcodes, const uint16_t *vscalars, int64_t cap,
+                           const int32_t *ctx_lens, int64_t max_ctx, float sm_scale, void *out,
+                           tq_dtype out_t, void *workspace, size_t ws_bytes, void *stream);
+size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t group,
+                                  int64_t max_ctx, int32_t d);
+
+/* Static description of a status code. */
+const char *tq_status_string(tq_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char *tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,278 @@
+// C ABI of libtq: argument validation, workspace layout and kernel dispatch.
+// Every check runs on the host before any launch, so malformed calls fail
+// with TQ_EINVAL / TQ_EUNSUPPORTED without touching the GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/tq.h"
+#include "tq_kernels.h"
+
+namespace tq {
+bool lloyd_max_positive_half(int d, int bits, std::vector<double> &c);
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tq_status fail(tq_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tq_status ok() {
+  g_err[0] = '\0';
+  return TQ_OK;
+}
+
+tq_status hip_status(hipError_t e, const char *where) {
+  if (e == hipSuccess) return ok();
+  return fail(TQ_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int dtype_size(tq_dtype t) { return t == TQ_F32 ? 4 : 2; }
+
+bool dtype_ok(tq_dtype t) { return t == TQ_F32 || t == TQ_BF16 || t == TQ_F16; }
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Codec checks shared by the device calls. `need_key` = 1 requires a key
+// codec, 0 a value codec, -1 either.
+tq_status check_codec(const tq_codec *c, int need_key, const char *name) {
+  if (!c) return fail(TQ_EINVAL, "%s: codec is NULL", name);
+  if (!pow2(c->d) || c->d < 8) return fail(TQ_EINVAL, "%s: d=%d is not a power of two >= 8", name, c->d);
+  if (c->d != 64 && c->d != 128) return fail(TQ_EUNSUPPORTED, "%s: d=%d (this build supports 64 and 128)", name, c->d);
+  if (c->lm_bits < 1) return fail(TQ_EINVAL, "%s: lm_bits=%d", name, c->lm_bits);
+  if (c->lm_bits > 4) return fail(TQ_EUNSUPPORTED, "%s: lm_bits=%d (this build supports 1..4)", name, c->lm_bits);
+  if (c->is_key != 0 && c->is_key != 1) return fail(TQ_EINVAL, "%s: is_key=%d", name, c->is_key);
+  if (need_key >= 0 && c->is_key != need_key)
+    return fail(TQ_EINVAL, "%s: expected a %s codec", name, need_key ? "key" : "value");
+  if (!c->signs || !c->centroids || !c->thresholds) return fail(TQ_EINVAL, "%s: codec array is NULL", name);
+  if (c->is_key && !c->sketch) return fail(TQ_EINVAL, "%s: key codec without a sketch", name);
+  return TQ_OK;
+}
+
+// Decode split size: a multiple of the 32-token value block, small enough
+// that the grid fills the chip and the block's LDS stays under 64 KiB.
+int choose_split(int32_t batch, int32_t n_kv, int32_t group, int64_t max_ctx, int d) {
+  int split = 512;
+  while (split > 64) {
+    const int64_t n_splits = (max_ctx + split - 1) / split;
+    if (static_cast<int64_t>(batch) * n_kv * n_splits >= 1024) break;
+    split /= 2;
+  }
+  while (split > 32 && tq::decode_split_smem(d, group, split) > 65536) split /= 2;
+  return split;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_EINVAL: return "TQ_EINVAL: invalid argument";
+    case TQ_EUNSUPPORTED: return "TQ_EUNSUPPORTED: not supported by this build";
+    case TQ_EHIP: return "TQ_EHIP: HIP runtime error";
+  }
+  return "unknown tq_status";
+}
+
+const char *tq_last_error(void) { return g_err; }
+
+tq_status tq_make_codebook(int32_t d, int32_t lm_bits, float *centroids, float *thresholds) {
+  if (d < 3) return fail(TQ_EINVAL, "tq_make_codebook: d=%d < 3", d);
+  if (lm_bits < 1 || lm_bits > 8) return fail(TQ_EINVAL, "tq_make_codebook: lm_bits=%d not in 1..8", lm_bits);
+  if (!centroids || !thresholds) return fail(TQ_EINVAL, "tq_make_codebook: NULL output");
+  std::vector<double> pos;
+  if (!tq::lloyd_max_positive_half(d, lm_bits, pos))
+    return fail(TQ_EINVAL, "tq_make_codebook: iteration did not settle (d=%d, bits=%d)", d, lm_bits);
+  const int L = 1 << lm_bits;
+  const int H = L / 2;
+  std::vector<double> c(L);
+  for (int k = 0; k < H; ++k) {
+    c[H + k] = pos[k];
+    c[H - 1 - k] = -pos[k];
+  }
+  for (int k = 0; k < L; ++k) centroids[k] = static_cast<float>(c[k]);
+  for (int k = 0; k + 1 < L; ++k) thresholds[k] = static_cast<float>(0.5 * (c[k] + c[k + 1]));
+  thresholds[H - 1] = 0.0f;
+  return ok();
+}
+
+size_t tq_key_record_bytes(int32_t d, int32_t lm_bits) {
+  if (!pow2(d) || d < 8 || lm_bits < 1 || lm_bits > 8) return 0;
+  return static_cast<size_t>(lm_bits + 1) * d / 8;
+}
+
+size_t tq_value_block_bytes(int32_t d, int32_t lm_bits) {
+  if (!pow2(d) || d < 8 || lm_bits < 1 || lm_bits > 8) return 0;
+  return static_cast<size_t>(4) * lm_bits * d;
+}
+
+tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_t n_seq, int64_t n_tok,
+                       int64_t x_seq_stride, int64_t x_tok_stride, void *codes, uint16_t *scalars, int64_t cap,
+                       int64_t t0, void *stream) {
+  const char *fn = "tq_encode_kv";
+  tq_status s = check_codec(codec, -1, fn);
+  if (s != TQ_OK) return s;
+  if (!dtype_ok(xt)) return fail(TQ_EINVAL, "%s: bad input dtype %d", fn, static_cast<int>(xt));
+  if (n_seq < 0 || n_tok < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (cap < 0 || t0 < 0 || t0 + n_tok > cap) return fail(TQ_EINVAL, "%s: slots [t0, t0+n_tok) exceed cap", fn);
+  if (!codec->is_key && cap % 32 != 0) return fail(TQ_EINVAL, "%s: value cache cap must be a multiple of 32", fn);
+  if (n_seq == 0 || n_tok == 0) return ok();
+  if (!x || !codes || !scalars) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  if (x_tok_stride < codec->d || (n_seq > 1 && x_seq_stride < 0))
+    return fail(TQ_EINVAL, "%s: token stride must be >= d", fn);
+  const int64_t g0 = t0 / 64;
+  const int64_t g1 = (t0 + n_tok - 1) / 64;
+  tq::EncodeParams p{};
+  p.x = x;
+  p.x_seq_stride = x_seq_stride;
+  p.x_tok_stride = x_tok_stride;
+  p.n_tok = n_tok;
+  p.t0 = t0;
+  p.cap = cap;
+  p.g0 = g0;
+  p.groups_per_seq = g1 - g0 + 1;
+  p.n_waves = n_seq * p.groups_per_seq;
+  p.signs = codec->signs;
+  p.centroids = codec->centroids;
+  p.thresholds = codec->thresholds;
+  p.sketch = codec->sketch;
+  p.codes = codes;
+  p.scalars = scalars;
+  p.xt = static_cast<int>(xt);
+  const int es = dtype_size(xt);
+  if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || (x_tok_stride * es) % 16 != 0 || (x_seq_stride * es) % 16 != 0)
+    return fail(TQ_EUNSUPPORTED, "%s: input rows must start on 16-byte boundaries", fn);
+  if (reinterpret_cast<uintptr_t>(codes) % 16 != 0 || reinterpret_cast<uintptr_t>(scalars) % 4 != 0)
+    return fail(TQ_EINVAL, "%s: codes must be 16-byte and scalars 4-byte aligned", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool key = codec->is_key != 0;
+  hipError_t e = codec->d == 64 ? tq::launch_encode_d<64>(p, codec->lm_bits, key, st)
+                                : tq::launch_encode_d<128>(p, codec->lm_bits, key, st);
+  return hip_status(e, fn);
+}
+
+size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d) {
+  if (batch < 0 || n_kv_heads < 0 || group < 0 || d <= 0) return 0;
+  return align_up(static_cast<size_t>(batch) * n_kv_heads * group * 2 * d * sizeof(float));
+}
+
+tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
+                    int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap, int64_t n_keys,
+                    float *logits, void *workspace, size_t ws_bytes, void *stream) {
+  const char *fn = "tq_logits";
+  tq_status s = check_codec(kc, 1, fn);
+  if (s != TQ_OK) return s;
+  if (!dtype_ok(qt)) return fail(TQ_EINVAL, "%s: bad query dtype", fn);
+  if (batch < 0 || n_kv_heads < 0 || group < 0 || n_keys < 0 || cap < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (n_keys > cap) return fail(TQ_EINVAL, "%s: n_keys > cap", fn);
+  if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (batch == 0 || n_kv_heads == 0 || group == 0 || n_keys == 0) return ok();
+  if (!q || !kcodes || !kscalars || !logits || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  const size_t need = tq_logits_workspace(batch, n_kv_heads, group, kc->d);
+  if (ws_bytes < need) return fail(TQ_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TQ_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 4)
+    return fail(TQ_EINVAL, "%s: kcodes must be 16-byte and kscalars 4-byte aligned", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float *qprep = static_cast<float *>(workspace);
+  tq::QueryPrepParams qp{q, static_cast<int>(qt), static_cast<int64_t>(batch) * n_kv_heads * group, kc->signs,
+                         kc->sketch, qprep};
+  hipError_t e = kc->d == 64 ? tq::launch_query_prep_d<64>(qp, st) : tq::launch_query_prep_d<128>(qp, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  tq::LogitsParams lp{qprep, kcodes, kscalars, kc->centroids, cap, n_keys, batch, n_kv_heads, group, logits};
+  e = kc->d == 64 ? tq::launch_logits_d<64>(lp, kc->lm_bits, st) : tq::launch_logits_d<128>(lp, kc->lm_bits, st);
+  return hip_status(e, fn);
+}
+
+size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int64_t max_ctx, int32_t d) {
+  if (batch < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
+  const int split = choose_split(batch, n_kv_heads, group, max_ctx, d);
+  const int64_t n_splits = (max_ctx + split - 1) / split;
+  const size_t qbytes = align_up(static_cast<size_t>(batch) * n_kv_heads * group * 2 * d * sizeof(float));
+  const size_t pbytes =
+      align_up(static_cast<size_t>(batch) * n_kv_heads * (n_splits > 0 ? n_splits : 1) * group * (d + 2) * sizeof(float));
+  return qbytes + pbytes;
+}
+
+tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
+                           int32_t n_kv_heads, int32_t group, const uint8_t *kcodes, const uint16_t *kscalars,
+                           const uint32_t *vcodes, const uint16_t *vscalars, int64_t cap, const int32_t *ctx_lens,
+                           int64_t max_ctx, float sm_scale, void *out, tq_dtype out_t, void *workspace,
+                           size_t ws_bytes, void *stream) {
+  const char *fn = "tq_decode_attend";
+  tq_status s = check_codec(kc, 1, fn);
+  if (s != TQ_OK) return s;
+  s = check_codec(vc, 0, fn);
+  if (s != TQ_OK) return s;
+  if (kc->d != vc->d) return fail(TQ_EINVAL, "%s: key d=%d and value d=%d differ", fn, kc->d, vc->d);
+  if (!dtype_ok(qt)) return fail(TQ_EINVAL, "%s: bad query dtype", fn);
+  if (out_t != TQ_F32 && out_t != TQ_BF16) return fail(TQ_EUNSUPPORTED, "%s: output dtype must be f32 or bf16", fn);
+  if (batch < 0 || n_kv_heads < 0 || group < 0 || cap < 0 || max_ctx < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (max_ctx > cap) return fail(TQ_EINVAL, "%s: max_ctx > cap", fn);
+  if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
+  if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!std::isfinite(sm_scale)) return fail(TQ_EINVAL, "%s: sm_scale is not finite", fn);
+  if (batch == 0 || n_kv_heads == 0 || group == 0) return ok();
+  if (!q || !out || !ctx_lens || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  if (max_ctx > 0 && (!kcodes || !kscalars || !vcodes || !vscalars)) return fail(TQ_EINVAL, "%s: NULL cache pointer", fn);
+  const size_t need = tq_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, kc->d);
+  if (ws_bytes < need) return fail(TQ_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TQ_EINVAL, "%s: workspace not 256-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 4 ||
+      reinterpret_cast<uintptr_t>(vcodes) % 4 || reinterpret_cast<uintptr_t>(vscalars) % 2)
+    return fail(TQ_EINVAL, "%s: misaligned cache pointer", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int d = kc->d;
+  const int split = choose_split(batch, n_kv_heads, group, max_ctx, d);
+  const int64_t n_splits64 = max_ctx > 0 ? (max_ctx + split - 1) / split : 1;
+  float *qprep = static_cast<float *>(workspace);
+  float *partials = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                              align_up(static_cast<size_t>(batch) * n_kv_heads * group * 2 * d * sizeof(float)));
+  tq::QueryPrepParams qp{q, static_cast<int>(qt), static_cast<int64_t>(batch) * n_kv_heads * group, kc->signs,
+                         kc->sketch, qprep};
+  hipError_t e = d == 64 ? tq::launch_query_prep_d<64>(qp, st) : tq::launch_query_prep_d<128>(qp, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  tq::DecodeParams dp{};
+  dp.qprep = qprep;
+  dp.kcodes = kcodes;
+  dp.kscalars = kscalars;
+  dp.vcodes = vcodes;
+  dp.vscalars = vscalars;
+  dp.kcent = kc->centroids;
+  dp.vcent = vc->centroids;
+  dp.vsigns = vc->signs;
+  dp.cap = cap;
+  dp.max_ctx = max_ctx;
+  dp.ctx_lens = ctx_lens;
+  dp.batch = batch;
+  dp.n_kv = n_kv_heads;
+  dp.group = group;
+  dp.split = split;
+  dp.n_splits = static_cast<int32_t>(n_splits64);
+  dp.sm_scale = sm_scale;
+  dp.partials = partials;
+  dp.out = out;
+  dp.out_t = static_cast<int>(out_t);
+  e = d == 64 ? tq::launch_decode_d<64>(dp, kc->lm_bits, vc->lm_bits, st)
+              : tq::launch_decode_d<128>(dp, kc->lm_bits, vc->lm_bits, st);
+  return hip_status(e, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+"""Host-side tests of libtq (no GPU): exported symbols, the host codebook
+solver against the oracle, and argument validation, which must reject bad
+calls before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_rht_amd as tq
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", tq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines()}
+    declared = _declared()
+    assert declared, "no declarations found in include/tq.h"
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    assert set(declared) == set(tq.EXPORTED)
+    for s in declared:
+        getattr(tq.lib, s)          # resolvable through ctypes
+
+
+@pytest.mark.parametrize("d", [3, 4, 16, 64, 128, 256])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_host_codebook_matches_oracle(d, bits):
+    c, t = tq.make_codebook(d, bits)
+    co, to = O.make_codebook(d, bits)
+    # both solve the same fixed point to ~1e-15; fp32 rounding must agree
+    cu = c.numpy().view(np.int32).astype(np.int64)
+    tu = t.numpy().view(np.int32).astype(np.int64)
+    assert np.max(np.abs(cu - co.view(np.int32))) <= 1
+    assert np.max(np.abs(tu - to.view(np.int32))) <= 1
+    assert np.all(c.numpy() == -c.numpy()[::-1])
+    assert t.numpy()[(1 << bits) // 2 - 1] == 0.0
+
+
+@pytest.mark.parametrize("d,bits", [(2, 2), (0, 1), (64, 0), (64, 9)])
+def test_codebook_rejects_bad_arguments(d, bits):
+    with pytest.raises(tq.TQError) as e:
+        tq.make_codebook(d, bits)
+    assert e.value.status == tq.TQ_EINVAL
+
+
+def test_record_sizes():
+    assert tq.key_record_bytes(128, 3) == 64
+    assert tq.key_record_bytes(128, 2) == 48
+    assert tq.key_record_bytes(64, 2) == 24
+    assert tq.value_block_bytes(128, 4) == 2048
+    assert tq.key_record_bytes(96, 2) == 0
+
+
+# ---------------------------------------------------------------- validation
+
+FAKE = 1 << 20      # an aligned, never-dereferenced address
+
+
+def _codec(d=128, w=2, key=1, sketch=True):
+    c = tq._Codec()
+    c.d, c.lm_bits, c.is_key, c.reserved = d, w, key, 0
+    c.signs = c.centroids = c.thresholds = FAKE
+    c.sketch = FAKE if sketch else None
+    return c
+
+
+def _p(v=FAKE):
+    return ctypes.c_void_p(v)
+
+
+def _encode(c, xt=tq.TQ_BF16, n_seq=1, n_tok=64, seq_stride=64 * 128, tok_stride=128, codes=FAKE,
+            scal=FAKE, cap=64, t0=0, x=FAKE):
+    return tq.lib.tq_encode_kv(ctypes.byref(c) if c is not None else None, _p(x), xt, n_seq, n_tok,
+                               seq_stride, tok_stride, _p(codes), _p(scal), cap, t0, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(c=None), tq.TQ_EINVAL),
+    (dict(c="d96"), tq.TQ_EINVAL),
+    (dict(c="d256"), tq.TQ_EUNSUPPORTED),
+    (dict(c="w0"), tq.TQ_EINVAL),
+    (dict(c="w5"), tq.TQ_EUNSUPPORTED),
+    (dict(c="nosketch"), tq.TQ_EINVAL),
+    (dict(xt=7), tq.TQ_EINVAL),
+    (dict(n_tok=-1), tq.TQ_EINVAL),
+    (dict(t0=32, n_tok=64, cap=64), tq.TQ_EINVAL),
+    (dict(c="value", cap=48, n_tok=16), tq.TQ_EINVAL),
+    (dict(x=0), tq.TQ_EINVAL),
+    (dict(codes=0), tq.TQ_EINVAL),
+    (dict(tok_stride=64), tq.TQ_EINVAL),
+    (dict(x=FAKE + 2), tq.TQ_EUNSUPPORTED),
+    (dict(tok_stride=129, seq_stride=129 * 64), tq.TQ_EUNSUPPORTED),
+    (dict(codes=FAKE + 4), tq.TQ_EINVAL),
+])
+def test_encode_validation(kwargs, status):
+    c = kwargs.pop("c", "key")
+    codec = {"key": _codec(), "d96": _codec(d=96), "d256": _codec(d=256), "w0": _codec(w=0),
+             "w5": _codec(w=5), "nosketch": _codec(sketch=False), "value": _codec(key=0),
+             None: None}[c]
+    assert _encode(codec, **kwargs) == status
+    assert tq.lib.tq_last_error().decode()
+
+
+def test_encode_empty_is_noop():
+    assert _encode(_codec(), n_seq=0) == tq.TQ_OK
+    assert _encode(_codec(), n_tok=0) == tq.TQ_OK
+
+
+def _logits(c, batch=1, n_kv=8, group=4, cap=1024, n_keys=1024, ws=None, ws_ptr=FAKE, q=FAKE, qt=tq.TQ_BF16):
+    if ws is None:
+        ws = tq.logits_workspace(batch, n_kv, group, 128)
+    return tq.lib.tq_logits(ctypes.byref(c), _p(q), qt, batch, n_kv, group, _p(), _p(), cap, n_keys, _p(),
+                            _p(ws_ptr), ws, None)
+
+
+def test_logits_validation():
+    assert _logits(_codec(key=0)) == tq.TQ_EINVAL
+    assert _logits(_codec(), n_keys=2048) == tq.TQ_EINVAL
+    assert _logits(_codec(), group=33) == tq.TQ_EUNSUPPORTED
+    assert _logits(_codec(), ws=16) == tq.TQ_EINVAL
+    assert _logits(_codec(), ws_ptr=FAKE + 64) == tq.TQ_EINVAL
+    assert _logits(_codec(), q=0) == tq.TQ_EINVAL
+    assert _logits(_codec(), qt=9) == tq.TQ_EINVAL
+    assert _logits(_codec(), batch=-1) == tq.TQ_EINVAL
+    assert _logits(_codec(), n_keys=0) == tq.TQ_OK
+    assert tq.logits_workspace(1, 8, 4, 128) == 32 * 2 * 128 * 4
+
+
+def _decode(kc, vc, batch=2, n_kv=2, group=4, cap=256, max_ctx=256, scale=0.1, out_t=tq.TQ_F32, ws=None,
+            ctx=FAKE):
+    if ws is None:
+        ws = tq.decode_attend_workspace(batch, n_kv, group, max_ctx, 128)
+    return tq.lib.tq_decode_attend(ctypes.byref(kc), ctypes.byref(vc), _p(), tq.TQ_BF16, batch, n_kv, group,
+                                   _p(), _p(), _p(), _p(), cap, _p(ctx), max_ctx, scale, _p(), out_t, _p(), ws,
+                                   None)
+
+
+def test_decode_validation():
+    k, v = _codec(), _codec(w=4, key=0, sketch=False)
+    assert _decode(v, v) == tq.TQ_EINVAL                       # key codec expected
+    assert _decode(k, k) == tq.TQ_EINVAL                       # value codec expected
+    assert _decode(k, _codec(d=64, w=4, key=0)) == tq.TQ_EINVAL
+    assert _decode(k, v, out_t=tq.TQ_F16) == tq.TQ_EUNSUPPORTED
+    assert _decode(k, v, max_ctx=512) == tq.TQ_EINVAL
+    assert _decode(k, v, cap=250, max_ctx=200) == tq.TQ_EINVAL
+    assert _decode(k, v, group=33) == tq.TQ_EUNSUPPORTED
+    assert _decode(k, v, scale=float("nan")) == tq.TQ_EINVAL
+    assert _decode(k, v, ws=64) == tq.TQ_EINVAL
+    assert _decode(k, v, ctx=0) == tq.TQ_EINVAL
+    assert _decode(k, v, batch=0) == tq.TQ_OK
+    assert tq.decode_attend_workspace(4, 8, 8, 131072, 128) > 0
+
+
+def test_status_strings():
+    for s in (tq.TQ_OK, tq.TQ_EINVAL, tq.TQ_EUNSUPPORTED, tq.TQ_EHIP):
+        assert tq.lib.tq_status_string(s).decode().startswith("TQ_")
