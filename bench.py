@@ -1,0 +1,333 @@
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+
+Headline workload: the Llama-3.1-8B-shaped decode layer (8 KV heads, 32
+query heads, d = 128, batch 1, context 32768, 4-bit keys = 3 Lloyd-Max bits
++ 1 QJL bit, bf16 inputs with lognormal channel scales). One step encodes
+the whole 32768-token key prefill of the layer into the packed cache and
+then computes every q.k logit of the 32 query heads from the packed codes.
+Inputs are resident in HBM before timing starts; each step uses a different
+one of `--copies` independent input/cache sets (together > 1 GiB) so that
+the 256 MB Infinity Cache cannot hold the working set.
+
+Printed: one JSON line. `value` is q.k logits per second over whole steps
+(encode + query preparation + logit scan). Per-kernel times come from HIP
+events recorded on the launch stream around every call in the timed region;
+`roofline` prices the kernel with the largest share of the step against
+HBM's 8 TB/s with the algorithmic bytes it must move. The extras time the
+fused decode attention on the batched (16 x 8192) and long-context
+(4 x 131072) decode workloads and the full-cache encode of the 22-layer
+TinyLlama-shaped prefill.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X datasheet
+METRIC = "q·k logits/s + encode tokens/s over packed TurboQuant KV; % of HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=16)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of sections: main,dec3,dec5,enc4")
+    return ap.parse_args()
+
+
+class Timer:
+    """Per-call HIP events on the current stream, summed per label."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def run(self, label, fn):
+        t = self.torch
+        s = t.cuda.Event(enable_timing=True)
+        e = t.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((label, s, e))
+
+    def summary(self):
+        out = {}
+        for label, s, e in self.pairs:
+            out.setdefault(label, []).append(s.elapsed_time(e) * 1e-3)
+        return {k: dict(n=len(v), total_s=sum(v), avg_s=sum(v) / len(v)) for k, v in out.items()}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def hbm(bytes_, seconds):
+    return bytes_ / seconds / HBM_PEAK if seconds > 0 else 0.0
+
+
+# ------------------------------------------------------------------ workloads
+
+
+def setup_codecs(torch, tq, syn, w, device):
+    s, S = syn.key_codec_randoms(w.cfg, w.d)
+    kc = tq.Codec.make(w.d, w.key_lm_bits, True, s, S, device=device)
+    vc = None
+    if w.val_bits:
+        vc = tq.Codec.make(w.d, w.val_bits, False, syn.value_codec_randoms(w.cfg, w.d), device=device)
+    return kc, vc, (s, S)
+
+
+def main_decode_layer(args, torch, tq, syn):
+    """Workload 2: encode prefill + logits, rotated over independent copies."""
+    w = syn.WORKLOADS[2]
+    dev = "cuda"
+    kc, _, _ = setup_codecs(torch, tq, syn, w, dev)
+    C = args.copies
+    log(f"[main] generating {C} copies of {w.name}")
+    xs = [syn.keys(w, device=dev, copy=c) for c in range(C)]
+    qs = [syn.queries(w, device=dev, copy=c) for c in range(C)]
+    caches = [tq.alloc_key_cache(w.n_seq, w.n_tok, kc) for _ in range(C)]
+    outs = [torch.empty((w.batch, w.n_q, w.n_tok), dtype=torch.float32, device=dev) for _ in range(C)]
+    ws = torch.empty(tq.logits_workspace(w.batch, w.n_kv, w.group, w.d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(c, timer):
+        codes, scal = caches[c]
+        timer.run("encode", lambda: tq.encode_kv(kc, xs[c], codes, scal))
+        timer.run("logits", lambda: tq.logits(kc, qs[c], codes, scal, n_kv_heads=w.n_kv, group=w.group,
+                                                n_keys=w.n_tok, out=outs[c], workspace=ws))
+
+    warm = Timer(torch)
+    for i in range(args.warmup):
+        step(i % C, warm)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step(i % C, timer)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total = t0.elapsed_time(t1) * 1e-3
+    ks = timer.summary()
+    n_vec = w.n_vec
+    rec = kc.record_bytes + 4
+    bytes_encode = n_vec * (w.d * 2 + rec)                       # bf16 in, codes + scalars out
+    bytes_logits = n_vec * rec + w.batch * w.n_q * w.n_tok * 4   # codes + scalars in, fp32 logits out
+    logits_per_step = w.batch * w.n_q * w.n_tok
+    kern = {
+        "encode": dict(avg_us=ks["encode"]["avg_s"] * 1e6, bytes_per_launch=bytes_encode,
+                       unit="key vectors", units_per_launch=n_vec,
+                       tokens_per_s=n_vec / ks["encode"]["avg_s"],
+                       hbm_frac=hbm(bytes_encode, ks["encode"]["avg_s"])),
+        "logits": dict(avg_us=ks["logits"]["avg_s"] * 1e6, bytes_per_launch=bytes_logits,
+                       unit="keys (x32 query heads)", units_per_launch=n_vec,
+                       logits_per_s=logits_per_step / ks["logits"]["avg_s"],
+                       hbm_frac=hbm(bytes_logits, ks["logits"]["avg_s"])),
+    }
+    return dict(w=w, total_s=total, wall_s=wall, steps=args.steps, kernels=kern,
+                value=logits_per_step * args.steps / total, unit="logits/s",
+                encode_tokens_per_s=n_vec * args.steps / total)
+
+
+def decode_workload(torch, tq, syn, cfg, copies, steps):
+    """Fused decode attention over a prefilled coded cache (workloads 3 and 5)."""
+    w = syn.WORKLOADS[cfg]
+    dev = "cuda"
+    kc, vc, _ = setup_codecs(torch, tq, syn, w, dev)
+    log(f"[dec{cfg}] encoding {copies} cache copies of {w.name}")
+    caches = []
+    for c in range(copies):
+        kcodes, kscal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+        vcodes, vscal = tq.alloc_value_cache(w.n_seq, w.n_tok, vc)
+        x = syn.keys(w, device=dev, copy=c)
+        tq.encode_kv(kc, x, kcodes, kscal)
+        del x
+        x = syn.values(w, device=dev, copy=c)
+        tq.encode_kv(vc, x, vcodes, vscal)
+        del x
+        caches.append((kcodes, kscal, vcodes, vscal))
+    qs = [syn.queries(w, device=dev, copy=c) for c in range(copies)]
+    ctx = torch.full((w.batch,), w.n_tok, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.decode_attend_workspace(w.batch, w.n_kv, w.group, w.n_tok, w.d), dtype=torch.uint8,
+                     device=dev)
+    outs = [torch.empty((w.batch, w.n_q, w.d), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    def step(c, timer):
+        kcodes, kscal, vcodes, vscal = caches[c]
+        timer.run("decode", lambda: tq.decode_attend(kc, vc, qs[c], kcodes, kscal, vcodes, vscal, ctx,
+                                                     n_kv_heads=w.n_kv, group=w.group, max_ctx=w.n_tok,
+                                                     out=outs[c], workspace=ws, out_dtype=torch.bfloat16))
+
+    warm = Timer(torch)
+    for i in range(3):
+        step(i % copies, warm)
+    timer = Timer(torch)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i % copies, timer)
+    torch.cuda.synchronize()
+    avg = timer.summary()["decode"]["avg_s"]
+    th = w.n_seq * w.n_tok
+    bytes_ = th * (kc.record_bytes + 4 + vc.lm_bits * w.d // 8 + 2) + w.batch * w.n_q * w.d * 4
+    return dict(workload=w.name, avg_us=avg * 1e6, bytes_per_launch=bytes_, unit="token-heads",
+                units_per_launch=th, attended_logits_per_s=w.batch * w.n_q * w.n_tok / avg,
+                hbm_frac=hbm(bytes_, avg), copies=copies)
+
+
+def encode_full_cache(torch, tq, syn, steps):
+    """Workload 4: encode every K and V vector of the 22-layer prefill."""
+    w = syn.WORKLOADS[4]
+    dev = "cuda"
+    kc, vc, _ = setup_codecs(torch, tq, syn, w, dev)
+    log(f"[enc4] generating inputs for {w.name} ({w.n_vec * 2} vectors)")
+    xk = syn.keys(w, device=dev)
+    xv = syn.values(w, device=dev)
+    kcodes, kscal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+    vcodes, vscal = tq.alloc_value_cache(w.n_seq, w.n_tok, vc)
+    torch.cuda.synchronize()
+
+    def step(timer):
+        timer.run("enc_k", lambda: tq.encode_kv(kc, xk, kcodes, kscal))
+        timer.run("enc_v", lambda: tq.encode_kv(vc, xv, vcodes, vscal))
+
+    step(Timer(torch))
+    timer = Timer(torch)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    s = timer.summary()
+    tk, tv = s["enc_k"]["avg_s"], s["enc_v"]["avg_s"]
+    bk = w.n_vec * (w.d * 2 + kc.record_bytes + 4)
+    bv = w.n_vec * (w.d * 2 + vc.lm_bits * w.d // 8 + 2)
+    out = dict(workload=w.name, keys_avg_us=tk * 1e6, values_avg_us=tv * 1e6,
+               tokens_per_s=(2 * w.n_vec) / (tk + tv), bytes_per_pass=bk + bv,
+               hbm_frac=hbm(bk + bv, tk + tv), keys_hbm_frac=hbm(bk, tk), values_hbm_frac=hbm(bv, tv))
+    del xk, xv
+    return out
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+
+def cpu_baseline(w, syn, torch):
+    """The oracle (numpy fp64) on the host cores, on a bounded sample of the
+    headline step: the prefill of 2 KV heads encoded, then the logits of
+    their query heads; scaled to the step's mix (encode of all keys + all
+    logits)."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    s, S = syn.key_codec_randoms(w.cfg, w.d)
+    c, t = O.make_codebook(w.d, w.key_lm_bits)
+    kv_heads = w.n_kv                          # all KV heads: the whole step, no extrapolation
+    import dataclasses
+    ws = dataclasses.replace(w, n_kv=kv_heads, batch=1)
+    x = syn.keys(ws).double().numpy()          # [kv_heads, n_tok, d]
+    q = syn.queries(ws).double().numpy()[0]    # [kv_heads * group, d]
+    n = kv_heads * w.n_tok
+    reps = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        encs = [O.encode(x[h], s.numpy(), c, t, S.numpy()) for h in range(kv_heads)]
+        t1 = time.perf_counter()
+        for h, enc in enumerate(encs):
+            O.key_logits(q[h * w.group:(h + 1) * w.group], s.numpy(), c, S.numpy(), enc["idx"], enc["sigma"],
+                         enc["nhat"], enc["ghat"])
+        t2 = time.perf_counter()
+        reps.append((t1 - t0, t2 - t1))
+    enc_s = sorted(r[0] for r in reps)[1]
+    lg_s = sorted(r[1] for r in reps)[1]
+    # whole step: encode all n_vec keys, compute all n_q * n_tok logits
+    step_s = enc_s * (w.n_vec / n) + lg_s * (w.batch * w.n_q * w.n_tok) / (kv_heads * w.group * w.n_tok)
+    return {"value": w.batch * w.n_q * w.n_tok / step_s, "unit": "logits/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"numpy fp64 oracle, median of 3 runs: encode of the {w.n_tok}-token prefill of "
+                      f"{kv_heads} of the {w.n_kv} KV heads ({n} keys) + all logits of their "
+                      f"{kv_heads * w.group} query heads; scaled linearly to the whole step (encode "
+                      f"{w.n_vec} keys + {w.batch * w.n_q * w.n_tok} logits)",
+            "host_cpus": len(os.sched_getaffinity(0)), "encode_keys_per_s": n / enc_s,
+            "logits_per_s": kv_heads * w.group * w.n_tok / lg_s}
+
+
+# ------------------------------------------------------------------ main
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the codec path has no "
+                                   "multi-GPU component (shard batch x KV heads across GPUs instead)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import kv_cache_vector_rht_amd as tq
+    import synthetic as syn
+    tq.load()
+    torch.cuda.set_device(0)
+    only = set(filter(None, args.only.split(",")))
+
+    res = main_decode_layer(args, torch, tq, syn)
+    w = res["w"]
+    kern = res["kernels"]
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    kd = kern[dom]
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kd["bytes_per_launch"] / (kd["avg_us"] * 1e-6) / 1e9,
+            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": kd["hbm_frac"], "traffic": None,
+            "bytes_per_unit": kd["bytes_per_launch"] / kd["units_per_launch"],
+            "units_per_launch": kd["units_per_launch"]}
+    extras = {}
+    if not args.no_extras:
+        if not only or "dec3" in only:
+            extras["decode_attend_batched"] = decode_workload(torch, tq, syn, 3, copies=9, steps=20)
+        torch.cuda.empty_cache()
+        if not only or "dec5" in only:
+            extras["decode_attend_long_context"] = decode_workload(torch, tq, syn, 5, copies=2, steps=10)
+        torch.cuda.empty_cache()
+        if not only or "enc4" in only:
+            extras["encode_full_cache"] = encode_full_cache(torch, tq, syn, steps=2)
+        torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[cpu] timing the oracle on a sample")
+        cpu = cpu_baseline(w, syn, torch)
+    line = {
+        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res["total_s"] / res["steps"] * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped decode layer: encode 32768-token key prefill + all q.k "
+                               "logits", "kv_heads": w.n_kv, "q_heads": w.n_q, "head_dim": w.d, "batch": w.batch,
+                   "context": w.n_tok, "key_bits": w.key_bits, "input_dtype": "bf16",
+                   "copies_rotated": args.copies},
+        "encode_tokens_per_s": res["encode_tokens_per_s"],
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kern, "extras": extras,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
