@@ -11,6 +11,7 @@
 
 #include "../../include/tq.h"
 #include "tq_kernels.h"
+#include "tq_mfma.h"
 
 namespace tq {
 bool lloyd_max_positive_half(int d, int bits, std::vector<double> &c);
@@ -64,8 +65,8 @@ tq_status check_codec(const tq_codec *c, int need_key, const char *name) {
   return TQ_OK;
 }
 
-// Decode split size: a multiple of the 32-token value block, small enough
-// that the grid fills the chip and the block's LDS stays under 64 KiB.
+// Decode split size: a multiple of 64 tokens, small enough that the grid
+// fills the chip and the block's LDS stays under 64 KiB.
 int choose_split(int32_t batch, int32_t n_kv, int32_t group, int64_t max_ctx, int d) {
   int split = 512;
   while (split > 64) {
@@ -73,8 +74,13 @@ int choose_split(int32_t batch, int32_t n_kv, int32_t group, int64_t max_ctx, in
     if (static_cast<int64_t>(batch) * n_kv * n_splits >= 1024) break;
     split /= 2;
   }
-  while (split > 32 && tq::decode_split_smem(d, group, split) > 65536) split /= 2;
+  while (split > 64 && tq::decode_split_smem(d, group, split) > 65536) split /= 2;
   return split;
+}
+
+// Workspace bytes of the prepared queries (sized for the widest key codec).
+size_t qprep_bytes(int32_t batch, int32_t n_kv, int32_t group, int d) {
+  return align_up(static_cast<size_t>(batch) * n_kv * tq::qprep_group_bytes(d, 4, group));
 }
 
 }  // namespace
@@ -170,7 +176,7 @@ tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_
 
 size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d) {
   if (batch < 0 || n_kv_heads < 0 || group < 0 || d <= 0) return 0;
-  return align_up(static_cast<size_t>(batch) * n_kv_heads * group * 2 * d * sizeof(float));
+  return qprep_bytes(batch, n_kv_heads, group, d);
 }
 
 tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
@@ -191,12 +197,32 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
   if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 4)
     return fail(TQ_EINVAL, "%s: kcodes must be 16-byte and kscalars 4-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float *qprep = static_cast<float *>(workspace);
-  tq::QueryPrepParams qp{q, static_cast<int>(qt), static_cast<int64_t>(batch) * n_kv_heads * group, kc->signs,
-                         kc->sketch, qprep};
+  tq::QueryPrepParams qp{};
+  qp.q = q;
+  qp.xt = static_cast<int>(qt);
+  qp.batch = batch;
+  qp.n_kv = n_kv_heads;
+  qp.group = group;
+  qp.kw = kc->lm_bits;
+  qp.signs = kc->signs;
+  qp.centroids = kc->centroids;
+  qp.sketch = kc->sketch;
+  qp.out = static_cast<uint8_t *>(workspace);
+  qp.group_bytes = tq::qprep_group_bytes(kc->d, kc->lm_bits, group);
   hipError_t e = kc->d == 64 ? tq::launch_query_prep_d<64>(qp, st) : tq::launch_query_prep_d<128>(qp, st);
   if (e != hipSuccess) return hip_status(e, fn);
-  tq::LogitsParams lp{qprep, kcodes, kscalars, kc->centroids, cap, n_keys, batch, n_kv_heads, group, logits};
+  tq::LogitsParams lp{};
+  lp.qprep = qp.out;
+  lp.group_bytes = qp.group_bytes;
+  lp.frag_bytes = tq::qprep_frag_bytes(kc->d, kc->lm_bits, group);
+  lp.kcodes = kcodes;
+  lp.kscalars = kscalars;
+  lp.cap = cap;
+  lp.n_keys = n_keys;
+  lp.batch = batch;
+  lp.n_kv = n_kv_heads;
+  lp.group = group;
+  lp.logits = logits;
   e = kc->d == 64 ? tq::launch_logits_d<64>(lp, kc->lm_bits, st) : tq::launch_logits_d<128>(lp, kc->lm_bits, st);
   return hip_status(e, fn);
 }
@@ -205,10 +231,9 @@ size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t gro
   if (batch < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
   const int split = choose_split(batch, n_kv_heads, group, max_ctx, d);
   const int64_t n_splits = (max_ctx + split - 1) / split;
-  const size_t qbytes = align_up(static_cast<size_t>(batch) * n_kv_heads * group * 2 * d * sizeof(float));
   const size_t pbytes =
       align_up(static_cast<size_t>(batch) * n_kv_heads * (n_splits > 0 ? n_splits : 1) * group * (d + 2) * sizeof(float));
-  return qbytes + pbytes;
+  return qprep_bytes(batch, n_kv_heads, group, d) + pbytes;
 }
 
 tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
@@ -242,20 +267,29 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   const int d = kc->d;
   const int split = choose_split(batch, n_kv_heads, group, max_ctx, d);
   const int64_t n_splits64 = max_ctx > 0 ? (max_ctx + split - 1) / split : 1;
-  float *qprep = static_cast<float *>(workspace);
-  float *partials = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                              align_up(static_cast<size_t>(batch) * n_kv_heads * group * 2 * d * sizeof(float)));
-  tq::QueryPrepParams qp{q, static_cast<int>(qt), static_cast<int64_t>(batch) * n_kv_heads * group, kc->signs,
-                         kc->sketch, qprep};
+  tq::QueryPrepParams qp{};
+  qp.q = q;
+  qp.xt = static_cast<int>(qt);
+  qp.batch = batch;
+  qp.n_kv = n_kv_heads;
+  qp.group = group;
+  qp.kw = kc->lm_bits;
+  qp.signs = kc->signs;
+  qp.centroids = kc->centroids;
+  qp.sketch = kc->sketch;
+  qp.out = static_cast<uint8_t *>(workspace);
+  qp.group_bytes = tq::qprep_group_bytes(d, kc->lm_bits, group);
+  float *partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + qprep_bytes(batch, n_kv_heads, group, d));
   hipError_t e = d == 64 ? tq::launch_query_prep_d<64>(qp, st) : tq::launch_query_prep_d<128>(qp, st);
   if (e != hipSuccess) return hip_status(e, fn);
   tq::DecodeParams dp{};
-  dp.qprep = qprep;
+  dp.qprep = qp.out;
+  dp.group_bytes = qp.group_bytes;
+  dp.frag_bytes = tq::qprep_frag_bytes(d, kc->lm_bits, group);
   dp.kcodes = kcodes;
   dp.kscalars = kscalars;
   dp.vcodes = vcodes;
   dp.vscalars = vscalars;
-  dp.kcent = kc->centroids;
   dp.vcent = vc->centroids;
   dp.vsigns = vc->signs;
   dp.cap = cap;

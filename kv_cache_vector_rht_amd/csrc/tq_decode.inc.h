@@ -1,17 +1,19 @@
-#pragma once
 // Query preparation, logit scan over packed keys, and split-context fused
-// decode attention over packed keys and values.
+// decode attention over packed keys and values, on the matrix cores.
 //
 // Estimator (pages: "TurboQuantとは？仕組み・実測精度・2026年7月時点の実装状況",
-// 第2段, the QJL residual bit makes the inner-product estimate unbiased; the
-// logit computation is the operation behind the 8x figure in its まとめ):
+// 第2段: the QJL residual bit makes the inner-product estimate unbiased; its
+// まとめ names the attention-logit computation as the accelerated operation):
 //   logit(q, k) = n ( sum_i q'_i c[idx_i]
-//                     + sqrt(pi/2)/D * gamma * sum_j p_j (2 sigma_j - 1) )
-// with q' = R q and p = S q'. The rotated query and its projection are
-// computed once per query head; the scan then reads each key record once for
-// all heads of its group.
+//                     + sqrt(pi/2)/D * gamma * sum_j p_j (2 sigma_j - 1) ),
+// q' = R q, p = S q'. Both sums are bit-plane contractions (tq_mfma.h); the
+// query side is prepared once per (batch, kv-head) group, then every key
+// record is read once for all heads of its group.
+#pragma once
+
 #include "tq_device.h"
 #include "tq_kernels.h"
+#include "tq_mfma.h"
 
 namespace tq {
 
@@ -19,273 +21,506 @@ constexpr float kSqrtHalfPi = 1.2533141373155002f;   // sqrt(pi / 2)
 
 // ------------------------------------------------------------------ query prep
 
+// One block (256 threads) per (batch, kv-head) group.
 template <int D>
-__global__ __launch_bounds__(D) void query_prep_kernel(QueryPrepParams p) {
-  __shared__ float s[D];
-  const int64_t h = blockIdx.x;
-  const int i = threadIdx.x;
-  float v;
-  if (p.xt == 0) v = static_cast<const float *>(p.q)[h * D + i];
-  else if (p.xt == 1) v = bf16_bits_to_float(static_cast<const uint16_t *>(p.q)[h * D + i]);
-  else v = f16_bits_to_float(static_cast<const uint16_t *>(p.q)[h * D + i]);
-  s[i] = v * p.signs[i];
+__global__ __launch_bounds__(256) void query_prep_kernel(QueryPrepParams p) {
+  extern __shared__ float qs[];              // [G][D] q', then [G][D] p, then stats
+  const int G = p.group;
+  const int n_q = p.n_kv * G;
+  const int64_t grp = blockIdx.x;            // b * n_kv + kvh
+  const int64_t b = grp / p.n_kv;
+  const int64_t kvh = grp % p.n_kv;
+  float *sq = qs;
+  float *sp = qs + G * D;
+  float *st = sp + G * D;                    // [G][4]: max|q'|, sum q', max|p|, sum p
+  float *sb = st + 4 * G;                    // [8] beta, [1] max |beta|
+  const int tid = threadIdx.x;
+  const int64_t q0 = (b * n_q + kvh * G) * D;
+
+  for (int e = tid; e < G * D; e += blockDim.x) {
+    const int i = e % D;
+    float v;
+    if (p.xt == 0) v = static_cast<const float *>(p.q)[q0 + e];
+    else if (p.xt == 1) v = bf16_bits_to_float(static_cast<const uint16_t *>(p.q)[q0 + e]);
+    else v = f16_bits_to_float(static_cast<const uint16_t *>(p.q)[q0 + e]);
+    sq[e] = v * p.signs[i];
+  }
+  const int NB = basis_size(p.kw);
+  if (tid < NB) sb[tid] = basis_coeff(p.centroids, p.kw, basis_mask(p.kw, tid));
   __syncthreads();
-#pragma unroll
+  // Walsh-Hadamard butterflies on every head, then 1/sqrt(D)
   for (int hs = 1; hs < D; hs <<= 1) {
-    const float a = s[i];
-    const float b = s[i ^ hs];
-    __syncthreads();
-    s[i] = (i & hs) ? (b - a) : (a + b);
+    for (int e = tid; e < G * D / 2; e += blockDim.x) {
+      const int h = e / (D / 2);
+      const int r = e % (D / 2);
+      const int i = (r / hs) * 2 * hs + (r % hs);
+      const float a = sq[h * D + i];
+      const float c = sq[h * D + i + hs];
+      sq[h * D + i] = a + c;
+      sq[h * D + i + hs] = a - c;
+    }
     __syncthreads();
   }
-  const float qr = s[i] * (1.0f / sqrtf(static_cast<float>(D)));
+  for (int e = tid; e < G * D; e += blockDim.x) sq[e] *= (1.0f / sqrtf(static_cast<float>(D)));
   __syncthreads();
-  s[i] = qr;
-  p.out[(h * 2 + 0) * D + i] = qr;
-  __syncthreads();
-  const uint32_t *row = reinterpret_cast<const uint32_t *>(p.sketch + static_cast<int64_t>(i) * D);
-  float acc = 0.f;
+  // p = S q'
+  for (int e = tid; e < G * D; e += blockDim.x) {
+    const int h = e / D, j = e % D;
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(p.sketch + static_cast<int64_t>(j) * D);
+    const float *qh = sq + h * D;
+    float acc = 0.f;
 #pragma unroll 8
-  for (int k = 0; k < D; k += 2) {
-    const uint32_t two = row[k / 2];
-    acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two & 0xffffu)), s[k], acc);
-    acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two >> 16)), s[k + 1], acc);
+    for (int k = 0; k < D; k += 2) {
+      const uint32_t two = row[k / 2];
+      acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two & 0xffffu)), qh[k], acc);
+      acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two >> 16)), qh[k + 1], acc);
+    }
+    sp[e] = acc;
   }
-  p.out[(h * 2 + 1) * D + i] = acc;
+  __syncthreads();
+  // per-head statistics, one wave per head
+  const int wave = tid / kWave, lane = lane_id(), n_waves = blockDim.x / kWave;
+  for (int h = wave; h < G; h += n_waves) {
+    float mq = 0.f, sqs = 0.f, mp = 0.f, sps = 0.f;
+    for (int i = lane; i < D; i += kWave) {
+      mq = fmaxf(mq, fabsf(sq[h * D + i]));
+      sqs += sq[h * D + i];
+      mp = fmaxf(mp, fabsf(sp[h * D + i]));
+      sps += sp[h * D + i];
+    }
+    mq = wave_max(mq); sqs = wave_sum(sqs); mp = wave_max(mp); sps = wave_sum(sps);
+    if (lane == 0) { st[4 * h] = mq; st[4 * h + 1] = sqs; st[4 * h + 2] = mp; st[4 * h + 3] = sps; }
+  }
+  if (tid == 0) {
+    float mb = 0.f;
+    for (int s = 0; s < NB; ++s) mb = fmaxf(mb, fabsf(sb[s]));
+    sb[8] = mb;
+  }
+  __syncthreads();
+
+  // A operands: rows = 4 local heads x 4 digits, one 16-byte vector per lane
+  const int RG = (G + 3) / 4;
+  const int NH = D / 64;
+  const int NMF = (NB + 1) * NH;
+  uint8_t *dst = p.out + grp * p.group_bytes;
+  const float cmax = p.centroids[(1 << p.kw) - 1];
+  for (int row = tid; row < RG * NMF * kWave; row += blockDim.x) {
+    const int l = row % kWave;
+    const int mf = (row / kWave) % NMF;
+    const int rg = row / (kWave * NMF);
+    const int m = l % 16, kg = l / 16;
+    const int h = 4 * rg + m / 4, s = m % 4;
+    const bool qjl = mf >= NB * NH;
+    const int plane = qjl ? 0 : mf / NH;
+    const int half = mf % NH;
+    uint32_t dw[4] = {0u, 0u, 0u, 0u};
+    if (h < G) {
+      const float coef = qjl ? 2.0f : 2.0f * sb[plane];
+      const float mx = qjl ? 2.0f * st[4 * h + 2] : 2.0f * sb[8] * st[4 * h];
+      const int e = fixed_exponent(mx);
+      const float *src = (qjl ? sp : sq) + h * D;
+      for (int j = 0; j < 16; ++j) {
+        const int coord = slot_coord(D, kg, j, half);
+        const int k = 4 * (kg & 1) + (j >> 2);
+        float v = ldexpf(coef * src[coord], 7 - k + e);
+        if (k == 7) v = -v;
+        const uint32_t dig = signed_digits(__float2int_rn(v));
+        dw[j >> 2] |= ((dig >> (8 * s)) & 0xffu) << (8 * (j & 3));
+      }
+    }
+    *reinterpret_cast<uint4 *>(dst + static_cast<size_t>(row) * 16) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  }
+  float *fl = reinterpret_cast<float *>(dst + qprep_frag_bytes(D, p.kw, G));
+  for (int h = tid; h < G; h += blockDim.x) {
+    const int el = fixed_exponent(2.0f * sb[8] * st[4 * h]);
+    const int eq = fixed_exponent(2.0f * st[4 * h + 2]);
+    fl[4 * h + 0] = ldexpf(1.0f, -7 - el);
+    fl[4 * h + 1] = cmax * st[4 * h + 1];
+    fl[4 * h + 2] = ldexpf(1.0f, -7 - eq);
+    fl[4 * h + 3] = st[4 * h + 3];
+  }
 }
 
 template <int D>
 hipError_t launch_query_prep_d(const QueryPrepParams &p, hipStream_t st) {
-  if (p.n_heads == 0) return hipSuccess;
-  hipLaunchKernelGGL((query_prep_kernel<D>), dim3(static_cast<uint32_t>(p.n_heads)), dim3(D), 0, st, p);
+  const uint32_t groups = static_cast<uint32_t>(p.batch) * p.n_kv;
+  if (groups == 0 || p.group == 0) return hipSuccess;
+  const size_t shm = (static_cast<size_t>(2) * p.group * D + 4 * p.group + 16) * sizeof(float);
+  hipLaunchKernelGGL((query_prep_kernel<D>), dim3(groups), dim3(256), shm, st, p);
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------ per-key logits
+// ------------------------------------------------------------ key tiles
 
-// Logits of one key against heads [h0, h0 + nh) (nh <= 4) of the group whose
-// prepared queries sit in LDS as sq[g][0][D] = q', sq[g][1][D] = p.
-template <int D, int W>
-__device__ __forceinline__ void key_logits4(const uint32_t (&rec)[(W + 1) * D / 32], float n, float gamma,
-                                            const float *sq, const float *cent, int h0, int nh,
-                                            float (&out)[4]) {
-  constexpr int NW = D / 32;
-  float lm[4] = {0.f, 0.f, 0.f, 0.f};
-  float qj[4] = {0.f, 0.f, 0.f, 0.f};
+// One 16-key tile of a wave: lane (kg = l/16, n = l%16) holds the plane words
+// of key n that its K slots need, and the key's fp16 scalars.
+template <int D, int KW>
+struct KeyTile {
+  static constexpr int NH = D / 64;
+  uint32_t w[KW + 1][NH];
+  float n, g;
+};
+
+template <int D, int KW>
+__device__ __forceinline__ void load_key_tile(const uint8_t *kcodes, const uint16_t *kscalars, int64_t slot0,
+                                              int64_t t, int64_t n_keys, KeyTile<D, KW> &kt) {
+  constexpr int REC = (KW + 1) * D / 8;
+  const int lane = lane_id();
+  const int wh = (lane / 16) >> 1;
+  if (t < n_keys) {
+    const uint8_t *rec = kcodes + (slot0 + t) * REC;
 #pragma unroll
-  for (int jw = 0; jw < NW; ++jw) {
-    const uint32_t sw = rec[W * NW + jw];
-#pragma unroll
-    for (int jb = 0; jb < 32; ++jb) {
-      const int i = jw * 32 + jb;
-      int idx = 0;
-#pragma unroll
-      for (int q = 0; q < W; ++q) idx |= static_cast<int>((rec[q * NW + jw] >> jb) & 1u) << q;
-      const float c = cent[idx];
-      const bool pos = (sw >> jb) & 1u;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g < nh) {
-          const float *qg = sq + (h0 + g) * 2 * D;
-          lm[g] = fmaf(qg[i], c, lm[g]);
-          const float pj = qg[D + i];
-          qj[g] += pos ? pj : -pj;
-        }
+    for (int q = 0; q <= KW; ++q) {
+      if (D == 128) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(rec + q * 16 + wh * 8);
+        kt.w[q][0] = u.x;
+        kt.w[q][D == 128 ? 1 : 0] = u.y;
+      } else {
+        kt.w[q][0] = *reinterpret_cast<const uint32_t *>(rec + q * 8 + wh * 4);
       }
     }
-  }
-  const float kg = kSqrtHalfPi / static_cast<float>(D) * gamma;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) out[g] = n * fmaf(kg, qj[g], lm[g]);
-}
-
-template <int D, int W>
-__device__ __forceinline__ void load_key(const uint8_t *kcodes, const uint16_t *kscalars, int64_t slot,
-                                         uint32_t (&rec)[(W + 1) * D / 32], float &n, float &gamma) {
-  constexpr int REC = (W + 1) * D / 8;
-  const uint8_t *r = kcodes + slot * REC;
-  if (D == 128) {
-#pragma unroll
-    for (int q = 0; q <= W; ++q) {
-      const uint4 u = *reinterpret_cast<const uint4 *>(r + q * 16);
-      rec[q * 4 + 0] = u.x; rec[q * 4 + 1] = u.y; rec[q * 4 + 2] = u.z; rec[q * 4 + 3] = u.w;
-    }
+    const uint32_t sc = reinterpret_cast<const uint32_t *>(kscalars)[slot0 + t];
+    kt.n = f16_bits_to_float(static_cast<uint16_t>(sc & 0xffffu));
+    kt.g = f16_bits_to_float(static_cast<uint16_t>(sc >> 16));
   } else {
 #pragma unroll
-    for (int q = 0; q <= W; ++q) {
-      const uint2 u = *reinterpret_cast<const uint2 *>(r + q * 8);
-      rec[q * 2 + 0] = u.x; rec[q * 2 + 1] = u.y;
+    for (int q = 0; q <= KW; ++q)
+#pragma unroll
+      for (int hf = 0; hf < KeyTile<D, KW>::NH; ++hf) kt.w[q][hf] = 0u;
+    kt.n = 0.f;
+    kt.g = 0.f;
+  }
+}
+
+// Accumulate the key planes and the sign plane of one tile for NRG row groups.
+template <int D, int KW, int NRG>
+__device__ __forceinline__ void key_tile_mfma(const KeyTile<D, KW> &kt, const v4i (&a)[NRG][(Basis<KW>::N + 1) * (D / 64)],
+                                              const uint32_t (&mask)[4], int nrg, v4i (&clm)[NRG], v4i (&cqj)[NRG]) {
+  constexpr int NB = Basis<KW>::N;
+  constexpr int NH = D / 64;
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) { clm[rg] = v4i{0, 0, 0, 0}; cqj[rg] = v4i{0, 0, 0, 0}; }
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      uint32_t w = 0u;
+#pragma unroll
+      for (int q = 0; q < KW; ++q)
+        if ((Basis<KW>::M[s] >> q) & 1) w ^= kt.w[q][hf];
+      const v4i bv = expand_bits(w, mask);
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg)
+        if (rg < nrg) clm[rg] = mfma_i8(a[rg][s * NH + hf], bv, clm[rg]);
     }
   }
-  const uint32_t sc = reinterpret_cast<const uint32_t *>(kscalars)[slot];
-  n = f16_bits_to_float(static_cast<uint16_t>(sc & 0xffffu));
-  gamma = f16_bits_to_float(static_cast<uint16_t>(sc >> 16));
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf) {
+    const v4i bv = expand_bits(kt.w[KW][hf], mask);
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+      if (rg < nrg) cqj[rg] = mfma_i8(a[rg][NB * NH + hf], bv, cqj[rg]);
+  }
+}
+
+__device__ __forceinline__ float tile_logit(const v4i &clm, const v4i &cqj, const float *fl, float n, float g,
+                                            float kappa) {
+  const float lm = fmaf(combine_digits(clm), fl[0], -fl[1]);
+  const float qj = fmaf(combine_digits(cqj), fl[2], -fl[3]);
+  return n * fmaf(kappa * g, qj, lm);
+}
+
+template <int D, int KW, int NRG>
+__device__ __forceinline__ void load_afrags(const uint8_t *frag, int rg0, int nrg, v4i (&a)[NRG][(Basis<KW>::N + 1) * (D / 64)]) {
+  constexpr int NMF = (Basis<KW>::N + 1) * (D / 64);
+  const int lane = lane_id();
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf) {
+      if (rg < nrg) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(frag + ((static_cast<size_t>(rg0 + rg) * NMF + mf) * kWave + lane) * 16);
+        a[rg][mf] = v4i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z), static_cast<int>(u.w)};
+      } else {
+        a[rg][mf] = v4i{0, 0, 0, 0};
+      }
+    }
+}
+
+__device__ __forceinline__ void lane_masks(uint32_t (&mask)[4]) {
+  const int kk = 4 * ((lane_id() / 16) & 1);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) mask[r] = 0x01010101u << (kk + r);
 }
 
 // ------------------------------------------------------------------ logits
 
-template <int D, int W>
+constexpr int kLogitTilesPerWave = 4;
+
+template <int D, int KW, int NRG>
 __global__ __launch_bounds__(256) void logits_kernel(LogitsParams p) {
-  extern __shared__ float smem[];
+  constexpr int NMF = (Basis<KW>::N + 1) * (D / 64);
   const int G = p.group;
   const int n_q = p.n_kv * G;
-  float *sq = smem;                          // [G][2][D]
-  float *cent = smem + G * 2 * D;            // [2^W]
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.n_kv;
   const int64_t kvh = bh % p.n_kv;
-  const float *qsrc = p.qprep + (b * n_q + kvh * G) * 2 * D;
-  for (int i = threadIdx.x; i < G * 2 * D; i += blockDim.x) sq[i] = qsrc[i];
-  if (threadIdx.x < (1 << W)) cent[threadIdx.x] = p.centroids[threadIdx.x];
-  __syncthreads();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (t >= p.n_keys) return;
-  uint32_t rec[(W + 1) * D / 32];
-  float n, gamma;
-  load_key<D, W>(p.kcodes, p.kscalars, bh * p.cap + t, rec, n, gamma);
-  float *dst = p.logits + (b * n_q + kvh * G) * p.n_keys + t;
-  for (int h0 = 0; h0 < G; h0 += 4) {
-    const int nh = min(4, G - h0);
-    float out[4];
-    key_logits4<D, W>(rec, n, gamma, sq, cent, h0, nh, out);
+  const uint8_t *prep = p.qprep + bh * p.group_bytes;
+  const float *fl = reinterpret_cast<const float *>(prep + p.frag_bytes);
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int kg = lane / 16;
+  uint32_t mask[4];
+  lane_masks(mask);
+  const int64_t slot0 = bh * p.cap;
+  const float kappa = kSqrtHalfPi / static_cast<float>(D);
+  const int64_t tile0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * kLogitTilesPerWave;
+  const int RG = (G + 3) / 4;
+  for (int rg0 = 0; rg0 < RG; rg0 += NRG) {
+    const int nrg = min(NRG, RG - rg0);
+    v4i a[NRG][NMF];
+    load_afrags<D, KW, NRG>(prep, rg0, nrg, a);
+    KeyTile<D, KW> kt;
+    load_key_tile<D, KW>(p.kcodes, p.kscalars, slot0, tile0 * 16 + (lane % 16), p.n_keys, kt);
+    for (int it = 0; it < kLogitTilesPerWave; ++it) {
+      const int64_t t = (tile0 + it) * 16 + (lane % 16);
+      if ((tile0 + it) * 16 >= p.n_keys) break;
+      KeyTile<D, KW> nx;
+      if (it + 1 < kLogitTilesPerWave) load_key_tile<D, KW>(p.kcodes, p.kscalars, slot0, t + 16, p.n_keys, nx);
+      v4i clm[NRG], cqj[NRG];
+      key_tile_mfma<D, KW, NRG>(kt, a, mask, nrg, clm, cqj);
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      if (g < nh) dst[(h0 + g) * p.n_keys] = out[g];
+      for (int rg = 0; rg < NRG; ++rg) {
+        const int h = 4 * (rg0 + rg) + kg;
+        if (rg < nrg && h < G && t < p.n_keys)
+          p.logits[(b * n_q + kvh * G + h) * p.n_keys + t] = tile_logit(clm[rg], cqj[rg], fl + 4 * h, kt.n, kt.g, kappa);
+      }
+      kt = nx;
+    }
   }
 }
 
 template <int D>
 hipError_t launch_logits_d(const LogitsParams &p, int w, hipStream_t st) {
   if (p.n_keys == 0 || p.batch == 0 || p.n_kv == 0) return hipSuccess;
-  dim3 grid(static_cast<uint32_t>((p.n_keys + 255) / 256), static_cast<uint32_t>(p.batch) * p.n_kv);
-  const size_t shm = (static_cast<size_t>(p.group) * 2 * D + 16) * sizeof(float);
+  const int64_t keys_per_block = 4 * kLogitTilesPerWave * 16;
+  dim3 grid(static_cast<uint32_t>((p.n_keys + keys_per_block - 1) / keys_per_block),
+            static_cast<uint32_t>(p.batch) * p.n_kv);
+  const bool two = p.group > 4 && w <= 3;
+#define TQ_LG(WW)                                                                          \
+  if (two) hipLaunchKernelGGL((logits_kernel<D, WW, 2>), grid, dim3(256), 0, st, p);      \
+  else hipLaunchKernelGGL((logits_kernel<D, WW, 1>), grid, dim3(256), 0, st, p);
   switch (w) {
-    case 1: hipLaunchKernelGGL((logits_kernel<D, 1>), grid, dim3(256), shm, st, p); break;
-    case 2: hipLaunchKernelGGL((logits_kernel<D, 2>), grid, dim3(256), shm, st, p); break;
-    case 3: hipLaunchKernelGGL((logits_kernel<D, 3>), grid, dim3(256), shm, st, p); break;
-    default: hipLaunchKernelGGL((logits_kernel<D, 4>), grid, dim3(256), shm, st, p);
+    case 1: TQ_LG(1); break;
+    case 2: TQ_LG(2); break;
+    case 3: TQ_LG(3); break;
+    default: TQ_LG(4);
   }
+#undef TQ_LG
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ decode attend
 
-// One block per (batch*kv-head, context split): logits for the split's tokens,
-// per-head softmax statistics (max m, sum l of exp(scaled logit - m)), and the
-// weighted sum of decoded values in the rotated domain. Partials are written
-// as [G][D+2] = {m, l, acc[D]}.
-template <int D, int KW, int VW>
+// One block (4 waves) per (batch*kv-head, context split of SPLIT tokens):
+//  1. scaled logits of the split's tokens for all G heads (key MFMA) -> LDS
+//  2. per head: m = max, l = sum exp(logit - m); weights exp(logit - m) * n_v
+//  3. weights -> fixed-point int8 digit operands in LDS (one shared
+//     exponent per block, from the largest value norm)
+//  4. value planes x weights on the matrix cores, int32 over the split
+//  5. partials {m, l, acc[D]} per head, acc in the rotated domain
+template <int D, int KW, int VW, int NRG>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
+  constexpr int NMF = (Basis<KW>::N + 1) * (D / 64);
+  constexpr int NBV = Basis<VW>::N;
+  constexpr int NT = D / 64;                 // value N-tiles (16 coords) per wave
   extern __shared__ float smem[];
   const int G = p.group;
-  const int n_q = p.n_kv * G;
   const int SPLIT = p.split;
-  float *sq = smem;                          // [G][2][D]
-  float *sl = sq + G * 2 * D;                // [G][SPLIT]
-  float *snv = sl + G * SPLIT;               // [SPLIT]
-  float *skc = snv + SPLIT;                  // [16]
-  float *svc = skc + 16;                     // [16]
-  float *sml = svc + 16;                     // [G][2]
+  const int RG = (G + 3) / 4;
+  float *sl = smem;                                        // [G][SPLIT]
+  float *snv = sl + G * SPLIT;                             // [SPLIT]
+  uint8_t *fragv = reinterpret_cast<uint8_t *>(snv + SPLIT);   // [RG][SPLIT/64][64][16]
+  float *sstat = reinterpret_cast<float *>(fragv + static_cast<size_t>(RG) * (SPLIT / 64) * 1024);  // [G][4]
+  double *ssw = reinterpret_cast<double *>(sstat + 4 * G);   // [G]
+  float *sred = reinterpret_cast<float *>(ssw + G);          // [8]
 
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.n_kv;
-  const int64_t kvh = bh % p.n_kv;
   const int split = blockIdx.x;
   int64_t ctx = p.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
   const int64_t t_beg = static_cast<int64_t>(split) * SPLIT;
-  const int64_t t_end = min(t_beg + SPLIT, ctx);
-  const int n_t = static_cast<int>(t_end - t_beg);
+  const int n_t = static_cast<int>(min(static_cast<int64_t>(SPLIT), ctx - t_beg));
   float *part = p.partials + (bh * p.n_splits + split) * G * (D + 2);
-
+  const int tid = threadIdx.x;
   if (n_t <= 0) {
-    for (int i = threadIdx.x; i < G * (D + 2); i += blockDim.x) {
-      const int c = i % (D + 2);
-      part[i] = (c == 0) ? -INFINITY : 0.f;
-    }
+    for (int i = tid; i < G * (D + 2); i += blockDim.x) part[i] = ((i % (D + 2)) == 0) ? -INFINITY : 0.f;
     return;
   }
-
-  const float *qsrc = p.qprep + (b * n_q + kvh * G) * 2 * D;
-  for (int i = threadIdx.x; i < G * 2 * D; i += blockDim.x) sq[i] = qsrc[i];
-  if (threadIdx.x < (1 << KW)) skc[threadIdx.x] = p.kcent[threadIdx.x];
-  if (threadIdx.x < (1 << VW)) svc[threadIdx.x] = p.vcent[threadIdx.x];
-  __syncthreads();
-
-  // phase 1: scaled logits and value norms
-  for (int tt = threadIdx.x; tt < n_t; tt += blockDim.x) {
-    const int64_t slot = bh * p.cap + t_beg + tt;
-    uint32_t rec[(KW + 1) * D / 32];
-    float n, gamma;
-    load_key<D, KW>(p.kcodes, p.kscalars, slot, rec, n, gamma);
-    for (int h0 = 0; h0 < G; h0 += 4) {
-      const int nh = min(4, G - h0);
-      float out[4];
-      key_logits4<D, KW>(rec, n, gamma, sq, skc, h0, nh, out);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        if (g < nh) sl[(h0 + g) * SPLIT + tt] = out[g] * p.sm_scale;
-    }
-    snv[tt] = f16_bits_to_float(p.vscalars[slot]);
-  }
-  __syncthreads();
-
-  // phase 2: softmax statistics, one wave per head
-  const int wave = threadIdx.x / kWave;
+  const uint8_t *prep = p.qprep + bh * p.group_bytes;
+  const float *fl = reinterpret_cast<const float *>(prep + p.frag_bytes);
+  const int wave = tid / kWave;
   const int lane = lane_id();
-  const int n_waves = blockDim.x / kWave;
-  for (int g = wave; g < G; g += n_waves) {
-    float m = -INFINITY;
-    for (int tt = lane; tt < n_t; tt += kWave) m = fmaxf(m, sl[g * SPLIT + tt]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int tt = lane; tt < n_t; tt += kWave) {
-      const float e = __expf(sl[g * SPLIT + tt] - m);
-      sl[g * SPLIT + tt] = e;
-      l += e;
-    }
-    l = wave_sum(l);
-    if (lane == 0) { sml[2 * g] = m; sml[2 * g + 1] = l; }
-  }
-  __syncthreads();
+  const int kg = lane / 16;
+  uint32_t mask[4];
+  lane_masks(mask);
+  const int64_t slot0 = bh * p.cap + t_beg;
+  const float kappa = kSqrtHalfPi / static_cast<float>(D);
+  const int n_tiles16 = (n_t + 15) / 16;
 
-  // phase 3: acc[g][i] = sum_t w[g][t] * n_t * c_v[idx_t,i]
-  constexpr int NP = 256 / D;                // threads per coordinate
-  constexpr int MAXH = 32 / NP;              // heads per thread (G <= 32)
-  const int i = threadIdx.x % D;
-  const int hp = threadIdx.x / D;
-  float acc[MAXH];
+  // 1. logits
+  for (int rg0 = 0; rg0 < RG; rg0 += NRG) {
+    const int nrg = min(NRG, RG - rg0);
+    v4i a[NRG][NMF];
+    load_afrags<D, KW, NRG>(prep, rg0, nrg, a);
+    for (int tile = wave; tile < n_tiles16; tile += 4) {
+      const int tt = tile * 16 + (lane % 16);
+      KeyTile<D, KW> kt;
+      load_key_tile<D, KW>(p.kcodes, p.kscalars, slot0, tt, n_t, kt);
+      v4i clm[NRG], cqj[NRG];
+      key_tile_mfma<D, KW, NRG>(kt, a, mask, nrg, clm, cqj);
 #pragma unroll
-  for (int s = 0; s < MAXH; ++s) acc[s] = 0.f;
-  const int64_t nblk = p.cap / kValueBlock;
-  const int64_t blk0 = t_beg / kValueBlock;
-  const int nb = (n_t + kValueBlock - 1) / kValueBlock;
-  for (int kb = 0; kb < nb; ++kb) {
-    uint32_t wv[VW];
-    const uint32_t *src = p.vcodes + ((bh * nblk + blk0 + kb) * VW) * D + i;
-#pragma unroll
-    for (int q = 0; q < VW; ++q) wv[q] = src[q * D];
-    const int jn = min(kValueBlock, n_t - kb * kValueBlock);
-    for (int j = 0; j < jn; ++j) {
-      int idx = 0;
-#pragma unroll
-      for (int q = 0; q < VW; ++q) idx |= static_cast<int>((wv[q] >> j) & 1u) << q;
-      const int tt = kb * kValueBlock + j;
-      const float val = svc[idx] * snv[tt];
-#pragma unroll
-      for (int s = 0; s < MAXH; ++s) {
-        const int g = hp + s * NP;
-        if (g < G) acc[s] = fmaf(sl[g * SPLIT + tt], val, acc[s]);
+      for (int rg = 0; rg < NRG; ++rg) {
+        const int h = 4 * (rg0 + rg) + kg;
+        if (rg < nrg && h < G && tt < n_t)
+          sl[h * SPLIT + tt] = tile_logit(clm[rg], cqj[rg], fl + 4 * h, kt.n, kt.g, kappa) * p.sm_scale;
       }
     }
   }
-#pragma unroll
-  for (int s = 0; s < MAXH; ++s) {
-    const int g = hp + s * NP;
-    if (g < G) {
-      part[g * (D + 2) + 2 + i] = acc[s];
-      if (i == 0) { part[g * (D + 2)] = sml[2 * g]; part[g * (D + 2) + 1] = sml[2 * g + 1]; }
+  for (int tt = tid; tt < n_t; tt += blockDim.x) snv[tt] = f16_bits_to_float(p.vscalars[slot0 + tt]);
+  __syncthreads();
+
+  // 2. softmax statistics and weights; the largest value norm fixes the exponent
+  float nvm = 0.f;
+  for (int tt = lane; tt < n_t; tt += kWave) nvm = fmaxf(nvm, snv[tt]);
+  nvm = wave_max(nvm);
+  const int ew = fixed_exponent(nvm);
+  for (int h = wave; h < G; h += 4) {
+    float m = -INFINITY;
+    for (int tt = lane; tt < n_t; tt += kWave) m = fmaxf(m, sl[h * SPLIT + tt]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int tt = lane; tt < n_t; tt += kWave) {
+      const float e = __expf(sl[h * SPLIT + tt] - m);
+      l += e;
+      sl[h * SPLIT + tt] = e * snv[tt];
     }
+    l = wave_sum(l);
+    if (lane == 0) { sstat[4 * h] = m; sstat[4 * h + 1] = l; }
+  }
+  __syncthreads();
+
+  // 3. weight operands: row (local head, digit), K slot -> token of a 64-token tile
+  const int n_tiles64 = (n_t + 63) / 64;
+  for (int row = tid; row < RG * n_tiles64 * kWave; row += blockDim.x) {
+    const int l = row % kWave;
+    const int tile = (row / kWave) % n_tiles64;
+    const int rg = row / (kWave * n_tiles64);
+    const int m = l % 16, kgl = l / 16;
+    const int h = 4 * rg + m / 4, s = m % 4;
+    uint32_t dw[4] = {0u, 0u, 0u, 0u};
+    if (h < G) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int tok = tile * 64 + slot_coord(64, kgl, j, 0);
+        const int k = 4 * (kgl & 1) + (j >> 2);
+        if (tok < n_t) {
+          float v = ldexpf(sl[h * SPLIT + tok], 7 - k + ew);
+          if (k == 7) v = -v;
+          const uint32_t dig = signed_digits(__float2int_rn(v));
+          dw[j >> 2] |= ((dig >> (8 * s)) & 0xffu) << (8 * (j & 3));
+        }
+      }
+    }
+    *reinterpret_cast<uint4 *>(fragv + (static_cast<size_t>(rg) * (SPLIT / 64) + tile) * 1024 + l * 16) =
+        make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  }
+  // exact sum of the effective weights: sum_t int(w_t 2^(7-k+ew)) 2^k, per head
+  for (int h = wave; h < G; h += 4) {
+    double acc = 0.0;
+    for (int tt = lane; tt < n_t; tt += kWave) {
+      const int k = tt & 7;   // token 8*jb + k of a 32-token word carries weight 2^k
+      float v = ldexpf(sl[h * SPLIT + tt], 7 - k + ew);
+      acc += static_cast<double>(__float2int_rn(v)) * static_cast<double>(1 << k);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+    if (lane == 0) ssw[h] = acc;
+  }
+  __syncthreads();
+
+  // 4. value planes on the matrix cores; wave w owns coordinates [16*NT*w, 16*NT*(w+1))
+  const int64_t nblk = p.cap / kValueBlock;
+  const int64_t blk0 = t_beg / kValueBlock;
+  float vb[NBV];
+  for (int s = 0; s < NBV; ++s) vb[s] = basis_coeff(p.vcent, VW, Basis<VW>::M[s]);
+  const float cvmax = p.vcent[(1 << VW) - 1];
+  for (int rg0 = 0; rg0 < RG; rg0 += NRG) {
+    const int nrg = min(NRG, RG - rg0);
+    v4i acc[NRG][NBV][NT];
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+      for (int s = 0; s < NBV; ++s)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rg][s][nt] = v4i{0, 0, 0, 0};
+    for (int tile = 0; tile < n_tiles64; ++tile) {
+      v4i av[NRG];
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) {
+        if (rg < nrg) {
+          const uint4 u = *reinterpret_cast<const uint4 *>(fragv + (static_cast<size_t>(rg0 + rg) * (SPLIT / 64) + tile) * 1024 + lane * 16);
+          av[rg] = v4i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z), static_cast<int>(u.w)};
+        }
+      }
+      const int64_t blk = blk0 + 2 * tile + (kg >> 1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int coord = (wave * NT + nt) * 16 + (lane % 16);
+        uint32_t pw[VW];
+        if (2 * tile + (kg >> 1) < (n_t + kValueBlock - 1) / kValueBlock) {
+          const uint32_t *src = p.vcodes + ((bh * nblk + blk) * VW) * D + coord;
+#pragma unroll
+          for (int q = 0; q < VW; ++q) pw[q] = src[q * D];
+        } else {
+#pragma unroll
+          for (int q = 0; q < VW; ++q) pw[q] = 0u;
+        }
+#pragma unroll
+        for (int s = 0; s < NBV; ++s) {
+          uint32_t w = 0u;
+#pragma unroll
+          for (int q = 0; q < VW; ++q)
+            if ((Basis<VW>::M[s] >> q) & 1) w ^= pw[q];
+          const v4i bv = expand_bits(w, mask);
+#pragma unroll
+          for (int rg = 0; rg < NRG; ++rg)
+            if (rg < nrg) acc[rg][s][nt] = mfma_i8(av[rg], bv, acc[rg][s][nt]);
+        }
+      }
+    }
+    // 5. epilogue: acc = (2 sum_S beta_S X_S - c_max SW) / 2^(7+ew)
+    const float inv = ldexpf(1.0f, -7 - ew);
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+      const int h = 4 * (rg0 + rg) + kg;
+      if (rg < nrg && h < G) {
+        const float sw = static_cast<float>(ssw[h]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float x = 0.f;
+#pragma unroll
+          for (int s = 0; s < NBV; ++s) x = fmaf(vb[s], combine_digits(acc[rg][s][nt]), x);
+          const int coord = (wave * NT + nt) * 16 + (lane % 16);
+          part[h * (D + 2) + 2 + coord] = fmaf(2.0f, x, -cvmax * sw) * inv;
+        }
+      }
+    }
+  }
+  for (int h = tid; h < G; h += blockDim.x) {
+    part[h * (D + 2)] = sstat[4 * h];
+    part[h * (D + 2) + 1] = sstat[4 * h + 1];
   }
 }
 
@@ -331,18 +566,23 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
   else static_cast<uint16_t *>(p.out)[bq * D + i] = float_to_bf16_bits(o);
 }
 
+template <int D, int KW, int VW>
+static void launch_decode_kv(const DecodeParams &p, dim3 grid, size_t shm, hipStream_t st) {
+  if (p.group > 4) hipLaunchKernelGGL((decode_split_kernel<D, KW, VW, 2>), grid, dim3(256), shm, st, p);
+  else hipLaunchKernelGGL((decode_split_kernel<D, KW, VW, 1>), grid, dim3(256), shm, st, p);
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeParams &p, int kw, int vw, hipStream_t st) {
   if (p.batch == 0 || p.n_kv == 0) return hipSuccess;
   dim3 grid(static_cast<uint32_t>(p.n_splits), static_cast<uint32_t>(p.batch) * p.n_kv);
   const size_t shm = decode_split_smem(D, p.group, p.split);
-#define TQ_DS(KK, VV) hipLaunchKernelGGL((decode_split_kernel<D, KK, VV>), grid, dim3(256), shm, st, p)
-#define TQ_DS_V(KK)                                       \
-  switch (vw) {                                           \
-    case 1: TQ_DS(KK, 1); break;                          \
-    case 2: TQ_DS(KK, 2); break;                          \
-    case 3: TQ_DS(KK, 3); break;                          \
-    default: TQ_DS(KK, 4);                                \
+#define TQ_DS_V(KK)                                            \
+  switch (vw) {                                                \
+    case 1: launch_decode_kv<D, KK, 1>(p, grid, shm, st); break; \
+    case 2: launch_decode_kv<D, KK, 2>(p, grid, shm, st); break; \
+    case 3: launch_decode_kv<D, KK, 3>(p, grid, shm, st); break; \
+    default: launch_decode_kv<D, KK, 4>(p, grid, shm, st);     \
   }
   switch (kw) {
     case 1: TQ_DS_V(1); break;
@@ -351,7 +591,6 @@ hipError_t launch_decode_d(const DecodeParams &p, int kw, int vw, hipStream_t st
     default: TQ_DS_V(4);
   }
 #undef TQ_DS_V
-#undef TQ_DS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t rows = static_cast<uint32_t>(p.batch) * p.n_kv * p.group;

@@ -23,24 +23,28 @@ struct EncodeParams {
 template <int D>
 hipError_t launch_encode_d(const EncodeParams &p, int w, bool key, hipStream_t st);
 
-// Prepared queries: per query head, q' = R q (D floats) then p = S q' (D floats).
+// Query preparation for one (batch, kv-head) group of `group` query heads:
+// q' = R q, p = S q', the fixed-point MFMA operands for the key planes and
+// the QJL plane, and per-head float constants (see tq_mfma.h).
 struct QueryPrepParams {
-  const void *q;
+  const void *q;                        // [batch][n_kv*group][D]
   int xt;
-  int64_t n_heads;                      // batch * n_q
-  const float *signs;
+  int32_t batch, n_kv, group;
+  int32_t kw;                           // key Lloyd-Max bits
+  const float *signs, *centroids;
   const uint16_t *sketch;
-  float *out;                           // [n_heads][2][D]
+  uint8_t *out;                         // [batch*n_kv][group_bytes]
+  size_t group_bytes;
 };
 
 template <int D>
 hipError_t launch_query_prep_d(const QueryPrepParams &p, hipStream_t st);
 
 struct LogitsParams {
-  const float *qprep;                   // [batch][n_q][2][D]
+  const uint8_t *qprep;                 // prepared groups, group_bytes apart
+  size_t group_bytes, frag_bytes;
   const uint8_t *kcodes;
   const uint16_t *kscalars;
-  const float *centroids;
   int64_t cap, n_keys;
   int32_t batch, n_kv, group;
   float *logits;                        // [batch][n_q][n_keys]
@@ -50,16 +54,17 @@ template <int D>
 hipError_t launch_logits_d(const LogitsParams &p, int w, hipStream_t st);
 
 struct DecodeParams {
-  const float *qprep;                   // [batch][n_q][2][D]
+  const uint8_t *qprep;
+  size_t group_bytes, frag_bytes;
   const uint8_t *kcodes;
   const uint16_t *kscalars;
   const uint32_t *vcodes;
   const uint16_t *vscalars;
-  const float *kcent, *vcent, *vsigns;
+  const float *vcent, *vsigns;
   int64_t cap, max_ctx;
   const int32_t *ctx_lens;
   int32_t batch, n_kv, group;
-  int32_t split;                        // tokens per context split
+  int32_t split;                        // tokens per context split (multiple of 64)
   int32_t n_splits;
   float sm_scale;
   float *partials;                      // [batch*n_kv][n_splits][group][D+2]
@@ -70,11 +75,14 @@ struct DecodeParams {
 template <int D>
 hipError_t launch_decode_d(const DecodeParams &p, int kw, int vw, hipStream_t st);
 
-// LDS bytes of one decode-split block: queries, weights, value norms,
-// codebooks, per-head softmax statistics.
+// LDS bytes of one decode-split block: scaled logits / weights [G][split],
+// value norms [split], value-weight MFMA operands [ceil(G/4)][split/64][1 KiB],
+// per-head statistics.
 inline size_t decode_split_smem(int d, int group, int split) {
-  return (static_cast<size_t>(group) * 2 * d + static_cast<size_t>(group) * split + split + 32 +
-          2 * static_cast<size_t>(group)) * sizeof(float);
+  (void)d;
+  const size_t rg = (group + 3) / 4;
+  return static_cast<size_t>(group) * split * 4 + static_cast<size_t>(split) * 4 +
+         rg * (split / 64) * 1024 + static_cast<size_t>(group) * 32 + 64;
 }
 
 }  // namespace tq

@@ -135,7 +135,7 @@ def test_logits_validation():
     assert _logits(_codec(), qt=9) == tq.TQ_EINVAL
     assert _logits(_codec(), batch=-1) == tq.TQ_EINVAL
     assert _logits(_codec(), n_keys=0) == tq.TQ_OK
-    assert tq.logits_workspace(1, 8, 4, 128) == 32 * 2 * 128 * 4
+    assert tq.logits_workspace(1, 8, 4, 128) >= 8 * (9 * 2 * 1024 + 4 * 4 * 4)
 
 
 def _decode(kc, vc, batch=2, n_kv=2, group=4, cap=256, max_ctx=256, scale=0.1, out_t=tq.TQ_F32, ws=None,
