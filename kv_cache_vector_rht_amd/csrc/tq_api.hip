@@ -143,8 +143,10 @@ tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_
   if (!x || !codes || !scalars) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
   if (x_tok_stride < codec->d || (n_seq > 1 && x_seq_stride < 0))
     return fail(TQ_EINVAL, "%s: token stride must be >= d", fn);
-  const int64_t g0 = t0 / 64;
-  const int64_t g1 = (t0 + n_tok - 1) / 64;
+  // one wave encodes 64 coordinates x 64 lanes: 64 tokens (d = 64) or 32 (d = 128)
+  const int64_t tpw = codec->d == 128 ? 32 : 64;
+  const int64_t g0 = t0 / tpw;
+  const int64_t g1 = (t0 + n_tok - 1) / tpw;
   tq::EncodeParams p{};
   p.x = x;
   p.x_seq_stride = x_seq_stride;

@@ -21,75 +21,86 @@ constexpr float kSqrtHalfPi = 1.2533141373155002f;   // sqrt(pi / 2)
 
 // ------------------------------------------------------------------ query prep
 
-// One block (256 threads) per (batch, kv-head) group.
+// One block (256 threads) per query head. The block stages the sketch in
+// LDS (coalesced), rotates its query, projects it, and writes the four
+// digit rows of its head into the group's MFMA operands.
 template <int D>
 __global__ __launch_bounds__(256) void query_prep_kernel(QueryPrepParams p) {
-  extern __shared__ float qs[];              // [G][D] q', then [G][D] p, then stats
+  __shared__ uint32_t s_sk[D * D / 2];       // the sketch, fp16 pairs
+  __shared__ float sq[D], sp[D], sb[9], sred[8];
   const int G = p.group;
   const int n_q = p.n_kv * G;
-  const int64_t grp = blockIdx.x;            // b * n_kv + kvh
-  const int64_t b = grp / p.n_kv;
-  const int64_t kvh = grp % p.n_kv;
-  float *sq = qs;
-  float *sp = qs + G * D;
-  float *st = sp + G * D;                    // [G][4]: max|q'|, sum q', max|p|, sum p
-  float *sb = st + 4 * G;                    // [8] beta, [1] max |beta|
+  const int64_t hq = blockIdx.x;             // global query-head index b * n_q + h
+  const int64_t b = hq / n_q;
+  const int hh = static_cast<int>(hq % n_q);
+  const int64_t grp = b * p.n_kv + hh / G;
+  const int h = hh % G;                      // head within the group
   const int tid = threadIdx.x;
-  const int64_t q0 = (b * n_q + kvh * G) * D;
+  const int wave = tid / kWave, lane = lane_id();
 
-  for (int e = tid; e < G * D; e += blockDim.x) {
-    const int i = e % D;
+  // issue the sketch and query loads first
+  const uint4 *src = reinterpret_cast<const uint4 *>(p.sketch);
+  for (int e = tid; e < D * D / 8; e += blockDim.x) reinterpret_cast<uint4 *>(s_sk)[e] = src[e];
+  if (tid < D) {
     float v;
-    if (p.xt == 0) v = static_cast<const float *>(p.q)[q0 + e];
-    else if (p.xt == 1) v = bf16_bits_to_float(static_cast<const uint16_t *>(p.q)[q0 + e]);
-    else v = f16_bits_to_float(static_cast<const uint16_t *>(p.q)[q0 + e]);
-    sq[e] = v * p.signs[i];
+    if (p.xt == 0) v = static_cast<const float *>(p.q)[hq * D + tid];
+    else if (p.xt == 1) v = bf16_bits_to_float(static_cast<const uint16_t *>(p.q)[hq * D + tid]);
+    else v = f16_bits_to_float(static_cast<const uint16_t *>(p.q)[hq * D + tid]);
+    sq[tid] = v * p.signs[tid];
   }
   const int NB = basis_size(p.kw);
   if (tid < NB) sb[tid] = basis_coeff(p.centroids, p.kw, basis_mask(p.kw, tid));
   __syncthreads();
-  // Walsh-Hadamard butterflies on every head, then 1/sqrt(D)
   for (int hs = 1; hs < D; hs <<= 1) {
-    for (int e = tid; e < G * D / 2; e += blockDim.x) {
-      const int h = e / (D / 2);
-      const int r = e % (D / 2);
-      const int i = (r / hs) * 2 * hs + (r % hs);
-      const float a = sq[h * D + i];
-      const float c = sq[h * D + i + hs];
-      sq[h * D + i] = a + c;
-      sq[h * D + i + hs] = a - c;
+    float a = 0.f, c = 0.f;
+    int i = 0;
+    if (tid < D / 2) {
+      i = (tid / hs) * 2 * hs + (tid % hs);
+      a = sq[i];
+      c = sq[i + hs];
+    }
+    __syncthreads();
+    if (tid < D / 2) {
+      sq[i] = a + c;
+      sq[i + hs] = a - c;
     }
     __syncthreads();
   }
-  for (int e = tid; e < G * D; e += blockDim.x) sq[e] *= (1.0f / sqrtf(static_cast<float>(D)));
+  if (tid < D) sq[tid] *= (1.0f / sqrtf(static_cast<float>(D)));
   __syncthreads();
-  // p = S q'
-  for (int e = tid; e < G * D; e += blockDim.x) {
-    const int h = e / D, j = e % D;
-    const uint32_t *row = reinterpret_cast<const uint32_t *>(p.sketch + static_cast<int64_t>(j) * D);
-    const float *qh = sq + h * D;
+  // p_j = sum_k S[j][k] q'_k, two threads per output
+  {
+    const int j = tid % D, part = tid / D;   // D = 128: part 0/1; D = 64: part 0..3
+    constexpr int PARTS = 256 / D;
+    constexpr int PW = D / PARTS / 2;         // sketch dwords per part (32 or 8)
     float acc = 0.f;
+    // rotated start so that neighbouring threads hit different LDS banks
 #pragma unroll 8
-    for (int k = 0; k < D; k += 2) {
-      const uint32_t two = row[k / 2];
-      acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two & 0xffffu)), qh[k], acc);
-      acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two >> 16)), qh[k + 1], acc);
+    for (int m = 0; m < PW; ++m) {
+      const int k = part * (D / PARTS) + 2 * ((m + j) % PW);
+      const uint32_t two = s_sk[(j * D + k) / 2];
+      acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two & 0xffffu)), sq[k], acc);
+      acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two >> 16)), sq[k + 1], acc);
     }
-    sp[e] = acc;
+    __syncthreads();                          // the sketch is no longer read below
+    float *red = reinterpret_cast<float *>(s_sk);
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < D) {
+      float v = 0.f;
+      for (int q = 0; q < PARTS; ++q) v += red[q * D + tid];
+      sp[tid] = v;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  // per-head statistics, one wave per head
-  const int wave = tid / kWave, lane = lane_id(), n_waves = blockDim.x / kWave;
-  for (int h = wave; h < G; h += n_waves) {
-    float mq = 0.f, sqs = 0.f, mp = 0.f, sps = 0.f;
-    for (int i = lane; i < D; i += kWave) {
-      mq = fmaxf(mq, fabsf(sq[h * D + i]));
-      sqs += sq[h * D + i];
-      mp = fmaxf(mp, fabsf(sp[h * D + i]));
-      sps += sp[h * D + i];
-    }
-    mq = wave_max(mq); sqs = wave_sum(sqs); mp = wave_max(mp); sps = wave_sum(sps);
-    if (lane == 0) { st[4 * h] = mq; st[4 * h + 1] = sqs; st[4 * h + 2] = mp; st[4 * h + 3] = sps; }
+  // statistics: wave 0 -> q', wave 1 -> p
+  if (wave < 2) {
+    const float *x = wave == 0 ? sq : sp;
+    float mx = 0.f, sm = 0.f;
+    for (int i = lane; i < D; i += kWave) { mx = fmaxf(mx, fabsf(x[i])); sm += x[i]; }
+    mx = wave_max(mx);
+    sm = wave_sum(sm);
+    if (lane == 0) { sred[2 * wave] = mx; sred[2 * wave + 1] = sm; }
   }
   if (tid == 0) {
     float mb = 0.f;
@@ -98,55 +109,60 @@ __global__ __launch_bounds__(256) void query_prep_kernel(QueryPrepParams p) {
   }
   __syncthreads();
 
-  // A operands: rows = 4 local heads x 4 digits, one 16-byte vector per lane
-  const int RG = (G + 3) / 4;
   const int NH = D / 64;
   const int NMF = (NB + 1) * NH;
+  const int rg = h / 4, hl = h % 4;
+  const int el = fixed_exponent(2.0f * sb[8] * sred[0]);
+  const int eq = fixed_exponent(2.0f * sred[2]);
   uint8_t *dst = p.out + grp * p.group_bytes;
-  const float cmax = p.centroids[(1 << p.kw) - 1];
-  for (int row = tid; row < RG * NMF * kWave; row += blockDim.x) {
-    const int l = row % kWave;
-    const int mf = (row / kWave) % NMF;
-    const int rg = row / (kWave * NMF);
-    const int m = l % 16, kg = l / 16;
-    const int h = 4 * rg + m / 4, s = m % 4;
+  // the 16 lanes of this head in each operand: rows 4 hl + s, k-groups kg
+  for (int item = tid; item < NMF * 16; item += blockDim.x) {
+    const int mf = item / 16;
+    const int s = (item % 16) % 4, kg = (item % 16) / 4;
+    const int l = 16 * kg + 4 * hl + s;
     const bool qjl = mf >= NB * NH;
     const int plane = qjl ? 0 : mf / NH;
     const int half = mf % NH;
+    const float coef = qjl ? 2.0f : 2.0f * sb[plane];
+    const int e = qjl ? eq : el;
+    const float *x = qjl ? sp : sq;
     uint32_t dw[4] = {0u, 0u, 0u, 0u};
-    if (h < G) {
-      const float coef = qjl ? 2.0f : 2.0f * sb[plane];
-      const float mx = qjl ? 2.0f * st[4 * h + 2] : 2.0f * sb[8] * st[4 * h];
-      const int e = fixed_exponent(mx);
-      const float *src = (qjl ? sp : sq) + h * D;
-      for (int j = 0; j < 16; ++j) {
-        const int coord = slot_coord(D, kg, j, half);
-        const int k = 4 * (kg & 1) + (j >> 2);
-        float v = ldexpf(coef * src[coord], 7 - k + e);
-        if (k == 7) v = -v;
-        const uint32_t dig = signed_digits(__float2int_rn(v));
-        dw[j >> 2] |= ((dig >> (8 * s)) & 0xffu) << (8 * (j & 3));
-      }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int coord = slot_coord(D, kg, j, half);
+      const int k = 4 * (kg & 1) + (j >> 2);
+      float v = ldexpf(coef * x[coord], 7 - k + e);
+      if (k == 7) v = -v;
+      const uint32_t dig = signed_digits(__float2int_rn(v));
+      dw[j >> 2] |= ((dig >> (8 * s)) & 0xffu) << (8 * (j & 3));
     }
-    *reinterpret_cast<uint4 *>(dst + static_cast<size_t>(row) * 16) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    *reinterpret_cast<uint4 *>(dst + (static_cast<size_t>(rg * NMF + mf) * kWave + l) * 16) =
+        make_uint4(dw[0], dw[1], dw[2], dw[3]);
   }
-  float *fl = reinterpret_cast<float *>(dst + qprep_frag_bytes(D, p.kw, G));
-  for (int h = tid; h < G; h += blockDim.x) {
-    const int el = fixed_exponent(2.0f * sb[8] * st[4 * h]);
-    const int eq = fixed_exponent(2.0f * st[4 * h + 2]);
-    fl[4 * h + 0] = ldexpf(1.0f, -7 - el);
-    fl[4 * h + 1] = cmax * st[4 * h + 1];
-    fl[4 * h + 2] = ldexpf(1.0f, -7 - eq);
-    fl[4 * h + 3] = st[4 * h + 3];
+  // rows of absent heads in this head's last row group stay zero: the
+  // group's first head of a row group clears them
+  const int RG = (G + 3) / 4;
+  if (hl == 0 && rg == RG - 1 && G % 4 != 0) {
+    for (int item = tid; item < NMF * 64; item += blockDim.x) {
+      const int mf = item / 64, l = item % 64;
+      if ((l % 16) / 4 >= G % 4)
+        *reinterpret_cast<uint4 *>(dst + (static_cast<size_t>(rg * NMF + mf) * kWave + l) * 16) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if (tid == 0) {
+    float *fl = reinterpret_cast<float *>(dst + qprep_frag_bytes(D, p.kw, G)) + 4 * h;
+    fl[0] = ldexpf(1.0f, -7 - el);
+    fl[1] = p.centroids[(1 << p.kw) - 1] * sred[1];
+    fl[2] = ldexpf(1.0f, -7 - eq);
+    fl[3] = sred[3];
   }
 }
 
 template <int D>
 hipError_t launch_query_prep_d(const QueryPrepParams &p, hipStream_t st) {
-  const uint32_t groups = static_cast<uint32_t>(p.batch) * p.n_kv;
-  if (groups == 0 || p.group == 0) return hipSuccess;
-  const size_t shm = (static_cast<size_t>(2) * p.group * D + 4 * p.group + 16) * sizeof(float);
-  hipLaunchKernelGGL((query_prep_kernel<D>), dim3(groups), dim3(256), shm, st, p);
+  const uint32_t heads = static_cast<uint32_t>(p.batch) * p.n_kv * p.group;
+  if (heads == 0) return hipSuccess;
+  hipLaunchKernelGGL((query_prep_kernel<D>), dim3(heads), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -280,22 +296,22 @@ __global__ __launch_bounds__(256) void logits_kernel(LogitsParams p) {
     const int nrg = min(NRG, RG - rg0);
     v4i a[NRG][NMF];
     load_afrags<D, KW, NRG>(prep, rg0, nrg, a);
-    KeyTile<D, KW> kt;
-    load_key_tile<D, KW>(p.kcodes, p.kscalars, slot0, tile0 * 16 + (lane % 16), p.n_keys, kt);
+    KeyTile<D, KW> kt[kLogitTilesPerWave];
+#pragma unroll
+    for (int it = 0; it < kLogitTilesPerWave; ++it)
+      load_key_tile<D, KW>(p.kcodes, p.kscalars, slot0, (tile0 + it) * 16 + (lane % 16), p.n_keys, kt[it]);
+#pragma unroll
     for (int it = 0; it < kLogitTilesPerWave; ++it) {
       const int64_t t = (tile0 + it) * 16 + (lane % 16);
       if ((tile0 + it) * 16 >= p.n_keys) break;
-      KeyTile<D, KW> nx;
-      if (it + 1 < kLogitTilesPerWave) load_key_tile<D, KW>(p.kcodes, p.kscalars, slot0, t + 16, p.n_keys, nx);
       v4i clm[NRG], cqj[NRG];
-      key_tile_mfma<D, KW, NRG>(kt, a, mask, nrg, clm, cqj);
+      key_tile_mfma<D, KW, NRG>(kt[it], a, mask, nrg, clm, cqj);
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
         const int h = 4 * (rg0 + rg) + kg;
         if (rg < nrg && h < G && t < p.n_keys)
-          p.logits[(b * n_q + kvh * G + h) * p.n_keys + t] = tile_logit(clm[rg], cqj[rg], fl + 4 * h, kt.n, kt.g, kappa);
+          p.logits[(b * n_q + kvh * G + h) * p.n_keys + t] = tile_logit(clm[rg], cqj[rg], fl + 4 * h, kt[it].n, kt[it].g, kappa);
       }
-      kt = nx;
     }
   }
 }

@@ -9,161 +9,205 @@
 // み・実測精度・2026年7月時点の実装状況" (第1段: randomized Hadamard rotation +
 // per-coordinate Lloyd-Max; 第2段: 1-bit JL projection of the residual).
 //
-// Mapping: one wave encodes 64 consecutive cache slots of one sequence, one
-// lane per token. The whole vector stays in the lane's registers, so the
-// rotation is a register-only butterfly network (no shuffles, no LDS), and
-// the threshold compares of a coordinate across the 64 lanes are exactly the
-// 64 token bits of a value-code word (one ballot per plane and coordinate).
-// Key records are assembled per lane. The QJL projection of a 64-token tile
-// is in tq_qjl.h.
+// Mapping: every lane holds 64 coordinates of one token. For d = 64 a wave
+// encodes 64 tokens (one lane each); for d = 128 it encodes 32 tokens, token
+// t in lanes t and t + 32 (coordinates [0, 64) and [64, 128)). The first six
+// butterfly stages of the rotation run in registers, the seventh (d = 128)
+// pairs lane t with lane t + 32. A ballot over the wave of one coordinate's
+// index bit yields 64 token bits: one 32-bit value-code word per 32-token
+// block (d = 64: two blocks of the same coordinate; d = 128: coordinates c
+// and c + 64 of one block). Key records are assembled per lane (each lane
+// writes its half of every plane). The QJL projection of the wave's
+// residuals runs on the matrix cores (tq_qjl.h).
 #include "tq_device.h"
 #include "tq_kernels.h"
 #include "tq_qjl.h"
 
 namespace tq {
 
+// dst[lane LANE] = value (wave-uniform): v_writelane_b32.
+template <int LANE>
+__device__ __forceinline__ void write_lane(uint32_t &dst, uint32_t value) {
+  const uint32_t v = __builtin_amdgcn_readfirstlane(value);
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(dst) : "s"(v), "i"(LANE));
+}
+
+// Lloyd-Max decision idx = #{j : y >= t_j} over sorted thresholds. Up to
+// two bits: count the thresholds. Wider: binary search, reading the
+// candidate threshold of each level from LDS (s_th).
+template <int W>
+__device__ __forceinline__ int quantize(float y, const float (&t)[(1 << W) - 1], const float *s_th) {
+  int idx = 0;
+  if constexpr (W <= 2) {
+#pragma unroll
+    for (int j = 0; j < (1 << W) - 1; ++j) idx += (y >= t[j]) ? 1 : 0;
+  } else {
+#pragma unroll
+    for (int level = W - 1; level >= 0; --level) {
+      const int cand = idx | (1 << level);
+      idx = (y >= s_th[cand - 1]) ? cand : idx;
+    }
+  }
+  return idx;
+}
+
+// The other half-wave's copy of x (lane l <-> lane l ^ 32).
+__device__ __forceinline__ float swap_half_f(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((lane_id() < 32) ? r[1] : r[0]);
+}
+
 template <int D, int W, bool KEY>
-__global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void encode_kernel(EncodeParams p) {
   constexpr int L = 1 << W;
-  constexpr int NW = D / 32;                 // 32-bit words per plane
+  constexpr int C = 64;                      // coordinates per lane
+  constexpr int LPT = D / C;                 // lanes per token (1 or 2)
+  constexpr int TPW = kWave / LPT;           // tokens per wave (64 or 32)
+  constexpr int NWL = C / 32;                // plane words per lane (2)
   __shared__ float s_cent[L];
+  __shared__ float s_th[L];
   __shared__ float s_sign[D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_sk[KEY ? D * (D + 8) : 8];
   if (threadIdx.x < L) s_cent[threadIdx.x] = p.centroids[threadIdx.x];
+  if (threadIdx.x < L - 1) s_th[threadIdx.x] = p.thresholds[threadIdx.x];
   for (int i = threadIdx.x; i < D; i += blockDim.x) s_sign[i] = p.signs[i];
+  if (KEY) stage_sketch<D>(p.sketch, s_sk);
   __syncthreads();
 
   const int lane = lane_id();
+  const int tok = lane % TPW;                // token within the wave
+  const int hv = lane / TPW;                 // which 64 coordinates (d = 128)
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (wave >= p.n_waves) return;             // whole wave exits together
   const int64_t seq = wave / p.groups_per_seq;
   const int64_t g = p.g0 + wave % p.groups_per_seq;
-  const int64_t pos = g * kWave + lane;      // cache slot
+  const int64_t pos = g * TPW + tok;         // cache slot
   const int64_t t = pos - p.t0;              // input token
   const bool active = (t >= 0) && (t < p.n_tok);
 
-  float v[D];
+  float v[C];
   if (active) {
-    if (p.xt == 0) {
-      load_row_vec_f32<D>(static_cast<const float *>(p.x) + seq * p.x_seq_stride + t * p.x_tok_stride, v);
-    } else {
-      const uint16_t *row = static_cast<const uint16_t *>(p.x) + seq * p.x_seq_stride + t * p.x_tok_stride;
-      if (p.xt == 1) load_row_vec_16<D, true>(row, v);
-      else load_row_vec_16<D, false>(row, v);
-    }
+    const int64_t off = seq * p.x_seq_stride + t * p.x_tok_stride + C * hv;
+    if (p.xt == 0) load_row_vec_f32<C>(static_cast<const float *>(p.x) + off, v);
+    else if (p.xt == 1) load_row_vec_16<C, true>(static_cast<const uint16_t *>(p.x) + off, v);
+    else load_row_vec_16<C, false>(static_cast<const uint16_t *>(p.x) + off, v);
   } else {
 #pragma unroll
-    for (int i = 0; i < D; ++i) v[i] = 0.f;
+    for (int i = 0; i < C; ++i) v[i] = 0.f;
   }
 
-  // (a1) norm, accumulated in fp32 in coordinate order
+  // (a1) norm, accumulated in fp32 in coordinate order (then the two halves)
   float n2 = 0.f;
 #pragma unroll
-  for (int i = 0; i < D; ++i) n2 = fmaf(v[i], v[i], n2);
+  for (int i = 0; i < C; ++i) n2 = fmaf(v[i], v[i], n2);
+  if (LPT == 2) {
+    const float o = swap_half_f(n2);
+    n2 = hv ? (o + n2) : (n2 + o);
+  }
   const float n = sqrtf(n2);
 
   // (a2) y = H diag(s) x / (n sqrt(D)); the zero vector maps to y = 0
 #pragma unroll
-  for (int i = 0; i < D; ++i) v[i] *= s_sign[i];
-  fwht_regs<D>(v);
+  for (int i = 0; i < C; ++i) v[i] *= s_sign[C * hv + i];
+  fwht_regs<C>(v);
+  if (LPT == 2) {
+    // stage 7: y_i = v_i + v_{i+64} (lane t), y_{i+64} = v_i - v_{i+64} (lane t + 32)
+    const float sgn = hv ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < C; ++i) v[i] = fmaf(sgn, v[i], swap_half_f(v[i]));
+  }
   const float inv = (n > 0.f) ? 1.0f / (n * sqrtf(static_cast<float>(D))) : 0.f;
 #pragma unroll
-  for (int i = 0; i < D; ++i) v[i] *= inv;
+  for (int i = 0; i < C; ++i) v[i] *= inv;
 
-  // (a3) idx = #{j : y >= t_j}; thresholds are wave-uniform
   float th[L - 1];
 #pragma unroll
-  for (int j = 0; j < L - 1; ++j) th[j] = p.thresholds[j];
+  for (int j = 0; j < L - 1; ++j) th[j] = s_th[j];
 
   if (KEY) {
-    uint32_t planes[W][NW];
+    // (a3) indices -> this lane's half of every plane; (a4) residual
+    uint32_t planes[W][NWL];
 #pragma unroll
     for (int q = 0; q < W; ++q)
 #pragma unroll
-      for (int k = 0; k < NW; ++k) planes[q][k] = 0u;
+      for (int k = 0; k < NWL; ++k) planes[q][k] = 0u;
     float g2 = 0.f;
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      int idx = 0;
+    for (int i = 0; i < C; ++i) {
+      const int idx = quantize<W>(v[i], th, s_th);
 #pragma unroll
-      for (int j = 0; j < L - 1; ++j) idx += (v[i] >= th[j]) ? 1 : 0;
-#pragma unroll
-      for (int q = 0; q < W; ++q) planes[q][i / 32] |= static_cast<uint32_t>((idx >> q) & 1) << (i % 32);
-      // (a4) residual in the rotated unit domain
+      for (int q = 0; q < W; ++q) {
+        planes[q][i / 32] |= static_cast<uint32_t>((idx >> q) & 1) << (i % 32);
+        asm volatile("" : "+v"(planes[q][i / 32]));   // materialise the bit now
+      }
       v[i] = v[i] - s_cent[idx];
       g2 = fmaf(v[i], v[i], g2);
     }
+    if (LPT == 2) {
+      const float o = swap_half_f(g2);
+      g2 = hv ? (o + g2) : (g2 + o);
+    }
     const float gamma = sqrtf(g2);
 
-    // (a5) QJL sign bits sigma_j = [ (S r)_j >= 0 ]
-    uint32_t sig[NW];
-    qjl_signs<D>(p.sketch, v, sig);
+    // (a5) QJL sign bits sigma_j = [ (S r)_j >= 0 ], on the matrix cores
+    uint32_t sig[D / 32];
+    qjl_signs_mfma<D>(s_sk, v, sig);
 
     if (active) {
-      // (a6) record: W index planes then the sign plane, D/8 bytes each
+      // (a6) record: W index planes then the sign plane, D/8 bytes each;
+      // this lane writes bytes [8 hv, 8 hv + 8) of every plane
       constexpr int REC = (W + 1) * D / 8;
-      uint8_t *rec = static_cast<uint8_t *>(p.codes) + (seq * p.cap + pos) * REC;
-      if (NW == 4) {
+      constexpr int PB = D / 8;
+      uint8_t *rec = static_cast<uint8_t *>(p.codes) + (seq * p.cap + pos) * REC + 8 * hv;
 #pragma unroll
-        for (int q = 0; q < W; ++q)
-          *reinterpret_cast<uint4 *>(rec + q * 16) = make_uint4(planes[q][0], planes[q][1], planes[q][2], planes[q][3]);
-        *reinterpret_cast<uint4 *>(rec + W * 16) = make_uint4(sig[0], sig[1], sig[2], sig[3]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < W; ++q)
-          *reinterpret_cast<uint2 *>(rec + q * 8) = make_uint2(planes[q][0], planes[q][1]);
-        *reinterpret_cast<uint2 *>(rec + W * 8) = make_uint2(sig[0], sig[1]);
+      for (int q = 0; q < W; ++q)
+        *reinterpret_cast<uint2 *>(rec + q * PB) = make_uint2(planes[q][0], planes[q][1]);
+      *reinterpret_cast<uint2 *>(rec + W * PB) = make_uint2(sig[2 * hv], sig[2 * hv + 1]);
+      if (hv == 0) {
+        const uint32_t sc = static_cast<uint32_t>(float_to_f16_bits(n)) |
+                            (static_cast<uint32_t>(float_to_f16_bits(gamma)) << 16);
+        reinterpret_cast<uint32_t *>(p.scalars)[seq * p.cap + pos] = sc;
       }
-      const uint32_t sc = static_cast<uint32_t>(float_to_f16_bits(n)) |
-                          (static_cast<uint32_t>(float_to_f16_bits(gamma)) << 16);
-      reinterpret_cast<uint32_t *>(p.scalars)[seq * p.cap + pos] = sc;
     }
   } else {
-    // values: one ballot per (plane, coordinate) gives the 64 token bits
-    constexpr int CPL = (D + kWave - 1) / kWave;   // coordinates owned per lane
-    uint32_t lo[W][CPL], hi[W][CPL];
+    // values: the ballot of coordinate slot c gives 64 token bits; lane c
+    // keeps them (lo: bits 0-31, hi: bits 32-63)
+    uint32_t lo[W], hi[W];
 #pragma unroll
-    for (int q = 0; q < W; ++q)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) { lo[q][c] = 0u; hi[q][c] = 0u; }
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      int idx = 0;
-#pragma unroll
-      for (int j = 0; j < L - 1; ++j) idx += (v[i] >= th[j]) ? 1 : 0;
+    for (int q = 0; q < W; ++q) { lo[q] = 0u; hi[q] = 0u; }
+    static_for<0, C>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int idx = quantize<W>(v[i], th, s_th);
 #pragma unroll
       for (int q = 0; q < W; ++q) {
         const uint64_t m = __ballot(active && ((idx >> q) & 1));
-        if (lane == (i % kWave)) {
-          lo[q][i / kWave] = static_cast<uint32_t>(m);
-          hi[q][i / kWave] = static_cast<uint32_t>(m >> 32);
-        }
+        write_lane<i>(lo[q], static_cast<uint32_t>(m));
+        write_lane<i>(hi[q], static_cast<uint32_t>(m >> 32));
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
     const uint64_t valid = __ballot(active);
-    const uint32_t vlo = static_cast<uint32_t>(valid);
-    const uint32_t vhi = static_cast<uint32_t>(valid >> 32);
     const int64_t nblk = p.cap / kValueBlock;
     uint32_t *words = static_cast<uint32_t *>(p.codes);
+    // d = 64: lo -> block 2g, hi -> block 2g + 1 (coordinate = lane)
+    // d = 128: both -> block g; lo -> coordinate lane, hi -> coordinate 64 + lane
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const uint32_t vm = half ? vhi : vlo;
+      const uint32_t vm = LPT == 2 ? static_cast<uint32_t>(valid) : static_cast<uint32_t>(valid >> (32 * half));
       if (vm == 0u) continue;
-      const int64_t blk = 2 * g + half;
-      uint32_t *base = words + (seq * nblk + blk) * W * D;
+      const int64_t blk = LPT == 2 ? g : 2 * g + half;
+      const int coord = LPT == 2 ? 64 * half + lane : lane;
+      uint32_t *base = words + (seq * nblk + blk) * W * D + coord;
 #pragma unroll
-      for (int q = 0; q < W; ++q)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int i = c * kWave + lane;
-          if (i < D) {
-            uint32_t w = half ? hi[q][c] : lo[q][c];
-            uint32_t *dst = base + q * D + i;
-            if (vm != 0xffffffffu) w = (*dst & ~vm) | (w & vm);
-            *dst = w;
-          }
-        }
+      for (int q = 0; q < W; ++q) {
+        uint32_t w = half ? hi[q] : lo[q];
+        uint32_t *dst = base + q * D;
+        if (vm != 0xffffffffu) w = (*dst & ~vm) | (w & vm);
+        *dst = w;
+      }
     }
-    if (active) p.scalars[seq * p.cap + pos] = float_to_f16_bits(n);
+    if (active && hv == 0) p.scalars[seq * p.cap + pos] = float_to_f16_bits(n);
   }
 }
 

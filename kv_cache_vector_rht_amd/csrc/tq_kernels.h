@@ -10,7 +10,7 @@ struct EncodeParams {
   const void *x;
   int64_t x_seq_stride, x_tok_stride;   // elements
   int64_t n_tok, t0, cap;
-  int64_t g0;                           // first 64-slot group touched
+  int64_t g0;                           // first slot group touched (64 or 32 slots)
   int64_t groups_per_seq;
   int64_t n_waves;                      // n_seq * groups_per_seq
   int xt;                               // 0 f32, 1 bf16, 2 f16

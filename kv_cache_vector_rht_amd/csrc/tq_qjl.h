@@ -1,34 +1,149 @@
-// QJL projection of a key residual: sigma_j = [ (S r)_j >= 0 ], j < D.
-// "TurboQuantとは？仕組み・実測精度・2026年7月時点の実装状況", section 第2段:
-// the 1-bit sign of a Johnson-Lindenstrauss random projection of the
-// residual. S is fp16 [D][D], row j = projection direction j.
+// QJL projection of key residuals on the matrix cores:
+//   sigma_j = [ (S r)_j >= 0 ],  j < D,
+// the 1-bit sign of a Johnson-Lindenstrauss projection of the residual
+// ("TurboQuantとは？仕組み・実測精度・2026年7月時点の実装状況", 第2段).
+//
+// Z^T = S R^T is computed with v_mfma_f32_32x32x16_f16: A = a 32x16 tile
+// of S (fp16, exact as stored), B = a 16x32 tile of R^T (one column per
+// token). Each residual is pre-scaled by 2^10
+// (exact) and split as r = hi + lo in fp16 (22 significant bits; the scaling
+// keeps lo out of the fp16 subnormal range), so two MFMAs with fp32
+// accumulation give the projection to about 2^-22 relative, far inside the
+// 1e-6 decision margin. The signs come back per token: the C tile holds, in
+// lane l, column l%32 (a token) and 16 of the 32 rows (projection indices);
+// a lane swap merges the two halves into the token's 32-bit word.
 #pragma once
 
 #include "tq_device.h"
 
 namespace tq {
 
-// Per-lane fp32 dot products, S rows read with wave-uniform addresses.
-// r: the lane's residual (registers); sig: D/32 words, bit j%32 of word j/32.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16f mfma_f16_32x32x16(const v8h &a, const v8h &b, const v16f &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+union V8H {
+  v8h h;
+  uint32_t u[4];
+};
+
+// Swap the upper half-wave of x with the lower half-wave of y (both 4 dwords).
+__device__ __forceinline__ void swap_halves(V8H &x, V8H &y) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    auto r = __builtin_amdgcn_permlane32_swap(x.u[k], y.u[k], false, false);
+    x.u[k] = r[0];
+    y.u[k] = r[1];
+  }
+}
+
+// Stage the fp16 sketch [D][D] in LDS with rows padded by 8 halves.
 template <int D>
-__device__ __forceinline__ void qjl_signs(const uint16_t *__restrict__ sketch, const float (&r)[D],
-                                          uint32_t (&sig)[D / 32]) {
+__device__ __forceinline__ void stage_sketch(const uint16_t *__restrict__ sketch, uint16_t *s_sk) {
+  constexpr int RP = D + 8;
+  for (int e = threadIdx.x; e < D * D / 8; e += blockDim.x) {
+    const int row = e / (D / 8), c8 = e % (D / 8);
+    const uint4 v = reinterpret_cast<const uint4 *>(sketch)[e];
+    *reinterpret_cast<uint4 *>(s_sk + row * RP + c8 * 8) = v;
+  }
+}
+
+// r: this lane's 64 residual coordinates (consumed); sig: the D/32 sign
+// words of this lane's token.
+//  d = 64  (one lane per token, 64 tokens): two 32-token N tiles; the
+//          lane-swap supplies the other half-wave's coordinates.
+//  d = 128 (lanes t, t+32 hold coordinates [0,64), [64,128) of token t):
+//          K slot (ks, half-wave hv, e) is coordinate 64 hv + 8 ks + e, so
+//          every lane feeds its own coordinates; one 32-token N tile.
+template <int D>
+__device__ __forceinline__ void qjl_signs_mfma(const uint16_t *s_sk, float (&r)[64], uint32_t (&sig)[D / 32]) {
+  constexpr int RP = D + 8;
+  const int lane = lane_id();
+  const int hw = lane / 32;
+  if constexpr (D == 128) {
+    constexpr int KS = 8;
+    V8H bh[KS], bl[KS];
 #pragma unroll
-  for (int jw = 0; jw < D / 32; ++jw) {
-    uint32_t word = 0u;
-    for (int jb = 0; jb < 32; ++jb) {
-      const int j = jw * 32 + jb;
-      const uint32_t *row = reinterpret_cast<const uint32_t *>(sketch + static_cast<int64_t>(j) * D);
-      float z = 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int k = 0; k < D; k += 2) {
-        const uint32_t two = row[k / 2];
-        z = fmaf(f16_bits_to_float(static_cast<uint16_t>(two & 0xffffu)), r[k], z);
-        z = fmaf(f16_bits_to_float(static_cast<uint16_t>(two >> 16)), r[k + 1], z);
+      for (int e = 0; e < 8; ++e) {
+        const float a = r[8 * ks + e] * 1024.0f;
+        const _Float16 ah = static_cast<_Float16>(a);
+        bh[ks].h[e] = ah;
+        bl[ks].h[e] = static_cast<_Float16>(a - static_cast<float>(ah));
       }
-      word |= static_cast<uint32_t>(z >= 0.f) << jb;
     }
-    sig[jw] = word;
+#pragma unroll
+    for (int jt = 0; jt < D / 32; ++jt) {
+      v16f c = {};
+      const uint16_t *arow = s_sk + (jt * 32 + (lane % 32)) * RP + 64 * hw;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        V8H a;
+        const uint4 u = *reinterpret_cast<const uint4 *>(arow + 8 * ks);
+        a.u[0] = u.x; a.u[1] = u.y; a.u[2] = u.z; a.u[3] = u.w;
+        c = mfma_f16_32x32x16(a.h, bh[ks].h, c);
+        c = mfma_f16_32x32x16(a.h, bl[ks].h, c);
+      }
+      // lane l holds rows 8(q/4) + 4 hw + q%4 of column l%32
+      uint32_t pw = 0u;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) pw |= static_cast<uint32_t>(c[q] >= 0.f) << (8 * (q / 4) + (q % 4));
+      pw <<= 4 * hw;
+      auto m = __builtin_amdgcn_permlane32_swap(pw, pw, false, false);
+      sig[jt] = pw | (hw ? m[0] : m[1]);
+    }
+  } else {
+    constexpr int KS = D / 16;
+    V8H bh0[KS], bl0[KS], bh1[KS], bl1[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      V8H xh, xl, yh, yl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = r[16 * ks + e] * 1024.0f;
+        const float b = r[16 * ks + 8 + e] * 1024.0f;
+        const _Float16 ah = static_cast<_Float16>(a);
+        const _Float16 bh = static_cast<_Float16>(b);
+        xh.h[e] = ah;
+        xl.h[e] = static_cast<_Float16>(a - static_cast<float>(ah));
+        yh.h[e] = bh;
+        yl.h[e] = static_cast<_Float16>(b - static_cast<float>(bh));
+      }
+      swap_halves(xh, yh);
+      swap_halves(xl, yl);
+      bh0[ks] = xh; bl0[ks] = xl;      // tokens 0..31 of the wave
+      bh1[ks] = yh; bl1[ks] = yl;      // tokens 32..63
+    }
+#pragma unroll
+    for (int jt = 0; jt < D / 32; ++jt) {
+      v16f c0 = {}, c1 = {};
+      const uint16_t *arow = s_sk + (jt * 32 + (lane % 32)) * RP + 8 * hw;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        V8H a;
+        const uint4 u = *reinterpret_cast<const uint4 *>(arow + 16 * ks);
+        a.u[0] = u.x; a.u[1] = u.y; a.u[2] = u.z; a.u[3] = u.w;
+        c0 = mfma_f16_32x32x16(a.h, bh0[ks].h, c0);
+        c0 = mfma_f16_32x32x16(a.h, bl0[ks].h, c0);
+        c1 = mfma_f16_32x32x16(a.h, bh1[ks].h, c1);
+        c1 = mfma_f16_32x32x16(a.h, bl1[ks].h, c1);
+      }
+      uint32_t p0 = 0u, p1 = 0u;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int bit = 8 * (q / 4) + (q % 4);
+        p0 |= static_cast<uint32_t>(c0[q] >= 0.f) << bit;
+        p1 |= static_cast<uint32_t>(c1[q] >= 0.f) << bit;
+      }
+      p0 <<= 4 * hw;
+      p1 <<= 4 * hw;
+      auto m = __builtin_amdgcn_permlane32_swap(p0, p1, false, false);
+      sig[jt] = m[0] | m[1];
+    }
   }
 }
 
