@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <vector>
 
 #include "../../include/tq.h"
@@ -65,17 +66,15 @@ tq_status check_codec(const tq_codec *c, int need_key, const char *name) {
   return TQ_OK;
 }
 
-// Decode split size: a multiple of 64 tokens, small enough that the grid
-// fills the chip and the block's LDS stays under 64 KiB.
-int choose_split(int32_t batch, int32_t n_kv, int32_t group, int64_t max_ctx, int d) {
-  int split = 512;
-  while (split > 64) {
-    const int64_t n_splits = (max_ctx + split - 1) / split;
-    if (static_cast<int64_t>(batch) * n_kv * n_splits >= 1024) break;
-    split /= 2;
-  }
-  while (split > 64 && tq::decode_split_smem(d, group, split) > 65536) split /= 2;
-  return split;
+// Decode blocks per (batch, kv-head) group: each block walks every
+// blocks-th split of kDecodeSplit tokens. One block fills a CU's LDS, so
+// aim for one block per CU (256), at most kDecodeMaxBlocks per group and
+// never more than the context has splits.
+int decode_blocks_per_group(int32_t batch, int32_t n_kv, int64_t max_ctx) {
+  const int64_t groups = std::max<int64_t>(1, static_cast<int64_t>(batch) * n_kv);
+  const int64_t splits = std::max<int64_t>(1, (max_ctx + tq::kDecodeSplit - 1) / tq::kDecodeSplit);
+  const int64_t want = std::min<int64_t>(tq::kDecodeMaxBlocks, std::max<int64_t>(1, (256 + groups - 1) / groups));
+  return static_cast<int>(std::min<int64_t>(splits, want));
 }
 
 // Workspace bytes of the prepared queries (sized for the widest key codec).
@@ -231,11 +230,10 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
 
 size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int64_t max_ctx, int32_t d) {
   if (batch < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
-  const int split = choose_split(batch, n_kv_heads, group, max_ctx, d);
-  const int64_t n_splits = (max_ctx + split - 1) / split;
-  const size_t pbytes =
-      align_up(static_cast<size_t>(batch) * n_kv_heads * (n_splits > 0 ? n_splits : 1) * group * (d + 2) * sizeof(float));
-  return qprep_bytes(batch, n_kv_heads, group, d) + pbytes;
+  const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx);
+  const size_t pbytes = align_up(static_cast<size_t>(batch) * n_kv_heads * nb * group * (d + 2) * sizeof(float));
+  const size_t cbytes = align_up(static_cast<size_t>(batch) * n_kv_heads * ((group + 7) / 8) * sizeof(int32_t));
+  return qprep_bytes(batch, n_kv_heads, group, d) + pbytes + cbytes;
 }
 
 tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
@@ -262,13 +260,13 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   const size_t need = tq_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, kc->d);
   if (ws_bytes < need) return fail(TQ_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TQ_EINVAL, "%s: workspace not 256-byte aligned", fn);
-  if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 4 ||
-      reinterpret_cast<uintptr_t>(vcodes) % 4 || reinterpret_cast<uintptr_t>(vscalars) % 2)
-    return fail(TQ_EINVAL, "%s: misaligned cache pointer", fn);
+  if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 16 ||
+      reinterpret_cast<uintptr_t>(vcodes) % 16 || reinterpret_cast<uintptr_t>(vscalars) % 16)
+    return fail(TQ_EINVAL, "%s: cache arrays must be 16-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int d = kc->d;
-  const int split = choose_split(batch, n_kv_heads, group, max_ctx, d);
-  const int64_t n_splits64 = max_ctx > 0 ? (max_ctx + split - 1) / split : 1;
+  const int split = tq::kDecodeSplit;
+  const int64_t n_splits64 = decode_blocks_per_group(batch, n_kv_heads, max_ctx);
   tq::QueryPrepParams qp{};
   qp.q = q;
   qp.xt = static_cast<int>(qt);
@@ -281,7 +279,13 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   qp.sketch = kc->sketch;
   qp.out = static_cast<uint8_t *>(workspace);
   qp.group_bytes = tq::qprep_group_bytes(d, kc->lm_bits, group);
+  const int n_hchunks = (group + 7) / 8;
+  const size_t pbytes =
+      align_up(static_cast<size_t>(batch) * n_kv_heads * n_splits64 * group * (d + 2) * sizeof(float));
   float *partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + qprep_bytes(batch, n_kv_heads, group, d));
+  int32_t *counters = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(partials) + pbytes);
+  qp.counters = counters;
+  qp.n_hchunks = n_hchunks;
   hipError_t e = d == 64 ? tq::launch_query_prep_d<64>(qp, st) : tq::launch_query_prep_d<128>(qp, st);
   if (e != hipSuccess) return hip_status(e, fn);
   tq::DecodeParams dp{};
@@ -304,6 +308,9 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   dp.n_splits = static_cast<int32_t>(n_splits64);
   dp.sm_scale = sm_scale;
   dp.partials = partials;
+  dp.counters = counters;
+  dp.n_hchunks = n_hchunks;
+  dp.h0 = 0;
   dp.out = out;
   dp.out_t = static_cast<int>(out_t);
   e = d == 64 ? tq::launch_decode_d<64>(dp, kc->lm_bits, vc->lm_bits, st)

@@ -35,6 +35,8 @@ struct QueryPrepParams {
   const uint16_t *sketch;
   uint8_t *out;                         // [batch*n_kv][group_bytes]
   size_t group_bytes;
+  int32_t *counters;                    // decode merge counters to zero (or null)
+  int32_t n_hchunks;
 };
 
 template <int D>
@@ -64,10 +66,13 @@ struct DecodeParams {
   int64_t cap, max_ctx;
   const int32_t *ctx_lens;
   int32_t batch, n_kv, group;
-  int32_t split;                        // tokens per context split (multiple of 64)
-  int32_t n_splits;
+  int32_t h0;                           // first head of this launch's head chunk (multiple of 8)
+  int32_t n_hchunks;                    // ceil(group / 8)
+  int32_t split;                        // tokens per context split (kDecodeSplit)
+  int32_t n_splits;                     // blocks per (batch, kv-head) group
   float sm_scale;
-  float *partials;                      // [batch*n_kv][n_splits][group][D+2]
+  float *partials;                      // [batch*n_kv][blocks per group][group][D+2]
+  int32_t *counters;                    // [batch*n_kv][n_hchunks], zero on entry
   void *out;
   int out_t;
 };
@@ -75,14 +80,9 @@ struct DecodeParams {
 template <int D>
 hipError_t launch_decode_d(const DecodeParams &p, int kw, int vw, hipStream_t st);
 
-// LDS bytes of one decode-split block: scaled logits / weights [G][split],
-// value norms [split], value-weight MFMA operands [ceil(G/4)][split/64][1 KiB],
-// per-head statistics.
-inline size_t decode_split_smem(int d, int group, int split) {
-  (void)d;
-  const size_t rg = (group + 3) / 4;
-  return static_cast<size_t>(group) * split * 4 + static_cast<size_t>(split) * 4 +
-         rg * (split / 64) * 1024 + static_cast<size_t>(group) * 32 + 64;
-}
+// Tokens per split of the decode kernel (one pipeline stage), and the most
+// blocks one (batch, kv-head) group is spread over.
+constexpr int kDecodeSplit = 256;
+constexpr int kDecodeMaxBlocks = 128;
 
 }  // namespace tq

@@ -40,14 +40,20 @@ __device__ __forceinline__ void swap_halves(V8H &x, V8H &y) {
   }
 }
 
-// Stage the fp16 sketch [D][D] in LDS with rows padded by 8 halves.
+// Stage the fp16 sketch [D][D] in LDS with rows padded by 8 halves. The
+// block has 256 threads; all loads are issued before the first store.
 template <int D>
 __device__ __forceinline__ void stage_sketch(const uint16_t *__restrict__ sketch, uint16_t *s_sk) {
   constexpr int RP = D + 8;
-  for (int e = threadIdx.x; e < D * D / 8; e += blockDim.x) {
+  constexpr int N = D * D / 8 / 256;         // 16-byte pieces per thread (8 or 2)
+  uint4 v[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = reinterpret_cast<const uint4 *>(sketch)[k * 256 + threadIdx.x];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int e = k * 256 + threadIdx.x;
     const int row = e / (D / 8), c8 = e % (D / 8);
-    const uint4 v = reinterpret_cast<const uint4 *>(sketch)[e];
-    *reinterpret_cast<uint4 *>(s_sk + row * RP + c8 * 8) = v;
+    *reinterpret_cast<uint4 *>(s_sk + row * RP + c8 * 8) = v[k];
   }
 }
 
