@@ -232,8 +232,7 @@ size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t gro
   if (batch < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
   const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx);
   const size_t pbytes = align_up(static_cast<size_t>(batch) * n_kv_heads * nb * group * (d + 2) * sizeof(float));
-  const size_t cbytes = align_up(static_cast<size_t>(batch) * n_kv_heads * ((group + 7) / 8) * sizeof(int32_t));
-  return qprep_bytes(batch, n_kv_heads, group, d) + pbytes + cbytes;
+  return qprep_bytes(batch, n_kv_heads, group, d) + pbytes;
 }
 
 tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
@@ -280,12 +279,7 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   qp.out = static_cast<uint8_t *>(workspace);
   qp.group_bytes = tq::qprep_group_bytes(d, kc->lm_bits, group);
   const int n_hchunks = (group + 7) / 8;
-  const size_t pbytes =
-      align_up(static_cast<size_t>(batch) * n_kv_heads * n_splits64 * group * (d + 2) * sizeof(float));
   float *partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + qprep_bytes(batch, n_kv_heads, group, d));
-  int32_t *counters = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(partials) + pbytes);
-  qp.counters = counters;
-  qp.n_hchunks = n_hchunks;
   hipError_t e = d == 64 ? tq::launch_query_prep_d<64>(qp, st) : tq::launch_query_prep_d<128>(qp, st);
   if (e != hipSuccess) return hip_status(e, fn);
   tq::DecodeParams dp{};
@@ -308,7 +302,6 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   dp.n_splits = static_cast<int32_t>(n_splits64);
   dp.sm_scale = sm_scale;
   dp.partials = partials;
-  dp.counters = counters;
   dp.n_hchunks = n_hchunks;
   dp.h0 = 0;
   dp.out = out;

@@ -156,7 +156,6 @@ __global__ __launch_bounds__(256) void query_prep_kernel(QueryPrepParams p) {
         *reinterpret_cast<uint4 *>(dst + (static_cast<size_t>(rg * NMF + mf) * kWave + l) * 16) = make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  if (tid == 0 && p.counters != nullptr && h % 8 == 0) p.counters[grp * p.n_hchunks + h / 8] = 0;
   if (tid == 0) {
     float *fl = reinterpret_cast<float *>(dst + qprep_frag_bytes(D, p.kw, G)) + 4 * h;
     fl[0] = ldexpf(1.0f, -7 - el);
@@ -516,9 +515,8 @@ __device__ __forceinline__ double sum16d(double v) {
 //     matrix cores (int32 over the split) and folds the result into its
 //     fp32 accumulators: acc = alpha acc + split sum
 //  4. refills the stage buffer with the split kStages ahead.
-// The block's partial {m, l, acc} goes to the workspace; the last block of
-// the (batch, kv-head, head chunk) to finish merges them (log-sum-exp
-// weights), rotates back with R_v^T and writes the output rows.
+// The block's partial {m, l, acc} goes to the workspace; merge_kernel
+// combines them.
 template <int D, int KW, int VW, int NRG>
 __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 D = (D / 16) waves
   using SH = DecodeShape<D, KW, VW>;
@@ -534,10 +532,7 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
   __shared__ float spm[NW][GMAX];
   __shared__ float spnv[NW];
   __shared__ double spsw[NW][GMAX];
-  __shared__ int sflag;
   __shared__ float svb[NBV];
-  static_assert(SH::STAGE_BYTES >= (4 * NRG * D + 4 * NRG * kDecodeMaxBlocks + 4 * NRG) * 4,
-                "the final merge reuses a stage buffer");
 
   const int G = p.group;
   const int n_q = p.n_kv * G;
@@ -787,66 +782,69 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
       }
     }
   }
+}
 
-  // the last block of this (batch, kv-head, head chunk) merges the partials
-  __threadfence();
-  __syncthreads();
-  int32_t *counter = p.counters + bh * p.n_hchunks + p.h0 / 8;
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    sflag = (prev == nb - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (sflag == 0) return;
-  __threadfence();
-  float *ob = reinterpret_cast<float *>(st0);                // [GMAX][D]
-  float *se = ob + GMAX * D;                                  // [GMAX][nb] merge weights
-  float *sL = se + GMAX * nb;                                 // [GMAX]
+// Merge of the split partials of one (batch, kv-head) group and head chunk
+// (8 heads): log-sum-exp weights over the blocks, division by the softmax
+// sum, inverse rotation out = diag(s_v) H acc / sqrt(D), store. A kernel of
+// its own: the partials are visible to it without any device-wide fence.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
+  __shared__ float ob[8][D];
+  __shared__ float se[8][kDecodeMaxBlocks];
+  __shared__ float sL[8];
+  const int G = p.group;
+  const int n_q = p.n_kv * G;
+  const int h0 = 8 * blockIdx.x;
+  const int GE = min(8, G - h0);
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / p.n_kv;
+  const int64_t kvh = bh % p.n_kv;
+  const int nb = p.n_splits;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const float *pbase = p.partials + bh * nb * G * (D + 2);
   const int64_t pstride = static_cast<int64_t>(G) * (D + 2);
-  for (int hl = wave; hl < GE; hl += NW) {
+  for (int hl = wave; hl < GE; hl += 4) {
     float M = -INFINITY;
-    for (int j = lane; j < nb; j += kWave) M = fmaxf(M, pbase[j * pstride + (p.h0 + hl) * (D + 2)]);
+    for (int j = lane; j < nb; j += kWave) M = fmaxf(M, pbase[j * pstride + (h0 + hl) * (D + 2)]);
     M = wave_max(M);
     float L = 0.f;
     for (int j = lane; j < nb; j += kWave) {
-      const float m = pbase[j * pstride + (p.h0 + hl) * (D + 2)];
+      const float m = pbase[j * pstride + (h0 + hl) * (D + 2)];
       const float e = (m == -INFINITY) ? 0.f : __expf(m - M);
-      se[hl * nb + j] = e;
-      L = fmaf(pbase[j * pstride + (p.h0 + hl) * (D + 2) + 1], e, L);
+      se[hl][j] = e;
+      L = fmaf(pbase[j * pstride + (h0 + hl) * (D + 2) + 1], e, L);
     }
     L = wave_sum(L);
     if (lane == 0) sL[hl] = L;
   }
   __syncthreads();
-  for (int e = tid; e < GE * D; e += SH::THREADS) {
+  for (int e = tid; e < GE * D; e += 256) {
     const int hl = e / D, i = e % D;
     float acc = 0.f;
-    for (int j = 0; j < nb; ++j) acc = fmaf(pbase[j * pstride + (p.h0 + hl) * (D + 2) + 2 + i], se[hl * nb + j], acc);
-    ob[e] = (sL[hl] > 0.f) ? acc / sL[hl] : 0.f;
+    for (int j = 0; j < nb; ++j) acc = fmaf(pbase[j * pstride + (h0 + hl) * (D + 2) + 2 + i], se[hl][j], acc);
+    ob[hl][i] = (sL[hl] > 0.f) ? acc / sL[hl] : 0.f;
   }
   __syncthreads();
-  // inverse rotation of every head: out = diag(s_v) H acc / sqrt(D)
   for (int hs = 1; hs < D; hs <<= 1) {
-    for (int e = tid; e < GE * D / 2; e += SH::THREADS) {
+    for (int e = tid; e < GE * D / 2; e += 256) {
       const int hl = e / (D / 2);
       const int r = e % (D / 2);
       const int j = (r / hs) * 2 * hs + (r % hs);
-      const float x = ob[hl * D + j];
-      const float y = ob[hl * D + j + hs];
-      ob[hl * D + j] = x + y;
-      ob[hl * D + j + hs] = x - y;
+      const float x = ob[hl][j];
+      const float y = ob[hl][j + hs];
+      ob[hl][j] = x + y;
+      ob[hl][j + hs] = x - y;
     }
     __syncthreads();
   }
-  for (int e = tid; e < GE * D; e += SH::THREADS) {
+  for (int e = tid; e < GE * D; e += 256) {
     const int hl = e / D, j = e % D;
-    const float o = ob[e] * p.vsigns[j] * (1.0f / sqrtf(static_cast<float>(D)));
-    const int64_t row = b * n_q + kvh * G + p.h0 + hl;
+    const float o = ob[hl][j] * p.vsigns[j] * (1.0f / sqrtf(static_cast<float>(D)));
+    const int64_t row = b * n_q + kvh * G + h0 + hl;
     if (p.out_t == 0) static_cast<float *>(p.out)[row * D + j] = o;
     else static_cast<uint16_t *>(p.out)[row * D + j] = float_to_bf16_bits(o);
   }
-  if (tid == 0) *counter = 0;
 }
 
 template <int D, int KW, int VW>
@@ -881,7 +879,8 @@ hipError_t launch_decode_d(const DecodeParams &p0, int kw, int vw, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(static_cast<uint32_t>(p0.n_hchunks), grid.y), dim3(256), 0, st, p0);
+  return hipGetLastError();
 }
 
 }  // namespace tq

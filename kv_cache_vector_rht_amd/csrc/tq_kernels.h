@@ -35,8 +35,6 @@ struct QueryPrepParams {
   const uint16_t *sketch;
   uint8_t *out;                         // [batch*n_kv][group_bytes]
   size_t group_bytes;
-  int32_t *counters;                    // decode merge counters to zero (or null)
-  int32_t n_hchunks;
 };
 
 template <int D>
@@ -72,7 +70,6 @@ struct DecodeParams {
   int32_t n_splits;                     // blocks per (batch, kv-head) group
   float sm_scale;
   float *partials;                      // [batch*n_kv][blocks per group][group][D+2]
-  int32_t *counters;                    // [batch*n_kv][n_hchunks], zero on entry
   void *out;
   int out_t;
 };
