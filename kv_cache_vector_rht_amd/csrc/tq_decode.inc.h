@@ -482,23 +482,6 @@ __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t
   }
 }
 
-// Max / sum over the 16 lanes that share lane / 16.
-__device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-__device__ __forceinline__ double sum16d(double v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
 // One block per (batch*kv-head, block index within the group) and the heads
 // [h0, h0 + GE) of the group, GE <= 4 NRG. The block walks the splits
 // blockIdx.x, blockIdx.x + gridDim.x, ... (kDecodeSplit tokens each)
@@ -626,16 +609,19 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
       v4i clm[NRG], cqj[NRG];
       key_tile_mfma<D, KW, NRG>(kt, a, mask, NRG, clm, cqj);
       const bool valid = tl < n;
+      const float kn = kt.norm(), kgm = kt.gamma();
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
-        lg[u][rg] = valid ? tile_logit(clm[rg], cqj[rg], fh[rg], kt.norm(), kt.gamma(), kappa) * p.sm_scale : -INFINITY;
+        const float l = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa) * p.sm_scale;
+        lg[u][rg] = valid ? l : -INFINITY;
         mx[rg] = fmaxf(mx[rg], lg[u][rg]);
       }
-      nvv[u] = valid ? f16_bits_to_float(nvb) : 0.f;
+      const float nvf = f16_bits_to_float(nvb);
+      nvv[u] = valid ? nvf : 0.f;
       nvm = fmaxf(nvm, nvv[u]);
     }
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) mx[rg] = max16(mx[rg]);
+    for (int rg = 0; rg < NRG; ++rg) mx[rg] = row_max16(mx[rg]);
     nvm = wave_max(nvm);
     if (col == 0) {
 #pragma unroll
@@ -684,7 +670,7 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
     }
 #pragma unroll
     for (int rg = 0; rg < NRG; ++rg) {
-      const double t = sum16d(sw[rg]);
+      const double t = row_sum16d(sw[rg]);
       if (col == 0) spsw[wave][4 * rg + kg] = t;
     }
     lds_barrier();
@@ -760,7 +746,7 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
   // partial of this block: {m, l, acc[D]} per head of the chunk
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
-    const float l = sum16(l_run[rg]);
+    const float l = row_sum16(l_run[rg]);
     if (col == 0) spm[wave][4 * rg + kg] = l;
   }
   __syncthreads();
@@ -821,8 +807,17 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   __syncthreads();
   for (int e = tid; e < GE * D; e += 256) {
     const int hl = e / D, i = e % D;
+    const float *src = pbase + (h0 + hl) * (D + 2) + 2 + i;
     float acc = 0.f;
-    for (int j = 0; j < nb; ++j) acc = fmaf(pbase[j * pstride + (h0 + hl) * (D + 2) + 2 + i], se[hl][j], acc);
+    int j = 0;
+    for (; j + 8 <= nb; j += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = src[(j + k) * pstride];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc = fmaf(v[k], se[hl][j + k], acc);
+    }
+    for (; j < nb; ++j) acc = fmaf(src[j * pstride], se[hl][j], acc);
     ob[hl][i] = (sL[hl] > 0.f) ? acc / sL[hl] : 0.f;
   }
   __syncthreads();

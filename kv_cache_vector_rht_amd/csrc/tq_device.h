@@ -109,16 +109,61 @@ __device__ __forceinline__ void fwht_regs(float (&v)[D]) {
 
 // ------------------------------------------------------------------ reductions
 
+// Lane exchange inside rows of 16 lanes with DPP (no LDS round trip).
+// quad_perm [1,0,3,2] and [2,3,0,1], then rotations of the row by 4 and 8:
+// after the four steps every lane holds the reduction over its row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __uint_as_float(dpp_u<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t r = static_cast<uint64_t>(dpp_u<CTRL>(static_cast<uint32_t>(u))) |
+                     (static_cast<uint64_t>(dpp_u<CTRL>(static_cast<uint32_t>(u >> 32))) << 32);
+  return __builtin_bit_cast(double, r);
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  return fmaxf(v, dpp_f<0x128>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x124>(v);
+  return v + dpp_f<0x128>(v);
+}
+__device__ __forceinline__ double row_sum16d(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x124>(v);
+  return v + dpp_d<0x128>(v);
+}
+
+// Whole-wave reductions: rows by DPP, then the four row results.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  v = row_max16(v);
+  const float a = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+  const float b = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+  const float c = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32));
+  const float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v = row_sum16(v);
+  const float a = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+  const float b = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+  const float c = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32));
+  const float d = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
+  return (a + b) + (c + d);
 }
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
