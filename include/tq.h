@@ -139,9 +139,13 @@ tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_
  *   q' = R q, p = S q', n and gamma the stored fp16 norms.
  *   q        device [batch][n_kv_heads*group][d], dtype qt
  *   query head h of batch b reads key sequence b*n_kv_heads + h/group
- *   kcodes, kscalars  key cache (layout above) with `cap` slots per sequence
+ *   kcodes, kscalars  key cache (layout above) with `cap` slots per
+ *            sequence; cap a multiple of 32, both arrays 16-byte aligned,
+ *            one sequence's codes below 4 GiB (else TQ_EUNSUPPORTED)
  *   logits   device float [batch][n_kv_heads*group][n_keys] out
- *   workspace  device, >= tq_logits_workspace(...) bytes, 256-byte aligned
+ *   workspace  unused (tq_logits_workspace returns 0; may be NULL)
+ * Every block prepares its queries (q', p and their fixed-point operands)
+ * itself; no other state is read or written.
  */
 tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch,
                     int32_t n_kv_heads, int32_t group, const uint8_t *kcodes,
@@ -162,7 +166,10 @@ size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int
  *   out      device [batch][n_kv_heads*group][d], dtype out_t (TQ_F32 or
  *            TQ_BF16, round to nearest even)
  *   workspace  device, >= tq_decode_attend_workspace(...) bytes, 256-byte
- *            aligned
+ *            aligned: the per-split partial softmax states {m, l, acc[d]}
+ *            of every (batch, kv-head, block, head), overwritten by each call
+ * Cache arrays must be 16-byte aligned and one sequence's key or value codes
+ * below 4 GiB (else TQ_EUNSUPPORTED).
  */
 tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt,
                            int32_t batch, int32_t n_kv_heads, int32_t group,

@@ -77,9 +77,33 @@ int decode_blocks_per_group(int32_t batch, int32_t n_kv, int64_t max_ctx) {
   return static_cast<int>(std::min<int64_t>(splits, want));
 }
 
-// Workspace bytes of the prepared queries (sized for the widest key codec).
-size_t qprep_bytes(int32_t batch, int32_t n_kv, int32_t group, int d) {
-  return align_up(static_cast<size_t>(batch) * n_kv * tq::qprep_group_bytes(d, 4, group));
+// The scan kernels address one sequence's arrays with 32-bit offsets.
+bool seq_offsets_fit(int64_t cap, int bytes_per_token) {
+  return cap * static_cast<int64_t>(bytes_per_token) < (static_cast<int64_t>(1) << 32);
+}
+
+// Common part of the scan parameters (queries, key codec, key cache).
+tq::ScanParams scan_params(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
+                           int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap,
+                           int64_t max_ctx) {
+  tq::ScanParams sp{};
+  sp.q = q;
+  sp.xt = static_cast<int>(qt);
+  sp.ksigns = kc->signs;
+  sp.kcent = kc->centroids;
+  sp.sketch = kc->sketch;
+  sp.kcodes = kcodes;
+  sp.kscalars = kscalars;
+  sp.cap = cap;
+  sp.max_ctx = max_ctx;
+  sp.batch = batch;
+  sp.n_kv = n_kv_heads;
+  sp.group = group;
+  sp.h0 = 0;
+  sp.n_hchunks = (group + 7) / 8;
+  sp.nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx);
+  sp.sm_scale = 1.0f;
+  return sp;
 }
 
 }  // namespace
@@ -176,63 +200,39 @@ tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_
 }
 
 size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d) {
-  if (batch < 0 || n_kv_heads < 0 || group < 0 || d <= 0) return 0;
-  return qprep_bytes(batch, n_kv_heads, group, d);
+  (void)batch; (void)n_kv_heads; (void)group; (void)d;
+  return 0;   // the scan prepares the queries in LDS
 }
 
 tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
                     int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap, int64_t n_keys,
                     float *logits, void *workspace, size_t ws_bytes, void *stream) {
   const char *fn = "tq_logits";
+  (void)workspace; (void)ws_bytes;
   tq_status s = check_codec(kc, 1, fn);
   if (s != TQ_OK) return s;
   if (!dtype_ok(qt)) return fail(TQ_EINVAL, "%s: bad query dtype", fn);
   if (batch < 0 || n_kv_heads < 0 || group < 0 || n_keys < 0 || cap < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (n_keys > cap) return fail(TQ_EINVAL, "%s: n_keys > cap", fn);
+  if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!seq_offsets_fit(cap, (kc->lm_bits + 1) * kc->d / 8))
+    return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (batch == 0 || n_kv_heads == 0 || group == 0 || n_keys == 0) return ok();
-  if (!q || !kcodes || !kscalars || !logits || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
-  const size_t need = tq_logits_workspace(batch, n_kv_heads, group, kc->d);
-  if (ws_bytes < need) return fail(TQ_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TQ_EINVAL, "%s: workspace not 256-byte aligned", fn);
-  if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 4)
-    return fail(TQ_EINVAL, "%s: kcodes must be 16-byte and kscalars 4-byte aligned", fn);
+  if (!q || !kcodes || !kscalars || !logits) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 16)
+    return fail(TQ_EINVAL, "%s: kcodes and kscalars must be 16-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  tq::QueryPrepParams qp{};
-  qp.q = q;
-  qp.xt = static_cast<int>(qt);
-  qp.batch = batch;
-  qp.n_kv = n_kv_heads;
-  qp.group = group;
-  qp.kw = kc->lm_bits;
-  qp.signs = kc->signs;
-  qp.centroids = kc->centroids;
-  qp.sketch = kc->sketch;
-  qp.out = static_cast<uint8_t *>(workspace);
-  qp.group_bytes = tq::qprep_group_bytes(kc->d, kc->lm_bits, group);
-  hipError_t e = kc->d == 64 ? tq::launch_query_prep_d<64>(qp, st) : tq::launch_query_prep_d<128>(qp, st);
-  if (e != hipSuccess) return hip_status(e, fn);
-  tq::LogitsParams lp{};
-  lp.qprep = qp.out;
-  lp.group_bytes = qp.group_bytes;
-  lp.frag_bytes = tq::qprep_frag_bytes(kc->d, kc->lm_bits, group);
-  lp.kcodes = kcodes;
-  lp.kscalars = kscalars;
-  lp.cap = cap;
-  lp.n_keys = n_keys;
-  lp.batch = batch;
-  lp.n_kv = n_kv_heads;
-  lp.group = group;
-  lp.logits = logits;
-  e = kc->d == 64 ? tq::launch_logits_d<64>(lp, kc->lm_bits, st) : tq::launch_logits_d<128>(lp, kc->lm_bits, st);
+  tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys);
+  sp.logits = logits;
+  hipError_t e = kc->d == 64 ? tq::launch_logits_d<64>(sp, kc->lm_bits, st) : tq::launch_logits_d<128>(sp, kc->lm_bits, st);
   return hip_status(e, fn);
 }
 
 size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int64_t max_ctx, int32_t d) {
   if (batch < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
   const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx);
-  const size_t pbytes = align_up(static_cast<size_t>(batch) * n_kv_heads * nb * group * (d + 2) * sizeof(float));
-  return qprep_bytes(batch, n_kv_heads, group, d) + pbytes;
+  return align_up(static_cast<size_t>(batch) * n_kv_heads * nb * group * (d + 2) * sizeof(float));
 }
 
 tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
@@ -252,6 +252,8 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   if (max_ctx > cap) return fail(TQ_EINVAL, "%s: max_ctx > cap", fn);
   if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!seq_offsets_fit(cap, std::max((kc->lm_bits + 1) * kc->d / 8, vc->lm_bits * kc->d / 8)))
+    return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (!std::isfinite(sm_scale)) return fail(TQ_EINVAL, "%s: sm_scale is not finite", fn);
   if (batch == 0 || n_kv_heads == 0 || group == 0) return ok();
   if (!q || !out || !ctx_lens || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
@@ -263,51 +265,18 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
       reinterpret_cast<uintptr_t>(vcodes) % 16 || reinterpret_cast<uintptr_t>(vscalars) % 16)
     return fail(TQ_EINVAL, "%s: cache arrays must be 16-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int d = kc->d;
-  const int split = tq::kDecodeSplit;
-  const int64_t n_splits64 = decode_blocks_per_group(batch, n_kv_heads, max_ctx);
-  tq::QueryPrepParams qp{};
-  qp.q = q;
-  qp.xt = static_cast<int>(qt);
-  qp.batch = batch;
-  qp.n_kv = n_kv_heads;
-  qp.group = group;
-  qp.kw = kc->lm_bits;
-  qp.signs = kc->signs;
-  qp.centroids = kc->centroids;
-  qp.sketch = kc->sketch;
-  qp.out = static_cast<uint8_t *>(workspace);
-  qp.group_bytes = tq::qprep_group_bytes(d, kc->lm_bits, group);
-  const int n_hchunks = (group + 7) / 8;
-  float *partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + qprep_bytes(batch, n_kv_heads, group, d));
-  hipError_t e = d == 64 ? tq::launch_query_prep_d<64>(qp, st) : tq::launch_query_prep_d<128>(qp, st);
-  if (e != hipSuccess) return hip_status(e, fn);
-  tq::DecodeParams dp{};
-  dp.qprep = qp.out;
-  dp.group_bytes = qp.group_bytes;
-  dp.frag_bytes = tq::qprep_frag_bytes(d, kc->lm_bits, group);
-  dp.kcodes = kcodes;
-  dp.kscalars = kscalars;
-  dp.vcodes = vcodes;
-  dp.vscalars = vscalars;
-  dp.vcent = vc->centroids;
-  dp.vsigns = vc->signs;
-  dp.cap = cap;
-  dp.max_ctx = max_ctx;
-  dp.ctx_lens = ctx_lens;
-  dp.batch = batch;
-  dp.n_kv = n_kv_heads;
-  dp.group = group;
-  dp.split = split;
-  dp.n_splits = static_cast<int32_t>(n_splits64);
-  dp.sm_scale = sm_scale;
-  dp.partials = partials;
-  dp.n_hchunks = n_hchunks;
-  dp.h0 = 0;
-  dp.out = out;
-  dp.out_t = static_cast<int>(out_t);
-  e = d == 64 ? tq::launch_decode_d<64>(dp, kc->lm_bits, vc->lm_bits, st)
-              : tq::launch_decode_d<128>(dp, kc->lm_bits, vc->lm_bits, st);
+  tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, max_ctx);
+  sp.vcodes = vcodes;
+  sp.vscalars = vscalars;
+  sp.vcent = vc->centroids;
+  sp.vsigns = vc->signs;
+  sp.ctx_lens = ctx_lens;
+  sp.sm_scale = sm_scale;
+  sp.partials = static_cast<float *>(workspace);
+  sp.out = out;
+  sp.out_t = static_cast<int>(out_t);
+  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, kc->lm_bits, vc->lm_bits, st)
+                             : tq::launch_decode_d<128>(sp, kc->lm_bits, vc->lm_bits, st);
   return hip_status(e, fn);
 }
 

@@ -1,5 +1,6 @@
-// Query preparation, logit scan over packed keys, and split-context fused
-// decode attention over packed keys and values, on the matrix cores.
+// Logit scan over packed keys and split-context fused decode attention over
+// packed keys and values, on the matrix cores, with the query preparation
+// done by each block in its prologue.
 //
 // Estimator (pages: "TurboQuantとは？仕組み・実測精度・2026年7月時点の実装状況",
 // 第2段: the QJL residual bit makes the inner-product estimate unbiased; its
@@ -7,8 +8,9 @@
 //   logit(q, k) = n ( sum_i q'_i c[idx_i]
 //                     + sqrt(pi/2)/D * gamma * sum_j p_j (2 sigma_j - 1) ),
 // q' = R q, p = S q'. Both sums are bit-plane contractions (tq_mfma.h); the
-// query side is prepared once per (batch, kv-head) group, then every key
-// record is read once for all heads of its group.
+// query side of a (batch, kv-head) group is prepared by every block that
+// scans its keys, and every key record is read once for all heads of a
+// chunk of up to 8 heads.
 #pragma once
 
 #include "tq_device.h"
@@ -18,160 +20,6 @@
 namespace tq {
 
 constexpr float kSqrtHalfPi = 1.2533141373155002f;   // sqrt(pi / 2)
-
-// ------------------------------------------------------------------ query prep
-
-// One block (256 threads) per query head. The block stages the sketch in
-// LDS (coalesced), rotates its query, projects it, and writes the four
-// digit rows of its head into the group's MFMA operands.
-template <int D>
-__global__ __launch_bounds__(256) void query_prep_kernel(QueryPrepParams p) {
-  __shared__ uint32_t s_sk[D * D / 2];       // the sketch, fp16 pairs
-  __shared__ float sq[D], sp[D], sb[9], sred[8];
-  const int G = p.group;
-  const int n_q = p.n_kv * G;
-  const int64_t hq = blockIdx.x;             // global query-head index b * n_q + h
-  const int64_t b = hq / n_q;
-  const int hh = static_cast<int>(hq % n_q);
-  const int64_t grp = b * p.n_kv + hh / G;
-  const int h = hh % G;                      // head within the group
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = lane_id();
-
-  // issue the sketch and query loads first
-  {
-    constexpr int N = D * D / 8 / 256;
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.sketch);
-    uint4 v[N];
-#pragma unroll
-    for (int k = 0; k < N; ++k) v[k] = src[k * 256 + tid];
-#pragma unroll
-    for (int k = 0; k < N; ++k) reinterpret_cast<uint4 *>(s_sk)[k * 256 + tid] = v[k];
-  }
-  if (tid < D) {
-    float v;
-    if (p.xt == 0) v = static_cast<const float *>(p.q)[hq * D + tid];
-    else if (p.xt == 1) v = bf16_bits_to_float(static_cast<const uint16_t *>(p.q)[hq * D + tid]);
-    else v = f16_bits_to_float(static_cast<const uint16_t *>(p.q)[hq * D + tid]);
-    sq[tid] = v * p.signs[tid];
-  }
-  const int NB = basis_size(p.kw);
-  if (tid < NB) sb[tid] = basis_coeff(p.centroids, p.kw, basis_mask(p.kw, tid));
-  __syncthreads();
-  for (int hs = 1; hs < D; hs <<= 1) {
-    float a = 0.f, c = 0.f;
-    int i = 0;
-    if (tid < D / 2) {
-      i = (tid / hs) * 2 * hs + (tid % hs);
-      a = sq[i];
-      c = sq[i + hs];
-    }
-    __syncthreads();
-    if (tid < D / 2) {
-      sq[i] = a + c;
-      sq[i + hs] = a - c;
-    }
-    __syncthreads();
-  }
-  if (tid < D) sq[tid] *= (1.0f / sqrtf(static_cast<float>(D)));
-  __syncthreads();
-  // p_j = sum_k S[j][k] q'_k, two threads per output
-  {
-    const int j = tid % D, part = tid / D;   // D = 128: part 0/1; D = 64: part 0..3
-    constexpr int PARTS = 256 / D;
-    constexpr int PW = D / PARTS / 2;         // sketch dwords per part (32 or 8)
-    float acc = 0.f;
-    // rotated start so that neighbouring threads hit different LDS banks
-#pragma unroll 8
-    for (int m = 0; m < PW; ++m) {
-      const int k = part * (D / PARTS) + 2 * ((m + j) % PW);
-      const uint32_t two = s_sk[(j * D + k) / 2];
-      acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two & 0xffffu)), sq[k], acc);
-      acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(two >> 16)), sq[k + 1], acc);
-    }
-    __syncthreads();                          // the sketch is no longer read below
-    float *red = reinterpret_cast<float *>(s_sk);
-    red[tid] = acc;
-    __syncthreads();
-    if (tid < D) {
-      float v = 0.f;
-      for (int q = 0; q < PARTS; ++q) v += red[q * D + tid];
-      sp[tid] = v;
-    }
-    __syncthreads();
-  }
-  // statistics: wave 0 -> q', wave 1 -> p
-  if (wave < 2) {
-    const float *x = wave == 0 ? sq : sp;
-    float mx = 0.f, sm = 0.f;
-    for (int i = lane; i < D; i += kWave) { mx = fmaxf(mx, fabsf(x[i])); sm += x[i]; }
-    mx = wave_max(mx);
-    sm = wave_sum(sm);
-    if (lane == 0) { sred[2 * wave] = mx; sred[2 * wave + 1] = sm; }
-  }
-  if (tid == 0) {
-    float mb = 0.f;
-    for (int s = 0; s < NB; ++s) mb = fmaxf(mb, fabsf(sb[s]));
-    sb[8] = mb;
-  }
-  __syncthreads();
-
-  const int NH = D / 64;
-  const int NMF = (NB + 1) * NH;
-  const int rg = h / 4, hl = h % 4;
-  const int el = fixed_exponent(2.0f * sb[8] * sred[0]);
-  const int eq = fixed_exponent(2.0f * sred[2]);
-  uint8_t *dst = p.out + grp * p.group_bytes;
-  // the 16 lanes of this head in each operand: rows 4 hl + s, k-groups kg
-  for (int item = tid; item < NMF * 16; item += blockDim.x) {
-    const int mf = item / 16;
-    const int s = (item % 16) % 4, kg = (item % 16) / 4;
-    const int l = 16 * kg + 4 * hl + s;
-    const bool qjl = mf >= NB * NH;
-    const int plane = qjl ? 0 : mf / NH;
-    const int half = mf % NH;
-    const float coef = qjl ? 2.0f : 2.0f * sb[plane];
-    const int e = qjl ? eq : el;
-    const float *x = qjl ? sp : sq;
-    uint32_t dw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int coord = slot_coord(D, kg, j, half);
-      const int k = 4 * (kg & 1) + (j >> 2);
-      float v = ldexpf(coef * x[coord], 7 - k + e);
-      if (k == 7) v = -v;
-      const uint32_t dig = signed_digits(__float2int_rn(v));
-      dw[j >> 2] |= ((dig >> (8 * s)) & 0xffu) << (8 * (j & 3));
-    }
-    *reinterpret_cast<uint4 *>(dst + (static_cast<size_t>(rg * NMF + mf) * kWave + l) * 16) =
-        make_uint4(dw[0], dw[1], dw[2], dw[3]);
-  }
-  // rows of absent heads in this head's last row group stay zero: the
-  // group's first head of a row group clears them
-  const int RG = (G + 3) / 4;
-  if (hl == 0 && rg == RG - 1 && G % 4 != 0) {
-    for (int item = tid; item < NMF * 64; item += blockDim.x) {
-      const int mf = item / 64, l = item % 64;
-      if ((l % 16) / 4 >= G % 4)
-        *reinterpret_cast<uint4 *>(dst + (static_cast<size_t>(rg * NMF + mf) * kWave + l) * 16) = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  if (tid == 0) {
-    float *fl = reinterpret_cast<float *>(dst + qprep_frag_bytes(D, p.kw, G)) + 4 * h;
-    fl[0] = ldexpf(1.0f, -7 - el);
-    fl[1] = p.centroids[(1 << p.kw) - 1] * sred[1];
-    fl[2] = ldexpf(1.0f, -7 - eq);
-    fl[3] = sred[3];
-  }
-}
-
-template <int D>
-hipError_t launch_query_prep_d(const QueryPrepParams &p, hipStream_t st) {
-  const uint32_t heads = static_cast<uint32_t>(p.batch) * p.n_kv * p.group;
-  if (heads == 0) return hipSuccess;
-  hipLaunchKernelGGL((query_prep_kernel<D>), dim3(heads), dim3(256), 0, st, p);
-  return hipGetLastError();
-}
 
 // ------------------------------------------------------------ key tiles
 
@@ -185,30 +33,6 @@ struct KeyTile {
   __device__ __forceinline__ float norm() const { return f16_bits_to_float(static_cast<uint16_t>(sc & 0xffffu)); }
   __device__ __forceinline__ float gamma() const { return f16_bits_to_float(static_cast<uint16_t>(sc >> 16)); }
 };
-
-// Loads are issued unconditionally (past the end the slot is clamped to the
-// first one): a key's words only feed its own MFMA column, and columns past
-// the end are never stored, so no branch holds the loads back.
-template <int D, int KW>
-__device__ __forceinline__ void load_key_tile(const uint8_t *kcodes, const uint16_t *kscalars, int64_t slot0,
-                                              int64_t t, int64_t n_keys, KeyTile<D, KW> &kt) {
-  constexpr int REC = (KW + 1) * D / 8;
-  const int lane = lane_id();
-  const int wh = (lane / 16) >> 1;
-  const int64_t tc = (t < n_keys) ? t : 0;
-  const uint8_t *rec = kcodes + (slot0 + tc) * REC;
-#pragma unroll
-  for (int q = 0; q <= KW; ++q) {
-    if (D == 128) {
-      const uint2 u = *reinterpret_cast<const uint2 *>(rec + q * 16 + wh * 8);
-      kt.w[q][0] = u.x;
-      kt.w[q][D == 128 ? 1 : 0] = u.y;
-    } else {
-      kt.w[q][0] = *reinterpret_cast<const uint32_t *>(rec + q * 8 + wh * 4);
-    }
-  }
-  kt.sc = reinterpret_cast<const uint32_t *>(kscalars)[slot0 + tc];
-}
 
 // Accumulate the key planes and the sign plane of one tile for NRG row groups.
 template <int D, int KW, int NRG>
@@ -241,42 +65,12 @@ __device__ __forceinline__ void key_tile_mfma(const KeyTile<D, KW> &kt, const v4
   }
 }
 
-// fl = {inv_lm, cst_lm, inv_qj, cst_qj} of the lane's head (held in
-// registers: a global load here would make the wait for it also wait for
-// every prefetched tile issued before it).
+// fl = {inv_lm, cst_lm, inv_qj, cst_qj} of the lane's head.
 __device__ __forceinline__ float tile_logit(const v4i &clm, const v4i &cqj, const float4 &fl, float n, float g,
                                             float kappa) {
   const float lm = fmaf(combine_digits(clm), fl.x, -fl.y);
   const float qj = fmaf(combine_digits(cqj), fl.z, -fl.w);
   return n * fmaf(kappa * g, qj, lm);
-}
-
-// Per-head constants of the NRG row groups this lane's C rows belong to.
-template <int NRG>
-__device__ __forceinline__ void load_head_consts(const float *fl, int h_base, int n_heads, float4 (&fh)[NRG]) {
-  const int kg = lane_id() / 16;
-#pragma unroll
-  for (int rg = 0; rg < NRG; ++rg) {
-    const int h = h_base + 4 * rg + kg;
-    fh[rg] = (h < n_heads) ? *reinterpret_cast<const float4 *>(fl + 4 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
-template <int D, int KW, int NRG>
-__device__ __forceinline__ void load_afrags(const uint8_t *frag, int rg0, int nrg, v4i (&a)[NRG][(Basis<KW>::N + 1) * (D / 64)]) {
-  constexpr int NMF = (Basis<KW>::N + 1) * (D / 64);
-  const int lane = lane_id();
-#pragma unroll
-  for (int rg = 0; rg < NRG; ++rg)
-#pragma unroll
-    for (int mf = 0; mf < NMF; ++mf) {
-      if (rg < nrg) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(frag + ((static_cast<size_t>(rg0 + rg) * NMF + mf) * kWave + lane) * 16);
-        a[rg][mf] = v4i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z), static_cast<int>(u.w)};
-      } else {
-        a[rg][mf] = v4i{0, 0, 0, 0};
-      }
-    }
 }
 
 __device__ __forceinline__ void lane_masks(uint32_t (&mask)[4]) {
@@ -285,92 +79,24 @@ __device__ __forceinline__ void lane_masks(uint32_t (&mask)[4]) {
   for (int r = 0; r < 4; ++r) mask[r] = 0x01010101u << (kk + r);
 }
 
-// ------------------------------------------------------------------ logits
+// ------------------------------------------------------------------ staging
 
-constexpr int kLogitTilesPerWave = 4;
-
-template <int D, int KW, int NRG>
-__global__ __launch_bounds__(256) void logits_kernel(LogitsParams p) {
-  constexpr int NMF = (Basis<KW>::N + 1) * (D / 64);
-  const int G = p.group;
-  const int n_q = p.n_kv * G;
-  const int64_t bh = blockIdx.y;
-  const int64_t b = bh / p.n_kv;
-  const int64_t kvh = bh % p.n_kv;
-  const uint8_t *prep = p.qprep + bh * p.group_bytes;
-  const float *fl = reinterpret_cast<const float *>(prep + p.frag_bytes);
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  const int kg = lane / 16;
-  uint32_t mask[4];
-  lane_masks(mask);
-  const int64_t slot0 = bh * p.cap;
-  const float kappa = kSqrtHalfPi / static_cast<float>(D);
-  const int64_t tile0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * kLogitTilesPerWave;
-  const int RG = (G + 3) / 4;
-  for (int rg0 = 0; rg0 < RG; rg0 += NRG) {
-    const int nrg = min(NRG, RG - rg0);
-    v4i a[NRG][NMF];
-    load_afrags<D, KW, NRG>(prep, rg0, nrg, a);
-    float4 fh[NRG];
-    load_head_consts<NRG>(fl, 4 * rg0, G, fh);
-    KeyTile<D, KW> kt[kLogitTilesPerWave];
-#pragma unroll
-    for (int it = 0; it < kLogitTilesPerWave; ++it)
-      load_key_tile<D, KW>(p.kcodes, p.kscalars, slot0, (tile0 + it) * 16 + (lane % 16), p.n_keys, kt[it]);
-#pragma unroll
-    for (int it = 0; it < kLogitTilesPerWave; ++it) {
-      const int64_t t = (tile0 + it) * 16 + (lane % 16);
-      if ((tile0 + it) * 16 >= p.n_keys) break;
-      v4i clm[NRG], cqj[NRG];
-      key_tile_mfma<D, KW, NRG>(kt[it], a, mask, nrg, clm, cqj);
-#pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) {
-        const int h = 4 * (rg0 + rg) + kg;
-        if (rg < nrg && h < G && t < p.n_keys)
-          p.logits[(b * n_q + kvh * G + h) * p.n_keys + t] = tile_logit(clm[rg], cqj[rg], fh[rg], kt[it].norm(), kt[it].gamma(), kappa);
-      }
-    }
-  }
-}
-
-template <int D>
-hipError_t launch_logits_d(const LogitsParams &p, int w, hipStream_t st) {
-  if (p.n_keys == 0 || p.batch == 0 || p.n_kv == 0) return hipSuccess;
-  const int64_t keys_per_block = 4 * kLogitTilesPerWave * 16;
-  dim3 grid(static_cast<uint32_t>((p.n_keys + keys_per_block - 1) / keys_per_block),
-            static_cast<uint32_t>(p.batch) * p.n_kv);
-  const bool two = p.group > 4 && w <= 3;
-#define TQ_LG(WW)                                                                          \
-  if (two) hipLaunchKernelGGL((logits_kernel<D, WW, 2>), grid, dim3(256), 0, st, p);      \
-  else hipLaunchKernelGGL((logits_kernel<D, WW, 1>), grid, dim3(256), 0, st, p);
-  switch (w) {
-    case 1: TQ_LG(1); break;
-    case 2: TQ_LG(2); break;
-    case 3: TQ_LG(3); break;
-    default: TQ_LG(4);
-  }
-#undef TQ_LG
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------ decode attend
-
-// Pipeline stages of the decode kernel: while the block computes on one
-// split, the direct-to-LDS loads of the next two are in flight.
+// Every scan block walks splits of kDecodeSplit tokens of one (batch,
+// kv-head) sequence through a ring of kStages LDS buffers; while it computes
+// on one split, the loads of the next two are in flight.
 constexpr int kStages = 3;
 
 // Block layout: D/16 waves. Wave w owns the 16-key tiles w, w + NW, ... of
-// every split (their logits and attention weights) and the value
-// coordinates [16 w, 16 w + 16). Its share of a split is staged in a region
-// of LDS that only it reads, so no barrier guards the staging:
+// every split and (decode) the value coordinates [16 w, 16 w + 16). Its
+// share of a split is staged in a region of LDS that only it reads, so no
+// barrier guards the staging:
 //   [0, OFF_S)         key tiles, 16 x REC bytes each; for d = 128 plane-major
 //                      (the 16 keys' words of plane 0, then of plane 1, ...)
-//   [OFF_S, OFF_V)     the tiles' key scalar pairs (64 B per tile), then their
-//                      value norms (32 B per tile)
-//   [OFF_V, ...)       value words: [32-token block][plane][16 coordinates]
-template <int D, int KW, int VW>
-struct DecodeShape {
+//   [OFF_S, OFF_V)     the tiles' key scalar pairs (64 B per tile), then
+//                      (decode) their value norms (32 B per tile)
+//   [OFF_V, ...)       (decode) value words: [32-token block][plane][16 coords]
+template <int D, int KW, int VW, bool LOGITS>
+struct ScanShape {
   static constexpr int S = kDecodeSplit;
   static constexpr int NW = D / 16;
   static constexpr int THREADS = NW * kWave;
@@ -378,8 +104,8 @@ struct DecodeShape {
   static constexpr int VT = S / 64;                  // 64-token value tiles
   static constexpr int REC = (KW + 1) * D / 8;       // record bytes = 16-byte units per key tile
   static constexpr int KI = (REC + 63) / 64;         // loads per key tile
-  static constexpr int SU = 6 * KT;                  // scalar units
-  static constexpr int VU = (S / 32) * VW * 4;       // value units
+  static constexpr int SU = (LOGITS ? 4 : 6) * KT;   // scalar units
+  static constexpr int VU = LOGITS ? 0 : (S / 32) * VW * 4;   // value units
   static constexpr int VI = (VU + 63) / 64;
   static constexpr int P = KT * KI + 1 + VI;         // loads per wave per split
   static constexpr int OFF_S = KT * REC * 16;
@@ -434,9 +160,13 @@ struct SeqArrays {
   int32_t cap, nblk;
 };
 
-template <int D, int KW, int VW>
+// Issue this wave's share of split sp into its region of a stage buffer.
+// Every wave issues exactly P loads. Tiles past the cache capacity load the
+// sequence's first tile instead (their keys are past the context and are
+// never used), so every address stays inside the caller's arrays.
+template <int D, int KW, int VW, bool LOGITS>
 __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t *stage, int wave) {
-  using SH = DecodeShape<D, KW, VW>;
+  using SH = ScanShape<D, KW, VW, LOGITS>;
   constexpr int REC = SH::REC;
   const int lane = lane_id();
   uint8_t *wb = stage + wave * SH::WAVE_BYTES;
@@ -482,36 +212,198 @@ __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t
   }
 }
 
+// ------------------------------------------------------------------ query prep
+
+// Scratch of the in-block query preparation (bytes): the int8 digit
+// operands [NRG][NMF][64 lanes][16], q' and p [8][D] floats, per-head
+// statistics [8][4] and constants [8][4], basis coefficients [8].
+template <int D, int KW, int NRG>
+struct PrepShape {
+  static constexpr int NB = Basis<KW>::N;
+  static constexpr int NMF = (NB + 1) * (D / 64);
+  static constexpr int FRAG = NRG * NMF * 1024;
+  static constexpr int BYTES = FRAG + 2 * 8 * D * 4 + 8 * 4 * 4 * 2 + 8 * 4;
+};
+
+// Query preparation of the heads [h0, h0 + GE) (GE <= 4 NRG) of group bh by
+// one block of THREADS threads (4 D): q' = R q, p = S q', then the digit
+// operands of the key planes (2 beta_s q') and of the sign plane (2 p), one
+// fixed-point exponent per head for each, and the per-head constants
+// {2^-(7+e_lm), c[L-1] sum q', 2^-(7+e_qj), sum p}. Rows of absent heads
+// stay zero. Results in `scratch` (PrepShape layout).
+template <int D, int KW, int NRG>
+__device__ __forceinline__ void group_prep(const ScanParams &p, int64_t bh, int GE, uint8_t *scratch) {
+  using PS = PrepShape<D, KW, NRG>;
+  constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64;
+  constexpr int THREADS = 4 * D;
+  constexpr int PARTS = THREADS / D;                 // threads per sketch row
+  float *sq = reinterpret_cast<float *>(scratch + PS::FRAG);     // [8][D]
+  float *sp = sq + 8 * D;                                        // [8][D]
+  float *sst = sp + 8 * D;                                       // [8][4]
+  float *scon = sst + 32;                                        // [8][4]
+  float *sb = scon + 32;                                         // [8]
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int G = p.group, n_q = p.n_kv * G;
+  const int64_t b = bh / p.n_kv, kvh = bh % p.n_kv;
+  const int64_t row0 = b * n_q + kvh * G + p.h0;
+
+  // this thread's sketch row j (fp16 pairs), loaded up front
+  const int j = tid % D, part = tid / D;
+  uint4 srow[D / 8];
+#pragma unroll
+  for (int k = 0; k < D / 8; ++k) srow[k] = reinterpret_cast<const uint4 *>(p.sketch + j * D)[k];
+  for (int e = tid; e < 8 * D; e += THREADS) {
+    const int h = e / D, i = e % D;
+    float v = 0.f;
+    if (h < GE) {
+      const int64_t at = (row0 + h) * D + i;
+      if (p.xt == 0) v = static_cast<const float *>(p.q)[at];
+      else if (p.xt == 1) v = bf16_bits_to_float(static_cast<const uint16_t *>(p.q)[at]);
+      else v = f16_bits_to_float(static_cast<const uint16_t *>(p.q)[at]);
+      v *= p.ksigns[i];
+    }
+    sq[e] = v;
+  }
+  if (tid < NB) sb[tid] = basis_coeff(p.kcent, KW, basis_mask(KW, tid));
+  lds_barrier();
+  // q' = H (s q) / sqrt(D), in place
+  for (int hs = 1; hs < D; hs <<= 1) {
+    for (int e = tid; e < GE * D / 2; e += THREADS) {
+      const int h = e / (D / 2), r = e % (D / 2);
+      const int i = (r / hs) * 2 * hs + (r % hs);
+      const float x = sq[h * D + i], y = sq[h * D + i + hs];
+      sq[h * D + i] = x + y;
+      sq[h * D + i + hs] = x - y;
+    }
+    lds_barrier();
+  }
+  for (int e = tid; e < GE * D; e += THREADS) sq[e] *= 1.0f / sqrtf(static_cast<float>(D));
+  lds_barrier();
+  // p_j = sum_k S[j][k] q'_k for the heads part, part + PARTS, ...
+  for (int h = part; h < GE; h += PARTS) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < D / 8; ++k) {
+      const uint32_t w[4] = {srow[k].x, srow[k].y, srow[k].z, srow[k].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w[m] & 0xffffu)), sq[h * D + 8 * k + 2 * m], acc);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w[m] >> 16)), sq[h * D + 8 * k + 2 * m + 1], acc);
+      }
+    }
+    sp[h * D + j] = acc;
+  }
+  lds_barrier();
+  // statistics: max |q'|, sum q', max |p|, sum p per head
+  for (int h = wave; h < GE; h += THREADS / kWave) {
+    float mq = 0.f, s1 = 0.f, mp = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = lane; i < D; i += kWave) {
+      mq = fmaxf(mq, fabsf(sq[h * D + i]));
+      s1 += sq[h * D + i];
+      mp = fmaxf(mp, fabsf(sp[h * D + i]));
+      s2 += sp[h * D + i];
+    }
+    mq = wave_max(mq);
+    s1 = wave_sum(s1);
+    mp = wave_max(mp);
+    s2 = wave_sum(s2);
+    if (lane == 0) {
+      float mb = 0.f;
+      for (int s = 0; s < NB; ++s) mb = fmaxf(mb, fabsf(sb[s]));
+      const int el = fixed_exponent(2.0f * mb * mq);
+      const int eq = fixed_exponent(2.0f * mp);
+      sst[4 * h] = static_cast<float>(el);
+      sst[4 * h + 1] = static_cast<float>(eq);
+      scon[4 * h] = ldexpf(1.0f, -7 - el);
+      scon[4 * h + 1] = p.kcent[(1 << KW) - 1] * s1;
+      scon[4 * h + 2] = ldexpf(1.0f, -7 - eq);
+      scon[4 * h + 3] = s2;
+    }
+  }
+  lds_barrier();
+  // digit operands: lane slot (rg, mf, l) = row l%16 (head 4 rg + (l%16)/4,
+  // digit l%4), K slots 16 (l/16) + j
+  for (int item = tid; item < NRG * NMF * kWave; item += THREADS) {
+    const int l = item % kWave, mf = (item / kWave) % NMF, rg = item / (kWave * NMF);
+    const int hl = 4 * rg + (l % 16) / 4, s = l % 4, kg = l / 16;
+    uint32_t dw[4] = {0u, 0u, 0u, 0u};
+    if (hl < GE) {
+      const bool qjl = mf >= NB * NH;
+      const int plane = qjl ? 0 : mf / NH;
+      const int half = mf % NH;
+      const float coef = qjl ? 2.0f : 2.0f * sb[plane];
+      const int e = static_cast<int>(sst[4 * hl + (qjl ? 1 : 0)]);
+      const float *x = (qjl ? sp : sq) + hl * D;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int coord = slot_coord(D, kg, jj, half);
+        const int k = 4 * (kg & 1) + (jj >> 2);
+        float v = ldexpf(coef * x[coord], 7 - k + e);
+        if (k == 7) v = -v;
+        const uint32_t dig = signed_digits(__float2int_rn(v));
+        dw[jj >> 2] |= ((dig >> (8 * s)) & 0xffu) << (8 * (jj & 3));
+      }
+    }
+    *reinterpret_cast<uint4 *>(scratch + item * 16) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  }
+  lds_barrier();
+}
+
+// The lane's operands and head constants from the prepared scratch.
+template <int D, int KW, int NRG>
+__device__ __forceinline__ void load_prepared(const uint8_t *scratch, int GE, v4i (&a)[NRG][PrepShape<D, KW, NRG>::NMF],
+                                              float4 (&fh)[NRG]) {
+  using PS = PrepShape<D, KW, NRG>;
+  const int lane = lane_id(), kg = lane / 16;
+  const float *scon = reinterpret_cast<const float *>(scratch + PS::FRAG) + 16 * D + 32;
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) {
+#pragma unroll
+    for (int mf = 0; mf < PS::NMF; ++mf) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(scratch + ((rg * PS::NMF + mf) * kWave + lane) * 16);
+      a[rg][mf] = v4i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z), static_cast<int>(u.w)};
+    }
+    const int h = 4 * rg + kg;
+    fh[rg] = (h < GE) ? *reinterpret_cast<const float4 *>(scon + 4 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ------------------------------------------------------------------ scan
+
 // One block per (batch*kv-head, block index within the group) and the heads
-// [h0, h0 + GE) of the group, GE <= 4 NRG. The block walks the splits
-// blockIdx.x, blockIdx.x + gridDim.x, ... (kDecodeSplit tokens each)
-// through a ring of kStages LDS buffers. Per split, each wave:
-//  1. computes the logits of its key tiles for every head (key MFMA),
-//     scaled by sm_scale; publishes its per-head maxima and largest value
-//     norm                                                     -- barrier
+// [h0, h0 + GE) of the group, GE <= 4 NRG. The block prepares the queries of
+// those heads, then walks the splits blockIdx.x, blockIdx.x + gridDim.x, ...
+// (kDecodeSplit tokens each) through the LDS ring. Per split, each wave:
+//  1. computes the logits of its key tiles for every head (key MFMA);
+//     LOGITS: stores them and moves on; decode: scales them by sm_scale and
+//     publishes its per-head maxima and largest value norm   -- barrier
 //  2. merges the split maximum into the running (m, l) (online softmax,
 //     m' = max(m, m_split), alpha = exp(m - m')), forms its tokens' weights
 //     exp(logit - m') n_v as fixed-point int8 digits (one exponent per
 //     split, from its largest value norm) written into the shared MFMA
-//     operand tiles, and publishes their exact per-head sums   -- barrier
+//     operand tiles, and publishes their exact per-head sums  -- barrier
 //  3. contracts the weights with its value coordinates' planes on the
 //     matrix cores (int32 over the split) and folds the result into its
 //     fp32 accumulators: acc = alpha acc + split sum
 //  4. refills the stage buffer with the split kStages ahead.
-// The block's partial {m, l, acc} goes to the workspace; merge_kernel
-// combines them.
-template <int D, int KW, int VW, int NRG>
-__global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 D = (D / 16) waves
-  using SH = DecodeShape<D, KW, VW>;
+// Decode writes the block's partial {m, l, acc} to the workspace;
+// merge_kernel combines them.
+template <int D, int KW, int VW, int NRG, bool LOGITS>
+__device__ __forceinline__ void scan_block(const ScanParams &p) {
+  using SH = ScanShape<D, KW, VW, LOGITS>;
+  using PS = PrepShape<D, KW, NRG>;
   constexpr int S = SH::S, NW = SH::NW, KT = SH::KT, VT = SH::VT, REC = SH::REC, P = SH::P;
-  constexpr int NMF = (Basis<KW>::N + 1) * (D / 64);
+  constexpr int NMF = PS::NMF;
   constexpr int NBV = Basis<VW>::N;
   constexpr int GMAX = 4 * NRG;
   constexpr int NBG = (NRG == 2 && NBV == 8) ? 4 : NBV;
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[SH::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[SH::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[SH::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sfrag[NRG * VT * 1024];
+  constexpr int SB = SH::STAGE_BYTES;
+  constexpr int RING = (3 * SB > SB + PS::BYTES) ? 3 * SB : SB + PS::BYTES;
+  // stage k at ring + k * SB; the query preparation uses [SB, SB + PS::BYTES)
+  // before stages 1 and 2 are first filled
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
+  __shared__ __attribute__((aligned(16))) uint8_t sfrag[LOGITS ? 16 : NRG * VT * 1024];
   __shared__ float spm[NW][GMAX];
   __shared__ float spnv[NW];
   __shared__ double spsw[NW][GMAX];
@@ -523,7 +415,7 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.n_kv;
   const int64_t kvh = bh % p.n_kv;
-  int64_t ctx64 = p.ctx_lens[b];
+  int64_t ctx64 = p.ctx_lens ? static_cast<int64_t>(p.ctx_lens[b]) : p.max_ctx;
   ctx64 = ctx64 < 0 ? 0 : (ctx64 > p.max_ctx ? p.max_ctx : ctx64);
   const int ctx = static_cast<int>(ctx64);
   const int n_splits = (ctx + S - 1) / S;
@@ -538,11 +430,8 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
   uint32_t mask[4];
   lane_masks(mask);
   const float kappa = kSqrtHalfPi / static_cast<float>(D);
-  const uint8_t *prep = p.qprep + bh * p.group_bytes;
-  const float *fl = reinterpret_cast<const float *>(prep + p.frag_bytes);
-
-  if (tid < NBV) svb[tid] = basis_coeff(p.vcent, VW, basis_mask(VW, tid));
-  const float cvmax = p.vcent[(1 << VW) - 1];
+  const float cvmax = LOGITS ? 0.f : p.vcent[(1 << VW) - 1];
+  if (!LOGITS && tid < NBV) svb[tid] = basis_coeff(p.vcent, VW, basis_mask(VW, tid));
 
   float m_run[NRG], l_run[NRG], accf[NRG];
 #pragma unroll
@@ -553,28 +442,22 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
   sa.nblk = static_cast<int32_t>(p.cap / kValueBlock);
   sa.kcodes = p.kcodes + bh * p.cap * REC;
   sa.kscal = reinterpret_cast<const uint8_t *>(p.kscalars) + bh * p.cap * 4;
-  sa.vcodes = reinterpret_cast<const uint8_t *>(p.vcodes + bh * sa.nblk * VW * D);
-  sa.vscal = reinterpret_cast<const uint8_t *>(p.vscalars) + bh * p.cap * 2;
+  sa.vcodes = LOGITS ? nullptr : reinterpret_cast<const uint8_t *>(p.vcodes + bh * sa.nblk * VW * D);
+  sa.vscal = LOGITS ? nullptr : reinterpret_cast<const uint8_t *>(p.vscalars) + bh * p.cap * 2;
   v4i a[NRG][NMF];
   float4 fh[NRG];
   if (ns > 0) {
-    // split 0 and the query operands travel together; both are waited for
-    // here, so no wait for the operands is left inside the split loop
-    issue_split<D, KW, VW>(sa, bx, st0, wave);
-    load_afrags<D, KW, NRG>(prep, p.h0 / 4, NRG, a);
-    load_head_consts<NRG>(fl, p.h0, p.h0 + GE, fh);
-    wait_vm<0>();
-#pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-#pragma unroll
-      for (int mf = 0; mf < NMF; ++mf) asm volatile("" ::"v"(a[rg][mf]));
-      asm volatile("" ::"v"(fh[rg].x), "v"(fh[rg].y), "v"(fh[rg].z), "v"(fh[rg].w));
-    }
-    if (ns > 1) issue_split<D, KW, VW>(sa, bx + nb, st1, wave);
-    if (ns > 2) issue_split<D, KW, VW>(sa, bx + 2 * nb, st2, wave);
+    // split 0 is in flight while the block prepares its queries
+    issue_split<D, KW, VW, LOGITS>(sa, bx, ring, wave);
+    group_prep<D, KW, NRG>(p, bh, GE, ring + SB);
+    load_prepared<D, KW, NRG>(ring + SB, GE, a, fh);
+    lds_barrier();                                 // every wave holds its operands
+    if (ns > 1) issue_split<D, KW, VW, LOGITS>(sa, bx + nb, ring + SB, wave);
+    if (ns > 2) issue_split<D, KW, VW, LOGITS>(sa, bx + 2 * nb, ring + 2 * SB, wave);
   }
 
-  auto step = [&](uint8_t *buf, int it) __attribute__((always_inline)) {
+  for (int it = 0; it < ns; ++it) {
+    uint8_t *buf = ring + (it % kStages) * SB;
     const int sp = bx + it * nb;
     const int n = min(S, ctx - sp * S);
     const int ahead = min(kStages - 1, ns - 1 - it);
@@ -605,143 +488,148 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
         }
       }
       kt.sc = *reinterpret_cast<const uint32_t *>(wb + SH::OFF_S + 64 * u + 4 * col);
-      const uint16_t nvb = *reinterpret_cast<const uint16_t *>(wb + SH::OFF_S + 64 * KT + 32 * u + 2 * col);
       v4i clm[NRG], cqj[NRG];
       key_tile_mfma<D, KW, NRG>(kt, a, mask, NRG, clm, cqj);
       const bool valid = tl < n;
       const float kn = kt.norm(), kgm = kt.gamma();
+      if constexpr (LOGITS) {
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) {
-        const float l = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa) * p.sm_scale;
-        lg[u][rg] = valid ? l : -INFINITY;
-        mx[rg] = fmaxf(mx[rg], lg[u][rg]);
-      }
-      const float nvf = f16_bits_to_float(nvb);
-      nvv[u] = valid ? nvf : 0.f;
-      nvm = fmaxf(nvm, nvv[u]);
-    }
+        for (int rg = 0; rg < NRG; ++rg) {
+          const int hl = 4 * rg + kg;
+          const float l = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa);
+          if (valid && hl < GE) p.logits[(b * n_q + kvh * G + p.h0 + hl) * p.max_ctx + sp * S + tl] = l;
+        }
+        (void)lg; (void)nvv;
+      } else {
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) mx[rg] = row_max16(mx[rg]);
-    nvm = wave_max(nvm);
-    if (col == 0) {
-#pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) spm[wave][4 * rg + kg] = mx[rg];
-    }
-    if (lane == 0) spnv[wave] = nvm;
-    lds_barrier();
-
-    // 2. running statistics, weights -> operand digits, their sums
-    float nvmax = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) nvmax = fmaxf(nvmax, spnv[w]);
-    const int ew = fixed_exponent(nvmax);
-    float alpha[NRG];
-#pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-      float ms = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) ms = fmaxf(ms, spm[w][4 * rg + kg]);
-      const float mn = fmaxf(m_run[rg], ms);
-      alpha[rg] = (m_run[rg] == -INFINITY) ? 0.f : __expf(m_run[rg] - mn);
-      m_run[rg] = mn;
-      l_run[rg] *= alpha[rg];
-    }
-    double sw[NRG];
-#pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) sw[rg] = 0.0;
-#pragma unroll
-    for (int u = 0; u < KT; ++u) {
-      const int tl = 16 * (wave + NW * u) + col;
-      const int vt = tl / 64, t64 = tl % 64;
-      const int k = t64 & 7;
-      const int kga = 2 * (t64 >> 5) + ((t64 >> 2) & 1);
-      const int jb = (t64 >> 3) & 3, r = t64 & 3;
-#pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) {
-        const float e = __expf(lg[u][rg] - m_run[rg]);
-        l_run[rg] += e;
-        const int fx = __float2int_rn(ldexpf(e * nvv[u], 7 - k + ew));
-        sw[rg] += static_cast<double>(fx) * static_cast<double>(1 << k);
-        const uint32_t dig = signed_digits(k == 7 ? -fx : fx);
-        uint8_t *dst = sfrag + (rg * VT + vt) * 1024 + (16 * kga + 4 * kg) * 16 + 4 * r + jb;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) dst[16 * s] = static_cast<uint8_t>(dig >> (8 * s));
+        for (int rg = 0; rg < NRG; ++rg) {
+          const float l = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa) * p.sm_scale;
+          lg[u][rg] = valid ? l : -INFINITY;
+          mx[rg] = fmaxf(mx[rg], lg[u][rg]);
+        }
+        const uint16_t nvb = *reinterpret_cast<const uint16_t *>(wb + SH::OFF_S + 64 * KT + 32 * u + 2 * col);
+        const float nvf = f16_bits_to_float(nvb);
+        nvv[u] = valid ? nvf : 0.f;
+        nvm = fmaxf(nvm, nvv[u]);
       }
     }
-#pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-      const double t = row_sum16d(sw[rg]);
-      if (col == 0) spsw[wave][4 * rg + kg] = t;
-    }
-    lds_barrier();
 
-    // 3. value planes x weights on the matrix cores, NBG planes at a time
-    //    (with 8 heads and 8 planes, two passes keep the int32 sums in registers)
-    float x[NRG];
+    if constexpr (!LOGITS) {
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) x[rg] = 0.f;
+      for (int rg = 0; rg < NRG; ++rg) mx[rg] = row_max16(mx[rg]);
+      nvm = wave_max(nvm);
+      if (col == 0) {
 #pragma unroll
-    for (int s0 = 0; s0 < NBV; s0 += NBG) {
-      v4i acc[NRG][NBG];
+        for (int rg = 0; rg < NRG; ++rg) spm[wave][4 * rg + kg] = mx[rg];
+      }
+      if (lane == 0) spnv[wave] = nvm;
+      lds_barrier();
+
+      // 2. running statistics, weights -> operand digits, their sums
+      float nvmax = 0.f;
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg)
+      for (int w = 0; w < NW; ++w) nvmax = fmaxf(nvmax, spnv[w]);
+      const int ew = fixed_exponent(nvmax);
+      float alpha[NRG];
 #pragma unroll
-        for (int s = 0; s < NBG; ++s) acc[rg][s] = v4i{0, 0, 0, 0};
+      for (int rg = 0; rg < NRG; ++rg) {
+        float ms = -INFINITY;
 #pragma unroll
-      for (int vt = 0; vt < VT; ++vt) {
-        if (vt * 64 < n) {
-          v4i av[NRG];
+        for (int w = 0; w < NW; ++w) ms = fmaxf(ms, spm[w][4 * rg + kg]);
+        const float mn = fmaxf(m_run[rg], ms);
+        alpha[rg] = (m_run[rg] == -INFINITY) ? 0.f : __expf(m_run[rg] - mn);
+        m_run[rg] = mn;
+        l_run[rg] *= alpha[rg];
+      }
+      double sw[NRG];
 #pragma unroll
-          for (int rg = 0; rg < NRG; ++rg) {
-            const uint4 q4 = *reinterpret_cast<const uint4 *>(sfrag + (rg * VT + vt) * 1024 + lane * 16);
-            av[rg] = v4i{static_cast<int>(q4.x), static_cast<int>(q4.y), static_cast<int>(q4.z), static_cast<int>(q4.w)};
-          }
-          uint32_t pw[VW];
+      for (int rg = 0; rg < NRG; ++rg) sw[rg] = 0.0;
 #pragma unroll
-          for (int q = 0; q < VW; ++q)
-            pw[q] = *reinterpret_cast<const uint32_t *>(wb + SH::OFF_V + ((2 * vt + (kg >> 1)) * VW + q) * 64 + 4 * col);
+      for (int u = 0; u < KT; ++u) {
+        const int tl = 16 * (wave + NW * u) + col;
+        const int vt = tl / 64, t64 = tl % 64;
+        const int k = t64 & 7;
+        const int kga = 2 * (t64 >> 5) + ((t64 >> 2) & 1);
+        const int jb = (t64 >> 3) & 3, r = t64 & 3;
 #pragma unroll
-          for (int s = 0; s < NBG; ++s) {
-            uint32_t w = 0u;
+        for (int rg = 0; rg < NRG; ++rg) {
+          const float e = __expf(lg[u][rg] - m_run[rg]);
+          l_run[rg] += e;
+          const int fx = __float2int_rn(ldexpf(e * nvv[u], 7 - k + ew));
+          sw[rg] += static_cast<double>(fx) * static_cast<double>(1 << k);
+          const uint32_t dig = signed_digits(k == 7 ? -fx : fx);
+          uint8_t *dst = sfrag + (rg * VT + vt) * 1024 + (16 * kga + 4 * kg) * 16 + 4 * r + jb;
 #pragma unroll
-            for (int q = 0; q < VW; ++q)
-              if ((Basis<VW>::M[s0 + s] >> q) & 1) w ^= pw[q];
-            const v4i bv = expand_bits(w, mask);
-#pragma unroll
-            for (int rg = 0; rg < NRG; ++rg) acc[rg][s] = mfma_i8(av[rg], bv, acc[rg][s]);
-          }
+          for (int s = 0; s < 4; ++s) dst[16 * s] = static_cast<uint8_t>(dig >> (8 * s));
         }
       }
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg)
+      for (int rg = 0; rg < NRG; ++rg) {
+        const double t = row_sum16d(sw[rg]);
+        if (col == 0) spsw[wave][4 * rg + kg] = t;
+      }
+      lds_barrier();
+
+      // 3. value planes x weights on the matrix cores, NBG planes at a time
+      //    (with 8 heads and 8 planes, two passes keep the int32 sums in registers)
+      float x[NRG];
 #pragma unroll
-        for (int s = 0; s < NBG; ++s) x[rg] = fmaf(svb[s0 + s], combine_digits(acc[rg][s]), x[rg]);
-    }
-    const float inv = ldexpf(1.0f, -7 - ew);
+      for (int rg = 0; rg < NRG; ++rg) x[rg] = 0.f;
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg) {
-      double swt = 0.0;
+      for (int s0 = 0; s0 < NBV; s0 += NBG) {
+        v4i acc[NRG][NBG];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) swt += spsw[w][4 * rg + kg];
-      const float ssum = fmaf(2.0f, x[rg], -cvmax * static_cast<float>(swt)) * inv;
-      accf[rg] = fmaf(accf[rg], alpha[rg], ssum);
+        for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+          for (int s = 0; s < NBG; ++s) acc[rg][s] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+          if (vt * 64 < n) {
+            v4i av[NRG];
+#pragma unroll
+            for (int rg = 0; rg < NRG; ++rg) {
+              const uint4 q4 = *reinterpret_cast<const uint4 *>(sfrag + (rg * VT + vt) * 1024 + lane * 16);
+              av[rg] = v4i{static_cast<int>(q4.x), static_cast<int>(q4.y), static_cast<int>(q4.z), static_cast<int>(q4.w)};
+            }
+            uint32_t pw[VW];
+#pragma unroll
+            for (int q = 0; q < VW; ++q)
+              pw[q] = *reinterpret_cast<const uint32_t *>(wb + SH::OFF_V + ((2 * vt + (kg >> 1)) * VW + q) * 64 + 4 * col);
+#pragma unroll
+            for (int s = 0; s < NBG; ++s) {
+              uint32_t w = 0u;
+#pragma unroll
+              for (int q = 0; q < VW; ++q)
+                if ((Basis<VW>::M[s0 + s] >> q) & 1) w ^= pw[q];
+              const v4i bv = expand_bits(w, mask);
+#pragma unroll
+              for (int rg = 0; rg < NRG; ++rg) acc[rg][s] = mfma_i8(av[rg], bv, acc[rg][s]);
+            }
+          }
+        }
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+          for (int s = 0; s < NBG; ++s) x[rg] = fmaf(svb[s0 + s], combine_digits(acc[rg][s]), x[rg]);
+      }
+      const float inv = ldexpf(1.0f, -7 - ew);
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) {
+        double swt = 0.0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) swt += spsw[w][4 * rg + kg];
+        const float ssum = fmaf(2.0f, x[rg], -cvmax * static_cast<float>(swt)) * inv;
+        accf[rg] = fmaf(accf[rg], alpha[rg], ssum);
+      }
     }
 
     // 4. refill this stage (this wave's region only; its reads are done)
     if (it + kStages < ns) {
       wait_lds();
-      issue_split<D, KW, VW>(sa, sp + kStages * nb, buf, wave);
+      issue_split<D, KW, VW, LOGITS>(sa, sp + kStages * nb, buf, wave);
     }
-  };
-
-  for (int it = 0; it < ns;) {
-    step(st0, it);
-    if (++it >= ns) break;
-    step(st1, it);
-    if (++it >= ns) break;
-    step(st2, it);
-    ++it;
   }
+  if constexpr (LOGITS) return;
 
   // partial of this block: {m, l, acc[D]} per head of the chunk
 #pragma unroll
@@ -770,12 +658,23 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(DecodeParams p) {   // 4 
   }
 }
 
+template <int D, int KW, int VW, int NRG>
+__global__ __launch_bounds__(4 * D) void decode_kernel(ScanParams p) {   // 4 D = (D / 16) waves
+  scan_block<D, KW, VW, NRG, false>(p);
+}
+
+template <int D, int KW, int NRG>
+__global__ __launch_bounds__(4 * D) void logits_kernel(ScanParams p) {
+  scan_block<D, KW, 1, NRG, true>(p);
+}
+
 // Merge of the split partials of one (batch, kv-head) group and head chunk
 // (8 heads): log-sum-exp weights over the blocks, division by the softmax
 // sum, inverse rotation out = diag(s_v) H acc / sqrt(D), store. A kernel of
-// its own: the partials are visible to it without any device-wide fence.
+// its own: the partials are visible to it without any device-wide fence
+// (inside one kernel that fence writes back every XCD's L2 per block).
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void merge_kernel(ScanParams p) {
   __shared__ float ob[8][D];
   __shared__ float se[8][kDecodeMaxBlocks];
   __shared__ float sL[8];
@@ -786,7 +685,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.n_kv;
   const int64_t kvh = bh % p.n_kv;
-  const int nb = p.n_splits;
+  const int nb = p.nb;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const float *pbase = p.partials + bh * nb * G * (D + 2);
   const int64_t pstride = static_cast<int64_t>(G) * (D + 2);
@@ -842,20 +741,49 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   }
 }
 
+// ------------------------------------------------------------------ dispatch
+
 template <int D, int KW, int VW>
-static void launch_decode_kv(const DecodeParams &p, dim3 grid, hipStream_t st) {
-  dim3 block(DecodeShape<D, KW, VW>::THREADS);
+static void launch_decode_kv(const ScanParams &p, dim3 grid, hipStream_t st) {
+  dim3 block(4 * D);
   if (p.group - p.h0 > 4) hipLaunchKernelGGL((decode_kernel<D, KW, VW, 2>), grid, block, 0, st, p);
   else hipLaunchKernelGGL((decode_kernel<D, KW, VW, 1>), grid, block, 0, st, p);
 }
 
+template <int D, int KW>
+static void launch_logits_k(const ScanParams &p, dim3 grid, hipStream_t st) {
+  dim3 block(4 * D);
+  if (p.group - p.h0 > 4) hipLaunchKernelGGL((logits_kernel<D, KW, 2>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((logits_kernel<D, KW, 1>), grid, block, 0, st, p);
+}
+
+// Head chunks of 8 heads: every launch reads the keys (and values) once for
+// its chunk.
 template <int D>
-hipError_t launch_decode_d(const DecodeParams &p0, int kw, int vw, hipStream_t st) {
-  if (p0.batch == 0 || p0.n_kv == 0) return hipSuccess;
-  // n_splits here is the number of blocks per (batch, kv-head) group
-  dim3 grid(static_cast<uint32_t>(p0.n_splits), static_cast<uint32_t>(p0.batch) * p0.n_kv);
+hipError_t launch_logits_d(const ScanParams &p0, int kw, hipStream_t st) {
+  if (p0.batch == 0 || p0.n_kv == 0 || p0.max_ctx == 0) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>(p0.nb), static_cast<uint32_t>(p0.batch) * p0.n_kv);
   for (int hc = 0; hc < p0.n_hchunks; ++hc) {
-    DecodeParams p = p0;
+    ScanParams p = p0;
+    p.h0 = 8 * hc;
+    switch (kw) {
+      case 1: launch_logits_k<D, 1>(p, grid, st); break;
+      case 2: launch_logits_k<D, 2>(p, grid, st); break;
+      case 3: launch_logits_k<D, 3>(p, grid, st); break;
+      default: launch_logits_k<D, 4>(p, grid, st);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_decode_d(const ScanParams &p0, int kw, int vw, hipStream_t st) {
+  if (p0.batch == 0 || p0.n_kv == 0) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>(p0.nb), static_cast<uint32_t>(p0.batch) * p0.n_kv);
+  for (int hc = 0; hc < p0.n_hchunks; ++hc) {
+    ScanParams p = p0;
     p.h0 = 8 * hc;
 #define TQ_DS_V(KK)                                          \
     switch (vw) {                                            \

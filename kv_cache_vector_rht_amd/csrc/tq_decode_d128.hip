@@ -1,8 +1,7 @@
-// Query preparation, logit scan and decode attention for head dimension 128.
+// Logit scan and decode attention for head dimension 128.
 #include "tq_decode.inc.h"
 
 namespace tq {
-template hipError_t launch_query_prep_d<128>(const QueryPrepParams &p, hipStream_t st);
-template hipError_t launch_logits_d<128>(const LogitsParams &p, int w, hipStream_t st);
-template hipError_t launch_decode_d<128>(const DecodeParams &p, int kw, int vw, hipStream_t st);
+template hipError_t launch_logits_d<128>(const ScanParams &p, int kw, hipStream_t st);
+template hipError_t launch_decode_d<128>(const ScanParams &p, int kw, int vw, hipStream_t st);
 }  // namespace tq

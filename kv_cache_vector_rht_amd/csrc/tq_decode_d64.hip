@@ -1,8 +1,7 @@
-// Query preparation, logit scan and decode attention for head dimension 64.
+// Logit scan and decode attention for head dimension 64.
 #include "tq_decode.inc.h"
 
 namespace tq {
-template hipError_t launch_query_prep_d<64>(const QueryPrepParams &p, hipStream_t st);
-template hipError_t launch_logits_d<64>(const LogitsParams &p, int w, hipStream_t st);
-template hipError_t launch_decode_d<64>(const DecodeParams &p, int kw, int vw, hipStream_t st);
+template hipError_t launch_logits_d<64>(const ScanParams &p, int kw, hipStream_t st);
+template hipError_t launch_decode_d<64>(const ScanParams &p, int kw, int vw, hipStream_t st);
 }  // namespace tq

@@ -23,59 +23,38 @@ struct EncodeParams {
 template <int D>
 hipError_t launch_encode_d(const EncodeParams &p, int w, bool key, hipStream_t st);
 
-// Query preparation for one (batch, kv-head) group of `group` query heads:
-// q' = R q, p = S q', the fixed-point MFMA operands for the key planes and
-// the QJL plane, and per-head float constants (see tq_mfma.h).
-struct QueryPrepParams {
+// Logit scan and decode attention over the coded cache (one parameter block
+// for both; the logit scan leaves the value fields unset).
+struct ScanParams {
+  // queries and the key codec (the scan kernels prepare the queries)
   const void *q;                        // [batch][n_kv*group][D]
   int xt;
-  int32_t batch, n_kv, group;
-  int32_t kw;                           // key Lloyd-Max bits
-  const float *signs, *centroids;
+  const float *ksigns, *kcent;
   const uint16_t *sketch;
-  uint8_t *out;                         // [batch*n_kv][group_bytes]
-  size_t group_bytes;
-};
-
-template <int D>
-hipError_t launch_query_prep_d(const QueryPrepParams &p, hipStream_t st);
-
-struct LogitsParams {
-  const uint8_t *qprep;                 // prepared groups, group_bytes apart
-  size_t group_bytes, frag_bytes;
-  const uint8_t *kcodes;
-  const uint16_t *kscalars;
-  int64_t cap, n_keys;
-  int32_t batch, n_kv, group;
-  float *logits;                        // [batch][n_q][n_keys]
-};
-
-template <int D>
-hipError_t launch_logits_d(const LogitsParams &p, int w, hipStream_t st);
-
-struct DecodeParams {
-  const uint8_t *qprep;
-  size_t group_bytes, frag_bytes;
+  // caches, `cap` slots per sequence
   const uint8_t *kcodes;
   const uint16_t *kscalars;
   const uint32_t *vcodes;
   const uint16_t *vscalars;
   const float *vcent, *vsigns;
-  int64_t cap, max_ctx;
-  const int32_t *ctx_lens;
+  int64_t cap;
+  int64_t max_ctx;                      // logits: n_keys
+  const int32_t *ctx_lens;              // decode: per batch row (null: max_ctx)
   int32_t batch, n_kv, group;
   int32_t h0;                           // first head of this launch's head chunk (multiple of 8)
   int32_t n_hchunks;                    // ceil(group / 8)
-  int32_t split;                        // tokens per context split (kDecodeSplit)
-  int32_t n_splits;                     // blocks per (batch, kv-head) group
+  int32_t nb;                           // blocks per (batch, kv-head) group
   float sm_scale;
-  float *partials;                      // [batch*n_kv][blocks per group][group][D+2]
-  void *out;
+  float *partials;                      // decode: [batch*n_kv][nb][group][D+2]
+  void *out;                            // decode: [batch][n_kv*group][D]
   int out_t;
+  float *logits;                        // logits: [batch][n_kv*group][max_ctx]
 };
 
 template <int D>
-hipError_t launch_decode_d(const DecodeParams &p, int kw, int vw, hipStream_t st);
+hipError_t launch_logits_d(const ScanParams &p, int kw, hipStream_t st);
+template <int D>
+hipError_t launch_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st);
 
 // Tokens per split of the decode kernel (one pipeline stage), and the most
 // blocks one (batch, kv-head) group is spread over.

@@ -112,17 +112,4 @@ __device__ __forceinline__ int fixed_exponent(float max_abs) {
   return 23 - E;
 }
 
-// Prepared-query block of one (batch, kv-head) group in the workspace:
-//   bytes  [RG][NMF][64 lanes][16]   A operands, RG = ceil(G/4),
-//          NMF = (planes + 1) * D/64 (key planes, then the QJL plane)
-//   floats [G][4]                    {inv_lm, cst_lm, inv_qj, cst_qj}
-__host__ __device__ inline size_t qprep_frag_bytes(int d, int w, int group) {
-  const int rg = (group + 3) / 4;
-  return static_cast<size_t>(rg) * (basis_size(w) + 1) * (d / 64) * 64 * 16;
-}
-__host__ __device__ inline size_t qprep_group_bytes(int d, int w, int group) {
-  const size_t b = qprep_frag_bytes(d, w, group) + static_cast<size_t>(group) * 4 * sizeof(float);
-  return (b + 255) / 256 * 256;
-}
-
 }  // namespace tq

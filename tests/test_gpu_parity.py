@@ -142,11 +142,13 @@ def test_encode_is_deterministic():
 @pytest.mark.parametrize("d,w,group,batch,n_kv,n_keys", [
     (128, 2, 16, 1, 1, 1000), (128, 3, 4, 2, 3, 777), (64, 2, 4, 2, 2, 513), (64, 1, 1, 1, 2, 65),
     (128, 1, 8, 1, 1, 1), (64, 3, 5, 1, 1, 200),
+    # 256 (batch, kv-head) groups: one block per group walks all 4 splits
+    (128, 3, 4, 4, 64, 1000),
 ])
 def test_logits_given_oracle_codes(d, w, group, batch, n_kv, n_keys):
     say(f"logits d={d} w={w} G={group} batch={batch} n_kv={n_kv} n_keys={n_keys}")
     kc = key_codec(600 + d + w, d, w)
-    cap = n_keys + 11
+    cap = (n_keys + 11 + 31) // 32 * 32
     k = _inputs(batch * n_kv, n_keys, d, torch.float32, seed=w, scale_channels=True)
     q = _inputs(batch, n_kv * group, d, torch.bfloat16, seed=w, stream=3)
     enc = kc.encode(to_f64(k))
@@ -175,6 +177,9 @@ def test_logits_given_oracle_codes(d, w, group, batch, n_kv, n_keys):
     (64, 2, 4, 4, 2, 2, 300, [300, 64]),
     (64, 1, 2, 1, 1, 3, 96, [95]),
     (128, 2, 3, 16, 1, 1, 64, [37]),
+    # 256 (batch, kv-head) groups: one block per group walks up to 5 splits
+    # through the staging ring (ragged lengths, one empty row)
+    (128, 2, 4, 4, 32, 8, 1100, [1100, 1, 700, 0, 257, 1024, 1099, 513] * 4),
 ])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_decode_attend_given_oracle_codes(d, kw, vw, group, batch, n_kv, T, lens, out_dtype):

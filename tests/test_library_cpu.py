@@ -129,13 +129,13 @@ def test_logits_validation():
     assert _logits(_codec(key=0)) == tq.TQ_EINVAL
     assert _logits(_codec(), n_keys=2048) == tq.TQ_EINVAL
     assert _logits(_codec(), group=33) == tq.TQ_EUNSUPPORTED
-    assert _logits(_codec(), ws=16) == tq.TQ_EINVAL
-    assert _logits(_codec(), ws_ptr=FAKE + 64) == tq.TQ_EINVAL
+    assert _logits(_codec(), cap=1000, n_keys=1000) == tq.TQ_EINVAL        # cap not a multiple of 32
+    assert _logits(_codec(), cap=1 << 27, n_keys=64) == tq.TQ_EUNSUPPORTED  # a sequence above 4 GiB
     assert _logits(_codec(), q=0) == tq.TQ_EINVAL
     assert _logits(_codec(), qt=9) == tq.TQ_EINVAL
     assert _logits(_codec(), batch=-1) == tq.TQ_EINVAL
     assert _logits(_codec(), n_keys=0) == tq.TQ_OK
-    assert tq.logits_workspace(1, 8, 4, 128) >= 8 * (9 * 2 * 1024 + 4 * 4 * 4)
+    assert tq.logits_workspace(1, 8, 4, 128) == 0                           # queries are prepared in LDS
 
 
 def _decode(kc, vc, batch=2, n_kv=2, group=4, cap=256, max_ctx=256, scale=0.1, out_t=tq.TQ_F32, ws=None,
@@ -158,6 +158,7 @@ def test_decode_validation():
     assert _decode(k, v, group=33) == tq.TQ_EUNSUPPORTED
     assert _decode(k, v, scale=float("nan")) == tq.TQ_EINVAL
     assert _decode(k, v, ws=64) == tq.TQ_EINVAL
+    assert _decode(k, v, cap=1 << 27, max_ctx=256) == tq.TQ_EUNSUPPORTED   # a sequence above 4 GiB
     assert _decode(k, v, ctx=0) == tq.TQ_EINVAL
     assert _decode(k, v, batch=0) == tq.TQ_OK
     assert tq.decode_attend_workspace(4, 8, 8, 131072, 128) > 0
