@@ -137,7 +137,8 @@ tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_
  *   logit = n * ( sum_i q'_i c[idx_i]
  *                 + sqrt(pi/2)/d * gamma * sum_j p_j (2 sigma_j - 1) ),
  *   q' = R q, p = S q', n and gamma the stored fp16 norms.
- *   q        device [batch][n_kv_heads*group][d], dtype qt
+ *   q        device [batch][n_kv_heads*group][d], dtype qt, 16-byte aligned
+ *            (as are the codec's signs and sketch)
  *   query head h of batch b reads key sequence b*n_kv_heads + h/group
  *   kcodes, kscalars  key cache (layout above) with `cap` slots per
  *            sequence; cap a multiple of 32, both arrays 16-byte aligned,
@@ -158,7 +159,8 @@ size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int
  * softmax of sm_scale*logit over tokens t < ctx_lens[b], and the weighted sum
  * of the decoded values n_t R_v^T c_v[idx_t] (accumulated in the rotated
  * domain, rotated back once per output row).
- *   q        device [batch][n_kv_heads*group][d], dtype qt
+ *   q        device [batch][n_kv_heads*group][d], dtype qt, 16-byte aligned
+ *            (as are the key codec's signs and sketch)
  *   kcodes, kscalars, vcodes, vscalars  key and value caches, `cap` slots
  *   ctx_lens device int32 [batch]; values are clamped to [0, max_ctx]; a
  *            row with no tokens gets zeros

@@ -82,6 +82,12 @@ bool seq_offsets_fit(int64_t cap, int bytes_per_token) {
   return cap * static_cast<int64_t>(bytes_per_token) < (static_cast<int64_t>(1) << 32);
 }
 
+// The scan kernels stage the queries, signs and sketch with 16-byte loads.
+bool staged_inputs_aligned(const tq_codec *kc, const void *q) {
+  return reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(kc->signs) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(kc->sketch) % 16 == 0;
+}
+
 // Common part of the scan parameters (queries, key codec, key cache).
 tq::ScanParams scan_params(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
                            int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap,
@@ -222,6 +228,7 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
   if (!q || !kcodes || !kscalars || !logits) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
   if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 16)
     return fail(TQ_EINVAL, "%s: kcodes and kscalars must be 16-byte aligned", fn);
+  if (!staged_inputs_aligned(kc, q)) return fail(TQ_EINVAL, "%s: q, signs and sketch must be 16-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
   tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys);
   sp.logits = logits;
@@ -264,6 +271,7 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 16 ||
       reinterpret_cast<uintptr_t>(vcodes) % 16 || reinterpret_cast<uintptr_t>(vscalars) % 16)
     return fail(TQ_EINVAL, "%s: cache arrays must be 16-byte aligned", fn);
+  if (!staged_inputs_aligned(kc, q)) return fail(TQ_EINVAL, "%s: q, signs and sketch must be 16-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
   tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, max_ctx);
   sp.vcodes = vcodes;

@@ -214,111 +214,164 @@ __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t
 
 // ------------------------------------------------------------------ query prep
 
-// Scratch of the in-block query preparation (bytes): the int8 digit
-// operands [NRG][NMF][64 lanes][16], q' and p [8][D] floats, per-head
-// statistics [8][4] and constants [8][4], basis coefficients [8].
+// Scratch of the in-block query preparation (byte offsets):
+//   FRAG   int8 digit operands [NRG][NMF][64 lanes][16]
+//   SQ, SP q' and p, [8][D] float
+//   SST    per-head exponents [8][4]; SCON per-head constants [8][4];
+//   SB     key basis coefficients [8]
+//   SK     the sketch [D][D] fp16, staged by direct-to-LDS loads
+//   QIN    the raw query rows [8][D] (input dtype) then the signs [D] float,
+//          staged by direct-to-LDS loads
 template <int D, int KW, int NRG>
 struct PrepShape {
   static constexpr int NB = Basis<KW>::N;
   static constexpr int NMF = (NB + 1) * (D / 64);
   static constexpr int FRAG = NRG * NMF * 1024;
-  static constexpr int BYTES = FRAG + 2 * 8 * D * 4 + 8 * 4 * 4 * 2 + 8 * 4;
+  static constexpr int SQ = FRAG;
+  static constexpr int SP = SQ + 8 * D * 4;
+  static constexpr int SST = SP + 8 * D * 4;
+  static constexpr int SCON = SST + 8 * 4 * 4;
+  static constexpr int SB = SCON + 8 * 4 * 4;
+  static constexpr int SK = SB + 64;
+  static constexpr int QIN = SK + D * D * 2;
+  static constexpr int QIN_BYTES = (D / 16) * 1024;  // one load per wave
+  static constexpr int BYTES = QIN + QIN_BYTES;
 };
 
-// Query preparation of the heads [h0, h0 + GE) (GE <= 4 NRG) of group bh by
-// one block of THREADS threads (4 D): q' = R q, p = S q', then the digit
-// operands of the key planes (2 beta_s q') and of the sign plane (2 p), one
-// fixed-point exponent per head for each, and the per-head constants
-// {2^-(7+e_lm), c[L-1] sum q', 2^-(7+e_qj), sum p}. Rows of absent heads
-// stay zero. Results in `scratch` (PrepShape layout).
+// Stage the preparation's inputs into the scratch: the sketch (every wave
+// an equal share) and the query rows of heads [h0, h0 + GE) plus the signs
+// (one load per wave; lanes past the end idle).
 template <int D, int KW, int NRG>
-__device__ __forceinline__ void group_prep(const ScanParams &p, int64_t bh, int GE, uint8_t *scratch) {
+__device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int GE, uint8_t *scratch, int wave) {
+  using PS = PrepShape<D, KW, NRG>;
+  constexpr int NW = D / 16;
+  constexpr int SKI = D * D * 2 / 1024 / NW;           // sketch loads per wave (4 or 2)
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < SKI; ++i) {
+    const int chunk = wave * SKI + i;
+    dma16(p.sketch, static_cast<uint32_t>(chunk * 1024 + lane * 16), scratch + PS::SK + chunk * 1024);
+  }
+  const int es = (p.xt == 0) ? 4 : 2;
+  const int q_units = GE * D * es / 16;
+  const int unit = wave * kWave + lane;
+  const int G = p.group, n_q = p.n_kv * G;
+  const int64_t row0 = (bh / p.n_kv) * n_q + (bh % p.n_kv) * G + p.h0;
+  if (unit < q_units) {
+    dma16_at(static_cast<const uint8_t *>(p.q) + row0 * D * es + unit * 16, scratch + PS::QIN + wave * 1024);
+  } else if (unit < q_units + D / 4) {
+    dma16_at(p.ksigns + (unit - q_units) * 4, scratch + PS::QIN + wave * 1024);
+  }
+}
+
+// Query preparation of the heads [h0, h0 + GE) (GE <= 4 NRG) of group bh by
+// one block of 4 D threads, from the staged inputs: q' = R q, p = S q', the
+// digit operands of the key planes (2 beta_s q') and of the sign plane
+// (2 p), one fixed-point exponent per head for each, and the per-head
+// constants {2^-(7+e_lm), c[L-1] sum q', 2^-(7+e_qj), sum p}. Rows of absent
+// heads stay zero.
+template <int D, int KW, int NRG>
+__device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t *scratch) {
   using PS = PrepShape<D, KW, NRG>;
   constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64;
-  constexpr int THREADS = 4 * D;
+  constexpr int THREADS = 4 * D, NW = D / 16;
   constexpr int PARTS = THREADS / D;                 // threads per sketch row
-  float *sq = reinterpret_cast<float *>(scratch + PS::FRAG);     // [8][D]
-  float *sp = sq + 8 * D;                                        // [8][D]
-  float *sst = sp + 8 * D;                                       // [8][4]
-  float *scon = sst + 32;                                        // [8][4]
-  float *sb = scon + 32;                                         // [8]
+  float *sq = reinterpret_cast<float *>(scratch + PS::SQ);      // [8][D]
+  float *sp = reinterpret_cast<float *>(scratch + PS::SP);      // [8][D]
+  float *sst = reinterpret_cast<float *>(scratch + PS::SST);    // [8][4]
+  float *scon = reinterpret_cast<float *>(scratch + PS::SCON);  // [8][4]
+  float *sb = reinterpret_cast<float *>(scratch + PS::SB);      // [8]
+  const uint16_t *ssk = reinterpret_cast<const uint16_t *>(scratch + PS::SK);
+  const uint8_t *qin = scratch + PS::QIN;
+  const float *sgn = reinterpret_cast<const float *>(qin + GE * D * ((p.xt == 0) ? 4 : 2));
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  const int G = p.group, n_q = p.n_kv * G;
-  const int64_t b = bh / p.n_kv, kvh = bh % p.n_kv;
-  const int64_t row0 = b * n_q + kvh * G + p.h0;
-
-  // this thread's sketch row j (fp16 pairs), loaded up front
-  const int j = tid % D, part = tid / D;
-  uint4 srow[D / 8];
-#pragma unroll
-  for (int k = 0; k < D / 8; ++k) srow[k] = reinterpret_cast<const uint4 *>(p.sketch + j * D)[k];
-  for (int e = tid; e < 8 * D; e += THREADS) {
-    const int h = e / D, i = e % D;
-    float v = 0.f;
-    if (h < GE) {
-      const int64_t at = (row0 + h) * D + i;
-      if (p.xt == 0) v = static_cast<const float *>(p.q)[at];
-      else if (p.xt == 1) v = bf16_bits_to_float(static_cast<const uint16_t *>(p.q)[at]);
-      else v = f16_bits_to_float(static_cast<const uint16_t *>(p.q)[at]);
-      v *= p.ksigns[i];
-    }
-    sq[e] = v;
-  }
   if (tid < NB) sb[tid] = basis_coeff(p.kcent, KW, basis_mask(KW, tid));
-  lds_barrier();
-  // q' = H (s q) / sqrt(D), in place
-  for (int hs = 1; hs < D; hs <<= 1) {
-    for (int e = tid; e < GE * D / 2; e += THREADS) {
-      const int h = e / (D / 2), r = e % (D / 2);
-      const int i = (r / hs) * 2 * hs + (r % hs);
-      const float x = sq[h * D + i], y = sq[h * D + i + hs];
-      sq[h * D + i] = x + y;
-      sq[h * D + i + hs] = x - y;
+
+  // q' = H (s q) / sqrt(D): one wave per head, in registers (lane l holds
+  // elements l and l + 64 for D = 128, element l for D = 64)
+  constexpr int E = D / kWave;
+  for (int h = wave; h < GE; h += NW) {
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = lane + kWave * e, at = h * D + i;
+      float v;
+      if (p.xt == 0) v = reinterpret_cast<const float *>(qin)[at];
+      else if (p.xt == 1) v = bf16_bits_to_float(reinterpret_cast<const uint16_t *>(qin)[at]);
+      else v = f16_bits_to_float(reinterpret_cast<const uint16_t *>(qin)[at]);
+      x[e] = v * sgn[i];
     }
-    lds_barrier();
-  }
-  for (int e = tid; e < GE * D; e += THREADS) sq[e] *= 1.0f / sqrtf(static_cast<float>(D));
-  lds_barrier();
-  // p_j = sum_k S[j][k] q'_k for the heads part, part + PARTS, ...
-  for (int h = part; h < GE; h += PARTS) {
-    float acc = 0.f;
+    if constexpr (E == 2) {
+      const float a0 = x[0] + x[1], a1 = x[0] - x[1];
+      x[0] = a0;
+      x[1] = a1;
+    }
 #pragma unroll
-    for (int k = 0; k < D / 8; ++k) {
-      const uint32_t w[4] = {srow[k].x, srow[k].y, srow[k].z, srow[k].w};
+    for (int hs = 1; hs < kWave; hs <<= 1) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w[m] & 0xffffu)), sq[h * D + 8 * k + 2 * m], acc);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w[m] >> 16)), sq[h * D + 8 * k + 2 * m + 1], acc);
+      for (int e = 0; e < E; ++e) {
+        const float o = __shfl_xor(x[e], hs, kWave);
+        x[e] = (lane & hs) ? (o - x[e]) : (x[e] + o);
       }
     }
-    sp[h * D + j] = acc;
-  }
-  lds_barrier();
-  // statistics: max |q'|, sum q', max |p|, sum p per head
-  for (int h = wave; h < GE; h += THREADS / kWave) {
-    float mq = 0.f, s1 = 0.f, mp = 0.f, s2 = 0.f;
+    float mq = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int i = lane; i < D; i += kWave) {
-      mq = fmaxf(mq, fabsf(sq[h * D + i]));
-      s1 += sq[h * D + i];
-      mp = fmaxf(mp, fabsf(sp[h * D + i]));
-      s2 += sp[h * D + i];
+    for (int e = 0; e < E; ++e) {
+      x[e] *= 1.0f / sqrtf(static_cast<float>(D));
+      sq[h * D + lane + kWave * e] = x[e];
+      mq = fmaxf(mq, fabsf(x[e]));
+      s1 += x[e];
     }
     mq = wave_max(mq);
     s1 = wave_sum(s1);
+    if (lane == 0) { sst[4 * h] = mq; sst[4 * h + 1] = s1; }
+  }
+  lds_barrier();
+  // p_j = sum_k S[j][k] q'_k: thread (row j, part) for the heads part, part + PARTS
+  {
+    const int j = tid % D, part = tid / D;
+    for (int h = part; h < GE; h += PARTS) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int k = 0; k < D; k += 8) {
+        const uint4 w4 = *reinterpret_cast<const uint4 *>(ssk + j * D + ((k + 8 * j) % D));
+        const float4 q0 = *reinterpret_cast<const float4 *>(sq + h * D + ((k + 8 * j) % D));
+        const float4 q1 = *reinterpret_cast<const float4 *>(sq + h * D + ((k + 8 * j) % D) + 4);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.x & 0xffffu)), q0.x, acc);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.x >> 16)), q0.y, acc);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.y & 0xffffu)), q0.z, acc);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.y >> 16)), q0.w, acc);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.z & 0xffffu)), q1.x, acc);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.z >> 16)), q1.y, acc);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.w & 0xffffu)), q1.z, acc);
+        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.w >> 16)), q1.w, acc);
+      }
+      sp[h * D + j] = acc;
+    }
+  }
+  lds_barrier();
+  // p statistics and the per-head exponents and constants
+  for (int h = wave; h < GE; h += NW) {
+    float mp = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float v = sp[h * D + lane + kWave * e];
+      mp = fmaxf(mp, fabsf(v));
+      s2 += v;
+    }
     mp = wave_max(mp);
     s2 = wave_sum(s2);
     if (lane == 0) {
       float mb = 0.f;
       for (int s = 0; s < NB; ++s) mb = fmaxf(mb, fabsf(sb[s]));
-      const int el = fixed_exponent(2.0f * mb * mq);
+      const int el = fixed_exponent(2.0f * mb * sst[4 * h]);
       const int eq = fixed_exponent(2.0f * mp);
-      sst[4 * h] = static_cast<float>(el);
-      sst[4 * h + 1] = static_cast<float>(eq);
       scon[4 * h] = ldexpf(1.0f, -7 - el);
-      scon[4 * h + 1] = p.kcent[(1 << KW) - 1] * s1;
+      scon[4 * h + 1] = p.kcent[(1 << KW) - 1] * sst[4 * h + 1];
       scon[4 * h + 2] = ldexpf(1.0f, -7 - eq);
       scon[4 * h + 3] = s2;
+      sst[4 * h + 2] = static_cast<float>(el);
+      sst[4 * h + 3] = static_cast<float>(eq);
     }
   }
   lds_barrier();
@@ -333,7 +386,7 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int64_t bh, int 
       const int plane = qjl ? 0 : mf / NH;
       const int half = mf % NH;
       const float coef = qjl ? 2.0f : 2.0f * sb[plane];
-      const int e = static_cast<int>(sst[4 * hl + (qjl ? 1 : 0)]);
+      const int e = static_cast<int>(sst[4 * hl + (qjl ? 3 : 2)]);
       const float *x = (qjl ? sp : sq) + hl * D;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
@@ -356,7 +409,7 @@ __device__ __forceinline__ void load_prepared(const uint8_t *scratch, int GE, v4
                                               float4 (&fh)[NRG]) {
   using PS = PrepShape<D, KW, NRG>;
   const int lane = lane_id(), kg = lane / 16;
-  const float *scon = reinterpret_cast<const float *>(scratch + PS::FRAG) + 16 * D + 32;
+  const float *scon = reinterpret_cast<const float *>(scratch + PS::SCON);
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
 #pragma unroll
@@ -366,6 +419,21 @@ __device__ __forceinline__ void load_prepared(const uint8_t *scratch, int GE, v4
     }
     const int h = 4 * rg + kg;
     fh[rg] = (h < GE) ? *reinterpret_cast<const float4 *>(scon + 4 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// Wait until at most n_after * P of this wave's loads are in flight
+// (n_after < 8): every load issued before the last n_after splits is done.
+template <int P>
+__device__ __forceinline__ void wait_splits(int n_after) {
+  switch (n_after) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<P>(); break;
+    case 2: wait_vm<2 * P>(); break;
+    case 3: wait_vm<3 * P>(); break;
+    case 4: wait_vm<4 * P < 63 ? 4 * P : 63>(); break;
+    case 5: wait_vm<5 * P < 63 ? 5 * P : 63>(); break;
+    default: wait_vm<6 * P < 63 ? 6 * P : 63>(); break;
   }
 }
 
@@ -386,7 +454,7 @@ __device__ __forceinline__ void load_prepared(const uint8_t *scratch, int GE, v4
 //  3. contracts the weights with its value coordinates' planes on the
 //     matrix cores (int32 over the split) and folds the result into its
 //     fp32 accumulators: acc = alpha acc + split sum
-//  4. refills the stage buffer with the split kStages ahead.
+//  4. refills the stage buffer with the split NST (ring depth) ahead.
 // Decode writes the block's partial {m, l, acc} to the workspace;
 // merge_kernel combines them.
 template <int D, int KW, int VW, int NRG, bool LOGITS>
@@ -399,9 +467,19 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int GMAX = 4 * NRG;
   constexpr int NBG = (NRG == 2 && NBV == 8) ? 4 : NBV;
   constexpr int SB = SH::STAGE_BYTES;
-  constexpr int RING = (3 * SB > SB + PS::BYTES) ? 3 * SB : SB + PS::BYTES;
-  // stage k at ring + k * SB; the query preparation uses [SB, SB + PS::BYTES)
-  // before stages 1 and 2 are first filled
+  // ring depth: 3 stages for decode; the logit scan (small stages, few
+  // splits per block) keeps up to 6 in flight, its query preparation in a
+  // region of its own so that every stage can be filled before it
+  constexpr int LDS_BUDGET = 160 * 1024 - 2048;
+  constexpr int NST_L = (LDS_BUDGET - PS::BYTES) / SB < 6 ? (LDS_BUDGET - PS::BYTES) / SB : 6;
+  constexpr bool SEP = LOGITS && NST_L >= 3;
+  constexpr int NST = SEP ? NST_L : kStages;
+  constexpr int PREP_AT = SEP ? NST * SB : SB;
+  constexpr int RING = (NST * SB > PREP_AT + PS::BYTES) ? NST * SB : PREP_AT + PS::BYTES;
+  static_assert(RING <= LDS_BUDGET - (LOGITS ? 0 : NRG * VT * 1024), "LDS budget");
+  static_assert(P * (NST - 1) < 64, "vmcnt range");
+  // stage k at ring + k * SB; the query preparation uses [PREP_AT,
+  // PREP_AT + PS::BYTES), which (decode) stages 1 and 2 reuse once it is done
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
   __shared__ __attribute__((aligned(16))) uint8_t sfrag[LOGITS ? 16 : NRG * VT * 1024];
   __shared__ float spm[NW][GMAX];
@@ -447,23 +525,24 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   v4i a[NRG][NMF];
   float4 fh[NRG];
   if (ns > 0) {
-    // split 0 is in flight while the block prepares its queries
-    issue_split<D, KW, VW, LOGITS>(sa, bx, ring, wave);
-    group_prep<D, KW, NRG>(p, bh, GE, ring + SB);
-    load_prepared<D, KW, NRG>(ring + SB, GE, a, fh);
+    // the preparation's inputs, then the splits that do not overlap its
+    // scratch, are in flight together; wait for the inputs only
+    issue_prep<D, KW, NRG>(p, bh, GE, ring + PREP_AT, wave);
+    const int first = SEP ? min(ns, NST) : 1;
+    for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS>(sa, bx + k * nb, ring + k * SB, wave);
+    wait_splits<P>(first);
+    lds_barrier();
+    group_prep<D, KW, NRG>(p, GE, ring + PREP_AT);
+    load_prepared<D, KW, NRG>(ring + PREP_AT, GE, a, fh);
     lds_barrier();                                 // every wave holds its operands
-    if (ns > 1) issue_split<D, KW, VW, LOGITS>(sa, bx + nb, ring + SB, wave);
-    if (ns > 2) issue_split<D, KW, VW, LOGITS>(sa, bx + 2 * nb, ring + 2 * SB, wave);
+    for (int k = first; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS>(sa, bx + k * nb, ring + k * SB, wave);
   }
 
   for (int it = 0; it < ns; ++it) {
-    uint8_t *buf = ring + (it % kStages) * SB;
+    uint8_t *buf = ring + (it % NST) * SB;
     const int sp = bx + it * nb;
     const int n = min(S, ctx - sp * S);
-    const int ahead = min(kStages - 1, ns - 1 - it);
-    if (ahead >= 2) wait_vm<2 * P>();
-    else if (ahead == 1) wait_vm<P>();
-    else wait_vm<0>();
+    wait_splits<P>(min(NST - 1, ns - 1 - it));
     const uint8_t *wb = buf + wave * SH::WAVE_BYTES;
 
     // 1. logits of this wave's key tiles
@@ -624,9 +703,9 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
     }
 
     // 4. refill this stage (this wave's region only; its reads are done)
-    if (it + kStages < ns) {
+    if (it + NST < ns) {
       wait_lds();
-      issue_split<D, KW, VW, LOGITS>(sa, sp + kStages * nb, buf, wave);
+      issue_split<D, KW, VW, LOGITS>(sa, sp + NST * nb, buf, wave);
     }
   }
   if constexpr (LOGITS) return;
