@@ -32,23 +32,59 @@ __device__ __forceinline__ void write_lane(uint32_t &dst, uint32_t value) {
   asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(dst) : "s"(v), "i"(LANE));
 }
 
-// Lloyd-Max decision idx = #{j : y >= t_j} over sorted thresholds. Up to
-// two bits: count the thresholds. Wider: binary search, reading the
-// candidate threshold of each level from LDS (s_th).
-template <int W>
-__device__ __forceinline__ int quantize(float y, const float (&t)[(1 << W) - 1], const float *s_th) {
-  int idx = 0;
-  if constexpr (W <= 2) {
-#pragma unroll
-    for (int j = 0; j < (1 << W) - 1; ++j) idx += (y >= t[j]) ? 1 : 0;
+// Lloyd-Max decisions by binary search over the sorted thresholds, most
+// significant bit first: bit l of idx = [y >= t[((P << 1) | 1) << l) - 1]],
+// P the bits above l. This gives idx = #{j : t_j <= y} (ties go up). The
+// candidate thresholds sit in registers; pick() selects among them with the
+// bits already decided (a tree of selects, no memory access).
+template <int NB, int OFF, int N>
+__device__ __forceinline__ float pick(const float (&cand)[N], const bool *dec) {
+  if constexpr (NB == 0) {
+    return cand[OFF];
   } else {
-#pragma unroll
-    for (int level = W - 1; level >= 0; --level) {
-      const int cand = idx | (1 << level);
-      idx = (y >= s_th[cand - 1]) ? cand : idx;
-    }
+    const float hi = pick<NB - 1, OFF + (1 << (NB - 1))>(cand, dec + 1);
+    const float lo = pick<NB - 1, OFF>(cand, dec + 1);
+    return dec[0] ? hi : lo;
   }
-  return idx;
+}
+
+// Thresholds grouped by level: lvl[l] holds the 2^(W-1-l) candidates of
+// level l, indexed by the higher bits.
+template <int W>
+struct Levels {
+  float t[(1 << W) - 1];
+  __device__ __forceinline__ void load(const float *th) {
+    int at = 0;
+#pragma unroll
+    for (int l = W - 1; l >= 0; --l)
+#pragma unroll
+      for (int P = 0; P < (1 << (W - 1 - l)); ++P) t[at++] = th[(((P << 1) | 1) << l) - 1];
+  }
+};
+
+// dec[0] is the most significant bit (W - 1), dec[W-1] bit 0.
+template <int W>
+__device__ __forceinline__ void decide(float y, const Levels<W> &lv, bool (&dec)[W]) {
+  static_for<0, W>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    dec[k] = y >= pick<k, (1 << k) - 1>(lv.t, dec);
+  });
+}
+
+// c[idx] of a symmetric codebook (c[L-1-i] = -c[i]) from the decided bits:
+// the upper half holds c_up[k], k = the lower bits; the lower half mirrors
+// it with the lower bits inverted and the sign flipped.
+template <int W>
+__device__ __forceinline__ float centroid(const float (&c_up)[(1 << W) / 2], const bool (&dec)[W]) {
+  if constexpr (W == 1) {
+    return dec[0] ? c_up[0] : -c_up[0];
+  } else {
+    bool k[W - 1];
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i) k[i] = dec[i + 1] == dec[0];
+    const float cp = pick<W - 1, 0>(c_up, k);
+    return dec[0] ? cp : -cp;
+  }
 }
 
 // The other half-wave's copy of x (lane l <-> lane l ^ 32).
@@ -112,21 +148,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   for (int i = 0; i < C; ++i) v[i] *= s_sign[C * hv + i];
   fwht_regs<C>(v);
   if (LPT == 2) {
-    // stage 7: y_i = v_i + v_{i+64} (lane t), y_{i+64} = v_i - v_{i+64} (lane t + 32)
+    // stage 7: y_i = v_i + v_{i+64} (lane t), y_{i+64} = v_i - v_{i+64} (lane t + 32).
+    // Swapping a value with itself across half-waves leaves the lower
+    // half's copy (v_i) in the first register and the upper half's
+    // (v_{i+64}) in the second, in every lane.
     const float sgn = hv ? -1.f : 1.f;
 #pragma unroll
-    for (int i = 0; i < C; ++i) v[i] = fmaf(sgn, v[i], swap_half_f(v[i]));
+    for (int i = 0; i < C; ++i) {
+      const uint32_t u = __float_as_uint(v[i]);
+      auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      v[i] = fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+    }
   }
   const float inv = (n > 0.f) ? 1.0f / (n * sqrtf(static_cast<float>(D))) : 0.f;
 #pragma unroll
   for (int i = 0; i < C; ++i) v[i] *= inv;
 
-  float th[L - 1];
-#pragma unroll
-  for (int j = 0; j < L - 1; ++j) th[j] = s_th[j];
+  Levels<W> lv;
+  lv.load(s_th);
 
   if (KEY) {
-    // (a3) indices -> this lane's half of every plane; (a4) residual
+    // (a3) indices -> this lane's half of every plane: each decision's lane
+    // mask is added in as the carry of plane + plane, coordinate 31 first,
+    // so coordinate i lands on bit i % 32;
+    // (a4) residual, kept as r' = 2^10 r = fma(y, 2^10, -2^10 c) (exactly
+    // 2^10 times the rounded y - c), the scale the QJL projection wants
+    float c_up[L / 2];
+#pragma unroll
+    for (int j = 0; j < L / 2; ++j) c_up[j] = 1024.0f * s_cent[L / 2 + j];
     uint32_t planes[W][NWL];
 #pragma unroll
     for (int q = 0; q < W; ++q)
@@ -134,21 +183,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       for (int k = 0; k < NWL; ++k) planes[q][k] = 0u;
     float g2 = 0.f;
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const int idx = quantize<W>(v[i], th, s_th);
+    for (int i = C - 1; i >= 0; --i) {
+      bool dec[W];
+      decide<W>(v[i], lv, dec);
 #pragma unroll
       for (int q = 0; q < W; ++q) {
-        planes[q][i / 32] |= static_cast<uint32_t>((idx >> q) & 1) << (i % 32);
-        asm volatile("" : "+v"(planes[q][i / 32]));   // materialise the bit now
+        const uint64_t m = __ballot(dec[W - 1 - q]);
+        uint64_t carry;
+        asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(planes[q][i / 32]), "=s"(carry) : "s"(m));
       }
-      v[i] = v[i] - s_cent[idx];
-      g2 = fmaf(v[i], v[i], g2);
+      v[i] = fmaf(v[i], 1024.0f, -centroid<W>(c_up, dec));
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int i = 0; i < C; ++i) g2 = fmaf(v[i], v[i], g2);
     if (LPT == 2) {
       const float o = swap_half_f(g2);
       g2 = hv ? (o + g2) : (g2 + o);
     }
-    const float gamma = sqrtf(g2);
+    const float gamma = sqrtf(g2) * (1.0f / 1024.0f);
 
     // (a5) QJL sign bits sigma_j = [ (S r)_j >= 0 ], on the matrix cores
     uint32_t sig[D / 32];
@@ -178,10 +231,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     for (int q = 0; q < W; ++q) { lo[q] = 0u; hi[q] = 0u; }
     static_for<0, C>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const int idx = quantize<W>(v[i], th, s_th);
+      bool dec[W];
+      decide<W>(v[i], lv, dec);
 #pragma unroll
       for (int q = 0; q < W; ++q) {
-        const uint64_t m = __ballot(active && ((idx >> q) & 1));
+        const uint64_t m = __ballot(active && dec[W - 1 - q]);
         write_lane<i>(lo[q], static_cast<uint32_t>(m));
         write_lane<i>(hi[q], static_cast<uint32_t>(m >> 32));
       }

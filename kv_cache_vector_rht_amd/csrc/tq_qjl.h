@@ -9,7 +9,8 @@
 // (exact) and split as r = hi + lo in fp16 (22 significant bits; the scaling
 // keeps lo out of the fp16 subnormal range), so two MFMAs with fp32
 // accumulation give the projection to about 2^-22 relative, far inside the
-// 1e-6 decision margin. The signs come back per token: the C tile holds, in
+// 1e-6 decision margin. The residual arrives already scaled by 2^10. The
+// signs come back per token: the C tile holds, in
 // lane l, column l%32 (a token) and 16 of the 32 rows (projection indices);
 // a lane swap merges the two halves into the token's 32-bit word.
 #pragma once
@@ -40,6 +41,19 @@ __device__ __forceinline__ void swap_halves(V8H &x, V8H &y) {
   }
 }
 
+// Two residual coordinates (already scaled by 2^10) as fp16 hi and lo parts,
+// each pair packed in one dword: hi = fp16(a) rounded toward zero, lo =
+// fp16(a - hi) likewise (a - hi is exact in fp32), so hi + lo carries 22
+// significant bits of a.
+__device__ __forceinline__ void split_pair(float a0, float a1, uint32_t &hi, uint32_t &lo) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(a0, a1);
+  const float d0 = a0 - static_cast<float>(h[0]);
+  const float d1 = a1 - static_cast<float>(h[1]);
+  const auto l = __builtin_amdgcn_cvt_pkrtz(d0, d1);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // Stage the fp16 sketch [D][D] in LDS with rows padded by 8 halves. The
 // block has 256 threads; all loads are issued before the first store.
 template <int D>
@@ -57,7 +71,7 @@ __device__ __forceinline__ void stage_sketch(const uint16_t *__restrict__ sketch
   }
 }
 
-// r: this lane's 64 residual coordinates (consumed); sig: the D/32 sign
+// r: this lane's 64 residual coordinates times 2^10 (consumed); sig: the D/32 sign
 // words of this lane's token.
 //  d = 64  (one lane per token, 64 tokens): two 32-token N tiles; the
 //          lane-swap supplies the other half-wave's coordinates.
@@ -75,12 +89,7 @@ __device__ __forceinline__ void qjl_signs_mfma(const uint16_t *s_sk, float (&r)[
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float a = r[8 * ks + e] * 1024.0f;
-        const _Float16 ah = static_cast<_Float16>(a);
-        bh[ks].h[e] = ah;
-        bl[ks].h[e] = static_cast<_Float16>(a - static_cast<float>(ah));
-      }
+      for (int e = 0; e < 8; e += 2) split_pair(r[8 * ks + e], r[8 * ks + e + 1], bh[ks].u[e / 2], bl[ks].u[e / 2]);
     }
 #pragma unroll
     for (int jt = 0; jt < D / 32; ++jt) {
@@ -109,15 +118,9 @@ __device__ __forceinline__ void qjl_signs_mfma(const uint16_t *s_sk, float (&r)[
     for (int ks = 0; ks < KS; ++ks) {
       V8H xh, xl, yh, yl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float a = r[16 * ks + e] * 1024.0f;
-        const float b = r[16 * ks + 8 + e] * 1024.0f;
-        const _Float16 ah = static_cast<_Float16>(a);
-        const _Float16 bh = static_cast<_Float16>(b);
-        xh.h[e] = ah;
-        xl.h[e] = static_cast<_Float16>(a - static_cast<float>(ah));
-        yh.h[e] = bh;
-        yl.h[e] = static_cast<_Float16>(b - static_cast<float>(bh));
+      for (int e = 0; e < 8; e += 2) {
+        split_pair(r[16 * ks + e], r[16 * ks + e + 1], xh.u[e / 2], xl.u[e / 2]);
+        split_pair(r[16 * ks + 8 + e], r[16 * ks + 8 + e + 1], yh.u[e / 2], yl.u[e / 2]);
       }
       swap_halves(xh, yh);
       swap_halves(xl, yl);
