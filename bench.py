@@ -12,8 +12,10 @@ one of `--copies` independent input/cache sets (together > 1 GiB) so that
 the 256 MB Infinity Cache cannot hold the working set.
 
 Printed: one JSON line. `value` is q.k logits per second over whole steps
-(encode + query preparation + logit scan). Per-kernel times come from HIP
-events recorded on the launch stream around every call in the timed region;
+(encode + logit scan with its query preparation), each step one HIP-graph
+replay of the two library calls on a fresh input copy, timed with HIP
+events on the replay stream. Per-kernel times come from graphs of
+back-to-back calls of one kind (HIP events around their replays);
 `roofline` prices the kernel with the largest share of the step against
 HBM's 8 TB/s with the algorithmic bytes it must move. The extras time the
 fused decode attention on the batched (16 x 8192) and long-context
@@ -48,27 +50,38 @@ def parse():
     return ap.parse_args()
 
 
-class Timer:
-    """Per-call HIP events on the current stream, summed per label."""
+def capture(torch, fns):
+    """One HIP graph that replays the library calls `fns` in order. The calls
+    are asynchronous launches on the current stream with preallocated
+    outputs; they run once eagerly on the capture stream first."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
 
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
 
-    def run(self, label, fn):
-        t = self.torch
-        s = t.cuda.Event(enable_timing=True)
-        e = t.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        self.pairs.append((label, s, e))
-
-    def summary(self):
-        out = {}
-        for label, s, e in self.pairs:
-            out.setdefault(label, []).append(s.elapsed_time(e) * 1e-3)
-        return {k: dict(n=len(v), total_s=sum(v), avg_s=sum(v) / len(v)) for k, v in out.items()}
+def time_replays(torch, graphs, reps):
+    """Seconds per replay, HIP events on the replay stream around `reps`
+    rounds over `graphs`."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for g in graphs:
+            g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * len(graphs))
 
 
 def log(*a):
@@ -105,29 +118,35 @@ def main_decode_layer(args, torch, tq, syn):
     ws = torch.empty(tq.logits_workspace(w.batch, w.n_kv, w.group, w.d), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step(c, timer):
+    def enc(c):
         codes, scal = caches[c]
-        timer.run("encode", lambda: tq.encode_kv(kc, xs[c], codes, scal))
-        timer.run("logits", lambda: tq.logits(kc, qs[c], codes, scal, n_kv_heads=w.n_kv, group=w.group,
-                                                n_keys=w.n_tok, out=outs[c], workspace=ws))
+        return lambda: tq.encode_kv(kc, xs[c], codes, scal)
 
-    warm = Timer(torch)
+    def lgt(c):
+        codes, scal = caches[c]
+        return lambda: tq.logits(kc, qs[c], codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok,
+                                 out=outs[c], workspace=ws)
+
+    # one graph per copy: the whole step (encode the prefill, then every
+    # logit), so the timed steps carry no host launch overhead
+    steps_g = [capture(torch, [enc(c), lgt(c)]) for c in range(C)]
     for i in range(args.warmup):
-        step(i % C, warm)
+        steps_g[i % C].replay()
     torch.cuda.synchronize()
-    timer = Timer(torch)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(args.steps):
-        step(i % C, timer)
+        steps_g[i % C].replay()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total = t0.elapsed_time(t1) * 1e-3
-    ks = timer.summary()
+    # per kernel: graphs of C back-to-back calls of one kind, over all copies
+    enc_s = time_replays(torch, [capture(torch, [enc(c) for c in range(C)])], 3) / C
+    lgt_s = time_replays(torch, [capture(torch, [lgt(c) for c in range(C)])], 3) / C
+    ks = {"encode": {"avg_s": enc_s}, "logits": {"avg_s": lgt_s}}
     n_vec = w.n_vec
     rec = kc.record_bytes + 4
     bytes_encode = n_vec * (w.d * 2 + rec)                       # bf16 in, codes + scalars out
@@ -172,21 +191,15 @@ def decode_workload(torch, tq, syn, cfg, copies, steps):
     outs = [torch.empty((w.batch, w.n_q, w.d), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
     torch.cuda.synchronize()
 
-    def step(c, timer):
+    def dec(c):
         kcodes, kscal, vcodes, vscal = caches[c]
-        timer.run("decode", lambda: tq.decode_attend(kc, vc, qs[c], kcodes, kscal, vcodes, vscal, ctx,
-                                                     n_kv_heads=w.n_kv, group=w.group, max_ctx=w.n_tok,
-                                                     out=outs[c], workspace=ws, out_dtype=torch.bfloat16))
+        return lambda: tq.decode_attend(kc, vc, qs[c], kcodes, kscal, vcodes, vscal, ctx, n_kv_heads=w.n_kv,
+                                        group=w.group, max_ctx=w.n_tok, out=outs[c], workspace=ws,
+                                        out_dtype=torch.bfloat16)
 
-    warm = Timer(torch)
-    for i in range(3):
-        step(i % copies, warm)
-    timer = Timer(torch)
-    torch.cuda.synchronize()
-    for i in range(steps):
-        step(i % copies, timer)
-    torch.cuda.synchronize()
-    avg = timer.summary()["decode"]["avg_s"]
+    g = capture(torch, [dec(c) for c in range(copies)])
+    g.replay()
+    avg = time_replays(torch, [g], max(1, steps // copies)) / copies
     th = w.n_seq * w.n_tok
     bytes_ = th * (kc.record_bytes + 4 + vc.lm_bits * w.d // 8 + 2) + w.batch * w.n_q * w.d * 4
     return dict(workload=w.name, avg_us=avg * 1e6, bytes_per_launch=bytes_, unit="token-heads",
@@ -206,18 +219,10 @@ def encode_full_cache(torch, tq, syn, steps):
     vcodes, vscal = tq.alloc_value_cache(w.n_seq, w.n_tok, vc)
     torch.cuda.synchronize()
 
-    def step(timer):
-        timer.run("enc_k", lambda: tq.encode_kv(kc, xk, kcodes, kscal))
-        timer.run("enc_v", lambda: tq.encode_kv(vc, xv, vcodes, vscal))
-
-    step(Timer(torch))
-    timer = Timer(torch)
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        step(timer)
-    torch.cuda.synchronize()
-    s = timer.summary()
-    tk, tv = s["enc_k"]["avg_s"], s["enc_v"]["avg_s"]
+    gk = capture(torch, [lambda: tq.encode_kv(kc, xk, kcodes, kscal)])
+    gv = capture(torch, [lambda: tq.encode_kv(vc, xv, vcodes, vscal)])
+    tk = time_replays(torch, [gk], steps)
+    tv = time_replays(torch, [gv], steps)
     bk = w.n_vec * (w.d * 2 + kc.record_bytes + 4)
     bv = w.n_vec * (w.d * 2 + vc.lm_bits * w.d // 8 + 2)
     out = dict(workload=w.name, keys_avg_us=tk * 1e6, values_avg_us=tv * 1e6,

@@ -210,3 +210,56 @@ def test_decode_attend_given_oracle_codes(d, kw, vw, group, batch, n_kv, T, lens
         expect = bf16_rne(out32.cpu().numpy())
         # identical kernels up to the final rounding: RNE of the fp32 result
         np.testing.assert_array_equal(got, expect)
+
+
+# ------------------------------------------------------------------ graphs
+
+
+def test_calls_replay_in_a_hip_graph():
+    """encode + logits + decode captured in one HIP graph: every replay, with
+    eager work and synchronisations in between, reproduces the eager
+    results bit for bit (the benchmark times such replays)."""
+    say("graph capture: encode + logits + decode, 3 replays")
+    d, kw, vw, batch, n_kv, group, T = 128, 3, 4, 2, 2, 4, 600
+    kc, vc = key_codec(801, d, kw), value_codec(802, d, vw)
+    cap = 608
+    k = _inputs(batch * n_kv, T, d, torch.bfloat16, seed=11, stream=1, scale_channels=True)
+    v = _inputs(batch * n_kv, T, d, torch.bfloat16, seed=12, stream=2)
+    q = _inputs(batch, n_kv * group, d, torch.bfloat16, seed=13, stream=3)
+    ctx = torch.tensor([T, 333], dtype=torch.int32, device="cuda")
+    kcodes, kscal = tq.alloc_key_cache(batch * n_kv, cap, kc.gpu)
+    vcodes, vscal = tq.alloc_value_cache(batch * n_kv, cap, vc.gpu)
+    lg = torch.empty((batch, n_kv * group, T), dtype=torch.float32, device="cuda")
+    out = torch.empty((batch, n_kv * group, d), dtype=torch.float32, device="cuda")
+    lws = torch.empty(max(256, tq.logits_workspace(batch, n_kv, group, d)), dtype=torch.uint8, device="cuda")
+    dws = torch.empty(tq.decode_attend_workspace(batch, n_kv, group, T, d), dtype=torch.uint8, device="cuda")
+
+    def calls():
+        tq.encode_kv(kc.gpu, k, kcodes, kscal)
+        tq.encode_kv(vc.gpu, v, vcodes, vscal)
+        tq.logits(kc.gpu, q, kcodes, kscal, n_kv_heads=n_kv, group=group, n_keys=T, out=lg, workspace=lws)
+        tq.decode_attend(kc.gpu, vc.gpu, q, kcodes, kscal, vcodes, vscal, ctx, n_kv_heads=n_kv, group=group,
+                         max_ctx=T, out=out, workspace=dws)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (kcodes, kscal, vcodes, vscal, lg, out)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        calls()
+    scratch = tq.alloc_key_cache(batch * n_kv, cap, kc.gpu)
+    for rep in range(3):
+        for t in (kcodes, kscal, vcodes, vscal, lg, out):
+            t.zero_()
+        tq.encode_kv(kc.gpu, k, *scratch)            # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((kcodes, kscal, vcodes, vscal, lg, out), ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
