@@ -10,15 +10,15 @@
 // per-coordinate Lloyd-Max; 第2段: 1-bit JL projection of the residual).
 //
 // Mapping: every lane holds 64 coordinates of one token. For d = 64 a wave
-// encodes 64 tokens (one lane each); for d = 128 it encodes 32 tokens, token
-// t in lanes t and t + 32 (coordinates [0, 64) and [64, 128)). The first six
-// butterfly stages of the rotation run in registers, the seventh (d = 128)
-// pairs lane t with lane t + 32. A ballot over the wave of one coordinate's
-// index bit yields 64 token bits: one 32-bit value-code word per 32-token
-// block (d = 64: two blocks of the same coordinate; d = 128: coordinates c
-// and c + 64 of one block). Key records are assembled per lane (each lane
-// writes its half of every plane). The QJL projection of the wave's
-// residuals runs on the matrix cores (tq_qjl.h).
+// encodes 64 tokens (one lane each) and rotates in registers. For d = 128 it
+// encodes 32 tokens, token t in lanes t and t + 32; the rotation
+// H_128 = H_4 (x) H_32 runs its 32-point blocks on the matrix cores for
+// 16-bit inputs (fp32 inputs: six butterfly stages in registers and one
+// across the half-waves). A ballot over the wave of one coordinate slot's
+// index bit yields 64 token bits: 32-bit value-code words (d = 64: two
+// 32-token blocks of one coordinate; d = 128: two coordinates of one
+// block). Key records are assembled per lane; the QJL projection of the
+// wave's residuals runs on the matrix cores (tq_qjl.h).
 #include "tq_device.h"
 #include "tq_kernels.h"
 #include "tq_qjl.h"
@@ -94,7 +94,22 @@ __device__ __forceinline__ float swap_half_f(float x) {
   return __uint_as_float((lane_id() < 32) ? r[1] : r[0]);
 }
 
-template <int D, int W, bool KEY>
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+union Frag8 {
+  uint4 u;
+  v8bf b;
+  v8h h;
+};
+
+// Output row r of a 32x32 MFMA tile is held by lane half (r / 4) % 2 as
+// accumulator 4 (r / 8) + r % 4; letting row r stand for coordinate
+// 16 ((r / 4) % 2) + 4 (r / 8) + r % 4 of the block gives lane half h the
+// block's coordinates 16 h .. 16 h + 15 in accumulator order.
+__host__ __device__ constexpr int mfma_row_coord(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// XT: the input's type, 0 fp32, 1 bf16, 2 fp16.
+template <int D, int W, bool KEY, int XT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void encode_kernel(EncodeParams p) {
   constexpr int L = 1 << W;
   constexpr int C = 64;                      // coordinates per lane
@@ -103,174 +118,317 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   constexpr int NWL = C / 32;                // plane words per lane (2)
   __shared__ float s_cent[L];
   __shared__ float s_th[L];
-  __shared__ float s_sign[D];
+  __shared__ __attribute__((aligned(16))) float s_sign[D];
   __shared__ __attribute__((aligned(16))) uint16_t s_sk[KEY ? D * (D + 8) : 8];
+  // d = 128, 16-bit input: A operands of the rotation's 32-point blocks,
+  // [block b][K step e][lane][8 halves]. Lane l holds row l % 32, standing
+  // for output coordinate rc = mfma_row_coord(l % 32), and input coordinates
+  // k = 16 (l / 32) + 8 e + j: the entry is (-1)^popcount(rc & k) s[32 b + k]
+  // (+-1 in the input's type), i.e. H_32 diag(s) restricted to the block.
+  constexpr bool MFMA_ROT = D == 128 && XT != 0;
+  __shared__ __attribute__((aligned(16))) uint32_t s_ha[MFMA_ROT ? 4 * 2 * kWave * 4 : 4];
   if (threadIdx.x < L) s_cent[threadIdx.x] = p.centroids[threadIdx.x];
   if (threadIdx.x < L - 1) s_th[threadIdx.x] = p.thresholds[threadIdx.x];
   for (int i = threadIdx.x; i < D; i += blockDim.x) s_sign[i] = p.signs[i];
+  if constexpr (MFMA_ROT) {
+    constexpr uint32_t one = XT == 2 ? 0x3C00u : 0x3F80u;
+    for (int idx = threadIdx.x; idx < 4 * 2 * kWave * 4; idx += blockDim.x) {
+      const int jj = idx & 3, ln = (idx >> 2) & 63, e = (idx >> 8) & 1, bb = idx >> 9;
+      const int rc = mfma_row_coord(ln & 31);
+      uint32_t w = 0u;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int k = 16 * (ln >> 5) + 8 * e + 2 * jj + u;
+        const uint32_t neg = (static_cast<uint32_t>(__popc(static_cast<unsigned>(rc & k))) +
+                              (p.signs[32 * bb + k] < 0.f ? 1u : 0u)) & 1u;
+        w |= (one | (neg << 15)) << (16 * u);
+      }
+      s_ha[idx] = w;
+    }
+  }
   if (KEY) stage_sketch<D>(p.sketch, s_sk);
   __syncthreads();
 
   const int lane = lane_id();
   const int tok = lane % TPW;                // token within the wave
-  const int hv = lane / TPW;                 // which 64 coordinates (d = 128)
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (wave >= p.n_waves) return;             // whole wave exits together
-  const int64_t seq = wave / p.groups_per_seq;
-  const int64_t g = p.g0 + wave % p.groups_per_seq;
-  const int64_t pos = g * TPW + tok;         // cache slot
-  const int64_t t = pos - p.t0;              // input token
-  const bool active = (t >= 0) && (t < p.n_tok);
-
-  float v[C];
-  if (active) {
-    const int64_t off = seq * p.x_seq_stride + t * p.x_tok_stride + C * hv;
-    if (p.xt == 0) load_row_vec_f32<C>(static_cast<const float *>(p.x) + off, v);
-    else if (p.xt == 1) load_row_vec_16<C, true>(static_cast<const uint16_t *>(p.x) + off, v);
-    else load_row_vec_16<C, false>(static_cast<const uint16_t *>(p.x) + off, v);
-  } else {
-#pragma unroll
-    for (int i = 0; i < C; ++i) v[i] = 0.f;
-  }
-
-  // (a1) norm, accumulated in fp32 in coordinate order (then the two halves)
-  float n2 = 0.f;
-#pragma unroll
-  for (int i = 0; i < C; ++i) n2 = fmaf(v[i], v[i], n2);
-  if (LPT == 2) {
-    const float o = swap_half_f(n2);
-    n2 = hv ? (o + n2) : (n2 + o);
-  }
-  const float n = sqrtf(n2);
-
-  // (a2) y = H diag(s) x / (n sqrt(D)); the zero vector maps to y = 0
-#pragma unroll
-  for (int i = 0; i < C; ++i) v[i] *= s_sign[C * hv + i];
-  fwht_regs<C>(v);
-  if (LPT == 2) {
-    // stage 7: y_i = v_i + v_{i+64} (lane t), y_{i+64} = v_i - v_{i+64} (lane t + 32).
-    // Swapping a value with itself across half-waves leaves the lower
-    // half's copy (v_i) in the first register and the upper half's
-    // (v_{i+64}) in the second, in every lane.
-    const float sgn = hv ? -1.f : 1.f;
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const uint32_t u = __float_as_uint(v[i]);
-      auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      v[i] = fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
-    }
-  }
-  const float inv = (n > 0.f) ? 1.0f / (n * sqrtf(static_cast<float>(D))) : 0.f;
-#pragma unroll
-  for (int i = 0; i < C; ++i) v[i] *= inv;
-
+  const int hv = lane / TPW;                 // d = 128: which half of every 32-coordinate block
   Levels<W> lv;
   lv.load(s_th);
+  // each wave encodes token groups wave, wave + (waves in the grid), ...
+  const int64_t wave_stride = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
+  for (int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
+       wave < p.n_waves; wave += wave_stride) {
+    const int64_t seq = wave / p.groups_per_seq;
+    const int64_t g = p.g0 + wave % p.groups_per_seq;
+    const int64_t pos = g * TPW + tok;         // cache slot
+    const int64_t t = pos - p.t0;              // input token
+    const bool active = (t >= 0) && (t < p.n_tok);
+    const int64_t off = seq * p.x_seq_stride + t * p.x_tok_stride;
 
-  if (KEY) {
-    // (a3) indices -> this lane's half of every plane: each decision's lane
-    // mask is added in as the carry of plane + plane, coordinate 31 first,
-    // so coordinate i lands on bit i % 32;
-    // (a4) residual, kept as r' = 2^10 r = fma(y, 2^10, -2^10 c) (exactly
-    // 2^10 times the rounded y - c), the scale the QJL projection wants
-    float c_up[L / 2];
+    // Lane layout. d = 64: one lane per token, coordinate i in v[i]. d = 128:
+    // lanes t and t + 32 hold token t; lane half h holds coordinates
+    // 32 b + 16 h + i (block b = 0..3, i = 0..15) in v[16 b + i].
+    float v[C];
+    if constexpr (D == 128) {
+      if constexpr (XT != 0) {
+        // (a2) z = H_32 diag(s) x per 32-coordinate block on the matrix cores
+        // (exact +-1 operands, fp32 sums), then H_4 across the blocks
+        Frag8 xb[4][2];
 #pragma unroll
-    for (int j = 0; j < L / 2; ++j) c_up[j] = 1024.0f * s_cent[L / 2 + j];
-    uint32_t planes[W][NWL];
+        for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-    for (int q = 0; q < W; ++q)
+          for (int e = 0; e < 2; ++e) {
+            if (active) xb[bb][e].u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + off + 32 * bb + 16 * hv + 8 * e);
+            else xb[bb][e].u = make_uint4(0u, 0u, 0u, 0u);
+          }
+        for (int bb = 0; bb < 4; ++bb) {
+          v16f c = {};
 #pragma unroll
-      for (int k = 0; k < NWL; ++k) planes[q][k] = 0u;
-    float g2 = 0.f;
+          for (int e = 0; e < 2; ++e) {
+            Frag8 a;
+            a.u = *reinterpret_cast<const uint4 *>(s_ha + ((bb * 2 + e) * kWave + lane) * 4);
+            if constexpr (XT == 2) c = mfma_f16_32x32x16(a.h, xb[bb][e].h, c);
+            else c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.b, xb[bb][e].b, c, 0, 0, 0);
+          }
 #pragma unroll
-    for (int i = C - 1; i >= 0; --i) {
-      bool dec[W];
-      decide<W>(v[i], lv, dec);
+          for (int q = 0; q < 16; ++q) v[16 * bb + q] = c[q];
+        }
 #pragma unroll
-      for (int q = 0; q < W; ++q) {
-        const uint64_t m = __ballot(dec[W - 1 - q]);
-        uint64_t carry;
-        asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(planes[q][i / 32]), "=s"(carry) : "s"(m));
+        for (int i = 0; i < 16; ++i) {
+          float a0 = v[i], a1 = v[16 + i], a2 = v[32 + i], a3 = v[48 + i];
+          const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+          v[i] = b0 + b2; v[16 + i] = b1 + b3; v[32 + i] = b0 - b2; v[48 + i] = b1 - b3;
+        }
+      } else {
+        // fp32 input: sign flip, the six in-lane butterfly stages (coordinate
+        // bits 0-3, 5, 6), then coordinate bit 4 across the half-waves
+        if (active) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            float w[16];
+            load_row_vec_f32<16>(static_cast<const float *>(p.x) + off + 32 * bb + 16 * hv, w);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[16 * bb + i] = w[i];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < C; ++i) v[i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) v[i] *= s_sign[32 * (i >> 4) + 16 * hv + (i & 15)];
+        fwht_regs<C>(v);
+        // Swapping a value with itself across half-waves leaves the lower
+        // half's copy in the first register and the upper half's in the
+        // second, in every lane.
+        const float sgn = hv ? -1.f : 1.f;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+          const uint32_t u = __float_as_uint(v[i]);
+          auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+          v[i] = fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+        }
       }
-      v[i] = fmaf(v[i], 1024.0f, -centroid<W>(c_up, dec));
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    } else {
+      if (active) {
+        if constexpr (XT == 0) load_row_vec_f32<C>(static_cast<const float *>(p.x) + off, v);
+        else if constexpr (XT == 1) load_row_vec_16<C, true>(static_cast<const uint16_t *>(p.x) + off, v);
+        else load_row_vec_16<C, false>(static_cast<const uint16_t *>(p.x) + off, v);
+      } else {
 #pragma unroll
-    for (int i = 0; i < C; ++i) g2 = fmaf(v[i], v[i], g2);
-    if (LPT == 2) {
-      const float o = swap_half_f(g2);
-      g2 = hv ? (o + g2) : (g2 + o);
+        for (int i = 0; i < C; ++i) v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < C; ++i) v[i] *= s_sign[i];
+      fwht_regs<C>(v);
     }
-    const float gamma = sqrtf(g2) * (1.0f / 1024.0f);
 
-    // (a5) QJL sign bits sigma_j = [ (S r)_j >= 0 ], on the matrix cores
-    uint32_t sig[D / 32];
-    qjl_signs_mfma<D>(s_sk, v, sig);
+    // (a1) norm from the rotated vector: ||H diag(s) x||^2 = D ||x||^2
+    float n2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < C; ++i) n2 = fmaf(v[i], v[i], n2);
+    if (LPT == 2) {
+      const float o = swap_half_f(n2);
+      n2 = hv ? (o + n2) : (n2 + o);
+    }
+    const float n = sqrtf(n2 * (1.0f / static_cast<float>(D)));
+    // y = v / ||v|| (v = H diag(s) x, ||v|| = n sqrt(D)). The decisions
+    // compare v with the thresholds scaled by ||v|| (y >= t <=> v >= t ||v||
+    // up to one rounding), the residual takes y - c = fma(v, 1 / ||v||, -c);
+    // the zero vector has v = 0, unscaled thresholds and y = 0.
+    const bool nz = n2 > 0.f;
+    const float vn = nz ? sqrtf(n2) : 1.0f;
+    Levels<W> ls;
+#pragma unroll
+    for (int k = 0; k < L - 1; ++k) ls.t[k] = lv.t[k] * vn;
 
-    if (active) {
-      // (a6) record: W index planes then the sign plane, D/8 bytes each;
-      // this lane writes bytes [8 hv, 8 hv + 8) of every plane
-      constexpr int REC = (W + 1) * D / 8;
-      constexpr int PB = D / 8;
-      uint8_t *rec = static_cast<uint8_t *>(p.codes) + (seq * p.cap + pos) * REC + 8 * hv;
+
+    if (KEY) {
+      // (a3) indices -> bit planes: each decision's lane mask is added in as
+      // the carry of half + half (coordinate order reversed, so the first
+      // coordinate lands on bit 0); (a4) residual, kept as r' = 2^10 r =
+      // fma(v, 2^10 / ||v||, -2^10 c), the scale the QJL projection wants
+      const float rs = nz ? 1024.0f / vn : 0.f;
+      constexpr int HB = D == 128 ? 4 : NWL;   // bit groups per lane and plane
+      constexpr int HW = C / HB;               // bits per group (16 or 32)
+      float c_up[L / 2];
+#pragma unroll
+      for (int j = 0; j < L / 2; ++j) c_up[j] = 1024.0f * s_cent[L / 2 + j];
+      uint32_t hw[W][HB];
 #pragma unroll
       for (int q = 0; q < W; ++q)
-        *reinterpret_cast<uint2 *>(rec + q * PB) = make_uint2(planes[q][0], planes[q][1]);
-      *reinterpret_cast<uint2 *>(rec + W * PB) = make_uint2(sig[2 * hv], sig[2 * hv + 1]);
-      if (hv == 0) {
-        const uint32_t sc = static_cast<uint32_t>(float_to_f16_bits(n)) |
-                            (static_cast<uint32_t>(float_to_f16_bits(gamma)) << 16);
-        reinterpret_cast<uint32_t *>(p.scalars)[seq * p.cap + pos] = sc;
-      }
-    }
-  } else {
-    // values: the ballot of coordinate slot c gives 64 token bits; lane c
-    // keeps them (lo: bits 0-31, hi: bits 32-63)
-    uint32_t lo[W], hi[W];
 #pragma unroll
-    for (int q = 0; q < W; ++q) { lo[q] = 0u; hi[q] = 0u; }
-    static_for<0, C>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      bool dec[W];
-      decide<W>(v[i], lv, dec);
+        for (int k = 0; k < HB; ++k) hw[q][k] = 0u;
+      float g2 = 0.f;
+#pragma unroll
+      for (int i = C - 1; i >= 0; --i) {
+        bool dec[W];
+        decide<W>(v[i], ls, dec);
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+          const uint64_t m = __ballot(dec[W - 1 - q]);
+          uint64_t carry;
+          asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(hw[q][i / HW]), "=s"(carry) : "s"(m));
+        }
+        v[i] = fmaf(v[i], rs, -centroid<W>(c_up, dec));
+        asm volatile("" : "+v"(v[i]));    // consume the decisions here
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // this lane's two words of every plane: d = 64 the groups themselves;
+      // d = 128 word b = half b of lane half 0 | half b of lane half 1 << 16,
+      // lane half h keeping words 2 h and 2 h + 1
+      uint32_t planes[W][NWL];
 #pragma unroll
       for (int q = 0; q < W; ++q) {
-        const uint64_t m = __ballot(active && dec[W - 1 - q]);
-        write_lane<i>(lo[q], static_cast<uint32_t>(m));
-        write_lane<i>(hi[q], static_cast<uint32_t>(m >> 32));
+        if constexpr (D == 128) {
+          const uint32_t send = hv ? (hw[q][0] | (hw[q][1] << 16)) : (hw[q][2] | (hw[q][3] << 16));
+          auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+          const uint32_t recv = hv ? r[0] : r[1];
+          planes[q][0] = hv ? ((recv & 0xffffu) | (hw[q][2] << 16)) : (hw[q][0] | (recv << 16));
+          planes[q][1] = hv ? ((recv >> 16) | (hw[q][3] << 16)) : (hw[q][1] | (recv & 0xffff0000u));
+        } else {
+          planes[q][0] = hw[q][0];
+          planes[q][1] = hw[q][1];
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    const uint64_t valid = __ballot(active);
-    const int64_t nblk = p.cap / kValueBlock;
-    uint32_t *words = static_cast<uint32_t *>(p.codes);
-    // d = 64: lo -> block 2g, hi -> block 2g + 1 (coordinate = lane)
-    // d = 128: both -> block g; lo -> coordinate lane, hi -> coordinate 64 + lane
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t vm = LPT == 2 ? static_cast<uint32_t>(valid) : static_cast<uint32_t>(valid >> (32 * half));
-      if (vm == 0u) continue;
-      const int64_t blk = LPT == 2 ? g : 2 * g + half;
-      const int coord = LPT == 2 ? 64 * half + lane : lane;
-      uint32_t *base = words + (seq * nblk + blk) * W * D + coord;
-#pragma unroll
-      for (int q = 0; q < W; ++q) {
-        uint32_t w = half ? hi[q] : lo[q];
-        uint32_t *dst = base + q * D;
-        if (vm != 0xffffffffu) w = (*dst & ~vm) | (w & vm);
-        *dst = w;
+      for (int i = 0; i < C; ++i) g2 = fmaf(v[i], v[i], g2);
+      if (LPT == 2) {
+        const float o = swap_half_f(g2);
+        g2 = hv ? (o + g2) : (g2 + o);
       }
+      const float gamma = sqrtf(g2) * (1.0f / 1024.0f);
+
+      // (a5) QJL sign bits sigma_j = [ (S r)_j >= 0 ], on the matrix cores
+      uint32_t sig[D / 32];
+      qjl_signs_mfma<D>(s_sk, v, sig);
+
+      if (active) {
+        // (a6) record: W index planes then the sign plane, D/8 bytes each;
+        // this lane writes bytes [8 hv, 8 hv + 8) of every plane
+        constexpr int REC = (W + 1) * D / 8;
+        constexpr int PB = D / 8;
+        uint8_t *rec = static_cast<uint8_t *>(p.codes) + (seq * p.cap + pos) * REC + 8 * hv;
+#pragma unroll
+        for (int q = 0; q < W; ++q)
+          *reinterpret_cast<uint2 *>(rec + q * PB) = make_uint2(planes[q][0], planes[q][1]);
+        *reinterpret_cast<uint2 *>(rec + W * PB) = make_uint2(sig[2 * hv], sig[2 * hv + 1]);
+        if (hv == 0) {
+          const uint32_t sc = static_cast<uint32_t>(float_to_f16_bits(n)) |
+                              (static_cast<uint32_t>(float_to_f16_bits(gamma)) << 16);
+          reinterpret_cast<uint32_t *>(p.scalars)[seq * p.cap + pos] = sc;
+        }
+      }
+    } else {
+      // values: the ballot of one coordinate slot gives 64 token bits; the
+      // word of coordinate c goes to lane c % 64 of lo (c < 64) or hi
+      uint32_t lo[W], hi[W];
+#pragma unroll
+      for (int q = 0; q < W; ++q) { lo[q] = 0u; hi[q] = 0u; }
+      static_for<0, C>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        bool dec[W];
+        decide<W>(v[i], ls, dec);
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+          const uint64_t m = __ballot(active && dec[W - 1 - q]);
+          if constexpr (D == 128) {
+            // lanes 0-31: coordinate c0 = 32 b + j; lanes 32-63: c0 + 16
+            constexpr int c0 = 32 * (i >> 4) + (i & 15), c1 = c0 + 16;
+            if constexpr (c0 < 64) {
+              write_lane<c0>(lo[q], static_cast<uint32_t>(m));
+              write_lane<c1>(lo[q], static_cast<uint32_t>(m >> 32));
+            } else {
+              write_lane<c0 - 64>(hi[q], static_cast<uint32_t>(m));
+              write_lane<c1 - 64>(hi[q], static_cast<uint32_t>(m >> 32));
+            }
+          } else {
+            write_lane<i>(lo[q], static_cast<uint32_t>(m));
+            write_lane<i>(hi[q], static_cast<uint32_t>(m >> 32));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      const uint64_t valid = __ballot(active);
+      const int64_t nblk = p.cap / kValueBlock;
+      uint32_t *words = static_cast<uint32_t *>(p.codes);
+      // d = 64: lo -> block 2g, hi -> block 2g + 1 (coordinate = lane)
+      // d = 128: both -> block g; lo -> coordinate lane, hi -> coordinate 64 + lane
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t vm = LPT == 2 ? static_cast<uint32_t>(valid) : static_cast<uint32_t>(valid >> (32 * half));
+        if (vm == 0u) continue;
+        const int64_t blk = LPT == 2 ? g : 2 * g + half;
+        const int coord = LPT == 2 ? 64 * half + lane : lane;
+        uint32_t *base = words + (seq * nblk + blk) * W * D + coord;
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+          uint32_t w = half ? hi[q] : lo[q];
+          uint32_t *dst = base + q * D;
+          if (vm != 0xffffffffu) w = (*dst & ~vm) | (w & vm);
+          *dst = w;
+        }
+      }
+      if (active && hv == 0) p.scalars[seq * p.cap + pos] = float_to_f16_bits(n);
     }
-    if (active && hv == 0) p.scalars[seq * p.cap + pos] = float_to_f16_bits(n);
   }
 }
 
 // ---------------------------------------------------------------- dispatch
 
+// Blocks of 256 threads that fit on the current device at once (cached per
+// device): the grid is capped at that so that every block stages the sketch
+// once and its waves loop over the token groups.
+template <typename K>
+static int64_t resident_blocks(K kernel) {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 30;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 || cus <= 0)
+      return 1 << 30;
+    cached[dev] = per_cu * cus;
+  }
+  return cached[dev];
+}
+
+template <int D, int W, bool KEY, int XT>
+static void launch_encode_x(const EncodeParams &p, hipStream_t st) {
+  const auto kernel = encode_kernel<D, W, KEY, XT>;
+  int64_t blocks = (p.n_waves + 3) / 4;
+  const int64_t cap = resident_blocks(kernel);
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, p);
+}
+
 template <int D, int W, bool KEY>
 static hipError_t launch_encode_dw(const EncodeParams &p, hipStream_t st) {
-  const int64_t blocks = (p.n_waves + 3) / 4;
-  hipLaunchKernelGGL((encode_kernel<D, W, KEY>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, p);
+  switch (p.xt) {
+    case 0: launch_encode_x<D, W, KEY, 0>(p, st); break;
+    case 1: launch_encode_x<D, W, KEY, 1>(p, st); break;
+    default: launch_encode_x<D, W, KEY, 2>(p, st); break;
+  }
   return hipGetLastError();
 }
 

@@ -46,12 +46,29 @@ __device__ __forceinline__ void swap_halves(V8H &x, V8H &y) {
 // fp16(a - hi) likewise (a - hi is exact in fp32), so hi + lo carries 22
 // significant bits of a.
 __device__ __forceinline__ void split_pair(float a0, float a1, uint32_t &hi, uint32_t &lo) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(a0, a1);
-  const float d0 = a0 - static_cast<float>(h[0]);
-  const float d1 = a1 - static_cast<float>(h[1]);
-  const auto l = __builtin_amdgcn_cvt_pkrtz(d0, d1);
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a0, a1));
+  // a - fp32(hi half) in one mixed-precision fma (the fp16 operand is
+  // widened inside the instruction; the difference is exact)
+  float d0, d1;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d0) : "v"(hi), "v"(a0));
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d1) : "v"(hi), "v"(a1));
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(d0, d1));
+}
+
+// Bit 8 (q / 4) + q % 4 set where c[q] >= 0, q < 16 (the C tile rows one
+// lane half holds). The sums start from +0, so no entry is -0 and c >= 0
+// exactly when the sign bit is clear; byte permutes gather the sign bytes
+// of c[b], c[b + 4], c[b + 8], c[b + 12] into one word per b.
+__device__ __forceinline__ uint32_t nonneg_bits(const v16f &c) {
+  uint32_t neg = 0u;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t t1 = __builtin_amdgcn_perm(__float_as_uint(c[b + 4]), __float_as_uint(c[b]), 0x0c0c0703u);
+    const uint32_t t2 = __builtin_amdgcn_perm(__float_as_uint(c[b + 12]), __float_as_uint(c[b + 8]), 0x0c0c0703u);
+    const uint32_t sb = __builtin_amdgcn_perm(t2, t1, 0x05040100u);
+    neg |= (sb >> (7 - b)) & (0x01010101u << b);
+  }
+  return ~neg & 0x0f0f0f0fu;
 }
 
 // Stage the fp16 sketch [D][D] in LDS with rows padded by 8 halves. The
@@ -67,7 +84,10 @@ __device__ __forceinline__ void stage_sketch(const uint16_t *__restrict__ sketch
   for (int k = 0; k < N; ++k) {
     const int e = k * 256 + threadIdx.x;
     const int row = e / (D / 8), c8 = e % (D / 8);
-    *reinterpret_cast<uint4 *>(s_sk + row * RP + c8 * 8) = v[k];
+    // d = 128: column unit 4 a + 2 h + b (coordinates 32 a + 16 h + 8 b ..)
+    // goes to position 8 h + 2 a + b, the K order of the encoder's lanes
+    const int pos = (D == 128) ? 8 * ((c8 >> 1) & 1) + 2 * (c8 >> 2) + (c8 & 1) : c8;
+    *reinterpret_cast<uint4 *>(s_sk + row * RP + pos * 8) = v[k];
   }
 }
 
@@ -75,9 +95,11 @@ __device__ __forceinline__ void stage_sketch(const uint16_t *__restrict__ sketch
 // words of this lane's token.
 //  d = 64  (one lane per token, 64 tokens): two 32-token N tiles; the
 //          lane-swap supplies the other half-wave's coordinates.
-//  d = 128 (lanes t, t+32 hold coordinates [0,64), [64,128) of token t):
-//          K slot (ks, half-wave hv, e) is coordinate 64 hv + 8 ks + e, so
-//          every lane feeds its own coordinates; one 32-token N tile.
+//  d = 128 (lane half h of token t holds coordinates 32 b + 16 h + i in
+//          r[16 b + i]): K slot (ks, h, e) is coordinate
+//          32 (ks / 2) + 16 h + 8 (ks % 2) + e = r[8 ks + e] of lane half h
+//          (the staged sketch's columns are in this order), so every lane
+//          feeds its own coordinates; one 32-token N tile.
 template <int D>
 __device__ __forceinline__ void qjl_signs_mfma(const uint16_t *s_sk, float (&r)[64], uint32_t (&sig)[D / 32]) {
   constexpr int RP = D + 8;
@@ -104,9 +126,7 @@ __device__ __forceinline__ void qjl_signs_mfma(const uint16_t *s_sk, float (&r)[
         c = mfma_f16_32x32x16(a.h, bl[ks].h, c);
       }
       // lane l holds rows 8(q/4) + 4 hw + q%4 of column l%32
-      uint32_t pw = 0u;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) pw |= static_cast<uint32_t>(c[q] >= 0.f) << (8 * (q / 4) + (q % 4));
+      uint32_t pw = nonneg_bits(c);
       pw <<= 4 * hw;
       auto m = __builtin_amdgcn_permlane32_swap(pw, pw, false, false);
       sig[jt] = pw | (hw ? m[0] : m[1]);
@@ -141,13 +161,7 @@ __device__ __forceinline__ void qjl_signs_mfma(const uint16_t *s_sk, float (&r)[
         c1 = mfma_f16_32x32x16(a.h, bh1[ks].h, c1);
         c1 = mfma_f16_32x32x16(a.h, bl1[ks].h, c1);
       }
-      uint32_t p0 = 0u, p1 = 0u;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int bit = 8 * (q / 4) + (q % 4);
-        p0 |= static_cast<uint32_t>(c0[q] >= 0.f) << bit;
-        p1 |= static_cast<uint32_t>(c1[q] >= 0.f) << bit;
-      }
+      uint32_t p0 = nonneg_bits(c0), p1 = nonneg_bits(c1);
       p0 <<= 4 * hw;
       p1 <<= 4 * hw;
       auto m = __builtin_amdgcn_permlane32_swap(p0, p1, false, false);
