@@ -87,6 +87,58 @@ __device__ __forceinline__ float centroid(const float (&c_up)[(1 << W) / 2], con
   }
 }
 
+// From w = 4 bits on, the decisions use the codebook's symmetry
+// (t[L-2-k] = -t[k], t[L/2-1] = 0): the sign of y gives the top index bit,
+// a binary search of |y| over the upper half's L/2 - 1 thresholds gives
+// j = #{t_{L/2+m} <= |y|}, and idx = L/2 + j (y >= 0) or L/2 - 1 - j'
+// (y < 0), where j' counts the thresholds strictly below |y| (ties of a
+// negative y go up in y, i.e. down in |y|) and equals j of the float just
+// below |y|. The lower index bits are then j's bits, inverted for y < 0.
+// Fewer selects than the plain search: the candidates per level halve.
+template <int W>
+struct DecLevels {
+  static constexpr bool kSym = W >= 4;
+  Levels<kSym ? W - 1 : W> lv;
+  // thresholds th[L-1] (LDS), scaled by s
+  __device__ __forceinline__ void load(const float *th, float s) {
+    lv.load(kSym ? th + (1 << W) / 2 : th);
+#pragma unroll
+    for (int k = 0; k < (kSym ? (1 << (W - 1)) - 1 : (1 << W) - 1); ++k) {
+      lv.t[k] *= s;
+      asm volatile("" : "+v"(lv.t[k]));   // scaled once, not after each select
+    }
+  }
+};
+
+// Lane masks m[q] of bit q of idx = #{t_j <= y} for one coordinate (y given
+// unscaled, the thresholds scaled alike), and with CENT c = c[idx] from
+// c_up, the upper half of the (symmetric) codebook.
+template <int W, bool CENT>
+__device__ __forceinline__ void decide_masks(float y, const DecLevels<W> &dl, const float (&c_up)[(1 << W) / 2],
+                                             uint64_t (&m)[W], float &c) {
+  if constexpr (DecLevels<W>::kSym) {
+    const bool up = y >= 0.f;                       // also for y = -0
+    const uint32_t ab = __float_as_uint(y) & 0x7fffffffu;
+    const float a = __uint_as_float(up ? ab : ab - 1u);   // y < 0: ab > 0
+    bool jd[W - 1];
+    decide<W - 1>(a, dl.lv, jd);
+    const uint64_t mu = __ballot(up);
+    m[W - 1] = mu;
+#pragma unroll
+    for (int q = 0; q < W - 1; ++q) m[q] = ~(__ballot(jd[W - 2 - q]) ^ mu);
+    if constexpr (CENT) {
+      const float cp = pick<W - 1, 0>(c_up, jd);
+      c = up ? cp : -cp;
+    }
+  } else {
+    bool dec[W];
+    decide<W>(y, dl.lv, dec);
+#pragma unroll
+    for (int q = 0; q < W; ++q) m[q] = __ballot(dec[W - 1 - q]);
+    if constexpr (CENT) c = centroid<W>(c_up, dec);
+  }
+}
+
 // The other half-wave's copy of x (lane l <-> lane l ^ 32).
 __device__ __forceinline__ float swap_half_f(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -152,8 +204,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   const int lane = lane_id();
   const int tok = lane % TPW;                // token within the wave
   const int hv = lane / TPW;                 // d = 128: which half of every 32-coordinate block
-  Levels<W> lv;
-  lv.load(s_th);
   // each wave encodes token groups wave, wave + (waves in the grid), ...
   const int64_t wave_stride = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
   for (int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
@@ -257,9 +307,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // the zero vector has v = 0, unscaled thresholds and y = 0.
     const bool nz = n2 > 0.f;
     const float vn = nz ? sqrtf(n2) : 1.0f;
-    Levels<W> ls;
-#pragma unroll
-    for (int k = 0; k < L - 1; ++k) ls.t[k] = lv.t[k] * vn;
+    // (read from LDS per group: the unscaled thresholds stay out of the
+    // registers that live across the loop)
+    asm volatile("" ::: "memory");
+    DecLevels<W> ls;
+    ls.load(s_th, vn);
 
 
     if (KEY) {
@@ -281,15 +333,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       float g2 = 0.f;
 #pragma unroll
       for (int i = C - 1; i >= 0; --i) {
-        bool dec[W];
-        decide<W>(v[i], ls, dec);
+        uint64_t m[W];
+        float cq;
+        decide_masks<W, true>(v[i], ls, c_up, m, cq);
 #pragma unroll
         for (int q = 0; q < W; ++q) {
-          const uint64_t m = __ballot(dec[W - 1 - q]);
           uint64_t carry;
-          asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(hw[q][i / HW]), "=s"(carry) : "s"(m));
+          asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(hw[q][i / HW]), "=s"(carry) : "s"(m[q]));
         }
-        v[i] = fmaf(v[i], rs, -centroid<W>(c_up, dec));
+        v[i] = fmaf(v[i], rs, -cq);
         asm volatile("" : "+v"(v[i]));    // consume the decisions here
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -344,13 +396,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       uint32_t lo[W], hi[W];
 #pragma unroll
       for (int q = 0; q < W; ++q) { lo[q] = 0u; hi[q] = 0u; }
+      // (the decision's own lane mask, masked on the scalar unit: a ballot
+      // of a combined condition would first widen it to a vector of 0/1)
+      const uint64_t valid = __ballot(active);
+      const float c_none[L / 2] = {};
       static_for<0, C>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        bool dec[W];
-        decide<W>(v[i], ls, dec);
+        uint64_t mq[W];
+        float unused;
+        decide_masks<W, false>(v[i], ls, c_none, mq, unused);
 #pragma unroll
         for (int q = 0; q < W; ++q) {
-          const uint64_t m = __ballot(active && dec[W - 1 - q]);
+          const uint64_t m = mq[q] & valid;
           if constexpr (D == 128) {
             // lanes 0-31: coordinate c0 = 32 b + j; lanes 32-63: c0 + 16
             constexpr int c0 = 32 * (i >> 4) + (i & 15), c1 = c0 + 16;
@@ -368,7 +425,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-      const uint64_t valid = __ballot(active);
       const int64_t nblk = p.cap / kValueBlock;
       uint32_t *words = static_cast<uint32_t *>(p.codes);
       // d = 64: lo -> block 2g, hi -> block 2g + 1 (coordinate = lane)
@@ -395,12 +451,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 
 // ---------------------------------------------------------------- dispatch
 
-// Blocks of 256 threads that fit on the current device at once (cached per
-// device): the grid is capped at that so that every block stages the sketch
-// once and its waves loop over the token groups.
+// Blocks of 256 threads of `kernel` that fit on the current device at once:
+// the grid is capped at that so that every block stages the codec once and
+// its waves loop over the token groups. `cached` belongs to one kernel.
 template <typename K>
-static int64_t resident_blocks(K kernel) {
-  static int cached[64] = {};
+static int64_t resident_blocks(K kernel, int (&cached)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 30;
   if (cached[dev] == 0) {
@@ -415,9 +470,10 @@ static int64_t resident_blocks(K kernel) {
 
 template <int D, int W, bool KEY, int XT>
 static void launch_encode_x(const EncodeParams &p, hipStream_t st) {
+  static int cached[64] = {};
   const auto kernel = encode_kernel<D, W, KEY, XT>;
   int64_t blocks = (p.n_waves + 3) / 4;
-  const int64_t cap = resident_blocks(kernel);
+  const int64_t cap = resident_blocks(kernel, cached);
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, p);
 }
