@@ -16,6 +16,7 @@
 #include "tq_device.h"
 #include "tq_kernels.h"
 #include "tq_mfma.h"
+#include "tq_qjl.h"
 
 namespace tq {
 
@@ -214,14 +215,50 @@ __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t
 
 // ------------------------------------------------------------------ query prep
 
+// Walsh-Hadamard butterflies over the 64 lanes of a wave, lane bit b being
+// index bit b: stage b pairs lane l with l ^ 2^b, the lower lane keeping the
+// sum and the upper one the difference (lower - upper). The exchanges stay
+// in the vector ALU: quad permutes (bits 0, 1), row rotates (bits 2, 3:
+// rotating a 16-lane row right by n hands lane l the value of lane l - n),
+// lane-row and half-wave swaps (bits 4, 5).
+__device__ __forceinline__ float wave_fwht(float x, int lane) {
+  auto bfly = [lane](float own, float other, int bit) { return ((lane >> bit) & 1) ? other - own : own + other; };
+  x = bfly(x, dpp_f<0xB1>(x), 0);
+  x = bfly(x, dpp_f<0x4E>(x), 1);
+  {
+    // both rotations by every lane before the select: a lane-exchange in a
+    // divergent branch would read lanes that are switched off
+    const float from_below = dpp_f<0x124>(x), from_above = dpp_f<0x12C>(x);
+    x = bfly(x, (lane & 4) ? from_below : from_above, 2);
+  }
+  x = bfly(x, dpp_f<0x128>(x), 3);
+  {
+    // a lane-row swap of x with itself leaves the even row's copy in the
+    // first register and the odd row's in the second
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaf((lane & 16) ? -1.f : 1.f, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  }
+  {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = fmaf((lane & 32) ? -1.f : 1.f, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  }
+  return x;
+}
+
 // Scratch of the in-block query preparation (byte offsets):
 //   FRAG   int8 digit operands [NRG][NMF][64 lanes][16]
 //   SQ, SP q' and p, [8][D] float
 //   SST    per-head exponents [8][4]; SCON per-head constants [8][4];
 //   SB     key basis coefficients [8]
-//   SK     the sketch [D][D] fp16, staged by direct-to-LDS loads
+//   SK     the sketch [D][D] fp16, staged by direct-to-LDS loads; the 16-byte
+//          chunk c of row j sits at chunk position c ^ (j % (D/8)), so that
+//          32 lanes reading the same columns of 32 rows hit distinct banks
 //   QIN    the raw query rows [8][D] (input dtype) then the signs [D] float,
 //          staged by direct-to-LDS loads
+//   TAB    (over SK and QIN once those are consumed) the digit words of the
+//          operands, [head][operand][coordinate]
 template <int D, int KW, int NRG>
 struct PrepShape {
   static constexpr int NB = Basis<KW>::N;
@@ -235,7 +272,9 @@ struct PrepShape {
   static constexpr int SK = SB + 64;
   static constexpr int QIN = SK + D * D * 2;
   static constexpr int QIN_BYTES = (D / 16) * 1024;  // one load per wave
-  static constexpr int BYTES = QIN + QIN_BYTES;
+  static constexpr int TAB = SK;                      // after the GEMV: [4 NRG][NB + 1][D] digit words
+  static constexpr int TAB_BYTES = 4 * NRG * (NB + 1) * D * 4;
+  static constexpr int BYTES = (QIN + QIN_BYTES > TAB + TAB_BYTES) ? QIN + QIN_BYTES : TAB + TAB_BYTES;
 };
 
 // Stage the preparation's inputs into the scratch: the sketch (every wave
@@ -250,7 +289,9 @@ __device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int 
 #pragma unroll
   for (int i = 0; i < SKI; ++i) {
     const int chunk = wave * SKI + i;
-    dma16(p.sketch, static_cast<uint32_t>(chunk * 1024 + lane * 16), scratch + PS::SK + chunk * 1024);
+    const int unit = chunk * kWave + lane;                 // LDS chunk position
+    const int j = unit / (D / 8), c = (unit % (D / 8)) ^ (j % (D / 8));
+    dma16(p.sketch, static_cast<uint32_t>((j * (D / 8) + c) * 16), scratch + PS::SK + chunk * 1024);
   }
   const int es = (p.xt == 0) ? 4 : 2;
   const int q_units = GE * D * es / 16;
@@ -275,13 +316,11 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
   using PS = PrepShape<D, KW, NRG>;
   constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64;
   constexpr int THREADS = 4 * D, NW = D / 16;
-  constexpr int PARTS = THREADS / D;                 // threads per sketch row
   float *sq = reinterpret_cast<float *>(scratch + PS::SQ);      // [8][D]
   float *sp = reinterpret_cast<float *>(scratch + PS::SP);      // [8][D]
   float *sst = reinterpret_cast<float *>(scratch + PS::SST);    // [8][4]
   float *scon = reinterpret_cast<float *>(scratch + PS::SCON);  // [8][4]
   float *sb = reinterpret_cast<float *>(scratch + PS::SB);      // [8]
-  const uint16_t *ssk = reinterpret_cast<const uint16_t *>(scratch + PS::SK);
   const uint8_t *qin = scratch + PS::QIN;
   const float *sgn = reinterpret_cast<const float *>(qin + GE * D * ((p.xt == 0) ? 4 : 2));
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
@@ -307,13 +346,7 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
       x[1] = a1;
     }
 #pragma unroll
-    for (int hs = 1; hs < kWave; hs <<= 1) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float o = __shfl_xor(x[e], hs, kWave);
-        x[e] = (lane & hs) ? (o - x[e]) : (x[e] + o);
-      }
-    }
+    for (int e = 0; e < E; ++e) x[e] = wave_fwht(x[e], lane);
     float mq = 0.f, s1 = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -327,26 +360,40 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
     if (lane == 0) { sst[4 * h] = mq; sst[4 * h + 1] = s1; }
   }
   lds_barrier();
-  // p_j = sum_k S[j][k] q'_k: thread (row j, part) for the heads part, part + PARTS
-  {
-    const int j = tid % D, part = tid / D;
-    for (int h = part; h < GE; h += PARTS) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < D; k += 8) {
-        const uint4 w4 = *reinterpret_cast<const uint4 *>(ssk + j * D + ((k + 8 * j) % D));
-        const float4 q0 = *reinterpret_cast<const float4 *>(sq + h * D + ((k + 8 * j) % D));
-        const float4 q1 = *reinterpret_cast<const float4 *>(sq + h * D + ((k + 8 * j) % D) + 4);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.x & 0xffffu)), q0.x, acc);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.x >> 16)), q0.y, acc);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.y & 0xffffu)), q0.z, acc);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.y >> 16)), q0.w, acc);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.z & 0xffffu)), q1.x, acc);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.z >> 16)), q1.y, acc);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.w & 0xffffu)), q1.z, acc);
-        acc = fmaf(f16_bits_to_float(static_cast<uint16_t>(w4.w >> 16)), q1.w, acc);
-      }
-      sp[h * D + j] = acc;
+  // p = S q' on the matrix cores (v_mfma_f32_32x32x16_f16), one 32-row tile
+  // of S per wave: A = 32 sketch rows x 16 columns (fp16, exact), B = 16
+  // entries of q' for the columns = heads (lanes of absent heads zero), each
+  // head scaled by a power of two (its max |q'| below 2^14) and split into
+  // fp16 hi + lo, two MFMAs per K step: fp32-grade sums.
+  if (wave < D / 32) {
+    constexpr int U = D / 8;
+    const int h = lane % 32, half = lane / 32;
+    const bool live = h < GE;
+    int ex = 0;
+    if (live) (void)frexpf(sst[4 * h], &ex);
+    const int sexp = min(14 - ex, 100);
+    const float up = live ? ldexpf(1.0f, sexp) : 0.f;
+    const int r = 32 * wave + h;                          // sketch row of this lane's A entries
+    v16f c = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int cl = 2 * ks + half;                       // logical 16-byte chunk of the row
+      const uint4 au = *reinterpret_cast<const uint4 *>(scratch + PS::SK + (r * U + (cl ^ (r % U))) * 16);
+      V8H a, bh, bl;
+      a.u[0] = au.x; a.u[1] = au.y; a.u[2] = au.z; a.u[3] = au.w;
+      const float *qx = sq + (live ? h : 0) * D + 16 * ks + 8 * half;
+      const float4 x0 = *reinterpret_cast<const float4 *>(qx), x1 = *reinterpret_cast<const float4 *>(qx + 4);
+      split_pair(x0.x * up, x0.y * up, bh.u[0], bl.u[0]);
+      split_pair(x0.z * up, x0.w * up, bh.u[1], bl.u[1]);
+      split_pair(x1.x * up, x1.y * up, bh.u[2], bl.u[2]);
+      split_pair(x1.z * up, x1.w * up, bh.u[3], bl.u[3]);
+      c = mfma_f16_32x32x16(a.h, bh.h, c);
+      c = mfma_f16_32x32x16(a.h, bl.h, c);
+    }
+    // lane holds rows 8 (q / 4) + 4 half + q % 4 of the tile, column h
+    if (live) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sp[h * D + 32 * wave + 8 * (q / 4) + 4 * half + (q % 4)] = ldexpf(c[q], -sexp);
     }
   }
   lds_barrier();
@@ -375,30 +422,51 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
     }
   }
   lds_barrier();
+  // digit words, once per (head, operand, coordinate c): the operand value
+  // in fixed point, 2 beta_s q'_c or 2 p_c times 2^(7 + e - c % 8) (c % 8
+  // is the bit of the plane word whose expanded byte weighs 2^(c % 8) in the
+  // MFMA; the top bit's byte is negative), as four signed 8-bit digits
+  constexpr int NK = NB + 1;
+  uint32_t *tab = reinterpret_cast<uint32_t *>(scratch + PS::TAB);
+  for (int e = tid; e < GE * NK * D; e += THREADS) {
+    const int c = e % D, m = (e / D) % NK, hl = e / (D * NK);
+    const bool qjl = m == NB;
+    const float coef = qjl ? 2.0f : 2.0f * sb[m];
+    const int ex = static_cast<int>(sst[4 * hl + (qjl ? 3 : 2)]);
+    const int k = c & 7;
+    float v = ldexpf(coef * (qjl ? sp : sq)[hl * D + c], 7 - k + ex);
+    if (k == 7) v = -v;
+    tab[e] = signed_digits(__float2int_rn(v));
+  }
+  lds_barrier();
   // digit operands: lane slot (rg, mf, l) = row l%16 (head 4 rg + (l%16)/4,
-  // digit l%4), K slots 16 (l/16) + j
+  // digit l%4), K slots 16 (l/16) + 4 r + jb <-> coordinate
+  // 32 word + 8 jb + 4 (kg & 1) + r (slot_coord): four table reads of four
+  // consecutive coordinates, digit bytes gathered by byte permutes
   for (int item = tid; item < NRG * NMF * kWave; item += THREADS) {
     const int l = item % kWave, mf = (item / kWave) % NMF, rg = item / (kWave * NMF);
-    const int hl = 4 * rg + (l % 16) / 4, s = l % 4, kg = l / 16;
-    uint32_t dw[4] = {0u, 0u, 0u, 0u};
+    const int hl = 4 * rg + (l % 16) / 4, sd = l % 4, kg = l / 16;
+    uint4 out = make_uint4(0u, 0u, 0u, 0u);
     if (hl < GE) {
       const bool qjl = mf >= NB * NH;
-      const int plane = qjl ? 0 : mf / NH;
-      const int half = mf % NH;
-      const float coef = qjl ? 2.0f : 2.0f * sb[plane];
-      const int e = static_cast<int>(sst[4 * hl + (qjl ? 3 : 2)]);
-      const float *x = (qjl ? sp : sq) + hl * D;
+      const int m = qjl ? NB : mf / NH, half = mf % NH;
+      const int word = (D == 128) ? (2 * (kg >> 1) + half) : (kg >> 1);
+      const uint32_t *row = tab + (hl * NK + m) * D + 32 * word + 4 * (kg & 1);
+      uint4 q4[4];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int coord = slot_coord(D, kg, jj, half);
-        const int k = 4 * (kg & 1) + (jj >> 2);
-        float v = ldexpf(coef * x[coord], 7 - k + e);
-        if (k == 7) v = -v;
-        const uint32_t dig = signed_digits(__float2int_rn(v));
-        dw[jj >> 2] |= ((dig >> (8 * s)) & 0xffu) << (8 * (jj & 3));
-      }
+      for (int jb = 0; jb < 4; ++jb) q4[jb] = *reinterpret_cast<const uint4 *>(row + 8 * jb);
+      const uint32_t sel = 0x0c0c0000u | (static_cast<uint32_t>(4 + sd) << 8) | static_cast<uint32_t>(sd);
+      auto gather = [&](uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3) {
+        const uint32_t t01 = __builtin_amdgcn_perm(e1, e0, sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(e3, e2, sel);
+        return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+      };
+      out.x = gather(q4[0].x, q4[1].x, q4[2].x, q4[3].x);
+      out.y = gather(q4[0].y, q4[1].y, q4[2].y, q4[3].y);
+      out.z = gather(q4[0].z, q4[1].z, q4[2].z, q4[3].z);
+      out.w = gather(q4[0].w, q4[1].w, q4[2].w, q4[3].w);
     }
-    *reinterpret_cast<uint4 *>(scratch + item * 16) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    *reinterpret_cast<uint4 *>(scratch + item * 16) = out;
   }
   lds_barrier();
 }
