@@ -66,13 +66,13 @@ tq_status check_codec(const tq_codec *c, int need_key, const char *name) {
   return TQ_OK;
 }
 
-// Decode blocks per (batch, kv-head) group: each block walks every
-// blocks-th split of kDecodeSplit tokens. One block fills a CU's LDS, so
-// aim for one block per CU (256), at most kDecodeMaxBlocks per group and
-// never more than the context has splits.
-int decode_blocks_per_group(int32_t batch, int32_t n_kv, int64_t max_ctx) {
+// Scan blocks per (batch, kv-head) group: each block walks every blocks-th
+// split of `split` tokens. One block fills a CU's LDS, so aim for one block
+// per CU (256), at most kDecodeMaxBlocks per group and never more than the
+// context has splits.
+int decode_blocks_per_group(int32_t batch, int32_t n_kv, int64_t max_ctx, int split) {
   const int64_t groups = std::max<int64_t>(1, static_cast<int64_t>(batch) * n_kv);
-  const int64_t splits = std::max<int64_t>(1, (max_ctx + tq::kDecodeSplit - 1) / tq::kDecodeSplit);
+  const int64_t splits = std::max<int64_t>(1, (max_ctx + split - 1) / split);
   const int64_t want = std::min<int64_t>(tq::kDecodeMaxBlocks, std::max<int64_t>(1, (256 + groups - 1) / groups));
   return static_cast<int>(std::min<int64_t>(splits, want));
 }
@@ -91,7 +91,7 @@ bool staged_inputs_aligned(const tq_codec *kc, const void *q) {
 // Common part of the scan parameters (queries, key codec, key cache).
 tq::ScanParams scan_params(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
                            int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap,
-                           int64_t max_ctx) {
+                           int64_t max_ctx, int split) {
   tq::ScanParams sp{};
   sp.q = q;
   sp.xt = static_cast<int>(qt);
@@ -107,7 +107,7 @@ tq::ScanParams scan_params(const tq_codec *kc, const void *q, tq_dtype qt, int32
   sp.group = group;
   sp.h0 = 0;
   sp.n_hchunks = (group + 7) / 8;
-  sp.nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx);
+  sp.nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, split);
   sp.sm_scale = 1.0f;
   return sp;
 }
@@ -230,7 +230,7 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
     return fail(TQ_EINVAL, "%s: kcodes and kscalars must be 16-byte aligned", fn);
   if (!staged_inputs_aligned(kc, q)) return fail(TQ_EINVAL, "%s: q, signs and sketch must be 16-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys);
+  tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys, tq::kLogitSplit);
   sp.logits = logits;
   hipError_t e = kc->d == 64 ? tq::launch_logits_d<64>(sp, kc->lm_bits, st) : tq::launch_logits_d<128>(sp, kc->lm_bits, st);
   return hip_status(e, fn);
@@ -238,7 +238,7 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
 
 size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int64_t max_ctx, int32_t d) {
   if (batch < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
-  const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx);
+  const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, tq::kAttendSplit);
   return align_up(static_cast<size_t>(batch) * n_kv_heads * nb * group * (d + 2) * sizeof(float));
 }
 
@@ -273,7 +273,7 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
     return fail(TQ_EINVAL, "%s: cache arrays must be 16-byte aligned", fn);
   if (!staged_inputs_aligned(kc, q)) return fail(TQ_EINVAL, "%s: q, signs and sketch must be 16-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, max_ctx);
+  tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, max_ctx, tq::kAttendSplit);
   sp.vcodes = vcodes;
   sp.vscalars = vscalars;
   sp.vcent = vc->centroids;

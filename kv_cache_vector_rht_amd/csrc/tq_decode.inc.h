@@ -82,9 +82,11 @@ __device__ __forceinline__ void lane_masks(uint32_t (&mask)[4]) {
 
 // ------------------------------------------------------------------ staging
 
-// Every scan block walks splits of kDecodeSplit tokens of one (batch,
-// kv-head) sequence through a ring of kStages LDS buffers; while it computes
-// on one split, the loads of the next two are in flight.
+// Every scan block walks splits of one (batch, kv-head) sequence through a
+// ring of LDS stage buffers; while it computes on one split, the loads of the
+// next ones are in flight. The logit scan takes 256-token splits; decode
+// attention 512-token splits in two stages where they fit in LDS (fewer
+// barriers and per-split steps per token), else 256 tokens in kStages.
 constexpr int kStages = 3;
 
 // Block layout: D/16 waves. Wave w owns the 16-key tiles w, w + NW, ... of
@@ -96,9 +98,9 @@ constexpr int kStages = 3;
 //   [OFF_S, OFF_V)     the tiles' key scalar pairs (64 B per tile), then
 //                      (decode) their value norms (32 B per tile)
 //   [OFF_V, ...)       (decode) value words: [32-token block][plane][16 coords]
-template <int D, int KW, int VW, bool LOGITS>
+template <int D, int KW, int VW, bool LOGITS, int SPLIT>
 struct ScanShape {
-  static constexpr int S = kDecodeSplit;
+  static constexpr int S = SPLIT;
   static constexpr int NW = D / 16;
   static constexpr int THREADS = NW * kWave;
   static constexpr int KT = S / 16 / NW;             // key tiles per wave
@@ -165,9 +167,9 @@ struct SeqArrays {
 // Every wave issues exactly P loads. Tiles past the cache capacity load the
 // sequence's first tile instead (their keys are past the context and are
 // never used), so every address stays inside the caller's arrays.
-template <int D, int KW, int VW, bool LOGITS>
+template <int D, int KW, int VW, bool LOGITS, int SPLIT>
 __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t *stage, int wave) {
-  using SH = ScanShape<D, KW, VW, LOGITS>;
+  using SH = ScanShape<D, KW, VW, LOGITS, SPLIT>;
   constexpr int REC = SH::REC;
   const int lane = lane_id();
   uint8_t *wb = stage + wave * SH::WAVE_BYTES;
@@ -276,6 +278,16 @@ struct PrepShape {
   static constexpr int TAB_BYTES = 4 * NRG * (NB + 1) * D * 4;
   static constexpr int BYTES = (QIN + QIN_BYTES > TAB + TAB_BYTES) ? QIN + QIN_BYTES : TAB + TAB_BYTES;
 };
+
+// Tokens per decode split: 512 (two stages) if those stages, the query
+// preparation's scratch and the weight operands fit in LDS, else 256.
+template <int D, int KW, int VW, int NRG>
+constexpr int attend_split() {
+  using S5 = ScanShape<D, KW, VW, false, 512>;
+  using PS = PrepShape<D, KW, NRG>;
+  constexpr int ring = S5::STAGE_BYTES + (S5::STAGE_BYTES > PS::BYTES ? S5::STAGE_BYTES : PS::BYTES);
+  return ring + NRG * (512 / 64) * 1024 <= 160 * 1024 - 4096 ? 512 : 256;
+}
 
 // Stage the preparation's inputs into the scratch: the sketch (every wave
 // an equal share) and the query rows of heads [h0, h0 + GE) plus the signs
@@ -510,7 +522,7 @@ __device__ __forceinline__ void wait_splits(int n_after) {
 // One block per (batch*kv-head, block index within the group) and the heads
 // [h0, h0 + GE) of the group, GE <= 4 NRG. The block prepares the queries of
 // those heads, then walks the splits blockIdx.x, blockIdx.x + gridDim.x, ...
-// (kDecodeSplit tokens each) through the LDS ring. Per split, each wave:
+// (SH::S tokens each) through the LDS ring. Per split, each wave:
 //  1. computes the logits of its key tiles for every head (key MFMA);
 //     LOGITS: stores them and moves on; decode: scales them by sm_scale and
 //     publishes its per-head maxima and largest value norm   -- barrier
@@ -527,7 +539,8 @@ __device__ __forceinline__ void wait_splits(int n_after) {
 // merge_kernel combines them.
 template <int D, int KW, int VW, int NRG, bool LOGITS>
 __device__ __forceinline__ void scan_block(const ScanParams &p) {
-  using SH = ScanShape<D, KW, VW, LOGITS>;
+  constexpr int SPLIT = LOGITS ? kLogitSplit : attend_split<D, KW, VW, NRG>();
+  using SH = ScanShape<D, KW, VW, LOGITS, SPLIT>;
   using PS = PrepShape<D, KW, NRG>;
   constexpr int S = SH::S, NW = SH::NW, KT = SH::KT, VT = SH::VT, REC = SH::REC, P = SH::P;
   constexpr int NMF = PS::NMF;
@@ -541,7 +554,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int LDS_BUDGET = 160 * 1024 - 2048;
   constexpr int NST_L = (LDS_BUDGET - PS::BYTES) / SB < 6 ? (LDS_BUDGET - PS::BYTES) / SB : 6;
   constexpr bool SEP = LOGITS && NST_L >= 3;
-  constexpr int NST = SEP ? NST_L : kStages;
+  constexpr int NST = SEP ? NST_L : (SPLIT == 512 ? 2 : kStages);
   constexpr int PREP_AT = SEP ? NST * SB : SB;
   constexpr int RING = (NST * SB > PREP_AT + PS::BYTES) ? NST * SB : PREP_AT + PS::BYTES;
   static_assert(RING <= LDS_BUDGET - (LOGITS ? 0 : NRG * VT * 1024), "LDS budget");
@@ -552,7 +565,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   __shared__ __attribute__((aligned(16))) uint8_t sfrag[LOGITS ? 16 : NRG * VT * 1024];
   __shared__ float spm[NW][GMAX];
   __shared__ float spnv[NW];
-  __shared__ double spsw[NW][GMAX];
+  __shared__ float spsw[NW][GMAX];
   __shared__ float svb[NBV];
 
   const int G = p.group;
@@ -597,13 +610,13 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
     // scratch, are in flight together; wait for the inputs only
     issue_prep<D, KW, NRG>(p, bh, GE, ring + PREP_AT, wave);
     const int first = SEP ? min(ns, NST) : 1;
-    for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS>(sa, bx + k * nb, ring + k * SB, wave);
+    for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
     wait_splits<P>(first);
     lds_barrier();
     group_prep<D, KW, NRG>(p, GE, ring + PREP_AT);
     load_prepared<D, KW, NRG>(ring + PREP_AT, GE, a, fh);
     lds_barrier();                                 // every wave holds its operands
-    for (int k = first; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS>(sa, bx + k * nb, ring + k * SB, wave);
+    for (int k = first; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
   }
 
   for (int it = 0; it < ns; ++it) {
@@ -688,9 +701,9 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
         m_run[rg] = mn;
         l_run[rg] *= alpha[rg];
       }
-      double sw[NRG];
+      float sw[NRG];
 #pragma unroll
-      for (int rg = 0; rg < NRG; ++rg) sw[rg] = 0.0;
+      for (int rg = 0; rg < NRG; ++rg) sw[rg] = 0.f;
 #pragma unroll
       for (int u = 0; u < KT; ++u) {
         const int tl = 16 * (wave + NW * u) + col;
@@ -703,7 +716,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
           const float e = __expf(lg[u][rg] - m_run[rg]);
           l_run[rg] += e;
           const int fx = __float2int_rn(ldexpf(e * nvv[u], 7 - k + ew));
-          sw[rg] += static_cast<double>(fx) * static_cast<double>(1 << k);
+          sw[rg] = fmaf(static_cast<float>(fx), static_cast<float>(1 << k), sw[rg]);
           const uint32_t dig = signed_digits(k == 7 ? -fx : fx);
           uint8_t *dst = sfrag + (rg * VT + vt) * 1024 + (16 * kga + 4 * kg) * 16 + 4 * r + jb;
 #pragma unroll
@@ -712,7 +725,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
       }
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
-        const double t = row_sum16d(sw[rg]);
+        const float t = row_sum16(sw[rg]);
         if (col == 0) spsw[wave][4 * rg + kg] = t;
       }
       lds_barrier();
@@ -762,7 +775,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
       const float inv = ldexpf(1.0f, -7 - ew);
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) {
-        double swt = 0.0;
+        float swt = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) swt += spsw[w][4 * rg + kg];
         const float ssum = fmaf(2.0f, x[rg], -cvmax * static_cast<float>(swt)) * inv;
@@ -773,7 +786,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
     // 4. refill this stage (this wave's region only; its reads are done)
     if (it + NST < ns) {
       wait_lds();
-      issue_split<D, KW, VW, LOGITS>(sa, sp + NST * nb, buf, wave);
+      issue_split<D, KW, VW, LOGITS, SPLIT>(sa, sp + NST * nb, buf, wave);
     }
   }
   if constexpr (LOGITS) return;

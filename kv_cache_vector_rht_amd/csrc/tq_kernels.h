@@ -56,9 +56,10 @@ hipError_t launch_logits_d(const ScanParams &p, int kw, hipStream_t st);
 template <int D>
 hipError_t launch_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st);
 
-// Tokens per split of the decode kernel (one pipeline stage), and the most
-// blocks one (batch, kv-head) group is spread over.
-constexpr int kDecodeSplit = 256;
+// Tokens per split (one pipeline stage) of the logit scan and of decode
+// attention, and the most blocks one (batch, kv-head) group is spread over.
+constexpr int kLogitSplit = 256;
+constexpr int kAttendSplit = 512;
 constexpr int kDecodeMaxBlocks = 128;
 
 }  // namespace tq
