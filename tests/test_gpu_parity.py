@@ -177,9 +177,14 @@ def test_logits_given_oracle_codes(d, w, group, batch, n_kv, n_keys):
     (64, 2, 4, 4, 2, 2, 300, [300, 64]),
     (64, 1, 2, 1, 1, 3, 96, [95]),
     (128, 2, 3, 16, 1, 1, 64, [37]),
-    # 256 (batch, kv-head) groups: one block per group walks up to 5 splits
+    # 256 (batch, kv-head) groups: one block per group walks up to 3 splits
     # through the staging ring (ragged lengths, one empty row)
     (128, 2, 4, 4, 32, 8, 1100, [1100, 1, 700, 0, 257, 1024, 1099, 513] * 4),
+    # 5-bit keys, 8 heads: stages of 512 tokens do not fit in LDS, 256-token splits
+    (128, 4, 4, 8, 1, 2, 900, [900, 511]),
+    # 8 heads, several 512-token splits per block and a ragged last one
+    (128, 3, 4, 8, 1, 1, 2100, [2100]),
+    (64, 3, 4, 8, 2, 1, 1600, [1600, 1025]),
 ])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_decode_attend_given_oracle_codes(d, kw, vw, group, batch, n_kv, T, lens, out_dtype):
