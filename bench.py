@@ -13,9 +13,9 @@ one of `--copies` independent input/cache sets (together > 1 GiB) so that
 the 256 MB Infinity Cache cannot hold the working set.
 
 Printed: one JSON line. `value` is q.k logits per second over whole steps
-(encode + logit scan with its query preparation), each step one HIP-graph
-replay of the two library calls on a fresh input copy, timed with HIP
-events on the replay stream. Per-kernel times come from graphs of
+(encode + logit scan with its query preparation); the K timed steps (the
+two library calls per step, each step on a fresh input copy) are captured
+as one HIP graph and timed with HIP events around its replay. Per-kernel times come from graphs of
 back-to-back calls of one kind (HIP events around their replays);
 `roofline` prices the kernel with the largest share of the step against
 HBM's 8 TB/s with the algorithmic bytes it must move (also against a
@@ -196,18 +196,22 @@ def main_decode_layer(args, torch, tq, syn):
         return lambda: tq.logits(kc, qs[c], codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok,
                                  out=outs[c], workspace=ws)
 
-    # one graph per copy: the whole step (encode the prefill, then every
-    # logit), so the timed steps carry no host launch overhead
-    steps_g = [capture(torch, [enc(c), lgt(c)]) for c in range(C)]
-    for i in range(args.warmup):
-        steps_g[i % C].replay()
+    # the warmup steps and the K timed steps each captured as one graph:
+    # step i encodes copy i % C's prefill, then computes all its logits, so
+    # the timed region holds exactly K whole steps and no host launch gaps
+    # (one graph launch per step would leave the GPU idle between steps)
+    def steps_graph(n):
+        return capture(torch, [f for i in range(n) for f in (enc(i % C), lgt(i % C))]) if n > 0 else None
+    warm_g = steps_graph(args.warmup)
+    timed_g = steps_graph(args.steps)
+    if warm_g is not None:
+        warm_g.replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
-    for i in range(args.steps):
-        steps_g[i % C].replay()
+    timed_g.replay()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -392,6 +396,9 @@ def main():
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the codec path has no "
                                    "multi-GPU component (shard batch x KV heads across GPUs instead)",
                           "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print(json.dumps({"error": "--steps must be >= 1 and --warmup >= 0"}))
         sys.exit(2)
     import torch
     import kv_cache_vector_rht_amd as tq
