@@ -95,16 +95,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sources_digest():
-    """sha256 over the library's kernel sources (csrc/*), so that counter
-    figures taken from an older build are recognised as stale."""
+# the library sources that define each timed kernel
+KERNEL_SOURCES = {
+    "encode": ["tq_encode.inc.h", "tq_qjl.h", "tq_device.h", "tq_kernels.h", "tq_encode_d128.hip",
+               "tq_encode_d64.hip"],
+    "logits": ["tq_decode.inc.h", "tq_mfma.h", "tq_qjl.h", "tq_device.h", "tq_kernels.h", "tq_decode_d128.hip",
+               "tq_decode_d64.hip"],
+}
+KERNEL_SOURCES["decode"] = KERNEL_SOURCES["logits"]
+
+
+def kernel_sources_digest(kernel):
+    """sha256 over the sources that define `kernel`, so that counter figures
+    taken from an older build of it are recognised as stale."""
     import hashlib
     d = os.path.join(ROOT, "kv_cache_vector_rht_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".h", ".hip", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in sorted(KERNEL_SOURCES[kernel]):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()
 
 
@@ -118,7 +127,7 @@ PROFILE_OF = {
 
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel sources changed since it was taken."""
+    there is none or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, PROFILE_OF.get(kernel, ""))
     if not os.path.isfile(path):
         return None
@@ -128,7 +137,7 @@ def measured_traffic(kernel):
         if sep:
             fields[k.strip()] = v.strip()
     try:
-        if fields.get("kernel_sources_sha256") != kernel_sources_digest():
+        if fields.get("kernel_sources_sha256") != kernel_sources_digest(kernel):
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
