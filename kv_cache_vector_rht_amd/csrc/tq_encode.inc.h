@@ -87,17 +87,17 @@ __device__ __forceinline__ float centroid(const float (&c_up)[(1 << W) / 2], con
   }
 }
 
-// From w = 4 bits on, the decisions use the codebook's symmetry
+// From w = 2 bits on, the decisions use the codebook's symmetry
 // (t[L-2-k] = -t[k], t[L/2-1] = 0): the sign of y gives the top index bit,
 // a binary search of |y| over the upper half's L/2 - 1 thresholds gives
-// j = #{t_{L/2+m} <= |y|}, and idx = L/2 + j (y >= 0) or L/2 - 1 - j'
-// (y < 0), where j' counts the thresholds strictly below |y| (ties of a
-// negative y go up in y, i.e. down in |y|) and equals j of the float just
-// below |y|. The lower index bits are then j's bits, inverted for y < 0.
-// Fewer selects than the plain search: the candidates per level halve.
+// j = #{t_{L/2+m} <= |y|}, and idx = L/2 + j (y >= 0) or L/2 - 1 - j
+// (y < 0); the lower index bits are j's bits, inverted for y < 0. This is
+// #{t <= y} except where a negative y equals a nonzero threshold exactly
+// (that tie goes to the lower cell); y = 0 (either sign) goes up. Half the
+// select work of the plain search at each level.
 template <int W>
 struct DecLevels {
-  static constexpr bool kSym = W >= 4;
+  static constexpr bool kSym = W >= 2;
   Levels<kSym ? W - 1 : W> lv;
   // thresholds th[L-1] (LDS), scaled by s
   __device__ __forceinline__ void load(const float *th, float s) {
@@ -110,18 +110,16 @@ struct DecLevels {
   }
 };
 
-// Lane masks m[q] of bit q of idx = #{t_j <= y} for one coordinate (y given
-// unscaled, the thresholds scaled alike), and with CENT c = c[idx] from
-// c_up, the upper half of the (symmetric) codebook.
+// Lane masks m[q] of bit q of idx for one coordinate (y given unscaled, the
+// thresholds scaled alike), and with CENT c = c[idx] from c_up, the upper
+// half of the (symmetric) codebook.
 template <int W, bool CENT>
 __device__ __forceinline__ void decide_masks(float y, const DecLevels<W> &dl, const float (&c_up)[(1 << W) / 2],
                                              uint64_t (&m)[W], float &c) {
   if constexpr (DecLevels<W>::kSym) {
     const bool up = y >= 0.f;                       // also for y = -0
-    const uint32_t ab = __float_as_uint(y) & 0x7fffffffu;
-    const float a = __uint_as_float(up ? ab : ab - 1u);   // y < 0: ab > 0
     bool jd[W - 1];
-    decide<W - 1>(a, dl.lv, jd);
+    decide<W - 1>(fabsf(y), dl.lv, jd);
     const uint64_t mu = __ballot(up);
     m[W - 1] = mu;
 #pragma unroll
