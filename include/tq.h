@@ -75,7 +75,10 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
  *               H the Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i&j)
  *   centroids   device float [L], ascending and symmetric (c[L-1-k] = -c[k]),
  *               e.g. from tq_make_codebook
- *   thresholds  device float [L-1], t_j between c[j-1] and c[j]
+ *   thresholds  device float [L-1], t_j between c[j-1] and c[j], antisymmetric
+ *               (t[L-2-k] = -t[k], middle one 0) as tq_make_codebook makes
+ *               them: the kernels use the upper halves of both arrays (the
+ *               sign of a rotated coordinate gives its top index bit)
  *   sketch      device fp16 bit patterns [d][d] (keys only, else NULL): the
  *               QJL projection S, row j = the j-th projection direction
  * The arrays are read, never written, and must stay alive while any call
