@@ -9,16 +9,15 @@
 // み・実測精度・2026年7月時点の実装状況" (第1段: randomized Hadamard rotation +
 // per-coordinate Lloyd-Max; 第2段: 1-bit JL projection of the residual).
 //
-// Mapping: every lane holds 64 coordinates of one token. For d = 64 a wave
-// encodes 64 tokens (one lane each) and rotates in registers. For d = 128 it
-// encodes 32 tokens, token t in lanes t and t + 32; the rotation
-// H_128 = H_4 (x) H_32 runs its 32-point blocks on the matrix cores for
-// 16-bit inputs (fp32 inputs: six butterfly stages in registers and one
-// across the half-waves). A ballot over the wave of one coordinate slot's
-// index bit yields 64 token bits: 32-bit value-code words (d = 64: two
-// 32-token blocks of one coordinate; d = 128: two coordinates of one
-// block). Key records are assembled per lane; the QJL projection of the
-// wave's residuals runs on the matrix cores (tq_qjl.h).
+// Mapping: a wave encodes 32 tokens (d = 128) or 64 (d = 64, two tiles of
+// 32); every token is split over lanes t and t + 32, each holding half of
+// every 32-coordinate block, 64 values per lane. The rotation
+// H_D = H_{D/32} (x) H_32 runs its 32-point blocks on the matrix cores for
+// 16-bit inputs (fp32 inputs: butterflies in registers and one stage across
+// the half-waves). A ballot over the wave of one value slot's index bit
+// yields two 32-bit value-code words (two coordinates of one 32-token
+// block). Key records are assembled per lane pair; the QJL projection of
+// each 32-token tile runs on the matrix cores (tq_qjl.h).
 #include "tq_device.h"
 #include "tq_kernels.h"
 #include "tq_qjl.h"
@@ -159,30 +158,36 @@ union Frag8 {
 __host__ __device__ constexpr int mfma_row_coord(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
 // XT: the input's type, 0 fp32, 1 bf16, 2 fp16.
+//
+// Lane layout (both head sizes): a wave holds NT = 128 / D tiles of 32
+// tokens; lane (t, h) = (l % 32, l / 32) holds, for tile T, coordinates
+// 32 b + 16 h + i (b < D / 32, i < 16) of token 32 T + t in
+// v[(D / 2) T + 16 b + i]: 64 values per lane, each token split over the two
+// half-waves.
 template <int D, int W, bool KEY, int XT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void encode_kernel(EncodeParams p) {
   constexpr int L = 1 << W;
-  constexpr int C = 64;                      // coordinates per lane
-  constexpr int LPT = D / C;                 // lanes per token (1 or 2)
-  constexpr int TPW = kWave / LPT;           // tokens per wave (64 or 32)
-  constexpr int NWL = C / 32;                // plane words per lane (2)
+  constexpr int NT = 128 / D;                // 32-token tiles per wave (1 or 2)
+  constexpr int TPW = 32 * NT;               // tokens per wave
+  constexpr int CT = D / 2;                  // values per lane and tile
+  constexpr int NB = D / 32;                 // 32-coordinate blocks
   __shared__ float s_cent[L];
   __shared__ float s_th[L];
   __shared__ __attribute__((aligned(16))) float s_sign[D];
   __shared__ __attribute__((aligned(16))) uint16_t s_sk[KEY ? D * (D + 8) : 8];
-  // d = 128, 16-bit input: A operands of the rotation's 32-point blocks,
+  // 16-bit input: A operands of the rotation's 32-point blocks,
   // [block b][K step e][lane][8 halves]. Lane l holds row l % 32, standing
   // for output coordinate rc = mfma_row_coord(l % 32), and input coordinates
   // k = 16 (l / 32) + 8 e + j: the entry is (-1)^popcount(rc & k) s[32 b + k]
   // (+-1 in the input's type), i.e. H_32 diag(s) restricted to the block.
-  constexpr bool MFMA_ROT = D == 128 && XT != 0;
-  __shared__ __attribute__((aligned(16))) uint32_t s_ha[MFMA_ROT ? 4 * 2 * kWave * 4 : 4];
+  constexpr bool MFMA_ROT = XT != 0;
+  __shared__ __attribute__((aligned(16))) uint32_t s_ha[MFMA_ROT ? NB * 2 * kWave * 4 : 4];
   if (threadIdx.x < L) s_cent[threadIdx.x] = p.centroids[threadIdx.x];
   if (threadIdx.x < L - 1) s_th[threadIdx.x] = p.thresholds[threadIdx.x];
   for (int i = threadIdx.x; i < D; i += blockDim.x) s_sign[i] = p.signs[i];
   if constexpr (MFMA_ROT) {
     constexpr uint32_t one = XT == 2 ? 0x3C00u : 0x3F80u;
-    for (int idx = threadIdx.x; idx < 4 * 2 * kWave * 4; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < NB * 2 * kWave * 4; idx += blockDim.x) {
       const int jj = idx & 3, ln = (idx >> 2) & 63, e = (idx >> 8) & 1, bb = idx >> 9;
       const int rc = mfma_row_coord(ln & 31);
       uint32_t w = 0u;
@@ -200,36 +205,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   __syncthreads();
 
   const int lane = lane_id();
-  const int tok = lane % TPW;                // token within the wave
-  const int hv = lane / TPW;                 // d = 128: which half of every 32-coordinate block
+  const int tt = lane % 32;                  // token within a tile
+  const int hv = lane / 32;                  // which half of every 32-coordinate block
   // each wave encodes token groups wave, wave + (waves in the grid), ...
   const int64_t wave_stride = static_cast<int64_t>(gridDim.x) * (blockDim.x / kWave);
   for (int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
        wave < p.n_waves; wave += wave_stride) {
     const int64_t seq = wave / p.groups_per_seq;
     const int64_t g = p.g0 + wave % p.groups_per_seq;
-    const int64_t pos = g * TPW + tok;         // cache slot
-    const int64_t t = pos - p.t0;              // input token
-    const bool active = (t >= 0) && (t < p.n_tok);
-    const int64_t off = seq * p.x_seq_stride + t * p.x_tok_stride;
-
-    // Lane layout. d = 64: one lane per token, coordinate i in v[i]. d = 128:
-    // lanes t and t + 32 hold token t; lane half h holds coordinates
-    // 32 b + 16 h + i (block b = 0..3, i = 0..15) in v[16 b + i].
-    float v[C];
-    if constexpr (D == 128) {
-      if constexpr (XT != 0) {
-        // (a2) z = H_32 diag(s) x per 32-coordinate block on the matrix cores
-        // (exact +-1 operands, fp32 sums), then H_4 across the blocks
-        Frag8 xb[4][2];
+    int64_t pos[NT];                           // cache slot of this lane's token in tile T
+    bool active[NT];
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb)
+    for (int T = 0; T < NT; ++T) {
+      pos[T] = g * TPW + 32 * T + tt;
+      const int64_t t = pos[T] - p.t0;         // input token
+      active[T] = (t >= 0) && (t < p.n_tok);
+    }
+    auto row = [&](int T) { return seq * p.x_seq_stride + (pos[T] - p.t0) * p.x_tok_stride; };
+
+    float v[64];
+    float n2[NT];                              // this lane's share of ||v||^2 per token
+    if constexpr (MFMA_ROT) {
+      // (a2) v = H_D diag(s) x with H_D = H_{D/32} (x) H_32: each 32-point
+      // block on the matrix cores (exact +-1 operands, fp32 sums), then the
+      // butterflies across blocks in registers
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        Frag8 xb[NB][2];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            if (active) xb[bb][e].u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + off + 32 * bb + 16 * hv + 8 * e);
+            if (active[T]) xb[bb][e].u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + row(T) + 32 * bb + 16 * hv + 8 * e);
             else xb[bb][e].u = make_uint4(0u, 0u, 0u, 0u);
           }
-        for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
           v16f c = {};
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
@@ -239,210 +250,223 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
             else c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.b, xb[bb][e].b, c, 0, 0, 0);
           }
 #pragma unroll
-          for (int q = 0; q < 16; ++q) v[16 * bb + q] = c[q];
+          for (int q = 0; q < 16; ++q) v[CT * T + 16 * bb + q] = c[q];
         }
+        float *vt = v + CT * T;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float a0 = v[i], a1 = v[16 + i], a2 = v[32 + i], a3 = v[48 + i];
-          const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
-          v[i] = b0 + b2; v[16 + i] = b1 + b3; v[32 + i] = b0 - b2; v[48 + i] = b1 - b3;
-        }
-      } else {
-        // fp32 input: sign flip, the six in-lane butterfly stages (coordinate
-        // bits 0-3, 5, 6), then coordinate bit 4 across the half-waves
-        if (active) {
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            float w[16];
-            load_row_vec_f32<16>(static_cast<const float *>(p.x) + off + 32 * bb + 16 * hv, w);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v[16 * bb + i] = w[i];
+          if constexpr (NB == 4) {
+            const float a0 = vt[i], a1 = vt[16 + i], a2 = vt[32 + i], a3 = vt[48 + i];
+            const float b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+            vt[i] = b0 + b2; vt[16 + i] = b1 + b3; vt[32 + i] = b0 - b2; vt[48 + i] = b1 - b3;
+          } else {
+            const float a0 = vt[i], a1 = vt[16 + i];
+            vt[i] = a0 + a1; vt[16 + i] = a0 - a1;
           }
-        } else {
-#pragma unroll
-          for (int i = 0; i < C; ++i) v[i] = 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < C; ++i) v[i] *= s_sign[32 * (i >> 4) + 16 * hv + (i & 15)];
-        fwht_regs<C>(v);
-        // Swapping a value with itself across half-waves leaves the lower
-        // half's copy in the first register and the upper half's in the
-        // second, in every lane.
-        const float sgn = hv ? -1.f : 1.f;
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-          const uint32_t u = __float_as_uint(v[i]);
-          auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-          v[i] = fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
         }
       }
     } else {
-      if (active) {
-        if constexpr (XT == 0) load_row_vec_f32<C>(static_cast<const float *>(p.x) + off, v);
-        else if constexpr (XT == 1) load_row_vec_16<C, true>(static_cast<const uint16_t *>(p.x) + off, v);
-        else load_row_vec_16<C, false>(static_cast<const uint16_t *>(p.x) + off, v);
-      } else {
+      // fp32 input: sign flip and the in-lane butterfly stages (coordinate
+      // bits 0-3 and 5 up) per tile, then coordinate bit 4 across the
+      // half-waves. Swapping a value with itself across half-waves leaves the
+      // lower half's copy in the first register and the upper half's in the
+      // second, in every lane.
+      const float sgn = hv ? -1.f : 1.f;
 #pragma unroll
-        for (int i = 0; i < C; ++i) v[i] = 0.f;
+      for (int T = 0; T < NT; ++T) {
+        float *vt = v + CT * T;
+        if (active[T]) {
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) {
+            float w[16];
+            load_row_vec_f32<16>(static_cast<const float *>(p.x) + row(T) + 32 * bb + 16 * hv, w);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vt[16 * bb + i] = w[i];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < CT; ++i) vt[i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < CT; ++i) vt[i] *= s_sign[32 * (i >> 4) + 16 * hv + (i & 15)];
+        fwht_regs<CT>(*reinterpret_cast<float (*)[CT]>(vt));
+#pragma unroll
+        for (int i = 0; i < CT; ++i) {
+          const uint32_t u = __float_as_uint(vt[i]);
+          auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+          vt[i] = fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+        }
       }
-#pragma unroll
-      for (int i = 0; i < C; ++i) v[i] *= s_sign[i];
-      fwht_regs<C>(v);
     }
 
-    // (a1) norm from the rotated vector: ||H diag(s) x||^2 = D ||x||^2
-    float n2 = 0.f;
+    // (a1) norm from the rotated vector: ||H diag(s) x||^2 = D ||x||^2, the
+    // two half-waves' shares added
+    float nrm[NT], vn[NT];
+    bool nz[NT];
+    DecLevels<W> ls[NT];
 #pragma unroll
-    for (int i = 0; i < C; ++i) n2 = fmaf(v[i], v[i], n2);
-    if (LPT == 2) {
-      const float o = swap_half_f(n2);
-      n2 = hv ? (o + n2) : (n2 + o);
+    for (int T = 0; T < NT; ++T) {
+      float s2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < CT; ++i) s2 = fmaf(v[CT * T + i], v[CT * T + i], s2);
+      const float o = swap_half_f(s2);
+      n2[T] = hv ? (o + s2) : (s2 + o);
+      nrm[T] = sqrtf(n2[T] * (1.0f / static_cast<float>(D)));
+      // y = v / ||v|| (v = H diag(s) x, ||v|| = n sqrt(D)). The decisions
+      // compare v with the thresholds scaled by ||v|| (y >= t <=> v >= t ||v||
+      // up to one rounding), the residual takes y - c = fma(v, 1 / ||v||, -c);
+      // the zero vector has v = 0, unscaled thresholds and y = 0.
+      nz[T] = n2[T] > 0.f;
+      vn[T] = nz[T] ? sqrtf(n2[T]) : 1.0f;
     }
-    const float n = sqrtf(n2 * (1.0f / static_cast<float>(D)));
-    // y = v / ||v|| (v = H diag(s) x, ||v|| = n sqrt(D)). The decisions
-    // compare v with the thresholds scaled by ||v|| (y >= t <=> v >= t ||v||
-    // up to one rounding), the residual takes y - c = fma(v, 1 / ||v||, -c);
-    // the zero vector has v = 0, unscaled thresholds and y = 0.
-    const bool nz = n2 > 0.f;
-    const float vn = nz ? sqrtf(n2) : 1.0f;
     // (read from LDS per group: the unscaled thresholds stay out of the
     // registers that live across the loop)
     asm volatile("" ::: "memory");
-    DecLevels<W> ls;
-    ls.load(s_th, vn);
-
+#pragma unroll
+    for (int T = 0; T < NT; ++T) ls[T].load(s_th, vn[T]);
 
     if (KEY) {
       // (a3) indices -> bit planes: each decision's lane mask is added in as
-      // the carry of half + half (coordinate order reversed, so the first
-      // coordinate lands on bit 0); (a4) residual, kept as r' = 2^10 r =
-      // fma(v, 2^10 / ||v||, -2^10 c), the scale the QJL projection wants
-      const float rs = nz ? 1024.0f / vn : 0.f;
-      constexpr int HB = D == 128 ? 4 : NWL;   // bit groups per lane and plane
-      constexpr int HW = C / HB;               // bits per group (16 or 32)
+      // the carry of half + half into the 16-bit group of its block
+      // (coordinate order reversed, so the first coordinate lands on bit 0);
+      // (a4) residual, kept as r' = 2^10 r = fma(v, 2^10 / ||v||, -2^10 c),
+      // the scale the QJL projection wants
+      float rs[NT];
+#pragma unroll
+      for (int T = 0; T < NT; ++T) rs[T] = nz[T] ? 1024.0f / vn[T] : 0.f;
       float c_up[L / 2];
 #pragma unroll
       for (int j = 0; j < L / 2; ++j) c_up[j] = 1024.0f * s_cent[L / 2 + j];
-      uint32_t hw[W][HB];
+      uint32_t hw[W][4];                       // group (T, b) = 2 T + b (d = 64) or b (d = 128)
 #pragma unroll
       for (int q = 0; q < W; ++q)
 #pragma unroll
-        for (int k = 0; k < HB; ++k) hw[q][k] = 0u;
-      float g2 = 0.f;
+        for (int k = 0; k < 4; ++k) hw[q][k] = 0u;
 #pragma unroll
-      for (int i = C - 1; i >= 0; --i) {
+      for (int i = 63; i >= 0; --i) {
+        const int T = i / CT;
         uint64_t m[W];
         float cq;
-        decide_masks<W, true>(v[i], ls, c_up, m, cq);
+        decide_masks<W, true>(v[i], ls[T], c_up, m, cq);
 #pragma unroll
         for (int q = 0; q < W; ++q) {
           uint64_t carry;
-          asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(hw[q][i / HW]), "=s"(carry) : "s"(m[q]));
+          asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(hw[q][i / 16]), "=s"(carry) : "s"(m[q]));
         }
-        v[i] = fmaf(v[i], rs, -cq);
+        v[i] = fmaf(v[i], rs[T], -cq);
         asm volatile("" : "+v"(v[i]));    // consume the decisions here
         __builtin_amdgcn_sched_barrier(0);
       }
-      // this lane's two words of every plane: d = 64 the groups themselves;
-      // d = 128 word b = half b of lane half 0 | half b of lane half 1 << 16,
-      // lane half h keeping words 2 h and 2 h + 1
-      uint32_t planes[W][NWL];
+      // plane words: word b of a token = its group b of lane half 0 | that of
+      // lane half 1 << 16. d = 128: lane half h keeps words 2 h, 2 h + 1 of
+      // its token; d = 64: word h of each of its two tokens.
+      uint32_t pw[W][2];
 #pragma unroll
       for (int q = 0; q < W; ++q) {
         if constexpr (D == 128) {
           const uint32_t send = hv ? (hw[q][0] | (hw[q][1] << 16)) : (hw[q][2] | (hw[q][3] << 16));
           auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
           const uint32_t recv = hv ? r[0] : r[1];
-          planes[q][0] = hv ? ((recv & 0xffffu) | (hw[q][2] << 16)) : (hw[q][0] | (recv << 16));
-          planes[q][1] = hv ? ((recv >> 16) | (hw[q][3] << 16)) : (hw[q][1] | (recv & 0xffff0000u));
+          pw[q][0] = hv ? ((recv & 0xffffu) | (hw[q][2] << 16)) : (hw[q][0] | (recv << 16));
+          pw[q][1] = hv ? ((recv >> 16) | (hw[q][3] << 16)) : (hw[q][1] | (recv & 0xffff0000u));
         } else {
-          planes[q][0] = hw[q][0];
-          planes[q][1] = hw[q][1];
+          const uint32_t send = hv ? (hw[q][0] | (hw[q][2] << 16)) : (hw[q][1] | (hw[q][3] << 16));
+          auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+          const uint32_t recv = hv ? r[0] : r[1];
+          pw[q][0] = hv ? ((recv & 0xffffu) | (hw[q][1] << 16)) : (hw[q][0] | (recv << 16));
+          pw[q][1] = hv ? ((recv >> 16) | (hw[q][3] << 16)) : (hw[q][2] | (recv & 0xffff0000u));
         }
       }
+      float gamma[NT];
 #pragma unroll
-      for (int i = 0; i < C; ++i) g2 = fmaf(v[i], v[i], g2);
-      if (LPT == 2) {
+      for (int T = 0; T < NT; ++T) {
+        float g2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < CT; ++i) g2 = fmaf(v[CT * T + i], v[CT * T + i], g2);
         const float o = swap_half_f(g2);
         g2 = hv ? (o + g2) : (g2 + o);
+        gamma[T] = sqrtf(g2) * (1.0f / 1024.0f);
       }
-      const float gamma = sqrtf(g2) * (1.0f / 1024.0f);
 
       // (a5) QJL sign bits sigma_j = [ (S r)_j >= 0 ], on the matrix cores
-      uint32_t sig[D / 32];
-      qjl_signs_mfma<D>(s_sk, v, sig);
-
-      if (active) {
-        // (a6) record: W index planes then the sign plane, D/8 bytes each;
-        // this lane writes bytes [8 hv, 8 hv + 8) of every plane
-        constexpr int REC = (W + 1) * D / 8;
-        constexpr int PB = D / 8;
-        uint8_t *rec = static_cast<uint8_t *>(p.codes) + (seq * p.cap + pos) * REC + 8 * hv;
+      constexpr int REC = (W + 1) * D / 8;
+      constexpr int PB = D / 8;
 #pragma unroll
-        for (int q = 0; q < W; ++q)
-          *reinterpret_cast<uint2 *>(rec + q * PB) = make_uint2(planes[q][0], planes[q][1]);
-        *reinterpret_cast<uint2 *>(rec + W * PB) = make_uint2(sig[2 * hv], sig[2 * hv + 1]);
-        if (hv == 0) {
-          const uint32_t sc = static_cast<uint32_t>(float_to_f16_bits(n)) |
-                              (static_cast<uint32_t>(float_to_f16_bits(gamma)) << 16);
-          reinterpret_cast<uint32_t *>(p.scalars)[seq * p.cap + pos] = sc;
+      for (int T = 0; T < NT; ++T) {
+        uint32_t sig[D / 32];
+        qjl_tile<D>(s_sk, v + CT * T, sig);
+        if (active[T]) {
+          // (a6) record: W index planes then the sign plane, D/8 bytes each;
+          // this lane writes bytes [PB/2 hv, PB/2 hv + PB/2) of every plane
+          uint8_t *rec = static_cast<uint8_t *>(p.codes) + (seq * p.cap + pos[T]) * REC + (PB / 2) * hv;
+          if constexpr (D == 128) {
+#pragma unroll
+            for (int q = 0; q < W; ++q)
+              *reinterpret_cast<uint2 *>(rec + q * PB) = make_uint2(pw[q][0], pw[q][1]);
+            *reinterpret_cast<uint2 *>(rec + W * PB) = make_uint2(sig[2 * hv], sig[2 * hv + 1]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < W; ++q) *reinterpret_cast<uint32_t *>(rec + q * PB) = pw[q][T];
+            *reinterpret_cast<uint32_t *>(rec + W * PB) = sig[hv];
+          }
+          if (hv == 0) {
+            const uint32_t sc = static_cast<uint32_t>(float_to_f16_bits(nrm[T])) |
+                                (static_cast<uint32_t>(float_to_f16_bits(gamma[T])) << 16);
+            reinterpret_cast<uint32_t *>(p.scalars)[seq * p.cap + pos[T]] = sc;
+          }
         }
       }
     } else {
-      // values: the ballot of one coordinate slot gives 64 token bits; the
-      // word of coordinate c goes to lane c % 64 of lo (c < 64) or hi
-      uint32_t lo[W], hi[W];
+      // values: the ballot of one value slot gives, in its low half, the bits
+      // of coordinate c0 = 32 b + i and, in its high half, of c0 + 16, for
+      // the 32 tokens of one tile. The word of coordinate c of 32-token block
+      // k goes to lane c % 64 of wr[k][.] (d = 128: k = c / 64 of block g;
+      // d = 64: k = T, block 2 g + T).
+      uint32_t wr[2][W];
 #pragma unroll
-      for (int q = 0; q < W; ++q) { lo[q] = 0u; hi[q] = 0u; }
+      for (int q = 0; q < W; ++q) { wr[0][q] = 0u; wr[1][q] = 0u; }
       // (the decision's own lane mask, masked on the scalar unit: a ballot
       // of a combined condition would first widen it to a vector of 0/1)
-      const uint64_t valid = __ballot(active);
+      uint64_t valid[NT];
+#pragma unroll
+      for (int T = 0; T < NT; ++T) valid[T] = __ballot(active[T]);
       const float c_none[L / 2] = {};
-      static_for<0, C>([&](auto ic) {
+      static_for<0, 64>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        constexpr int T = i / CT, b = (i % CT) / 16, j = i % 16;
+        constexpr int c0 = 32 * b + j, c1 = c0 + 16;
+        constexpr int k = (D == 128) ? c0 / 64 : T;
         uint64_t mq[W];
         float unused;
-        decide_masks<W, false>(v[i], ls, c_none, mq, unused);
+        decide_masks<W, false>(v[i], ls[T], c_none, mq, unused);
 #pragma unroll
         for (int q = 0; q < W; ++q) {
-          const uint64_t m = mq[q] & valid;
-          if constexpr (D == 128) {
-            // lanes 0-31: coordinate c0 = 32 b + j; lanes 32-63: c0 + 16
-            constexpr int c0 = 32 * (i >> 4) + (i & 15), c1 = c0 + 16;
-            if constexpr (c0 < 64) {
-              write_lane<c0>(lo[q], static_cast<uint32_t>(m));
-              write_lane<c1>(lo[q], static_cast<uint32_t>(m >> 32));
-            } else {
-              write_lane<c0 - 64>(hi[q], static_cast<uint32_t>(m));
-              write_lane<c1 - 64>(hi[q], static_cast<uint32_t>(m >> 32));
-            }
-          } else {
-            write_lane<i>(lo[q], static_cast<uint32_t>(m));
-            write_lane<i>(hi[q], static_cast<uint32_t>(m >> 32));
-          }
+          const uint64_t m = mq[q] & valid[T];
+          write_lane<c0 % 64>(wr[k][q], static_cast<uint32_t>(m));
+          write_lane<c1 % 64>(wr[k][q], static_cast<uint32_t>(m >> 32));
         }
         __builtin_amdgcn_sched_barrier(0);
       });
       const int64_t nblk = p.cap / kValueBlock;
       uint32_t *words = static_cast<uint32_t *>(p.codes);
-      // d = 64: lo -> block 2g, hi -> block 2g + 1 (coordinate = lane)
-      // d = 128: both -> block g; lo -> coordinate lane, hi -> coordinate 64 + lane
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const uint32_t vm = LPT == 2 ? static_cast<uint32_t>(valid) : static_cast<uint32_t>(valid >> (32 * half));
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t vm = static_cast<uint32_t>(valid[D == 128 ? 0 : k]);
         if (vm == 0u) continue;
-        const int64_t blk = LPT == 2 ? g : 2 * g + half;
-        const int coord = LPT == 2 ? 64 * half + lane : lane;
+        const int64_t blk = (D == 128) ? g : 2 * g + k;
+        const int coord = (D == 128) ? 64 * k + lane : lane;
         uint32_t *base = words + (seq * nblk + blk) * W * D + coord;
 #pragma unroll
         for (int q = 0; q < W; ++q) {
-          uint32_t w = half ? hi[q] : lo[q];
+          uint32_t w = wr[k][q];
           uint32_t *dst = base + q * D;
           if (vm != 0xffffffffu) w = (*dst & ~vm) | (w & vm);
           *dst = w;
         }
       }
-      if (active && hv == 0) p.scalars[seq * p.cap + pos] = float_to_f16_bits(n);
+#pragma unroll
+      for (int T = 0; T < NT; ++T)
+        if (active[T] && hv == 0) p.scalars[seq * p.cap + pos[T]] = float_to_f16_bits(nrm[T]);
     }
   }
 }

@@ -31,16 +31,6 @@ union V8H {
   uint32_t u[4];
 };
 
-// Swap the upper half-wave of x with the lower half-wave of y (both 4 dwords).
-__device__ __forceinline__ void swap_halves(V8H &x, V8H &y) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    auto r = __builtin_amdgcn_permlane32_swap(x.u[k], y.u[k], false, false);
-    x.u[k] = r[0];
-    y.u[k] = r[1];
-  }
-}
-
 // Two residual coordinates (already scaled by 2^10) as fp16 hi and lo parts,
 // each pair packed in one dword: hi = fp16(a) rounded toward zero, lo =
 // fp16(a - hi) likewise (a - hi is exact in fp32), so hi + lo carries 22
@@ -84,89 +74,49 @@ __device__ __forceinline__ void stage_sketch(const uint16_t *__restrict__ sketch
   for (int k = 0; k < N; ++k) {
     const int e = k * 256 + threadIdx.x;
     const int row = e / (D / 8), c8 = e % (D / 8);
-    // d = 128: column unit 4 a + 2 h + b (coordinates 32 a + 16 h + 8 b ..)
-    // goes to position 8 h + 2 a + b, the K order of the encoder's lanes
-    const int pos = (D == 128) ? 8 * ((c8 >> 1) & 1) + 2 * (c8 >> 2) + (c8 & 1) : c8;
+    // column unit 4 a + 2 h + b (coordinates 32 a + 16 h + 8 b ..) goes to
+    // position (D / 16) h + 2 a + b, the K order of the encoder's lanes
+    const int pos = (D / 16) * ((c8 >> 1) & 1) + 2 * (c8 >> 2) + (c8 & 1);
     *reinterpret_cast<uint4 *>(s_sk + row * RP + pos * 8) = v[k];
   }
 }
 
-// r: this lane's 64 residual coordinates times 2^10 (consumed); sig: the D/32 sign
-// words of this lane's token.
-//  d = 64  (one lane per token, 64 tokens): two 32-token N tiles; the
-//          lane-swap supplies the other half-wave's coordinates.
-//  d = 128 (lane half h of token t holds coordinates 32 b + 16 h + i in
-//          r[16 b + i]): K slot (ks, h, e) is coordinate
-//          32 (ks / 2) + 16 h + 8 (ks % 2) + e = r[8 ks + e] of lane half h
-//          (the staged sketch's columns are in this order), so every lane
-//          feeds its own coordinates; one 32-token N tile.
+// Sign words of one 32-token tile: lane half h of token t holds the tile's
+// residual coordinates 32 b + 16 h + i (times 2^10) in r[16 b + i], b < D/32.
+// K slot (ks, h, e) of the projection is coordinate
+// 32 (ks / 2) + 16 h + 8 (ks % 2) + e = r[8 ks + e] of lane half h (the
+// staged sketch's columns are in this order), so every lane feeds its own
+// coordinates. sig[jt] is the token's sign word of projections
+// 32 jt .. 32 jt + 31.
 template <int D>
-__device__ __forceinline__ void qjl_signs_mfma(const uint16_t *s_sk, float (&r)[64], uint32_t (&sig)[D / 32]) {
+__device__ __forceinline__ void qjl_tile(const uint16_t *s_sk, const float *r, uint32_t (&sig)[D / 32]) {
   constexpr int RP = D + 8;
+  constexpr int KS = D / 16;
   const int lane = lane_id();
   const int hw = lane / 32;
-  if constexpr (D == 128) {
-    constexpr int KS = 8;
-    V8H bh[KS], bl[KS];
+  V8H bh[KS], bl[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) split_pair(r[8 * ks + e], r[8 * ks + e + 1], bh[ks].u[e / 2], bl[ks].u[e / 2]);
+  }
+#pragma unroll
+  for (int jt = 0; jt < D / 32; ++jt) {
+    v16f c = {};
+    const uint16_t *arow = s_sk + (jt * 32 + (lane % 32)) * RP + (D / 2) * hw;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) split_pair(r[8 * ks + e], r[8 * ks + e + 1], bh[ks].u[e / 2], bl[ks].u[e / 2]);
+      V8H a;
+      const uint4 u = *reinterpret_cast<const uint4 *>(arow + 8 * ks);
+      a.u[0] = u.x; a.u[1] = u.y; a.u[2] = u.z; a.u[3] = u.w;
+      c = mfma_f16_32x32x16(a.h, bh[ks].h, c);
+      c = mfma_f16_32x32x16(a.h, bl[ks].h, c);
     }
-#pragma unroll
-    for (int jt = 0; jt < D / 32; ++jt) {
-      v16f c = {};
-      const uint16_t *arow = s_sk + (jt * 32 + (lane % 32)) * RP + 64 * hw;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        V8H a;
-        const uint4 u = *reinterpret_cast<const uint4 *>(arow + 8 * ks);
-        a.u[0] = u.x; a.u[1] = u.y; a.u[2] = u.z; a.u[3] = u.w;
-        c = mfma_f16_32x32x16(a.h, bh[ks].h, c);
-        c = mfma_f16_32x32x16(a.h, bl[ks].h, c);
-      }
-      // lane l holds rows 8(q/4) + 4 hw + q%4 of column l%32
-      uint32_t pw = nonneg_bits(c);
-      pw <<= 4 * hw;
-      auto m = __builtin_amdgcn_permlane32_swap(pw, pw, false, false);
-      sig[jt] = pw | (hw ? m[0] : m[1]);
-    }
-  } else {
-    constexpr int KS = D / 16;
-    V8H bh0[KS], bl0[KS], bh1[KS], bl1[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      V8H xh, xl, yh, yl;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        split_pair(r[16 * ks + e], r[16 * ks + e + 1], xh.u[e / 2], xl.u[e / 2]);
-        split_pair(r[16 * ks + 8 + e], r[16 * ks + 8 + e + 1], yh.u[e / 2], yl.u[e / 2]);
-      }
-      swap_halves(xh, yh);
-      swap_halves(xl, yl);
-      bh0[ks] = xh; bl0[ks] = xl;      // tokens 0..31 of the wave
-      bh1[ks] = yh; bl1[ks] = yl;      // tokens 32..63
-    }
-#pragma unroll
-    for (int jt = 0; jt < D / 32; ++jt) {
-      v16f c0 = {}, c1 = {};
-      const uint16_t *arow = s_sk + (jt * 32 + (lane % 32)) * RP + 8 * hw;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        V8H a;
-        const uint4 u = *reinterpret_cast<const uint4 *>(arow + 16 * ks);
-        a.u[0] = u.x; a.u[1] = u.y; a.u[2] = u.z; a.u[3] = u.w;
-        c0 = mfma_f16_32x32x16(a.h, bh0[ks].h, c0);
-        c0 = mfma_f16_32x32x16(a.h, bl0[ks].h, c0);
-        c1 = mfma_f16_32x32x16(a.h, bh1[ks].h, c1);
-        c1 = mfma_f16_32x32x16(a.h, bl1[ks].h, c1);
-      }
-      uint32_t p0 = nonneg_bits(c0), p1 = nonneg_bits(c1);
-      p0 <<= 4 * hw;
-      p1 <<= 4 * hw;
-      auto m = __builtin_amdgcn_permlane32_swap(p0, p1, false, false);
-      sig[jt] = m[0] | m[1];
-    }
+    // lane l holds rows 8(q/4) + 4 hw + q%4 of column l%32
+    uint32_t pw = nonneg_bits(c);
+    pw <<= 4 * hw;
+    auto m = __builtin_amdgcn_permlane32_swap(pw, pw, false, false);
+    sig[jt] = pw | (hw ? m[0] : m[1]);
   }
 }
 
