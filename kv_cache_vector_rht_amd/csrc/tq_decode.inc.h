@@ -252,8 +252,9 @@ __device__ __forceinline__ float wave_fwht(float x, int lane) {
 // Scratch of the in-block query preparation (byte offsets):
 //   FRAG   int8 digit operands [NRG][NMF][64 lanes][16]
 //   SQ, SP q' and p, [8][D] float
-//   SST    per-head exponents [8][4]; SCON per-head constants [8][4];
+//   SST    per head: max |q'| and sum q' [8][4]; SCON per-head constants [8][4];
 //   SB     key basis coefficients [8]
+//   SPS    per 32-row tile of S and head: max |p| and sum p over the tile
 //   SK     the sketch [D][D] fp16, staged by direct-to-LDS loads; the 16-byte
 //          chunk c of row j sits at chunk position c ^ (j % (D/8)), so that
 //          32 lanes reading the same columns of 32 rows hit distinct banks
@@ -271,7 +272,8 @@ struct PrepShape {
   static constexpr int SST = SP + 8 * D * 4;
   static constexpr int SCON = SST + 8 * 4 * 4;
   static constexpr int SB = SCON + 8 * 4 * 4;
-  static constexpr int SK = SB + 64;
+  static constexpr int SPS = SB + 64;                 // per row tile and head: max |p|, sum p
+  static constexpr int SK = SPS + (D / 32) * 8 * 2 * 4;
   static constexpr int QIN = SK + D * D * 2;
   static constexpr int QIN_BYTES = (D / 16) * 1024;  // one load per wave
   static constexpr int TAB = SK;                      // after the GEMV: [4 NRG][NB + 1][D] digit words
@@ -327,7 +329,7 @@ template <int D, int KW, int NRG>
 __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t *scratch) {
   using PS = PrepShape<D, KW, NRG>;
   constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64;
-  constexpr int THREADS = 4 * D, NW = D / 16;
+  constexpr int NW = D / 16;
   float *sq = reinterpret_cast<float *>(scratch + PS::SQ);      // [8][D]
   float *sp = reinterpret_cast<float *>(scratch + PS::SP);      // [8][D]
   float *sst = reinterpret_cast<float *>(scratch + PS::SST);    // [8][4]
@@ -377,6 +379,8 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
   // entries of q' for the columns = heads (lanes of absent heads zero), each
   // head scaled by a power of two (its max |q'| below 2^14) and split into
   // fp16 hi + lo, two MFMAs per K step: fp32-grade sums.
+  // The epilogue also leaves the tile's max |p| and sum p per head.
+  float *sps = reinterpret_cast<float *>(scratch + PS::SPS);    // [D/32][8][2]
   if (wave < D / 32) {
     constexpr int U = D / 8;
     const int h = lane % 32, half = lane / 32;
@@ -403,67 +407,82 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
       c = mfma_f16_32x32x16(a.h, bl.h, c);
     }
     // lane holds rows 8 (q / 4) + 4 half + q % 4 of the tile, column h
-    if (live) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) sp[h * D + 32 * wave + 8 * (q / 4) + 4 * half + (q % 4)] = ldexpf(c[q], -sexp);
-    }
-  }
-  lds_barrier();
-  // p statistics and the per-head exponents and constants
-  for (int h = wave; h < GE; h += NW) {
     float mp = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float v = sp[h * D + lane + kWave * e];
+    for (int q = 0; q < 16; ++q) {
+      const float v = ldexpf(c[q], -sexp);
+      if (live) sp[h * D + 32 * wave + 8 * (q / 4) + 4 * half + (q % 4)] = v;
       mp = fmaxf(mp, fabsf(v));
       s2 += v;
     }
-    mp = wave_max(mp);
-    s2 = wave_sum(s2);
-    if (lane == 0) {
-      float mb = 0.f;
-      for (int s = 0; s < NB; ++s) mb = fmaxf(mb, fabsf(sb[s]));
-      const int el = fixed_exponent(2.0f * mb * sst[4 * h]);
-      const int eq = fixed_exponent(2.0f * mp);
-      scon[4 * h] = ldexpf(1.0f, -7 - el);
-      scon[4 * h + 1] = p.kcent[(1 << KW) - 1] * sst[4 * h + 1];
-      scon[4 * h + 2] = ldexpf(1.0f, -7 - eq);
-      scon[4 * h + 3] = s2;
-      sst[4 * h + 2] = static_cast<float>(el);
-      sst[4 * h + 3] = static_cast<float>(eq);
-    }
+    mp = fmaxf(mp, swap_half_f(mp));
+    s2 += swap_half_f(s2);
+    if (live && half == 0) { sps[(wave * 8 + h) * 2] = mp; sps[(wave * 8 + h) * 2 + 1] = s2; }
   }
   lds_barrier();
-  // digit words, once per (head, operand, coordinate c): the operand value
-  // in fixed point, 2 beta_s q'_c or 2 p_c times 2^(7 + e - c % 8) (c % 8
-  // is the bit of the plane word whose expanded byte weighs 2^(c % 8) in the
-  // MFMA; the top bit's byte is negative), as four signed 8-bit digits
+
+  // Per head: exponents and constants {2^-(7+e_lm), c[L-1] sum q',
+  // 2^-(7+e_qj), sum p} (every wave derives the ones it needs from the
+  // statistics; wave 0 also records them). Then one wave per operand slot
+  // group (rg, mf): lane slot l = row l%16 (head 4 rg + (l%16)/4, digit
+  // l%4), K slots 16 (l/16) + 4 r + jb <-> coordinate
+  // 32 word + 8 jb + 4 (kg & 1) + r (slot_coord). The wave first writes the
+  // digit words of exactly the entries it reads -- the operand value in
+  // fixed point, 2 beta_s q'_c or 2 p_c times 2^(7 + e - c % 8) (c % 8 is the
+  // bit of the plane word whose expanded byte weighs 2^(c % 8) in the MFMA;
+  // the top bit's byte is negative), as four signed 8-bit digits -- then
+  // gathers the digit bytes with byte permutes: no block barrier between.
+  float mb = 0.f;
+#pragma unroll
+  for (int s = 0; s < NB; ++s) mb = fmaxf(mb, fabsf(sb[s]));
+  auto head_exps = [&](int hl, int &el, int &eq, float &sp_sum) {
+    float mp = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) { mp = fmaxf(mp, sps[(t * 8 + hl) * 2]); s2 += sps[(t * 8 + hl) * 2 + 1]; }
+    el = fixed_exponent(2.0f * mb * sst[4 * hl]);
+    eq = fixed_exponent(2.0f * mp);
+    sp_sum = s2;
+  };
+  if (wave == 0 && lane < GE) {
+    int el, eq;
+    float s2;
+    head_exps(lane, el, eq, s2);
+    scon[4 * lane] = ldexpf(1.0f, -7 - el);
+    scon[4 * lane + 1] = p.kcent[(1 << KW) - 1] * sst[4 * lane + 1];
+    scon[4 * lane + 2] = ldexpf(1.0f, -7 - eq);
+    scon[4 * lane + 3] = s2;
+  }
   constexpr int NK = NB + 1;
   uint32_t *tab = reinterpret_cast<uint32_t *>(scratch + PS::TAB);
-  for (int e = tid; e < GE * NK * D; e += THREADS) {
-    const int c = e % D, m = (e / D) % NK, hl = e / (D * NK);
-    const bool qjl = m == NB;
+  for (int grp = wave; grp < NRG * NMF; grp += NW) {
+    const int mf = grp % NMF, rg = grp / NMF;
+    const bool qjl = mf >= NB * NH;
+    const int m = qjl ? NB : mf / NH, half = mf % NH;
     const float coef = qjl ? 2.0f : 2.0f * sb[m];
-    const int ex = static_cast<int>(sst[4 * hl + (qjl ? 3 : 2)]);
-    const int k = c & 7;
-    float v = ldexpf(coef * (qjl ? sp : sq)[hl * D + c], 7 - k + ex);
-    if (k == 7) v = -v;
-    tab[e] = signed_digits(__float2int_rn(v));
-  }
-  lds_barrier();
-  // digit operands: lane slot (rg, mf, l) = row l%16 (head 4 rg + (l%16)/4,
-  // digit l%4), K slots 16 (l/16) + 4 r + jb <-> coordinate
-  // 32 word + 8 jb + 4 (kg & 1) + r (slot_coord): four table reads of four
-  // consecutive coordinates, digit bytes gathered by byte permutes
-  for (int item = tid; item < NRG * NMF * kWave; item += THREADS) {
-    const int l = item % kWave, mf = (item / kWave) % NMF, rg = item / (kWave * NMF);
-    const int hl = 4 * rg + (l % 16) / 4, sd = l % 4, kg = l / 16;
+    // entries: head 4 rg + u (u < 4), this half's coordinate ci = lane:
+    // word 2 (ci / 32) + half (d = 128) or ci / 32 (d = 64)
+    const int ci = lane;
+    const int word = (D == 128) ? (2 * (ci / 32) + half) : (ci / 32);
+    const int coord = 32 * word + (ci % 32);
+    const int k = coord & 7;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int hl = 4 * rg + u;
+      if (hl < GE) {
+        int el, eq;
+        float s2;
+        head_exps(hl, el, eq, s2);
+        float v = ldexpf(coef * (qjl ? sp : sq)[hl * D + coord], 7 - k + (qjl ? eq : el));
+        if (k == 7) v = -v;
+        tab[(hl * NK + m) * D + coord] = signed_digits(__float2int_rn(v));
+      }
+    }
+    wait_lds();                                   // this wave's table writes before its reads
+    const int l = lane, hl = 4 * rg + (l % 16) / 4, sd = l % 4, kg = l / 16;
     uint4 out = make_uint4(0u, 0u, 0u, 0u);
     if (hl < GE) {
-      const bool qjl = mf >= NB * NH;
-      const int m = qjl ? NB : mf / NH, half = mf % NH;
-      const int word = (D == 128) ? (2 * (kg >> 1) + half) : (kg >> 1);
-      const uint32_t *row = tab + (hl * NK + m) * D + 32 * word + 4 * (kg & 1);
+      const int w2 = (D == 128) ? (2 * (kg >> 1) + half) : (kg >> 1);
+      const uint32_t *row = tab + (hl * NK + m) * D + 32 * w2 + 4 * (kg & 1);
       uint4 q4[4];
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) q4[jb] = *reinterpret_cast<const uint4 *>(row + 8 * jb);
@@ -478,7 +497,7 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
       out.z = gather(q4[0].z, q4[1].z, q4[2].z, q4[3].z);
       out.w = gather(q4[0].w, q4[1].w, q4[2].w, q4[3].w);
     }
-    *reinterpret_cast<uint4 *>(scratch + item * 16) = out;
+    *reinterpret_cast<uint4 *>(scratch + (grp * kWave + l) * 16) = out;
   }
   lds_barrier();
 }

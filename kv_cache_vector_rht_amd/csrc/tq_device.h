@@ -168,6 +168,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 
+// The other half-wave's copy of x (lane l <-> lane l ^ 32).
+__device__ __forceinline__ float swap_half_f(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((lane_id() < 32) ? r[1] : r[0]);
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int I>
 struct IntC {

@@ -136,13 +136,6 @@ __device__ __forceinline__ void decide_masks(float y, const DecLevels<W> &dl, co
   }
 }
 
-// The other half-wave's copy of x (lane l <-> lane l ^ 32).
-__device__ __forceinline__ float swap_half_f(float x) {
-  const uint32_t u = __float_as_uint(x);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float((lane_id() < 32) ? r[1] : r[0]);
-}
-
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 union Frag8 {
