@@ -185,6 +185,28 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
 size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t group,
                                   int64_t max_ctx, int32_t d);
 
+/*
+ * Row-wise top-k of a score matrix: the ranking step of inner-product search
+ * over a coded database (the pages name vector-search indexes as a target of
+ * the same codes and estimator: "メモリの壁を砕く圧縮革命、TurboQuant始動",
+ * sections TurboQuantの全体像 and 仕組みをほどく). With the database encoded
+ * as the keys of one KV head and up to 32 queries as its query heads,
+ * tq_logits followed by tq_topk is the search scan.
+ *   scores      device float [n_rows][ld], columns [0, n_cols) used
+ *   top_scores  device float [n_rows][k] out: the k largest scores of each
+ *               row, descending (ties: smaller column first)
+ *   top_idx     device int32 [n_rows][k] out: their columns
+ *   workspace   device, >= tq_topk_workspace(n_rows, n_cols, k) bytes,
+ *               8-byte aligned: per-chunk candidates, overwritten
+ * 0 <= k <= n_cols, k <= 1024, n_cols < 2^31; k == 0 or n_rows == 0 is a
+ * no-op. Data values are not inspected: a NaN with the sign bit clear ranks
+ * above +Inf, one with it set below -Inf; -0.0 ties with +0.0.
+ */
+tq_status tq_topk(const float *scores, int64_t n_rows, int64_t n_cols, int64_t ld, int32_t k,
+                  float *top_scores, int32_t *top_idx, void *workspace, size_t ws_bytes,
+                  void *stream);
+size_t tq_topk_workspace(int64_t n_rows, int64_t n_cols, int32_t k);
+
 /* Static description of a status code. */
 const char *tq_status_string(tq_status s);
 /* Message of the last failing call on this thread ("" if none). */

@@ -59,6 +59,8 @@ def _load():
         "tq_logits_workspace": ([I32, I32, I32, I32], SZ),
         "tq_decode_attend": ([CP, CP, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
         "tq_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
+        "tq_topk": ([P, I64, I64, I64, I32, P, P, P, SZ, P], I32),
+        "tq_topk_workspace": ([I64, I64, I32], SZ),
         "tq_status_string": ([I32], ctypes.c_char_p),
         "tq_last_error": ([], ctypes.c_char_p),
     }
@@ -89,7 +91,7 @@ def load():
 
 EXPORTED = ("tq_make_codebook", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
             "tq_logits", "tq_logits_workspace", "tq_decode_attend", "tq_decode_attend_workspace",
-            "tq_status_string", "tq_last_error")
+            "tq_topk", "tq_topk_workspace", "tq_status_string", "tq_last_error")
 
 
 def _check(status: int, what: str):
@@ -268,3 +270,44 @@ def decode_attend(kc: Codec, vc: Codec, q: torch.Tensor, kcodes, kscalars, vcode
                               workspace.numel(), _stream(stream))
     _check(st, "tq_decode_attend")
     return out
+
+
+def topk_workspace(n_rows: int, n_cols: int, k: int) -> int:
+    return int(lib.tq_topk_workspace(n_rows, n_cols, k))
+
+
+def topk(scores: torch.Tensor, k: int, n_cols: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+         stream=None):
+    """The k largest entries of each row of a float32 [n_rows, >= n_cols] matrix (rows may be padded:
+    stride(0) is the leading dimension): (values [n_rows, k] descending, columns int32 [n_rows, k]);
+    ties go to the smaller column."""
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be a float32 [n_rows, n] matrix with unit column stride")
+    n_rows = scores.shape[0]
+    if n_cols is None:
+        n_cols = scores.shape[1]
+    vals = torch.empty((n_rows, k), dtype=torch.float32, device=scores.device)
+    idx = torch.empty((n_rows, k), dtype=torch.int32, device=scores.device)
+    need = topk_workspace(n_rows, n_cols, k)
+    if workspace is None:
+        workspace = _workspace(need, scores.device)
+    st = lib.tq_topk(_ptr(scores), n_rows, n_cols, scores.stride(0), k, _ptr(vals), _ptr(idx), _ptr(workspace),
+                     workspace.numel(), _stream(stream))
+    _check(st, "tq_topk")
+    return vals, idx
+
+
+def search(codec: Codec, q: torch.Tensor, codes: torch.Tensor, scalars: torch.Tensor, n_db: int, k: int,
+           scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Inner-product search of up to 32 queries [n_q, d] over a coded database (the keys of one
+    sequence: codes/scalars of a key cache with one sequence, its first n_db slots): the
+    estimated scores by the logit scan, then their top k per query.
+    Returns (values [n_q, k], columns int32 [n_q, k])."""
+    if q.dim() != 2:
+        raise ValueError("q must be [n_q, d]")
+    n_q = q.shape[0]
+    if scores is None:
+        scores = torch.empty((1, n_q, n_db), dtype=torch.float32, device=q.device)
+    logits(codec, q.unsqueeze(0), codes, scalars, n_kv_heads=1, group=n_q, n_keys=n_db, out=scores, stream=stream)
+    return topk(scores.view(n_q, n_db), k, workspace=workspace, stream=stream)
+

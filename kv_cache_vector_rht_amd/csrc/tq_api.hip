@@ -236,6 +236,31 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
   return hip_status(e, fn);
 }
 
+size_t tq_topk_workspace(int64_t n_rows, int64_t n_cols, int32_t k) {
+  if (n_rows < 0 || n_cols < 0 || k < 0 || k > tq::kTopkMaxK) return 0;
+  const int64_t n_chunks = (n_cols + tq::kTopkChunk - 1) / tq::kTopkChunk;
+  return align_up(static_cast<size_t>(n_rows) * static_cast<size_t>(n_chunks) * static_cast<size_t>(k) * sizeof(uint64_t));
+}
+
+tq_status tq_topk(const float *scores, int64_t n_rows, int64_t n_cols, int64_t ld, int32_t k, float *top_scores,
+                  int32_t *top_idx, void *workspace, size_t ws_bytes, void *stream) {
+  const char *fn = "tq_topk";
+  if (n_rows < 0 || n_cols < 0 || k < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (ld < n_cols) return fail(TQ_EINVAL, "%s: ld=%lld < n_cols=%lld", fn, static_cast<long long>(ld),
+                               static_cast<long long>(n_cols));
+  if (k > n_cols) return fail(TQ_EINVAL, "%s: k=%d > n_cols=%lld", fn, k, static_cast<long long>(n_cols));
+  if (k > tq::kTopkMaxK) return fail(TQ_EUNSUPPORTED, "%s: k=%d > %d", fn, k, tq::kTopkMaxK);
+  if (n_cols > INT32_MAX) return fail(TQ_EUNSUPPORTED, "%s: n_cols above 2^31 - 1", fn);
+  if (n_rows == 0 || k == 0) return ok();
+  if (!scores || !top_scores || !top_idx || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  if (reinterpret_cast<uintptr_t>(workspace) % 8) return fail(TQ_EINVAL, "%s: workspace must be 8-byte aligned", fn);
+  const size_t need = tq_topk_workspace(n_rows, n_cols, k);
+  if (ws_bytes < need) return fail(TQ_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  hipError_t e = tq::launch_topk(scores, n_rows, n_cols, ld, k, top_scores, top_idx,
+                                 static_cast<uint64_t *>(workspace), static_cast<hipStream_t>(stream));
+  return hip_status(e, fn);
+}
+
 size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int64_t max_ctx, int32_t d) {
   if (batch < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
   const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, tq::kAttendSplit);

@@ -62,4 +62,10 @@ constexpr int kLogitSplit = 256;
 constexpr int kAttendSplit = 512;
 constexpr int kDecodeMaxBlocks = 128;
 
+// Row-wise top-k: columns per first-stage block, largest k.
+constexpr int kTopkChunk = 4096;
+constexpr int kTopkMaxK = 1024;
+hipError_t launch_topk(const float *scores, int64_t n_rows, int64_t n_cols, int64_t ld, int k, float *top_scores,
+                       int32_t *top_idx, uint64_t *cand, hipStream_t st);
+
 }  // namespace tq

@@ -62,6 +62,7 @@ __all__ = [
     "make_codebook", "hadamard", "rotate", "rotate_inverse",
     "encode", "pack_key_codes", "unpack_key_codes", "pack_value_codes",
     "unpack_value_codes", "prepare_query", "key_logits", "pair_logits", "decode_attend",
+    "top_k", "search",
     "QJL_CONST",
 ]
 
@@ -433,3 +434,36 @@ def decode_attend(q, k_signs, k_centroids, sketch, kidx, ksigma, knhat, kghat,
             acc = a @ vr                                       # [G, d] rotated domain
             out[b, hk * group:(hk + 1) * group] = rotate_inverse(acc, v_signs)
     return out
+
+
+# --------------------------------------------------------------------------
+# inner-product search over a coded database
+# --------------------------------------------------------------------------
+
+def top_k(scores, k: int):
+    """The k largest entries of every row of scores [n_rows, n], ranked by
+    score descending and, among equal scores, by column ascending (-0.0 and
+    +0.0 are equal). Returns (values [n_rows, k], columns [n_rows, k]).
+
+    The ranking step of inner-product search over a coded database: the
+    pages name vector-search indexes as a target of the same codes and
+    estimator, ranked by inner product ("メモリの壁を砕く圧縮革命、TurboQuant
+    始動", sections TurboQuantの全体像 and 仕組みをほどく)."""
+    s = np.asarray(scores)
+    n_rows, n = s.shape
+    cols = np.arange(n)
+    vals = np.empty((n_rows, k), dtype=s.dtype)
+    idx = np.empty((n_rows, k), dtype=np.int64)
+    for r in range(n_rows):
+        order = np.lexsort((cols, -s[r]))[:k]        # primary: -score, then column
+        idx[r] = order
+        vals[r] = s[r, order]
+    return vals, idx
+
+
+def search(q, signs, centroids, sketch, idx, sigma, nhat, ghat, k: int):
+    """Inner-product search of the query rows q [nq, d] over a database of
+    coded vectors (key records idx, sigma, nhat, ghat): the estimated inner
+    products (key_logits), then their top k per query (top_k)."""
+    return top_k(key_logits(q, signs, centroids, sketch, idx, sigma, nhat, ghat), k)
+

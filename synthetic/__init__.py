@@ -243,3 +243,45 @@ def gaussian_rows(n: int, d: int, cfg: int, stream: int, device="cpu", dtype=tor
     """n iid N(0, I_d) rows."""
     g = generator(cfg, stream, copy, device=device)
     return torch.randn((n, d), generator=g, dtype=torch.float32, device=device).to(dtype)
+
+
+# --------------------------------------------------------------------------
+# inner-product search over a coded database
+# --------------------------------------------------------------------------
+
+
+@dataclasses.dataclass(frozen=True)
+class SearchWorkload:
+    cfg: int
+    name: str
+    d: int
+    n_db: int            # database vectors (one coded sequence)
+    n_q: int             # queries per scan (<= 32: the query heads of one KV head)
+    k: int               # results per query
+    key_bits: int        # b: (b-1) Lloyd-Max bits + 1 QJL bit
+    in_dtype: torch.dtype
+
+    @property
+    def key_lm_bits(self) -> int:
+        return self.key_bits - 1
+
+
+SEARCH = SearchWorkload(6, "inner-product search: 32 queries over 1,048,576 coded vectors, d128, 4-bit codes, top 100",
+                        d=128, n_db=1 << 20, n_q=32, k=100, key_bits=4, in_dtype=torch.bfloat16)
+
+
+def search_database(w: SearchWorkload, device="cpu") -> torch.Tensor:
+    """Database rows [1, n_db, d]: N(0, 1) with per-channel lognormal(0, 1)
+    scales (the key recipe of the decode-layer workloads), in w.in_dtype."""
+    sc = channel_scales(w.cfg, 1, w.d, 0).to(device)            # [1, d]
+    out = torch.empty((1, w.n_db, w.d), dtype=w.in_dtype, device=device)
+
+    def scale_fn(r0, r1, x):
+        x.mul_(sc[None, :, :])
+    return _randn_into(out, generator(w.cfg, STREAM_K, device=device), scale_fn, chunk_elems=1 << 24)
+
+
+def search_queries(w: SearchWorkload, device="cpu") -> torch.Tensor:
+    """Queries [n_q, d] N(0, 1) in w.in_dtype."""
+    g = generator(w.cfg, STREAM_Q, device=device)
+    return torch.randn((w.n_q, w.d), generator=g, dtype=torch.float32, device=device).to(w.in_dtype)

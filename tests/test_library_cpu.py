@@ -164,6 +164,28 @@ def test_decode_validation():
     assert tq.decode_attend_workspace(4, 8, 8, 131072, 128) > 0
 
 
+def _topk(n_rows=4, n_cols=5000, ld=5000, k=10, ws=None, scores=FAKE, out=FAKE):
+    if ws is None:
+        ws = tq.topk_workspace(n_rows, n_cols, k)
+    return tq.lib.tq_topk(_p(scores), n_rows, n_cols, ld, k, _p(out), _p(out), _p(FAKE), ws, None)
+
+
+def test_topk_validation():
+    assert _topk(ld=4000) == tq.TQ_EINVAL                      # ld < n_cols
+    assert _topk(k=5001) == tq.TQ_EINVAL                       # k > n_cols
+    assert _topk(k=-1) == tq.TQ_EINVAL
+    assert _topk(n_rows=-1) == tq.TQ_EINVAL
+    assert _topk(k=1025, n_cols=5000) == tq.TQ_EUNSUPPORTED
+    assert _topk(n_cols=1 << 31, ld=1 << 31) == tq.TQ_EUNSUPPORTED
+    assert _topk(ws=8) == tq.TQ_EINVAL                         # workspace too small
+    assert _topk(scores=0) == tq.TQ_EINVAL
+    assert _topk(k=0) == tq.TQ_OK                              # no-ops launch nothing
+    assert _topk(n_rows=0) == tq.TQ_OK
+    # one 8-byte candidate per (row, 4096-column chunk, rank)
+    assert tq.topk_workspace(32, 1 << 20, 100) == 32 * 256 * 100 * 8
+    assert tq.topk_workspace(1, 4097, 10) >= 2 * 10 * 8
+
+
 def test_status_strings():
     for s in (tq.TQ_OK, tq.TQ_EINVAL, tq.TQ_EUNSUPPORTED, tq.TQ_EHIP):
         assert tq.lib.tq_status_string(s).decode().startswith("TQ_")

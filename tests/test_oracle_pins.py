@@ -583,3 +583,53 @@ def test_decode_attend_special_cases_and_textbook_softmax():
     for b in range(B):
         for h in range(Hkv * G):
             np.testing.assert_allclose(out_eq[b, h], Vhat[b * Hkv + h // G].mean(0), atol=1e-12)
+
+
+# ---------------------------------------------------------------- search
+
+
+def _brute_top_k(row, k):
+    """Plain Python ranking: score descending, column ascending on ties."""
+    order = sorted(range(len(row)), key=lambda i: (-float(row[i]), i))[:k]
+    return [float(row[i]) for i in order], order
+
+
+@pytest.mark.parametrize("k", [1, 3, 7, 16])
+def test_top_k_matches_brute_force_with_ties(k):
+    rng = np.random.default_rng(11)
+    s = rng.integers(-3, 4, size=(6, 16)).astype(np.float32)      # many ties
+    s[0, :] = 0.0
+    s[1, ::2] = -0.0                                               # -0.0 ties with +0.0
+    s[2, :] = np.float32(np.inf)
+    s[2, 5] = np.float32(-np.inf)
+    vals, idx = O.top_k(s, k)
+    for r in range(s.shape[0]):
+        bv, bi = _brute_top_k(s[r], k)
+        assert list(idx[r]) == bi
+        assert list(vals[r]) == bv
+
+
+def test_search_is_explicit_scores_ranked():
+    """search() on a small coded database: the explicit-matrix estimator
+    (R, S, centroids as matrices) ranked by brute force."""
+    d, w = 64, 3
+    rng, s, S, c, t = _toy_codec(d, w, 21)
+    db = rng.standard_normal((300, d))
+    q = rng.standard_normal((4, d))
+    enc = O.encode(db, s, c, t, S)
+    vals, idx = O.search(q, s, c, S, enc["idx"], enc["sigma"], enc["nhat"], enc["ghat"], 10)
+    R = scipy.linalg.hadamard(d) @ np.diag(s) / math.sqrt(d)
+    chat = c.astype(np.float64)[enc["idx"]]
+    pm = 2.0 * enc["sigma"] - 1.0
+    est = (enc["nhat"].astype(np.float64)[None, :] *
+           ((R @ q.T).T @ chat.T + math.sqrt(math.pi / 2) / d *
+            enc["ghat"].astype(np.float64)[None, :] * ((S.astype(np.float64) @ R @ q.T).T @ pm.T)))
+    for r in range(4):
+        bv, bi = _brute_top_k(est[r], 10)
+        assert list(idx[r]) == bi
+        np.testing.assert_allclose(vals[r], bv, rtol=1e-12)
+    # the estimator ranks the exact inner products well: the true best match
+    # of each query is among the estimated top 10
+    exact = q @ db.T
+    for r in range(4):
+        assert int(np.argmax(exact[r])) in set(idx[r].tolist())
