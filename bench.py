@@ -24,7 +24,8 @@ measured 4 GiB device copy), and carries the HBM bytes the counters saw
 committed profile summary while the kernel sources are unchanged. The extras time the
 fused decode attention on the batched (16 x 8192) and long-context
 (4 x 131072) decode workloads and the full-cache encode of the 22-layer
-TinyLlama-shaped prefill.
+TinyLlama-shaped prefill, and the search scan (32 queries over 1,048,576
+coded vectors, then the top 100 of each).
 """
 from __future__ import annotations
 
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of sections: main,dec3,dec5,enc4")
+    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,dec5,enc4,search")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each timed kernel a few times eagerly, after a 1 GiB calibration copy, "
                          "for hardware-counter runs; prints no JSON line")
@@ -314,6 +315,58 @@ def encode_full_cache(torch, tq, syn, steps):
     return out
 
 
+def search_workload(torch, tq, syn, copies, steps):
+    """Inner-product search: 32 queries scanned over 1,048,576 coded vectors
+    (the logit scan with the queries as the query heads of one KV head),
+    then the top 100 per query; `copies` independent databases and score
+    buffers rotated so that the working set exceeds the Infinity Cache."""
+    w = syn.SEARCH
+    dev = "cuda"
+    s, S = syn.key_codec_randoms(w.cfg, w.d)
+    kc = tq.Codec.make(w.d, w.key_lm_bits, True, s, S, device=dev)
+    log(f"[search] encoding {copies} database copies of {w.name}")
+    dbs = []
+    for c in range(copies):
+        codes, scal = tq.alloc_key_cache(1, w.n_db, kc)
+        x = syn.search_database(w, device=dev)
+        if c:
+            x = x[:, torch.randperm(w.n_db, device=dev)]       # another database of the same law
+        tq.encode_kv(kc, x, codes, scal)
+        del x
+        dbs.append((codes, scal))
+    q = syn.search_queries(w, device=dev)
+    scores = [torch.empty((1, w.n_q, w.n_db), dtype=torch.float32, device=dev) for _ in range(copies)]
+    ws = torch.empty(tq.topk_workspace(w.n_q, w.n_db, w.k), dtype=torch.uint8, device=dev)
+    vals = torch.empty((w.n_q, w.k), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.n_q, w.k), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def scan(c):
+        codes, scal = dbs[c]
+        return lambda: tq.logits(kc, q.unsqueeze(0), codes, scal, n_kv_heads=1, group=w.n_q, n_keys=w.n_db,
+                                 out=scores[c])
+
+    def rank(c):
+        return lambda: tq.lib.tq_topk(tq._ptr(scores[c]), w.n_q, w.n_db, w.n_db, w.k, tq._ptr(vals), tq._ptr(idx),
+                                      tq._ptr(ws), ws.numel(), tq._stream(None))
+
+    g_all = capture(torch, [f for c in range(copies) for f in (scan(c), rank(c))])
+    g_scan = capture(torch, [scan(c) for c in range(copies)])
+    g_rank = capture(torch, [rank(c) for c in range(copies)])
+    g_all.replay()
+    reps = max(1, steps // copies)
+    t_all = time_replays(torch, [g_all], reps) / copies
+    t_scan = time_replays(torch, [g_scan], reps) / copies
+    t_rank = time_replays(torch, [g_rank], reps) / copies
+    rec = kc.record_bytes + 4
+    b_scan = w.n_db * rec + w.n_q * w.n_db * 4          # coded database in, scores out
+    b_rank = w.n_q * w.n_db * 4                         # scores in (candidates are a few MB)
+    return dict(workload=w.name, search_avg_us=t_all * 1e6, scan_avg_us=t_scan * 1e6, topk_avg_us=t_rank * 1e6,
+                scores_per_s=w.n_q * w.n_db / t_all, queries_per_s=w.n_q / t_all,
+                scan_bytes_per_launch=b_scan, scan_hbm_frac=hbm(b_scan, t_scan),
+                topk_bytes_per_launch=b_rank, topk_hbm_frac=hbm(b_rank, t_rank), k=w.k, copies=copies)
+
+
 # ------------------------------------------------------------------ CPU baseline
 
 
@@ -442,6 +495,9 @@ def main():
         torch.cuda.empty_cache()
         if not only or "enc4" in only:
             extras["encode_full_cache"] = encode_full_cache(torch, tq, syn, steps=2)
+        torch.cuda.empty_cache()
+        if not only or "search" in only:
+            extras["search_scan"] = search_workload(torch, tq, syn, copies=4, steps=20)
         torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:

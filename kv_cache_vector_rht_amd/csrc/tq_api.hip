@@ -238,8 +238,9 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
 
 size_t tq_topk_workspace(int64_t n_rows, int64_t n_cols, int32_t k) {
   if (n_rows < 0 || n_cols < 0 || k < 0 || k > tq::kTopkMaxK) return 0;
-  const int64_t n_chunks = (n_cols + tq::kTopkChunk - 1) / tq::kTopkChunk;
-  return align_up(static_cast<size_t>(n_rows) * static_cast<size_t>(n_chunks) * static_cast<size_t>(k) * sizeof(uint64_t));
+  int64_t sa = 0, sb = 0;
+  tq::topk_buffers(n_cols, k, sa, sb);
+  return align_up(static_cast<size_t>(n_rows) * static_cast<size_t>(sa + sb) * sizeof(uint64_t));
 }
 
 tq_status tq_topk(const float *scores, int64_t n_rows, int64_t n_cols, int64_t ld, int32_t k, float *top_scores,

@@ -65,6 +65,7 @@ constexpr int kDecodeMaxBlocks = 128;
 // Row-wise top-k: columns per first-stage block, largest k.
 constexpr int kTopkChunk = 4096;
 constexpr int kTopkMaxK = 1024;
+void topk_buffers(int64_t n_cols, int k, int64_t &stride_a, int64_t &stride_b);   // pairs per row
 hipError_t launch_topk(const float *scores, int64_t n_rows, int64_t n_cols, int64_t ld, int k, float *top_scores,
                        int32_t *top_idx, uint64_t *cand, hipStream_t st);
 

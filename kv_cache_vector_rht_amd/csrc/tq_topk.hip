@@ -4,13 +4,15 @@
 // 革命、TurboQuant始動", sections TurboQuantの全体像 and 仕組みをほどく); the
 // scores come from the logit scan over the coded vectors.
 //
-// Two launches per call:
+// Select passes, then a sort:
 //  1. one block per (row, 4096-column chunk): the chunk's k largest scores
 //     by radix selection on order-preserving 32-bit keys, written to the
 //     workspace in column order (at most k per chunk);
-//  2. one block per row: the same selection over the row's candidates, then
-//     a bitonic sort of the k winners (score descending, column ascending on
-//     ties) and the store.
+//  2. while a row has more than 4096 candidates, the same selection over
+//     chunks of 4096 candidates (each pass shrinks them at least 4-fold);
+//  3. one block per row: the k largest of the last <= 4096 candidates,
+//     sorted (score descending, column ascending on ties) by a bitonic sort,
+//     stored.
 // Ties at the k-th score go to the smaller column in both stages, so the
 // result is the first k entries of the row in (score desc, column asc)
 // order. A NaN score ranks above +Inf; -0.0 ranks as +0.0.
@@ -25,6 +27,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPer = kTopkChunk / kThreads;   // chunk columns per thread
 constexpr int kCopies = 16;                   // histogram copies (lane % 16)
+static_assert(kThreads == 256, "one thread per digit");
 
 // Larger float -> larger key (sign-magnitude to offset binary).
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -55,8 +58,14 @@ __device__ __forceinline__ int block_incl_scan(int v, int *sh) {
   return v + before;
 }
 
+// Digit histogram in kCopies copies (copy = lane % kCopies), digit-major
+// with an odd row pitch: lanes adding to one digit hit distinct banks, and a
+// thread summing one digit's copies reads a bank pattern free of conflicts.
+constexpr int kPitch = kCopies + 1;
+
 struct SelectShared {
-  int hist[256 * kCopies];   // [digit][copy]
+  int hist[256 * kPitch];
+  int4 tot[64];              // per-digit totals, digits 4i .. 4i+3
   int sh[8];
 };
 
@@ -69,25 +78,26 @@ __device__ __forceinline__ void radix_select(Each each, int k, SelectShared &s, 
   uint32_t prefix = 0, mask = 0;
   need = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256 * kCopies; i += kThreads) s.hist[i] = 0;
+    for (int i = threadIdx.x; i < 256 * kPitch; i += kThreads) s.hist[i] = 0;
     __syncthreads();
     const int copy = lane % kCopies;
     each([&](uint32_t u) {
-      if ((u & mask) == prefix) atomicAdd(&s.hist[((u >> shift) & 255u) * kCopies + copy], 1);
+      if ((u & mask) == prefix) atomicAdd(&s.hist[((u >> shift) & 255u) * kPitch + copy], 1);
     });
+    __syncthreads();
+    {
+      const int dg = threadIdx.x;             // kThreads == 256 digits
+      int t = 0;
+#pragma unroll
+      for (int cp = 0; cp < kCopies; ++cp) t += s.hist[dg * kPitch + cp];
+      reinterpret_cast<int *>(s.tot)[dg] = t;
+    }
     __syncthreads();
     if (threadIdx.x < 64) {
       // lane l: digits 255 - 4l .. 252 - 4l, from the top
-      int c[4], sum = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int dg = 255 - 4 * lane - j;
-        int t = 0;
-#pragma unroll
-        for (int cp = 0; cp < kCopies; ++cp) t += s.hist[dg * kCopies + cp];
-        c[j] = t;
-        sum += t;
-      }
+      const int4 q = s.tot[63 - lane];
+      const int c[4] = {q.w, q.z, q.y, q.x};
+      const int sum = c[0] + c[1] + c[2] + c[3];
       const int incl = wave_incl_scan(sum, lane);
       const int excl = incl - sum;
       if (excl < need && need <= incl) {
@@ -131,19 +141,45 @@ __device__ __forceinline__ void compact(Each each, uint32_t T, int need, SelectS
   });
 }
 
-__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(const float *__restrict__ scores, int64_t ld,
-                                                              int64_t n_cols, int k, int64_t row0, int64_t n_chunks,
-                                                              uint64_t *__restrict__ cand) {
+// One block per (row, chunk of kTopkChunk items): the chunk's min(k, len)
+// largest items, written in column order at out + row * out_stride +
+// chunk * k. FROM_SCORES: the items are the row's scores (column = position);
+// else (key, column) pairs from an earlier pass, in column order.
+template <bool FROM_SCORES>
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(const void *__restrict__ in, int64_t in_stride,
+                                                               int64_t m, int k, int64_t row0,
+                                                               uint64_t *__restrict__ out, int64_t out_stride,
+                                                               bool vec4) {
   __shared__ SelectShared s;
   const int64_t row = row0 + blockIdx.y;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTopkChunk;
-  const int len = static_cast<int>((n_cols - c0 < kTopkChunk) ? n_cols - c0 : kTopkChunk);
-  const float *src = scores + row * ld + c0;
+  const int len = static_cast<int>((m - c0 < kTopkChunk) ? m - c0 : kTopkChunk);
   const int lo = threadIdx.x * kPer;
   const int cnt = min(max(len - lo, 0), kPer);
-  uint32_t u[kPer];
+  uint32_t u[kPer], col[kPer];
+  if constexpr (FROM_SCORES) {
+    const float *src = static_cast<const float *>(in) + row * in_stride + c0 + lo;
+    if (vec4 && cnt == kPer) {
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) u[j] = (j < cnt) ? order_key(src[lo + j]) : 0u;
+      for (int j = 0; j < kPer; j += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(src + j);
+        u[j] = order_key(v.x); u[j + 1] = order_key(v.y); u[j + 2] = order_key(v.z); u[j + 3] = order_key(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) u[j] = (j < cnt) ? order_key(src[j]) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) col[j] = static_cast<uint32_t>(c0 + lo + j);
+  } else {
+    const uint64_t *src = static_cast<const uint64_t *>(in) + row * in_stride + c0 + lo;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint64_t v = (j < cnt) ? src[j] : 0ull;
+      u[j] = static_cast<uint32_t>(v >> 32);
+      col[j] = static_cast<uint32_t>(v);
+    }
+  }
   const int kc = min(k, len);
   uint32_t T;
   int need;
@@ -152,34 +188,43 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(const float *__res
     for (int j = 0; j < kPer; ++j)
       if (j < cnt) f(u[j]);
   }, kc, s, T, need);
-  uint64_t *out = cand + (row * n_chunks + blockIdx.x) * k;
+  uint64_t *dst = out + row * out_stride + static_cast<int64_t>(blockIdx.x) * k;
   compact([&](auto f) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      if (j < cnt) f(u[j], static_cast<uint32_t>(c0 + lo + j));
-  }, T, need, s, [&](int pos, uint32_t key, uint32_t col) {
-    out[pos] = (static_cast<uint64_t>(key) << 32) | col;
+      if (j < cnt) f(u[j], col[j]);
+  }, T, need, s, [&](int pos, uint32_t key, uint32_t c) {
+    dst[pos] = (static_cast<uint64_t>(key) << 32) | c;
   });
 }
 
-__global__ __launch_bounds__(kThreads) void topk_final_kernel(const float *__restrict__ scores, int64_t ld,
-                                                              int64_t n_cols, int k, int64_t row0, int64_t n_chunks,
-                                                              const uint64_t *__restrict__ cand,
-                                                              float *__restrict__ top_scores,
-                                                              int32_t *__restrict__ top_idx) {
+// One block per row: the k largest of the row's last m <= kTopkChunk
+// candidates (column order), sorted (key descending, column ascending) by a
+// bitonic sort in LDS, stored with their original scores.
+__global__ __launch_bounds__(kThreads) void topk_sort_kernel(const float *__restrict__ scores, int64_t ld,
+                                                             const uint64_t *__restrict__ cand, int64_t cand_stride,
+                                                             int m, int k, int64_t row0,
+                                                             float *__restrict__ top_scores,
+                                                             int32_t *__restrict__ top_idx) {
   __shared__ SelectShared s;
   __shared__ uint64_t srt[kTopkMaxK];
   const int64_t row = row0 + blockIdx.x;
-  const int64_t last = n_cols - (n_chunks - 1) * kTopkChunk;
-  const int64_t m = (n_chunks - 1) * k + ((last < k) ? last : k);   // the row's candidates, in column order
-  const uint64_t *c = cand + row * n_chunks * k;
-  const int64_t per = (m + kThreads - 1) / kThreads;
-  const int64_t lo = threadIdx.x * per;
-  const int64_t hi = (lo + per < m) ? lo + per : m;
+  const uint64_t *c = cand + row * cand_stride;
+  const int lo = threadIdx.x * kPer;
+  const int cnt = min(max(m - lo, 0), kPer);
+  uint32_t u[kPer], col[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint64_t v = (j < cnt) ? c[lo + j] : 0ull;
+    u[j] = static_cast<uint32_t>(v >> 32);
+    col[j] = static_cast<uint32_t>(v);
+  }
   uint32_t T;
   int need;
   radix_select([&](auto f) {
-    for (int64_t i = lo; i < hi; ++i) f(static_cast<uint32_t>(c[i] >> 32));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (j < cnt) f(u[j]);
   }, k, s, T, need);
   // winners -> (key, ~column) composites; padding 0 sorts below every winner
   int P = 1;
@@ -187,12 +232,13 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const float *__res
   for (int i = threadIdx.x; i < P; i += kThreads) srt[i] = 0;
   __syncthreads();
   compact([&](auto f) {
-    for (int64_t i = lo; i < hi; ++i) f(static_cast<uint32_t>(c[i] >> 32), static_cast<uint32_t>(c[i]));
-  }, T, need, s, [&](int pos, uint32_t key, uint32_t col) {
-    srt[pos] = (static_cast<uint64_t>(key) << 32) | (0xffffffffu - col);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (j < cnt) f(u[j], col[j]);
+  }, T, need, s, [&](int pos, uint32_t key, uint32_t cl) {
+    srt[pos] = (static_cast<uint64_t>(key) << 32) | (0xffffffffu - cl);
   });
   __syncthreads();
-  // bitonic sort, descending
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int t = threadIdx.x; t < P / 2; t += kThreads) {
@@ -206,25 +252,55 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const float *__res
     }
   }
   for (int r = threadIdx.x; r < k; r += kThreads) {
-    const uint32_t col = 0xffffffffu - static_cast<uint32_t>(srt[r]);
-    top_idx[row * k + r] = static_cast<int32_t>(col);
-    top_scores[row * k + r] = scores[row * ld + col];
+    const uint32_t cl = 0xffffffffu - static_cast<uint32_t>(srt[r]);
+    top_idx[row * k + r] = static_cast<int32_t>(cl);
+    top_scores[row * k + r] = scores[row * ld + cl];
   }
+}
+
+int64_t chunks_of(int64_t m) { return (m + kTopkChunk - 1) / kTopkChunk; }
+
+// Candidates left after a select pass over m items per row.
+int64_t after_pass(int64_t m, int k) {
+  const int64_t n = chunks_of(m);
+  const int64_t last = m - (n - 1) * kTopkChunk;
+  return (n - 1) * k + ((last < k) ? last : k);
 }
 
 }  // namespace
 
+// The two candidate buffers (pairs per row): the first pass's output and the
+// second's; later passes alternate between them and only shrink.
+void topk_buffers(int64_t n_cols, int k, int64_t &stride_a, int64_t &stride_b) {
+  stride_a = chunks_of(n_cols) * k;
+  stride_b = chunks_of(stride_a) * k;
+}
+
 hipError_t launch_topk(const float *scores, int64_t n_rows, int64_t n_cols, int64_t ld, int k, float *top_scores,
                        int32_t *top_idx, uint64_t *cand, hipStream_t st) {
-  const int64_t n_chunks = (n_cols + kTopkChunk - 1) / kTopkChunk;
+  int64_t sa, sb;
+  topk_buffers(n_cols, k, sa, sb);
+  uint64_t *bufs[2] = {cand, cand + n_rows * sa};
+  const int64_t strides[2] = {sa, sb};
+  const bool vec4 = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
   for (int64_t r0 = 0; r0 < n_rows; r0 += 65535) {
-    const int64_t nr = (n_rows - r0 < 65535) ? n_rows - r0 : 65535;
-    hipLaunchKernelGGL(topk_chunk_kernel, dim3(static_cast<uint32_t>(n_chunks), static_cast<uint32_t>(nr)),
-                       dim3(kThreads), 0, st, scores, ld, n_cols, k, r0, n_chunks, cand);
+    const uint32_t nr = static_cast<uint32_t>((n_rows - r0 < 65535) ? n_rows - r0 : 65535);
+    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(static_cast<uint32_t>(chunks_of(n_cols)), nr), dim3(kThreads),
+                       0, st, scores, ld, n_cols, k, r0, bufs[0], strides[0], vec4);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_final_kernel, dim3(static_cast<uint32_t>(nr)), dim3(kThreads), 0, st, scores, ld,
-                       n_cols, k, r0, n_chunks, cand, top_scores, top_idx);
+    int64_t m = after_pass(n_cols, k);
+    int cur = 0;
+    while (m > kTopkChunk) {
+      hipLaunchKernelGGL(topk_select_kernel<false>, dim3(static_cast<uint32_t>(chunks_of(m)), nr), dim3(kThreads),
+                         0, st, bufs[cur], strides[cur], m, k, r0, bufs[cur ^ 1], strides[cur ^ 1], false);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      m = after_pass(m, k);
+      cur ^= 1;
+    }
+    hipLaunchKernelGGL(topk_sort_kernel, dim3(nr), dim3(kThreads), 0, st, scores, ld, bufs[cur], strides[cur],
+                       static_cast<int>(m), k, r0, top_scores, top_idx);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
