@@ -181,9 +181,9 @@ def test_topk_validation():
     assert _topk(scores=0) == tq.TQ_EINVAL
     assert _topk(k=0) == tq.TQ_OK                              # no-ops launch nothing
     assert _topk(n_rows=0) == tq.TQ_OK
-    # one 8-byte candidate per (row, 4096-column chunk, rank)
-    assert tq.topk_workspace(32, 1 << 20, 100) == 32 * 256 * 100 * 8
-    assert tq.topk_workspace(1, 4097, 10) >= 2 * 10 * 8
+    # 8-byte candidates: k per 4096-column chunk, then k per 4096 candidates
+    assert tq.topk_workspace(32, 1 << 20, 100) == 32 * (256 * 100 + 7 * 100) * 8
+    assert tq.topk_workspace(1, 4097, 10) >= (2 * 10 + 10) * 8
 
 
 def test_status_strings():
