@@ -24,8 +24,9 @@ measured 4 GiB device copy), and carries the HBM bytes the counters saw
 committed profile summary while the kernel sources are unchanged. The extras time the
 fused decode attention on the batched (16 x 8192) and long-context
 (4 x 131072) decode workloads and the full-cache encode of the 22-layer
-TinyLlama-shaped prefill, and the search scan (32 queries over 1,048,576
-coded vectors, then the top 100 of each).
+TinyLlama-shaped prefill, the search scan (32 queries over 1,048,576
+coded vectors, then the top 100 of each), and the MSE-only ablation of the
+logit scan (the estimator without its QJL term, against exact q.k).
 """
 from __future__ import annotations
 
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,dec5,enc4,search")
+    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,dec5,enc4,search,ablation")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each timed kernel a few times eagerly, after a 1 GiB calibration copy, "
                          "for hardware-counter runs; prints no JSON line")
@@ -367,6 +368,41 @@ def search_workload(torch, tq, syn, copies, steps):
                 topk_bytes_per_launch=b_rank, topk_hbm_frac=hbm(b_rank, t_rank), k=w.k, copies=copies)
 
 
+def mse_keys_ablation(torch, tq, syn, steps):
+    """The MSE-only ablation on the decode-layer workload (8 KV / 32 Q heads,
+    32768 keys, 4-bit keys): the logit scan with and without the QJL term on
+    the same records (times), and both estimates against the exact q.k of
+    the unquantized keys: least-squares slope (the shrinkage the QJL bit
+    removes) and RMS error relative to the exact logits' RMS."""
+    w = syn.WORKLOADS[2]
+    dev = "cuda"
+    kc, _, _ = setup_codecs(torch, tq, syn, w, dev)
+    x = syn.keys(w, device=dev)
+    q = syn.queries(w, device=dev)
+    codes, scal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+    tq.encode_kv(kc, x, codes, scal)
+    full = torch.empty((w.batch, w.n_q, w.n_tok), dtype=torch.float32, device=dev)
+    mse = torch.empty_like(full)
+    f_full = lambda: tq.logits(kc, q, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok, out=full)
+    f_mse = lambda: tq.logits(kc, q, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok, out=mse,
+                              mse_only=True)
+    # 8 back-to-back calls per graph (no launch gaps between them)
+    t_full = time_replays(torch, [capture(torch, [f_full] * 8)], steps) / 8
+    t_mse = time_replays(torch, [capture(torch, [f_mse] * 8)], steps) / 8
+    # exact logits: query head h against the keys of KV head h // group
+    qf = q[0].float().view(w.n_kv, w.group, w.d)
+    exact = torch.bmm(qf, x.float().transpose(1, 2).contiguous()).view(1, w.n_q, w.n_tok)
+    ex = exact.double()
+    out = dict(workload=w.name, logits_us=t_full * 1e6, logits_mse_us=t_mse * 1e6,
+               record_bytes=kc.record_bytes + 4, mse_only_record_bytes=w.key_lm_bits * w.d // 8 + 2)
+    for name, est in (("full", full), ("mse_only", mse)):
+        e = est.double()
+        out[f"slope_{name}"] = float((e * ex).sum() / (ex * ex).sum())
+        out[f"rel_rms_err_{name}"] = float(((e - ex) ** 2).mean().sqrt() / (ex ** 2).mean().sqrt())
+    del x
+    return out
+
+
 # ------------------------------------------------------------------ CPU baseline
 
 
@@ -498,6 +534,9 @@ def main():
         torch.cuda.empty_cache()
         if not only or "search" in only:
             extras["search_scan"] = search_workload(torch, tq, syn, copies=4, steps=20)
+        torch.cuda.empty_cache()
+        if not only or "ablation" in only:
+            extras["mse_keys_ablation"] = mse_keys_ablation(torch, tq, syn, steps=20)
         torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:

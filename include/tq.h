@@ -158,6 +158,20 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
 size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d);
 
 /*
+ * The MSE-only ablation of tq_logits: the estimator's first term alone,
+ *   logit = n * sum_i q'_i c[idx_i],
+ * from the same key records (their sign plane and residual norm are read
+ * and left out). It is the biased estimate that the QJL bit corrects: the
+ * MSE-optimal codebook shrinks inner products by about the per-coordinate
+ * distortion ("TurboQuantとは？…", 第2段: the 1-bit residual removes the
+ * inner-product bias). Arguments and errors as tq_logits.
+ */
+tq_status tq_logits_mse(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch,
+                        int32_t n_kv_heads, int32_t group, const uint8_t *kcodes,
+                        const uint16_t *kscalars, int64_t cap, int64_t n_keys, float *logits,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Fused decode attention over the coded cache: logits as tq_logits, exact
  * softmax of sm_scale*logit over tokens t < ctx_lens[b], and the weighted sum
  * of the decoded values n_t R_v^T c_v[idx_t] (accumulated in the rotated

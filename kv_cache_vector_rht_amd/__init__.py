@@ -57,6 +57,7 @@ def _load():
         "tq_encode_kv": ([CP, P, I32, I64, I64, I64, I64, P, P, I64, I64, P], I32),
         "tq_logits": ([CP, P, I32, I32, I32, I32, P, P, I64, I64, P, P, SZ, P], I32),
         "tq_logits_workspace": ([I32, I32, I32, I32], SZ),
+        "tq_logits_mse": ([CP, P, I32, I32, I32, I32, P, P, I64, I64, P, P, SZ, P], I32),
         "tq_decode_attend": ([CP, CP, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
         "tq_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
         "tq_topk": ([P, I64, I64, I64, I32, P, P, P, SZ, P], I32),
@@ -90,7 +91,7 @@ def load():
     return lib.tq_status_string
 
 EXPORTED = ("tq_make_codebook", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
-            "tq_logits", "tq_logits_workspace", "tq_decode_attend", "tq_decode_attend_workspace",
+            "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_decode_attend", "tq_decode_attend_workspace",
             "tq_topk", "tq_topk_workspace", "tq_status_string", "tq_last_error")
 
 
@@ -220,8 +221,9 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 def logits(codec: Codec, q: torch.Tensor, codes: torch.Tensor, scalars: torch.Tensor, n_kv_heads: int,
            group: int, n_keys: int, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-           stream=None) -> torch.Tensor:
-    """Estimated q.k logits, float32 [batch, n_kv_heads*group, n_keys]. q: [batch, n_q, d]."""
+           stream=None, mse_only: bool = False) -> torch.Tensor:
+    """Estimated q.k logits, float32 [batch, n_kv_heads*group, n_keys]. q: [batch, n_q, d].
+    mse_only: the estimator's first term alone (tq_logits_mse, the ablation without the QJL bit)."""
     q = q.contiguous()
     batch = q.shape[0]
     n_q = n_kv_heads * group
@@ -234,9 +236,10 @@ def logits(codec: Codec, q: torch.Tensor, codes: torch.Tensor, scalars: torch.Te
     if workspace is None:
         workspace = _workspace(need, q.device)
     cs = codec.struct()
-    st = lib.tq_logits(ctypes.byref(cs), _ptr(q), _DTYPE[q.dtype], batch, n_kv_heads, group, _ptr(codes),
-                       _ptr(scalars), cap, n_keys, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(st, "tq_logits")
+    fn = lib.tq_logits_mse if mse_only else lib.tq_logits
+    st = fn(ctypes.byref(cs), _ptr(q), _DTYPE[q.dtype], batch, n_kv_heads, group, _ptr(codes),
+            _ptr(scalars), cap, n_keys, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "tq_logits_mse" if mse_only else "tq_logits")
     return out
 
 

@@ -109,6 +109,7 @@ tq::ScanParams scan_params(const tq_codec *kc, const void *q, tq_dtype qt, int32
   sp.n_hchunks = (group + 7) / 8;
   sp.nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, split);
   sp.sm_scale = 1.0f;
+  sp.qjl = 1;
   return sp;
 }
 
@@ -210,10 +211,10 @@ size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int
   return 0;   // the scan prepares the queries in LDS
 }
 
-tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
-                    int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap, int64_t n_keys,
-                    float *logits, void *workspace, size_t ws_bytes, void *stream) {
-  const char *fn = "tq_logits";
+static tq_status logits_call(const char *fn, int qjl, const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch,
+                             int32_t n_kv_heads, int32_t group, const uint8_t *kcodes, const uint16_t *kscalars,
+                             int64_t cap, int64_t n_keys, float *logits, void *workspace, size_t ws_bytes,
+                             void *stream) {
   (void)workspace; (void)ws_bytes;
   tq_status s = check_codec(kc, 1, fn);
   if (s != TQ_OK) return s;
@@ -232,8 +233,23 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
   hipStream_t st = static_cast<hipStream_t>(stream);
   tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys, tq::kLogitSplit);
   sp.logits = logits;
+  sp.qjl = qjl;
   hipError_t e = kc->d == 64 ? tq::launch_logits_d<64>(sp, kc->lm_bits, st) : tq::launch_logits_d<128>(sp, kc->lm_bits, st);
   return hip_status(e, fn);
+}
+
+tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
+                    int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap, int64_t n_keys,
+                    float *logits, void *workspace, size_t ws_bytes, void *stream) {
+  return logits_call("tq_logits", 1, kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys, logits,
+                     workspace, ws_bytes, stream);
+}
+
+tq_status tq_logits_mse(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
+                        int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap, int64_t n_keys,
+                        float *logits, void *workspace, size_t ws_bytes, void *stream) {
+  return logits_call("tq_logits_mse", 0, kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys,
+                     logits, workspace, ws_bytes, stream);
 }
 
 size_t tq_topk_workspace(int64_t n_rows, int64_t n_cols, int32_t k) {

@@ -607,7 +607,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   const int col = lane % 16;
   uint32_t mask[4];
   lane_masks(mask);
-  const float kappa = kSqrtHalfPi / static_cast<float>(D);
+  const float kappa = p.qjl ? kSqrtHalfPi / static_cast<float>(D) : 0.f;
   const float cvmax = LOGITS ? 0.f : p.vcent[(1 << VW) - 1];
   if (!LOGITS && tid < NBV) svb[tid] = basis_coeff(p.vcent, VW, basis_mask(VW, tid));
 

@@ -45,6 +45,7 @@ struct ScanParams {
   int32_t n_hchunks;                    // ceil(group / 8)
   int32_t nb;                           // blocks per (batch, kv-head) group
   float sm_scale;
+  int32_t qjl;                          // 1: full estimator; 0 (logit scan only): its first (MSE) term
   float *partials;                      // decode: [batch*n_kv][nb][group][D+2]
   void *out;                            // decode: [batch][n_kv*group][D]
   int out_t;

@@ -61,7 +61,7 @@ __all__ = [
     "sphere_coord_density", "coord_cdf", "interval_mass", "interval_moment",
     "make_codebook", "hadamard", "rotate", "rotate_inverse",
     "encode", "pack_key_codes", "unpack_key_codes", "pack_value_codes",
-    "unpack_value_codes", "prepare_query", "key_logits", "pair_logits", "decode_attend",
+    "unpack_value_codes", "prepare_query", "key_logits", "key_logits_mse", "pair_logits", "decode_attend",
     "top_k", "search",
     "QJL_CONST",
 ]
@@ -379,6 +379,17 @@ def key_logits(q, signs, centroids, sketch, idx, sigma, nhat, ghat):
     n = np.asarray(nhat, dtype=np.float16).astype(np.float64)
     g = np.asarray(ghat, dtype=np.float16).astype(np.float64)
     return n[None, :] * (lm + (QJL_CONST / d) * g[None, :] * qjl)
+
+
+def key_logits_mse(q, signs, centroids, idx, nhat):
+    """The MSE-only estimate of <q, k>: the first term of key_logits alone,
+    n sum_i q'_i c[idx_i] with q' = R q -- the biased estimate that the QJL
+    bit corrects ("TurboQuantとは？仕組み・実測精度・2026年7月時点の実装状況",
+    第2段). q: [nq, d]; idx: [N, d]; nhat: [N]. Returns fp64 [nq, N]."""
+    qr = rotate(np.asarray(q, dtype=np.float64), signs)
+    c = np.asarray(centroids, dtype=np.float32).astype(np.float64)
+    n = np.asarray(nhat, dtype=np.float16).astype(np.float64)
+    return n[None, :] * (qr @ c[np.asarray(idx)].T)
 
 
 def pair_logits(q, signs, centroids, sketch, idx, sigma, nhat, ghat):

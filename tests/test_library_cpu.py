@@ -136,6 +136,14 @@ def test_logits_validation():
     assert _logits(_codec(), batch=-1) == tq.TQ_EINVAL
     assert _logits(_codec(), n_keys=0) == tq.TQ_OK
     assert tq.logits_workspace(1, 8, 4, 128) == 0                           # queries are prepared in LDS
+    # the MSE-only ablation validates exactly like tq_logits
+    cs = _codec()
+    assert tq.lib.tq_logits_mse(ctypes.byref(cs), _p(), tq.TQ_BF16, 1, 8, 33, _p(), _p(), 256, 64, _p(), None, 0,
+                                None) == tq.TQ_EUNSUPPORTED
+    assert tq.lib.tq_logits_mse(ctypes.byref(cs), _p(), tq.TQ_BF16, 1, 8, 4, _p(), _p(), 256, 512, _p(), None, 0,
+                                None) == tq.TQ_EINVAL
+    assert tq.lib.tq_logits_mse(ctypes.byref(cs), _p(), tq.TQ_BF16, 1, 8, 4, _p(), _p(), 256, 0, _p(), None, 0,
+                                None) == tq.TQ_OK
 
 
 def _decode(kc, vc, batch=2, n_kv=2, group=4, cap=256, max_ctx=256, scale=0.1, out_t=tq.TQ_F32, ws=None,

@@ -536,6 +536,22 @@ def test_zero_residual_drops_qjl_term():
     np.testing.assert_allclose(a, 2.0 * O.rotate(q, s) @ c.astype(np.float64)[idx].T, rtol=1e-13)
 
 
+def test_key_logits_mse_is_the_first_term():
+    """key_logits_mse against explicit matrices, and against key_logits with
+    the residual norms set to zero (which drops the QJL term)."""
+    d, w = 64, 3
+    rng, s, S, c, t = _toy_codec(d, w, 9)
+    k = rng.standard_normal((50, d))
+    q = rng.standard_normal((6, d))
+    enc = O.encode(k, s, c, t, S)
+    got = O.key_logits_mse(q, s, c, enc["idx"], enc["nhat"])
+    R = scipy.linalg.hadamard(d) @ np.diag(s) / math.sqrt(d)
+    explicit = enc["nhat"].astype(np.float64)[None, :] * ((R @ q.T).T @ c.astype(np.float64)[enc["idx"]].T)
+    np.testing.assert_allclose(got, explicit, rtol=1e-12, atol=1e-12)
+    zero_g = O.key_logits(q, s, c, S, enc["idx"], enc["sigma"], enc["nhat"], np.zeros(50, dtype=np.float16))
+    np.testing.assert_allclose(got, zero_g, rtol=1e-12, atol=1e-12)
+
+
 def _toy_cache(B, Hkv, T, d, kw, vw, seed):
     rng, s, S, c, t = _toy_codec(d, kw, seed)
     sv = rng.choice([-1.0, 1.0], size=d)
