@@ -105,6 +105,7 @@ KERNEL_SOURCES = {
                "tq_decode_d64.hip"],
 }
 KERNEL_SOURCES["decode"] = KERNEL_SOURCES["logits"]
+KERNEL_SOURCES["topk"] = ["tq_topk.hip", "tq_kernels.h"]
 
 
 def kernel_sources_digest(kernel):
@@ -457,7 +458,7 @@ def pmc_pass(torch, tq, syn):
     """Launches for hardware-counter runs: a 1 GiB device copy (the
     calibration kernel: 1 GiB read, 1 GiB written), each kernel of the
     headline step three times eagerly, then the decode-attention workloads
-    (one cache copy each)."""
+    (one cache copy each) and the search scan (one database)."""
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -482,7 +483,9 @@ def pmc_pass(torch, tq, syn):
     for cfg in (3, 5):
         decode_workload(torch, tq, syn, cfg, copies=1, steps=3)
         torch.cuda.empty_cache()
-    log("[pmc] done: copy 1 GiB x2, encode x3, logits x3, decode attention of workloads 3 and 5")
+    search_workload(torch, tq, syn, copies=1, steps=2)
+    torch.cuda.empty_cache()
+    log("[pmc] done: copy 1 GiB x2, encode x3, logits x3, decode attention of workloads 3 and 5, search scan")
 
 
 # ------------------------------------------------------------------ main
