@@ -46,6 +46,7 @@ def _scores(n_rows, n_cols, kind, seed, ld=None):
     (3, 333, 333, "ties", None),          # k = n_cols
     (2, 70001, 64, "specials", None),
     (3, 5000, 17, "normal", 5003),        # padded rows (ld > n_cols)
+    (2, 100000, 1024, "ties", None),      # three select passes (25600 -> 7168 -> 2048 candidates)
 ])
 def test_topk_matches_oracle_ranking(n_rows, n_cols, k, kind, ld):
     say(f"topk rows={n_rows} cols={n_cols} k={k} {kind} ld={ld}")
@@ -54,6 +55,16 @@ def test_topk_matches_oracle_ranking(n_rows, n_cols, k, kind, ld):
     vals, idx = tq.topk(dev, k, n_cols=n_cols)
     torch.cuda.synchronize()
     rv, ri = O.top_k(host[:, :n_cols].numpy(), k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_array_equal(vals.cpu().numpy(), rv)
+
+
+def test_topk_more_rows_than_one_launch_grid():
+    say("topk rows=70001 cols=64 k=5 (rows in launches of 65535)")
+    host = _scores(70001, 64, "ties", 3)
+    vals, idx = tq.topk(host.to("cuda"), 5)
+    torch.cuda.synchronize()
+    rv, ri = O.top_k(host.numpy(), 5)
     np.testing.assert_array_equal(idx.cpu().numpy(), ri)
     np.testing.assert_array_equal(vals.cpu().numpy(), rv)
 
