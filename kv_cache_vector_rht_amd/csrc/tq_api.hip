@@ -68,12 +68,13 @@ tq_status check_codec(const tq_codec *c, int need_key, const char *name) {
 
 // Scan blocks per (batch, kv-head) group: each block walks every blocks-th
 // split of `split` tokens. One block fills a CU's LDS, so aim for one block
-// per CU (256), at most kDecodeMaxBlocks per group and never more than the
-// context has splits.
-int decode_blocks_per_group(int32_t batch, int32_t n_kv, int64_t max_ctx, int split) {
+// per CU (256), at most max_blocks per group (decode: the merge's bound
+// kDecodeMaxBlocks) and never more than the context has splits.
+int decode_blocks_per_group(int32_t batch, int32_t n_kv, int64_t max_ctx, int split,
+                            int max_blocks = tq::kDecodeMaxBlocks) {
   const int64_t groups = std::max<int64_t>(1, static_cast<int64_t>(batch) * n_kv);
   const int64_t splits = std::max<int64_t>(1, (max_ctx + split - 1) / split);
-  const int64_t want = std::min<int64_t>(tq::kDecodeMaxBlocks, std::max<int64_t>(1, (256 + groups - 1) / groups));
+  const int64_t want = std::min<int64_t>(max_blocks, std::max<int64_t>(1, (256 + groups - 1) / groups));
   return static_cast<int>(std::min<int64_t>(splits, want));
 }
 
@@ -107,7 +108,9 @@ tq::ScanParams scan_params(const tq_codec *kc, const void *q, tq_dtype qt, int32
   sp.group = group;
   sp.h0 = 0;
   sp.n_hchunks = (group + 7) / 8;
-  sp.nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, split);
+  // the logit scan merges nothing, so one group may spread over every CU
+  sp.nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, split,
+                                  split == tq::kLogitSplit ? 256 : tq::kDecodeMaxBlocks);
   sp.sm_scale = 1.0f;
   sp.qjl = 1;
   return sp;
