@@ -324,9 +324,11 @@ __device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int 
 // digit operands of the key planes (2 beta_s q') and of the sign plane
 // (2 p), one fixed-point exponent per head for each, and the per-head
 // constants {2^-(7+e_lm), c[L-1] sum q', 2^-(7+e_qj), sum p}. Rows of absent
-// heads stay zero.
-template <int D, int KW, int NRG>
-__device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t *scratch) {
+// heads stay zero. after_rotation() runs once q' is in LDS (the caller issues
+// its first key loads there: issued earlier, their traffic slows the
+// preparation's own input loads and instruction fetch).
+template <int D, int KW, int NRG, class AfterRotation>
+__device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t *scratch, AfterRotation after_rotation) {
   using PS = PrepShape<D, KW, NRG>;
   constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64;
   constexpr int NW = D / 16;
@@ -374,6 +376,7 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
     if (lane == 0) { sst[4 * h] = mq; sst[4 * h + 1] = s1; }
   }
   lds_barrier();
+  after_rotation();
   // p = S q' on the matrix cores (v_mfma_f32_32x32x16_f16), one 32-row tile
   // of S per wave: A = 32 sketch rows x 16 columns (fp16, exact), B = 16
   // entries of q' for the columns = heads (lanes of absent heads zero), each
@@ -625,14 +628,15 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   v4i a[NRG][NMF];
   float4 fh[NRG];
   if (ns > 0) {
-    // the preparation's inputs, then the splits that do not overlap its
-    // scratch, are in flight together; wait for the inputs only
+    // the preparation's inputs first, alone; the splits that do not
+    // overlap its scratch are issued once the queries are rotated
     issue_prep<D, KW, NRG>(p, bh, GE, ring + PREP_AT, wave);
     const int first = SEP ? min(ns, NST) : 1;
-    for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
-    wait_splits<P>(first);
+    wait_vm<0>();
     lds_barrier();
-    group_prep<D, KW, NRG>(p, GE, ring + PREP_AT);
+    group_prep<D, KW, NRG>(p, GE, ring + PREP_AT, [&] {
+      for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+    });
     load_prepared<D, KW, NRG>(ring + PREP_AT, GE, a, fh);
     lds_barrier();                                 // every wave holds its operands
     for (int k = first; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
