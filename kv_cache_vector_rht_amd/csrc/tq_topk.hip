@@ -69,27 +69,34 @@ struct SelectShared {
   int sh[8];
 };
 
-// The k-th largest key T among the block's items and how many of the items
-// equal to T belong to the k largest (need). Every thread visits its items
-// with each(f), f(key); k <= number of items.
+// A key prefix T (the bits under M) that splits the block's items: every
+// item whose masked key exceeds T is among the k largest, and so are the
+// first `need` items whose masked key equals T. The digits are refined from
+// the top until that bucket is taken whole or the key is exhausted. Every
+// thread visits its items with each(f), f(key); k <= number of items.
 template <class Each>
-__device__ __forceinline__ void radix_select(Each each, int k, SelectShared &s, uint32_t &T, int &need) {
+__device__ __forceinline__ void radix_select(Each each, int k, SelectShared &s, uint32_t &T, uint32_t &M, int &need) {
   const int lane = threadIdx.x & 63;
   uint32_t prefix = 0, mask = 0;
   need = k;
+  for (int i = threadIdx.x; i < 256 * kPitch; i += kThreads) s.hist[i] = 0;
+  __syncthreads();
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256 * kPitch; i += kThreads) s.hist[i] = 0;
-    __syncthreads();
     const int copy = lane % kCopies;
     each([&](uint32_t u) {
       if ((u & mask) == prefix) atomicAdd(&s.hist[((u >> shift) & 255u) * kPitch + copy], 1);
     });
     __syncthreads();
     {
+      // one thread per digit: its total, and the copies cleared for the next
+      // round (two barriers pass before any thread adds to them again)
       const int dg = threadIdx.x;             // kThreads == 256 digits
       int t = 0;
 #pragma unroll
-      for (int cp = 0; cp < kCopies; ++cp) t += s.hist[dg * kPitch + cp];
+      for (int cp = 0; cp < kCopies; ++cp) {
+        t += s.hist[dg * kPitch + cp];
+        s.hist[dg * kPitch + cp] = 0;
+      }
       reinterpret_cast<int *>(s.tot)[dg] = t;
     }
     __syncthreads();
@@ -107,27 +114,30 @@ __device__ __forceinline__ void radix_select(Each each, int k, SelectShared &s, 
           if (acc + c[j] < need) { acc += c[j]; ++j; }
         s.sh[4] = 255 - 4 * lane - j;
         s.sh[5] = need - acc;
+        s.sh[6] = (need - acc == c[j]) ? 1 : 0;   // the whole bucket is taken
       }
     }
     __syncthreads();
+    // (wave 0 writes sh[4..6] again only after two more barriers)
     prefix |= static_cast<uint32_t>(s.sh[4]) << shift;
     mask |= 255u << shift;
     need = s.sh[5];
-    __syncthreads();
+    if (s.sh[6]) break;
   }
   T = prefix;
+  M = mask;
 }
 
-// Emit the k largest items in column order: every item above T and the
-// first `need` items equal to T. each(f) visits f(key, column) in column
+// Emit the k largest items in column order: every item whose masked key is
+// above T and the first `need` items whose masked key equals T. each(f) visits f(key, column) in column
 // order within the thread (threads hold consecutive column ranges);
 // emit(pos, key, column) with pos in [0, k).
 template <class Each, class Emit>
-__device__ __forceinline__ void compact(Each each, uint32_t T, int need, SelectShared &s, Emit emit) {
+__device__ __forceinline__ void compact(Each each, uint32_t T, uint32_t M, int need, SelectShared &s, Emit emit) {
   int gt = 0, eq = 0;
   each([&](uint32_t u, uint32_t) {
-    gt += (u > T) ? 1 : 0;
-    eq += (u == T) ? 1 : 0;
+    gt += ((u & M) > T) ? 1 : 0;
+    eq += ((u & M) == T) ? 1 : 0;
   });
   const int eq_before = block_incl_scan(eq, s.sh) - eq;
   const int take = min(max(need - eq_before, 0), eq);
@@ -135,8 +145,8 @@ __device__ __forceinline__ void compact(Each each, uint32_t T, int need, SelectS
   int pos = block_incl_scan(sel, s.sh) - sel;
   int seen = 0;
   each([&](uint32_t u, uint32_t col) {
-    bool keep = u > T;
-    if (u == T) keep = (seen++ < take);
+    bool keep = (u & M) > T;
+    if ((u & M) == T) keep = (seen++ < take);
     if (keep) emit(pos++, u, col);
   });
 }
@@ -181,19 +191,19 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const void *__res
     }
   }
   const int kc = min(k, len);
-  uint32_t T;
+  uint32_t T, M;
   int need;
   radix_select([&](auto f) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (j < cnt) f(u[j]);
-  }, kc, s, T, need);
+  }, kc, s, T, M, need);
   uint64_t *dst = out + row * out_stride + static_cast<int64_t>(blockIdx.x) * k;
   compact([&](auto f) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (j < cnt) f(u[j], col[j]);
-  }, T, need, s, [&](int pos, uint32_t key, uint32_t c) {
+  }, T, M, need, s, [&](int pos, uint32_t key, uint32_t c) {
     dst[pos] = (static_cast<uint64_t>(key) << 32) | c;
   });
 }
@@ -219,13 +229,13 @@ __global__ __launch_bounds__(kThreads) void topk_sort_kernel(const float *__rest
     u[j] = static_cast<uint32_t>(v >> 32);
     col[j] = static_cast<uint32_t>(v);
   }
-  uint32_t T;
+  uint32_t T, M;
   int need;
   radix_select([&](auto f) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (j < cnt) f(u[j]);
-  }, k, s, T, need);
+  }, k, s, T, M, need);
   // winners -> (key, ~column) composites; padding 0 sorts below every winner
   int P = 1;
   while (P < k) P <<= 1;
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void topk_sort_kernel(const float *__rest
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (j < cnt) f(u[j], col[j]);
-  }, T, need, s, [&](int pos, uint32_t key, uint32_t cl) {
+  }, T, M, need, s, [&](int pos, uint32_t key, uint32_t cl) {
     srt[pos] = (static_cast<uint64_t>(key) << 32) | (0xffffffffu - cl);
   });
   __syncthreads();
