@@ -151,3 +151,36 @@ def test_search_full_database_size():
     ref = O.key_logits(to_f64(q.cpu()), s.numpy().astype(np.float64), cent, S.numpy().astype(np.float16), kidx,
                        ksig, sc[:, 0], sc[:, 1])
     assert_close(got[:, cols], ref, "search scores (sampled)")
+
+
+def test_topk_in_hip_graph_replays():
+    """tq_topk captured in a HIP graph and replayed three times, the scores
+    rewritten eagerly between replays; every replay against the oracle."""
+    say("topk in a HIP graph: 3 replays over changing scores")
+    n_rows, n_cols, k = 4, 30000, 50
+    scores = torch.empty((n_rows, n_cols), dtype=torch.float32, device="cuda")
+    vals = torch.empty((n_rows, k), dtype=torch.float32, device="cuda")
+    idx = torch.empty((n_rows, k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(tq.topk_workspace(n_rows, n_cols, k), dtype=torch.uint8, device="cuda")
+    call = lambda: tq.lib.tq_topk(tq._ptr(scores), n_rows, n_cols, n_cols, k, tq._ptr(vals), tq._ptr(idx),
+                                  tq._ptr(ws), ws.numel(), tq._stream(None))
+    scores.copy_(_scores(n_rows, n_cols, "ties", 0).to("cuda"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert call() == tq.TQ_OK
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        assert call() == tq.TQ_OK
+    torch.cuda.synchronize()
+    for rep in range(3):
+        host = _scores(n_rows, n_cols, "ties" if rep % 2 else "normal", 10 + rep)
+        scores.copy_(host.to("cuda"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rv, ri = O.top_k(host.numpy(), k)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+        np.testing.assert_array_equal(vals.cpu().numpy(), rv)
