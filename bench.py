@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,dec5,enc4,search,ablation")
+    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,app3,dec5,enc4,search,ablation")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each timed kernel a few times eagerly, after a 1 GiB calibration copy, "
                          "for hardware-counter runs; prints no JSON line")
@@ -292,6 +292,63 @@ def decode_workload(torch, tq, syn, cfg, copies, steps):
                 hbm_frac=hbm(bytes_, avg), copies=copies)
 
 
+def append_step_workload(torch, tq, syn, cfg, copies, steps):
+    """A whole decoding step on workload 3: the new token's key and value
+    encoded into slot n_tok - 1 of every sequence and attention over all
+    n_tok tokens, as one fused call (tq_append_decode_attend) and as the
+    two-call path (tq_encode_kv of the new key and value, tq_decode_attend)."""
+    w = syn.WORKLOADS[cfg]
+    dev = "cuda"
+    kc, vc, _ = setup_codecs(torch, tq, syn, w, dev)
+    log(f"[app{cfg}] encoding {copies} cache copies of {w.name}")
+    caches, news = [], []
+    for c in range(copies):
+        kcodes, kscal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+        vcodes, vscal = tq.alloc_value_cache(w.n_seq, w.n_tok, vc)
+        x = syn.keys(w, device=dev, copy=c)
+        tq.encode_kv(kc, x, kcodes, kscal)
+        news.append([x[:, -1:].clone()])
+        del x
+        x = syn.values(w, device=dev, copy=c)
+        tq.encode_kv(vc, x, vcodes, vscal)
+        news[-1].append(x[:, -1:].clone())
+        del x
+        caches.append((kcodes, kscal, vcodes, vscal))
+    qs = [syn.queries(w, device=dev, copy=c) for c in range(copies)]
+    ctx = torch.full((w.batch,), w.n_tok, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.append_decode_attend_workspace(w.batch, w.n_kv, w.group, w.n_tok, w.d), dtype=torch.uint8,
+                     device=dev)
+    outs = [torch.empty((w.batch, w.n_q, w.d), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    def fused(c):
+        kcodes, kscal, vcodes, vscal = caches[c]
+        kn, vn = (t.view(w.batch, w.n_kv, w.d) for t in news[c])
+        return lambda: tq.append_decode_attend(kc, vc, qs[c], kn, vn, kcodes, kscal, vcodes, vscal, ctx,
+                                               n_kv_heads=w.n_kv, group=w.group, max_ctx=w.n_tok, out=outs[c],
+                                               workspace=ws, out_dtype=torch.bfloat16)
+
+    def two_calls(c):
+        kcodes, kscal, vcodes, vscal = caches[c]
+        kn, vn = news[c]
+
+        def run():
+            tq.encode_kv(kc, kn, kcodes, kscal, t0=w.n_tok - 1)
+            tq.encode_kv(vc, vn, vcodes, vscal, t0=w.n_tok - 1)
+            tq.decode_attend(kc, vc, qs[c], kcodes, kscal, vcodes, vscal, ctx, n_kv_heads=w.n_kv, group=w.group,
+                             max_ctx=w.n_tok, out=outs[c], workspace=ws, out_dtype=torch.bfloat16)
+        return run
+
+    res = {}
+    for name, mk in (("fused_us", fused), ("two_calls_us", two_calls)):
+        g = capture(torch, [mk(c) for c in range(copies)])
+        g.replay()
+        res[name] = time_replays(torch, [g], max(1, steps // copies)) / copies * 1e6
+    th = w.n_seq * w.n_tok
+    return dict(workload=w.name + ", new token appended each step", unit="token-heads", units_per_launch=th,
+                attended_logits_per_s=w.batch * w.n_q * w.n_tok / (res["fused_us"] * 1e-6), copies=copies, **res)
+
+
 def encode_full_cache(torch, tq, syn, steps):
     """Workload 4: encode every K and V vector of the 22-layer prefill."""
     w = syn.WORKLOADS[4]
@@ -528,6 +585,9 @@ def main():
     if not args.no_extras:
         if not only or "dec3" in only:
             extras["decode_attend_batched"] = decode_workload(torch, tq, syn, 3, copies=9, steps=20)
+        torch.cuda.empty_cache()
+        if not only or "app3" in only:
+            extras["append_decode_step"] = append_step_workload(torch, tq, syn, 3, copies=9, steps=20)
         torch.cuda.empty_cache()
         if not only or "dec5" in only:
             extras["decode_attend_long_context"] = decode_workload(torch, tq, syn, 5, copies=2, steps=10)

@@ -200,6 +200,40 @@ size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t gro
                                   int64_t max_ctx, int32_t d);
 
 /*
+ * One decoding step in one launch: the new token's key and value of every
+ * (batch, kv-head) sequence are encoded into the caches (as tq_encode_kv
+ * would, into slot ctx_lens[b] - 1) and the query heads attend over the
+ * whole context including that token (as tq_decode_attend). The pages count
+ * the encoding against decode-heavy serving, whose throughput sits at the
+ * low end of the measured range ("TurboQuantとは？…", section 「精度劣化ゼロ」
+ * の出所と、マージ後に判明した実測値; "TurboQuant と RotorQuant を DGX Spark
+ * で試してみた", section vLLM 本家 PR と llama.cpp の進捗): here the
+ * encoding runs beside the context scan instead of in a launch of its own.
+ *   k_new, v_new  device [batch][n_kv_heads][d], dtype kvt (TQ_F32 / TQ_BF16
+ *                 / TQ_F16): the new token's key and value rows
+ *   kcodes, kscalars, vcodes, vscalars  the caches (layouts above), written
+ *                 at slot ctx_lens[b] - 1 only (value words of that slot's
+ *                 32-token block change in the slot's bit only)
+ *   ctx_lens      device int32 [batch]: context lengths INCLUDING the new
+ *                 token, clamped to [0, max_ctx]; a row with 0 appends
+ *                 nothing and gets zeros
+ *   workspace     >= tq_append_decode_attend_workspace(...) bytes (one more
+ *                 partial per group than tq_decode_attend)
+ * The remaining arguments, the output and the errors are those of
+ * tq_decode_attend; in addition k_new/v_new NULL or a bad kvt is TQ_EINVAL.
+ * The new token's slot must not be read by other work in flight.
+ */
+tq_status tq_append_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt,
+                                  const void *k_new, const void *v_new, tq_dtype kvt,
+                                  int32_t batch, int32_t n_kv_heads, int32_t group,
+                                  uint8_t *kcodes, uint16_t *kscalars, uint32_t *vcodes,
+                                  uint16_t *vscalars, int64_t cap, const int32_t *ctx_lens,
+                                  int64_t max_ctx, float sm_scale, void *out, tq_dtype out_t,
+                                  void *workspace, size_t ws_bytes, void *stream);
+size_t tq_append_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t group,
+                                         int64_t max_ctx, int32_t d);
+
+/*
  * Row-wise top-k of a score matrix: the ranking step of inner-product search
  * over a coded database (the pages name vector-search indexes as a target of
  * the same codes and estimator: "メモリの壁を砕く圧縮革命、TurboQuant始動",

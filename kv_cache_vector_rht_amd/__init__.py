@@ -60,6 +60,9 @@ def _load():
         "tq_logits_mse": ([CP, P, I32, I32, I32, I32, P, P, I64, I64, P, P, SZ, P], I32),
         "tq_decode_attend": ([CP, CP, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
         "tq_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
+        "tq_append_decode_attend": ([CP, CP, P, I32, P, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P,
+                                     SZ, P], I32),
+        "tq_append_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
         "tq_topk": ([P, I64, I64, I64, I32, P, P, P, SZ, P], I32),
         "tq_topk_workspace": ([I64, I64, I32], SZ),
         "tq_status_string": ([I32], ctypes.c_char_p),
@@ -92,6 +95,7 @@ def load():
 
 EXPORTED = ("tq_make_codebook", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
             "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_decode_attend", "tq_decode_attend_workspace",
+            "tq_append_decode_attend", "tq_append_decode_attend_workspace",
             "tq_topk", "tq_topk_workspace", "tq_status_string", "tq_last_error")
 
 
@@ -272,6 +276,45 @@ def decode_attend(kc: Codec, vc: Codec, q: torch.Tensor, kcodes, kscalars, vcode
                               _ptr(ctx_lens), max_ctx, float(sm_scale), _ptr(out), ot, _ptr(workspace),
                               workspace.numel(), _stream(stream))
     _check(st, "tq_decode_attend")
+    return out
+
+
+def append_decode_attend_workspace(batch: int, n_kv_heads: int, group: int, max_ctx: int, d: int) -> int:
+    return int(lib.tq_append_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, d))
+
+
+def append_decode_attend(kc: Codec, vc: Codec, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, kcodes,
+                         kscalars, vcodes, vscalars, ctx_lens: torch.Tensor, n_kv_heads: int, group: int,
+                         max_ctx: Optional[int] = None, sm_scale: Optional[float] = None, out_dtype=torch.float32,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """One decoding step in one launch: k_new / v_new [batch, n_kv_heads, d] are encoded into slot
+    ctx_lens[b] - 1 of the caches (ctx_lens counts the new token) and the queries attend over the whole
+    context: [batch, n_q, d] in out_dtype."""
+    q = q.contiguous()
+    k_new, v_new = k_new.contiguous(), v_new.contiguous()
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same dtype")
+    batch = q.shape[0]
+    n_q = n_kv_heads * group
+    cap = kscalars.shape[1]
+    if max_ctx is None:
+        max_ctx = cap
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(kc.d)
+    if out is None:
+        out = torch.empty((batch, n_q, kc.d), dtype=out_dtype, device=q.device)
+    need = append_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, kc.d)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    ks, vs = kc.struct(), vc.struct()
+    ot = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[out.dtype]
+    st = lib.tq_append_decode_attend(ctypes.byref(ks), ctypes.byref(vs), _ptr(q), _DTYPE[q.dtype], _ptr(k_new),
+                                     _ptr(v_new), _DTYPE[k_new.dtype], batch, n_kv_heads, group, _ptr(kcodes),
+                                     _ptr(kscalars), _ptr(vcodes), _ptr(vscalars), cap, _ptr(ctx_lens), max_ctx,
+                                     float(sm_scale), _ptr(out), ot, _ptr(workspace), workspace.numel(),
+                                     _stream(stream))
+    _check(st, "tq_append_decode_attend")
     return out
 
 

@@ -20,7 +20,8 @@ OUT = os.path.join(HERE, "libtq.so")
 BUILD = os.path.join(HERE, "_build")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["tq_decode_d128.hip", "tq_encode_d128.hip", "tq_decode_d64.hip", "tq_encode_d64.hip",
+SOURCES = ["tq_decode_d128.hip", "tq_append_d128.hip", "tq_encode_d128.hip", "tq_decode_d64.hip",
+           "tq_append_d64.hip", "tq_encode_d64.hip",
            "tq_topk.hip", "tq_api.hip", "tq_codebook.cpp"]
 
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")

@@ -539,6 +539,282 @@ __device__ __forceinline__ void wait_splits(int n_after) {
   }
 }
 
+// ------------------------------------------------------------------ append
+
+// Element i of a row of dtype xt (0 f32, 1 bf16, 2 f16).
+__device__ __forceinline__ float load_elem(const void *base, int64_t i, int xt) {
+  if (xt == 0) return static_cast<const float *>(base)[i];
+  const uint16_t u = static_cast<const uint16_t *>(base)[i];
+  return xt == 1 ? bf16_bits_to_float(u) : f16_bits_to_float(u);
+}
+
+// Lloyd-Max decision of one rotated coordinate v against the thresholds
+// scaled by ||v|| (th, cent: the codebook in LDS): idx = #{j : v >= t_j ||v||}
+// and c = cent[idx].
+template <int W>
+__device__ __forceinline__ void decide_scaled(float v, float vn, const float *th, const float *cent, int &idx,
+                                              float &c) {
+  idx = 0;
+  c = cent[0];
+#pragma unroll
+  for (int j = 0; j < (1 << W) - 1; ++j) {
+    const bool up = v >= th[j] * vn;
+    idx += up ? 1 : 0;
+    c = up ? cent[j + 1] : c;
+  }
+}
+
+// The new token of group bh, encoded by the one extra block of an append
+// launch (4 D threads), which also contributes that token's softmax partial
+// for the heads [h0, h0 + GE): the cached context ends one slot earlier for
+// the scan blocks, so every head still attends over all ctx_lens[b] tokens.
+// Encoding as the encode kernels (store the norm, rotate, Lloyd-Max
+// decisions against the thresholds scaled by ||H diag(s) x||; keys: the
+// residual, its norm and the signs of its projection S r), written into slot
+// t = ctx_lens[b] - 1 of both caches; the value words of slot t's 32-token
+// block change in bit t % 32 only. The token's logit takes the same
+// estimator from the stored (fp16) norms, in floating point (the queries'
+// q' and p = S q' formed here as well); its partial is {m = sm_scale * logit,
+// l = 1, acc = n_v c_v[idx]} in the rotated value domain.
+// The block shares the CUs with the scan blocks, so it is written for
+// latency: every global load it needs is issued first.
+// Scratch (over the block's LDS ring): ROT [10][D] floats, the rotated rows
+// (q' of each head, the key's residual r, the value's rotation); PZ [9][D]
+// their projections (p of each head, z = S r); CK [D] the key's c[idx]; VH
+// [D] the decoded value; the key record and stored norms; CB the key and
+// value codebooks [4][16] (thresholds, centroids); PART [4][9][D] doubles,
+// the projections' partial sums over quarters of the columns of S.
+template <int D, int KW, int VW>
+__device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, int GE, int nb, uint8_t *scratch) {
+  constexpr int NW = D / 16, E = D / kWave;
+  constexpr int RPW = (10 + NW - 1) / NW;                  // rows per wave
+  constexpr int REC = (KW + 1) * D / 8;
+  constexpr int KQ = D / 4;                                 // columns of S per thread
+  float *rot = reinterpret_cast<float *>(scratch);
+  float *pz = rot + 10 * D;
+  float *ck = pz + 9 * D;
+  float *vh = ck + D;
+  uint32_t *rec = reinterpret_cast<uint32_t *>(vh + D);      // REC bytes
+  float *shat = reinterpret_cast<float *>(rec + REC / 4);     // stored key norm, gamma
+  float *cb = reinterpret_cast<float *>(scratch) + 21 * D + 64;                 // [4][16]
+  double *part_s = reinterpret_cast<double *>(scratch + (21 * D + 128) * 4);  // [4][9][D]
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int G = p.group, n_q = p.n_kv * G;
+  const int64_t b = bh / p.n_kv, kvh = bh % p.n_kv;
+  int64_t ctx = p.ctx_lens ? static_cast<int64_t>(p.ctx_lens[b]) : p.max_ctx;
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  float *part = p.partials + (bh * (nb + 1) + nb) * G * (D + 2);
+  if (ctx < 1) {                                   // nothing to append: an empty partial
+    for (int e = tid; e < GE * (D + 2); e += 4 * D) {
+      const int hl = e / (D + 2), i = e % (D + 2);
+      part[(p.h0 + hl) * (D + 2) + i] = (i == 0) ? -INFINITY : 0.f;
+    }
+    return;
+  }
+  const int64_t t = ctx - 1;
+  const int64_t slot = bh * p.cap + t;
+  const int64_t nblk = p.cap / kValueBlock;
+  const uint32_t vbit = 1u << (t % kValueBlock);
+
+  // 0. loads: this thread's quarter row of S (row j, columns [KQ kq, KQ kq +
+  //    KQ)), the rows of this wave (query heads, key, value; as float) and
+  //    their signs, for the value row the words its bits go into, and the
+  //    codebooks (into LDS)
+  if (tid < 64) {
+    const int which = tid / 16, k = tid % 16;
+    const int lv = 1 << ((which < 2) ? KW : VW);
+    const float *src = (which == 0) ? p.kthr : (which == 1) ? p.kcent : (which == 2) ? p.vthr : p.vcent;
+    if (k < lv - ((which & 1) ? 0 : 1)) cb[tid] = src[k];
+  }
+  const int j = tid % D, kq = tid / D;
+  uint4 sk[KQ / 8];
+#pragma unroll
+  for (int u = 0; u < KQ / 8; ++u)
+    sk[u] = *reinterpret_cast<const uint4 *>(p.sketch + static_cast<int64_t>(j) * D + KQ * kq + 8 * u);
+  float x[RPW][E], sgn[RPW][E];
+  uint32_t vw_old[E][VW];
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int r = wave + NW * k;
+    if (r < GE + 2) {
+      const bool isq = r < GE;
+      const float *sg = (r == GE + 1) ? p.vsigns : p.ksigns;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = lane + kWave * e;
+        x[k][e] = isq ? load_elem(p.q, (b * n_q + kvh * G + p.h0 + r) * D + i, p.xt)
+                      : load_elem(r == GE ? p.k_new : p.v_new, bh * D + i, p.kv_t);
+        sgn[k][e] = sg[i];
+      }
+      if (r == GE + 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int q = 0; q < VW; ++q)
+            vw_old[e][q] = p.vcodes_w[((bh * nblk + t / kValueBlock) * VW + q) * D + lane + kWave * e];
+      }
+    }
+  }
+
+  __syncthreads();                                 // the codebooks
+
+  // 1. rotations, one wave per row; the key and value rows are encoded
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int r = wave + NW * k;
+    if (r >= GE + 2) break;
+    const bool isq = r < GE, isv = r == GE + 1;
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = x[k][e] * sgn[k][e];
+    if constexpr (E == 2) {
+      const float a0 = y[0] + y[1], a1 = y[0] - y[1];
+      y[0] = a0;
+      y[1] = a1;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = wave_fwht(y[e], lane);
+    if (isq) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) rot[r * D + lane + kWave * e] = y[e] * (1.0f / sqrtf(static_cast<float>(D)));
+      continue;
+    }
+    // v = H diag(s) x: ||v||^2 = D ||x||^2
+    float s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) s2 = fmaf(y[e], y[e], s2);
+    const float n2 = wave_sum(s2);
+    const float nrm = sqrtf(n2 * (1.0f / static_cast<float>(D)));
+    const bool nz = n2 > 0.f;
+    const float vn = nz ? sqrtf(n2) : 1.0f;
+    int idx[E];
+    float cq[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (isv) decide_scaled<VW>(y[e], vn, cb + 32, cb + 48, idx[e], cq[e]);
+      else decide_scaled<KW>(y[e], vn, cb, cb + 16, idx[e], cq[e]);
+    }
+    const uint16_t nh = float_to_f16_bits(nrm);
+    if (isv) {
+      const float nv = f16_bits_to_float(nh);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = lane + kWave * e;
+        vh[i] = nv * cq[e];
+#pragma unroll
+        for (int q = 0; q < VW; ++q)
+          p.vcodes_w[((bh * nblk + t / kValueBlock) * VW + q) * D + i] =
+              ((idx[e] >> q) & 1) ? (vw_old[e][q] | vbit) : (vw_old[e][q] & ~vbit);
+      }
+      if (lane == 0) p.vscal_w[slot] = nh;
+      continue;
+    }
+    // key: r = y - c[idx] (y = v / ||v||; the zero vector has y = 0), gamma,
+    // the index planes of the record
+    const float rs = nz ? 1.0f / vn : 0.f;
+    float g2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = lane + kWave * e;
+      const float rr = fmaf(y[e], rs, -cq[e]);
+      ck[i] = cq[e];
+      rot[GE * D + i] = rr;
+      g2 = fmaf(rr, rr, g2);
+    }
+    const float gamma = sqrtf(wave_sum(g2));
+#pragma unroll
+    for (int q = 0; q < KW; ++q)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint64_t m = __ballot((idx[e] >> q) & 1);
+        if (lane == 0) {
+          rec[q * (D / 32) + 2 * e] = static_cast<uint32_t>(m);
+          rec[q * (D / 32) + 2 * e + 1] = static_cast<uint32_t>(m >> 32);
+        }
+      }
+    if (lane == 0) {
+      const uint16_t gh = float_to_f16_bits(gamma);
+      shat[0] = f16_bits_to_float(nh);
+      shat[1] = f16_bits_to_float(gh);
+      reinterpret_cast<uint32_t *>(p.kscal_w)[slot] = static_cast<uint32_t>(nh) | (static_cast<uint32_t>(gh) << 16);
+    }
+  }
+  __syncthreads();
+
+  // 2. projections PZ[c] = S ROT[c], c <= GE (c = GE: z = S r) in fp64:
+  //    thread (j, kq) sums its quarter of row j for every column, then the
+  //    four quarters are added
+  {
+    double acc[9];
+#pragma unroll
+    for (int c = 0; c < 9; ++c) acc[c] = 0.0;
+#pragma unroll
+    for (int u = 0; u < KQ / 8; ++u) {
+      const uint32_t wv[4] = {sk[u].x, sk[u].y, sk[u].z, sk[u].w};
+      float sv[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sv[2 * k] = f16_bits_to_float(static_cast<uint16_t>(wv[k] & 0xffffu));
+        sv[2 * k + 1] = f16_bits_to_float(static_cast<uint16_t>(wv[k] >> 16));
+      }
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        if (c <= GE) {
+          const float4 r0 = *reinterpret_cast<const float4 *>(rot + c * D + KQ * kq + 8 * u);
+          const float4 r1 = *reinterpret_cast<const float4 *>(rot + c * D + KQ * kq + 8 * u + 4);
+          const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[c] = fma(static_cast<double>(sv[k]), static_cast<double>(rv[k]), acc[c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 9; ++c)
+      if (c <= GE) part_s[(kq * 9 + c) * D + j] = acc[c];
+  }
+  __syncthreads();
+  for (int e = tid; e < (GE + 1) * D; e += 4 * D) {
+    const int c = e / D, jj = e % D;
+    const double s = (part_s[c * D + jj] + part_s[(9 + c) * D + jj]) +
+                     (part_s[(18 + c) * D + jj] + part_s[(27 + c) * D + jj]);
+    pz[c * D + jj] = static_cast<float>(s);
+  }
+  __syncthreads();
+
+  // 3. the sign plane and the key record
+  if (wave == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint64_t m = __ballot(pz[GE * D + lane + kWave * e] >= 0.f);
+      if (lane == 0) {
+        rec[KW * (D / 32) + 2 * e] = static_cast<uint32_t>(m);
+        rec[KW * (D / 32) + 2 * e + 1] = static_cast<uint32_t>(m >> 32);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < REC / 4) reinterpret_cast<uint32_t *>(p.kcodes_w + slot * REC)[tid] = rec[tid];
+
+  // 4. the token's logit for each head and its partial
+  const float kappa = kSqrtHalfPi / static_cast<float>(D);
+  for (int hl = wave; hl < GE; hl += NW) {
+    float slm = 0.f, sqj = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = lane + kWave * e;
+      slm = fmaf(rot[hl * D + i], ck[i], slm);
+      sqj += (pz[GE * D + i] >= 0.f) ? pz[hl * D + i] : -pz[hl * D + i];
+    }
+    slm = wave_sum(slm);
+    sqj = wave_sum(sqj);
+    const float logit = shat[0] * fmaf(kappa * shat[1], sqj, slm);
+    float *ph = part + (p.h0 + hl) * (D + 2);
+    if (lane == 0) { ph[0] = logit * p.sm_scale; ph[1] = 1.0f; }
+#pragma unroll
+    for (int e = 0; e < E; ++e) ph[2 + lane + kWave * e] = vh[lane + kWave * e];
+  }
+}
+
 // ------------------------------------------------------------------ scan
 
 // One block per (batch*kv-head, block index within the group) and the heads
@@ -559,7 +835,7 @@ __device__ __forceinline__ void wait_splits(int n_after) {
 //  4. refills the stage buffer with the split NST (ring depth) ahead.
 // Decode writes the block's partial {m, l, acc} to the workspace;
 // merge_kernel combines them.
-template <int D, int KW, int VW, int NRG, bool LOGITS>
+template <int D, int KW, int VW, int NRG, bool LOGITS, bool APPEND = false>
 __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int SPLIT = LOGITS ? kLogitSplit : attend_split<D, KW, VW, NRG>();
   using SH = ScanShape<D, KW, VW, LOGITS, SPLIT>;
@@ -580,6 +856,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int PREP_AT = SEP ? NST * SB : SB;
   constexpr int RING = (NST * SB > PREP_AT + PS::BYTES) ? NST * SB : PREP_AT + PS::BYTES;
   static_assert(RING <= LDS_BUDGET - (LOGITS ? 0 : NRG * VT * 1024), "LDS budget");
+  static_assert(!APPEND || RING >= (21 * D + 128) * 4 + 4 * 9 * D * 8, "append scratch");
   static_assert(P * (NST - 1) < 64, "vmcnt range");
   // stage k at ring + k * SB; the query preparation uses [PREP_AT,
   // PREP_AT + PS::BYTES), which (decode) stages 1 and 2 reuse once it is done
@@ -593,15 +870,27 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   const int G = p.group;
   const int n_q = p.n_kv * G;
   const int GE = min(GMAX, G - p.h0);
-  const int64_t bh = blockIdx.y;
+  // append launches: grid (groups, nb + 1) with the append blocks at y = 0,
+  // so that they are dispatched before every scan block (interleaved with
+  // the scan blocks, each finishing one would start another scan block late)
+  const int64_t bh = APPEND ? blockIdx.x : blockIdx.y;
   const int64_t b = bh / p.n_kv;
   const int64_t kvh = bh % p.n_kv;
   int64_t ctx64 = p.ctx_lens ? static_cast<int64_t>(p.ctx_lens[b]) : p.max_ctx;
   ctx64 = ctx64 < 0 ? 0 : (ctx64 > p.max_ctx ? p.max_ctx : ctx64);
+  // append: one block per group encodes the new token (the last slot of the
+  // context) and the others scan the context before it
+  const int nb = APPEND ? static_cast<int>(gridDim.y) - 1 : static_cast<int>(gridDim.x);
+  const int bx = APPEND ? static_cast<int>(blockIdx.y) - 1 : static_cast<int>(blockIdx.x);
+  if constexpr (APPEND) {
+    if (bx < 0) {
+      append_block<D, KW, VW>(p, bh, GE, nb, ring);
+      return;
+    }
+    ctx64 = ctx64 > 0 ? ctx64 - 1 : 0;
+  }
   const int ctx = static_cast<int>(ctx64);
   const int n_splits = (ctx + S - 1) / S;
-  const int nb = gridDim.x;
-  const int bx = blockIdx.x;
   const int ns = (n_splits > bx) ? (n_splits - bx + nb - 1) / nb : 0;   // splits of this block
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -821,7 +1110,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
     if (col == 0) spm[wave][4 * rg + kg] = l;
   }
   __syncthreads();
-  float *part = p.partials + (bh * nb + bx) * G * (D + 2);
+  float *part = p.partials + (bh * (nb + (APPEND ? 1 : 0)) + bx) * G * (D + 2);
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
     const int hl = 4 * rg + kg;
@@ -846,6 +1135,13 @@ __global__ __launch_bounds__(4 * D) void decode_kernel(ScanParams p) {   // 4 D 
   scan_block<D, KW, VW, NRG, false>(p);
 }
 
+// Decode attention whose launch also appends the new token (one more block
+// per group; the partials hold one more split).
+template <int D, int KW, int VW, int NRG>
+__global__ __launch_bounds__(4 * D) void append_decode_kernel(ScanParams p) {
+  scan_block<D, KW, VW, NRG, false, true>(p);
+}
+
 template <int D, int KW, int NRG>
 __global__ __launch_bounds__(4 * D) void logits_kernel(ScanParams p) {
   scan_block<D, KW, 1, NRG, true>(p);
@@ -859,7 +1155,7 @@ __global__ __launch_bounds__(4 * D) void logits_kernel(ScanParams p) {
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(ScanParams p) {
   __shared__ float ob[8][D];
-  __shared__ float se[8][kDecodeMaxBlocks];
+  __shared__ float se[8][kDecodeMaxBlocks + 1];
   __shared__ float sL[8];
   const int G = p.group;
   const int n_q = p.n_kv * G;
@@ -868,7 +1164,7 @@ __global__ __launch_bounds__(256) void merge_kernel(ScanParams p) {
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.n_kv;
   const int64_t kvh = bh % p.n_kv;
-  const int nb = p.nb;
+  const int nb = p.nb + p.append;                  // partials per group
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const float *pbase = p.partials + bh * nb * G * (D + 2);
   const int64_t pstride = static_cast<int64_t>(G) * (D + 2);
@@ -926,11 +1222,16 @@ __global__ __launch_bounds__(256) void merge_kernel(ScanParams p) {
 
 // ------------------------------------------------------------------ dispatch
 
-template <int D, int KW, int VW>
+template <int D, int KW, int VW, bool APPEND>
 static void launch_decode_kv(const ScanParams &p, dim3 grid, hipStream_t st) {
   dim3 block(4 * D);
-  if (p.group - p.h0 > 4) hipLaunchKernelGGL((decode_kernel<D, KW, VW, 2>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((decode_kernel<D, KW, VW, 1>), grid, block, 0, st, p);
+  if constexpr (APPEND) {
+    if (p.group - p.h0 > 4) hipLaunchKernelGGL((append_decode_kernel<D, KW, VW, 2>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((append_decode_kernel<D, KW, VW, 1>), grid, block, 0, st, p);
+  } else {
+    if (p.group - p.h0 > 4) hipLaunchKernelGGL((decode_kernel<D, KW, VW, 2>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((decode_kernel<D, KW, VW, 1>), grid, block, 0, st, p);
+  }
 }
 
 template <int D, int KW>
@@ -961,19 +1262,23 @@ hipError_t launch_logits_d(const ScanParams &p0, int kw, hipStream_t st) {
   return hipSuccess;
 }
 
-template <int D>
-hipError_t launch_decode_d(const ScanParams &p0, int kw, int vw, hipStream_t st) {
+// Head chunks of 8 heads, then the merge. APPEND: nb + 1 blocks per group,
+// one of them encoding the group's new token (every head chunk's launch
+// encodes it again, to the same bytes, for that chunk's partials).
+template <int D, bool APPEND>
+hipError_t launch_decode_da(const ScanParams &p0, int kw, int vw, hipStream_t st) {
   if (p0.batch == 0 || p0.n_kv == 0) return hipSuccess;
-  dim3 grid(static_cast<uint32_t>(p0.nb), static_cast<uint32_t>(p0.batch) * p0.n_kv);
+  const uint32_t groups = static_cast<uint32_t>(p0.batch) * p0.n_kv;
+  dim3 grid = APPEND ? dim3(groups, static_cast<uint32_t>(p0.nb + 1)) : dim3(static_cast<uint32_t>(p0.nb), groups);
   for (int hc = 0; hc < p0.n_hchunks; ++hc) {
     ScanParams p = p0;
     p.h0 = 8 * hc;
-#define TQ_DS_V(KK)                                          \
-    switch (vw) {                                            \
-      case 1: launch_decode_kv<D, KK, 1>(p, grid, st); break; \
-      case 2: launch_decode_kv<D, KK, 2>(p, grid, st); break; \
-      case 3: launch_decode_kv<D, KK, 3>(p, grid, st); break; \
-      default: launch_decode_kv<D, KK, 4>(p, grid, st);      \
+#define TQ_DS_V(KK)                                                   \
+    switch (vw) {                                                     \
+      case 1: launch_decode_kv<D, KK, 1, APPEND>(p, grid, st); break; \
+      case 2: launch_decode_kv<D, KK, 2, APPEND>(p, grid, st); break; \
+      case 3: launch_decode_kv<D, KK, 3, APPEND>(p, grid, st); break; \
+      default: launch_decode_kv<D, KK, 4, APPEND>(p, grid, st);       \
     }
     switch (kw) {
       case 1: TQ_DS_V(1); break;
@@ -985,8 +1290,18 @@ hipError_t launch_decode_d(const ScanParams &p0, int kw, int vw, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(static_cast<uint32_t>(p0.n_hchunks), grid.y), dim3(256), 0, st, p0);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(static_cast<uint32_t>(p0.n_hchunks), groups), dim3(256), 0, st, p0);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st) {
+  return launch_decode_da<D, false>(p, kw, vw, st);
+}
+
+template <int D>
+hipError_t launch_append_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st) {
+  return launch_decode_da<D, true>(p, kw, vw, st);
 }
 
 }  // namespace tq

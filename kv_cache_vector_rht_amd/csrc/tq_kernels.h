@@ -50,12 +50,26 @@ struct ScanParams {
   void *out;                            // decode: [batch][n_kv*group][D]
   int out_t;
   float *logits;                        // logits: [batch][n_kv*group][max_ctx]
+  // decode with append (append = 1): the launch also encodes the new token of
+  // every sequence, k_new / v_new [batch][n_kv][D] (dtype kv_t), into slot
+  // ctx_lens[b] - 1 of the caches and attends over it; the partials then
+  // hold nb + 1 splits per group, the last one that token's
+  int32_t append;
+  int kv_t;
+  const void *k_new, *v_new;
+  const float *kthr, *vthr;
+  uint8_t *kcodes_w;
+  uint16_t *kscal_w;
+  uint32_t *vcodes_w;
+  uint16_t *vscal_w;
 };
 
 template <int D>
 hipError_t launch_logits_d(const ScanParams &p, int kw, hipStream_t st);
 template <int D>
 hipError_t launch_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st);
+template <int D>
+hipError_t launch_append_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st);
 
 // Tokens per split (one pipeline stage) of the logit scan and of decode
 // attention, and the most blocks one (batch, kv-head) group is spread over.

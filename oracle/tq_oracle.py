@@ -62,7 +62,7 @@ __all__ = [
     "make_codebook", "hadamard", "rotate", "rotate_inverse",
     "encode", "pack_key_codes", "unpack_key_codes", "pack_value_codes",
     "unpack_value_codes", "prepare_query", "key_logits", "key_logits_mse", "pair_logits", "decode_attend",
-    "top_k", "search",
+    "append_decode_attend", "top_k", "search",
     "QJL_CONST",
 ]
 
@@ -445,6 +445,45 @@ def decode_attend(q, k_signs, k_centroids, sketch, kidx, ksigma, knhat, kghat,
             acc = a @ vr                                       # [G, d] rotated domain
             out[b, hk * group:(hk + 1) * group] = rotate_inverse(acc, v_signs)
     return out
+
+
+def append_decode_attend(q, k_new, v_new, k_signs, k_centroids, k_thresholds, sketch, kidx, ksigma, knhat,
+                         kghat, v_signs, v_centroids, v_thresholds, vidx, vnhat, ctx_lens, sm_scale, group: int):
+    """One decoding step: the new token's key and value (k_new, v_new
+    [B, Hkv, d]) are encoded and stored in slot ctx_lens[b] - 1 of every KV
+    sequence of batch row b (ctx_lens counts the new token; rows with
+    ctx_lens <= 0 append nothing), then decode_attend runs over the updated
+    cache. The encode step sits beside decode on the serving path: the pages
+    place decode-heavy serving at the low end of the measured throughput
+    ("TurboQuantとは？仕組み・実測精度・2026年7月時点の実装状況", section
+    「精度劣化ゼロ」の出所と、マージ後に判明した実測値).
+
+    The cache arrays are [B*Hkv, T, ...] as in decode_attend and are not
+    modified; returns (out [B, Hq, d], updated cache dict, key encoding and
+    value encoding of the new rows, each [B, Hkv, ...])."""
+    k_new = np.asarray(k_new, dtype=np.float64)
+    B, Hkv, d = k_new.shape
+    ek = encode(k_new.reshape(B * Hkv, d), k_signs, k_centroids, k_thresholds, sketch)
+    ev = encode(np.asarray(v_new, dtype=np.float64).reshape(B * Hkv, d), v_signs, v_centroids, v_thresholds)
+    cache = {"kidx": np.array(kidx), "ksigma": np.array(ksigma), "knhat": np.array(knhat),
+             "kghat": np.array(kghat), "vidx": np.array(vidx), "vnhat": np.array(vnhat)}
+    for b in range(B):
+        t = int(ctx_lens[b]) - 1
+        if t < 0:
+            continue
+        for hk in range(Hkv):
+            s = b * Hkv + hk
+            cache["kidx"][s, t] = ek["idx"][s]
+            cache["ksigma"][s, t] = ek["sigma"][s]
+            cache["knhat"][s, t] = ek["nhat"][s]
+            cache["kghat"][s, t] = ek["ghat"][s]
+            cache["vidx"][s, t] = ev["idx"][s]
+            cache["vnhat"][s, t] = ev["nhat"][s]
+    out = decode_attend(q, k_signs, k_centroids, sketch, cache["kidx"], cache["ksigma"], cache["knhat"],
+                        cache["kghat"], v_signs, v_centroids, cache["vidx"], cache["vnhat"], ctx_lens, sm_scale,
+                        group)
+    shape = lambda e: {k: v.reshape((B, Hkv) + v.shape[1:]) for k, v in e.items()}
+    return out, cache, shape(ek), shape(ev)
 
 
 # --------------------------------------------------------------------------

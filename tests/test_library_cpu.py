@@ -172,6 +172,31 @@ def test_decode_validation():
     assert tq.decode_attend_workspace(4, 8, 8, 131072, 128) > 0
 
 
+def _append(kc, vc, batch=2, n_kv=2, group=4, cap=256, max_ctx=256, out_t=tq.TQ_F32, kvt=tq.TQ_BF16, ws=None,
+            knew=FAKE, ctx=FAKE):
+    if ws is None:
+        ws = tq.append_decode_attend_workspace(batch, n_kv, group, max_ctx, 128)
+    return tq.lib.tq_append_decode_attend(ctypes.byref(kc), ctypes.byref(vc), _p(), tq.TQ_BF16, _p(knew), _p(),
+                                          kvt, batch, n_kv, group, _p(), _p(), _p(), _p(), cap, _p(ctx), max_ctx,
+                                          0.1, _p(), out_t, _p(), ws, None)
+
+
+def test_append_decode_validation():
+    k, v = _codec(), _codec(w=4, key=0, sketch=False)
+    assert _append(v, v) == tq.TQ_EINVAL                       # key codec expected
+    assert _append(k, v, out_t=tq.TQ_F16) == tq.TQ_EUNSUPPORTED
+    assert _append(k, v, max_ctx=512) == tq.TQ_EINVAL            # max_ctx > cap
+    assert _append(k, v, group=33) == tq.TQ_EUNSUPPORTED
+    assert _append(k, v, kvt=7) == tq.TQ_EINVAL                  # bad k_new/v_new dtype
+    assert _append(k, v, knew=0) == tq.TQ_EINVAL                 # NULL k_new
+    assert _append(k, v, ctx=0) == tq.TQ_EINVAL
+    # one more partial per group than tq_decode_attend
+    small = tq.decode_attend_workspace(2, 2, 4, 256, 128)
+    assert tq.append_decode_attend_workspace(2, 2, 4, 256, 128) > small
+    assert _append(k, v, ws=small) == tq.TQ_EINVAL
+    assert _append(k, v, batch=0) == tq.TQ_OK
+
+
 def _topk(n_rows=4, n_cols=5000, ld=5000, k=10, ws=None, scores=FAKE, out=FAKE):
     if ws is None:
         ws = tq.topk_workspace(n_rows, n_cols, k)

@@ -601,6 +601,44 @@ def test_decode_attend_special_cases_and_textbook_softmax():
             np.testing.assert_allclose(out_eq[b, h], Vhat[b * Hkv + h // G].mean(0), atol=1e-12)
 
 
+def test_append_decode_attend_places_the_new_token():
+    """Appending row T-1 of every sequence to a cache holding rows < T-1 and
+    attending equals attending over the full encoding (slot, KV-head and
+    batch placement); ctx_lens = 1 gives the new value itself, rebuilt with an
+    explicit rotation matrix; a row with ctx_lens = 0 appends nothing."""
+    B, Hkv, G, T, d, kw, vw = 2, 3, 2, 21, 64, 2, 3
+    rng, s, S, c, t = _toy_codec(d, kw, 12)
+    sv = rng.choice([-1.0, 1.0], size=d)
+    cv, tv = O.make_codebook(d, vw)
+    K = rng.standard_normal((B * Hkv, T, d))
+    V = rng.standard_normal((B * Hkv, T, d))
+    q = rng.standard_normal((B, Hkv * G, d))
+    ek, ev = O.encode(K, s, c, t, S), O.encode(V, sv, cv, tv)
+    scale = 1 / math.sqrt(d)
+    full = O.decode_attend(q, s, c, S, ek["idx"], ek["sigma"], ek["nhat"], ek["ghat"], sv, cv, ev["idx"],
+                           ev["nhat"], [T, T], scale, G)
+    # the cache's slot T-1 holds another token's codes before the append
+    stale = lambda a: np.concatenate([a[:, :T - 1], a[:, :1]], axis=1)
+    args = (s, c, t, S, stale(ek["idx"]), stale(ek["sigma"]), stale(ek["nhat"]), stale(ek["ghat"]), sv, cv, tv,
+            stale(ev["idx"]), stale(ev["nhat"]))
+    k_new = K[:, T - 1].reshape(B, Hkv, d)
+    v_new = V[:, T - 1].reshape(B, Hkv, d)
+    out, cache, nk, nv = O.append_decode_attend(q, k_new, v_new, *args, ctx_lens=[T, T], sm_scale=scale, group=G)
+    np.testing.assert_allclose(out, full, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(cache["kidx"], ek["idx"])
+    np.testing.assert_array_equal(cache["vidx"], ev["idx"])
+    np.testing.assert_array_equal(nk["sigma"].reshape(B * Hkv, d), ek["sigma"][:, T - 1])
+    # an empty cache: the output is the new value, n R_v^T c_v[idx], from an explicit matrix
+    out1, cache1, _, nv1 = O.append_decode_attend(q, k_new, v_new, *args, ctx_lens=[1, 0], sm_scale=scale, group=G)
+    Rv = scipy.linalg.hadamard(d) @ np.diag(sv) / math.sqrt(d)
+    for h in range(Hkv * G):
+        vh = nv1["nhat"][0, h // G].astype(np.float64) * (cv.astype(np.float64)[nv1["idx"][0, h // G]] @ Rv)
+        np.testing.assert_allclose(out1[0, h], vh, atol=1e-12)
+    assert np.all(out1[1] == 0)
+    np.testing.assert_array_equal(cache1["kidx"][Hkv:], args[4][Hkv:])     # row 1 untouched
+    np.testing.assert_array_equal(cache1["vnhat"][Hkv:], args[12][Hkv:])
+
+
 # ---------------------------------------------------------------- search
 
 
