@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,app3,dec5,enc4,search,ablation")
+    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,app3,pre3,dec5,enc4,search,ablation")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each timed kernel a few times eagerly, after a 1 GiB calibration copy, "
                          "for hardware-counter runs; prints no JSON line")
@@ -349,6 +349,49 @@ def append_step_workload(torch, tq, syn, cfg, copies, steps):
                 attended_logits_per_s=w.batch * w.n_q * w.n_tok / (res["fused_us"] * 1e-6), copies=copies, **res)
 
 
+def prefill_chunk_workload(torch, tq, syn, cfg, chunk, copies, steps):
+    """Causal attention of a `chunk`-token prefill chunk at the end of the
+    workload's context (positions n_tok - chunk .. n_tok - 1), over a cache
+    that already holds the chunk."""
+    w = syn.WORKLOADS[cfg]
+    dev = "cuda"
+    kc, vc, _ = setup_codecs(torch, tq, syn, w, dev)
+    log(f"[pre{cfg}] encoding {copies} cache copies of {w.name}")
+    caches = []
+    for c in range(copies):
+        kcodes, kscal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+        vcodes, vscal = tq.alloc_value_cache(w.n_seq, w.n_tok, vc)
+        x = syn.keys(w, device=dev, copy=c)
+        tq.encode_kv(kc, x, kcodes, kscal)
+        del x
+        x = syn.values(w, device=dev, copy=c)
+        tq.encode_kv(vc, x, vcodes, vscal)
+        del x
+        caches.append((kcodes, kscal, vcodes, vscal))
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg * 1000 + chunk)
+    qs = [torch.randn((w.batch, chunk, w.n_q, w.d), generator=g, device=dev).to(w.in_dtype) for _ in range(copies)]
+    pos0 = torch.full((w.batch,), w.n_tok - chunk, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.prefill_attend_workspace(w.batch, chunk, w.n_kv, w.group, w.n_tok, w.d), dtype=torch.uint8,
+                     device=dev)
+    outs = [torch.empty((w.batch, chunk, w.n_q, w.d), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    def pre(c):
+        kcodes, kscal, vcodes, vscal = caches[c]
+        return lambda: tq.prefill_attend(kc, vc, qs[c], kcodes, kscal, vcodes, vscal, pos0, n_kv_heads=w.n_kv,
+                                         group=w.group, max_ctx=w.n_tok, out=outs[c], workspace=ws,
+                                         out_dtype=torch.bfloat16)
+
+    gr = capture(torch, [pre(c) for c in range(copies)])
+    gr.replay()
+    avg = time_replays(torch, [gr], max(1, steps // copies)) / copies
+    pairs = w.batch * w.n_q * sum(w.n_tok - chunk + i + 1 for i in range(chunk))
+    return dict(workload=f"{w.name}, causal prefill chunk of {chunk} tokens at the end of the context",
+                avg_us=avg * 1e6, attended_logits_per_s=pairs / avg, chunk=chunk,
+                launches=(chunk * w.group + 7) // 8, copies=copies)
+
+
 def encode_full_cache(torch, tq, syn, steps):
     """Workload 4: encode every K and V vector of the 22-layer prefill."""
     w = syn.WORKLOADS[4]
@@ -588,6 +631,9 @@ def main():
         torch.cuda.empty_cache()
         if not only or "app3" in only:
             extras["append_decode_step"] = append_step_workload(torch, tq, syn, 3, copies=9, steps=20)
+        torch.cuda.empty_cache()
+        if not only or "pre3" in only:
+            extras["prefill_chunk"] = prefill_chunk_workload(torch, tq, syn, 3, chunk=16, copies=4, steps=8)
         torch.cuda.empty_cache()
         if not only or "dec5" in only:
             extras["decode_attend_long_context"] = decode_workload(torch, tq, syn, 5, copies=2, steps=10)

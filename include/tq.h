@@ -234,6 +234,35 @@ size_t tq_append_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int3
                                          int64_t max_ctx, int32_t d);
 
 /*
+ * Causal attention of a prefill chunk over the coded cache: the pages put
+ * long-prefill workloads at the high end of the measured throughput range,
+ * decode-heavy ones at the low end ("TurboQuantとは？…", section 「精度劣化
+ * ゼロ」の出所と、マージ後に判明した実測値). The chunk's own keys and values
+ * must already be in the caches (tq_encode_kv at t0 = pos0[b]); query
+ * position i of batch row b then attends to the tokens t <= pos0[b] + i
+ * (logits as tq_logits, exact softmax, values decoded as in
+ * tq_decode_attend).
+ *   q       device [batch][chunk][n_kv_heads*group][d], dtype qt, 16-byte
+ *           aligned; query head h of position i reads KV head h/group
+ *   pos0    device int32 [batch]: cache position of each row's first chunk
+ *           token; the context of position i, pos0[b] + i + 1, is clamped
+ *           to [0, max_ctx] (so pos0[b] + chunk <= max_ctx <= cap)
+ *   out     device [batch][chunk][n_kv_heads*group][d], dtype out_t
+ *   workspace  >= tq_prefill_attend_workspace(...) bytes, 256-byte aligned
+ * chunk*group <= 1024 (else TQ_EUNSUPPORTED); chunk == 0 is a no-op. The
+ * other arguments and errors are those of tq_decode_attend. Every launch
+ * covers 8 (position, head) pairs of a KV head and reads its context once.
+ */
+tq_status tq_prefill_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt,
+                            int32_t batch, int32_t chunk, int32_t n_kv_heads, int32_t group,
+                            const uint8_t *kcodes, const uint16_t *kscalars, const uint32_t *vcodes,
+                            const uint16_t *vscalars, int64_t cap, const int32_t *pos0,
+                            int64_t max_ctx, float sm_scale, void *out, tq_dtype out_t,
+                            void *workspace, size_t ws_bytes, void *stream);
+size_t tq_prefill_attend_workspace(int32_t batch, int32_t chunk, int32_t n_kv_heads,
+                                   int32_t group, int64_t max_ctx, int32_t d);
+
+/*
  * Row-wise top-k of a score matrix: the ranking step of inner-product search
  * over a coded database (the pages name vector-search indexes as a target of
  * the same codes and estimator: "メモリの壁を砕く圧縮革命、TurboQuant始動",

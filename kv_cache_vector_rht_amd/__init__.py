@@ -63,6 +63,8 @@ def _load():
         "tq_append_decode_attend": ([CP, CP, P, I32, P, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P,
                                      SZ, P], I32),
         "tq_append_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
+        "tq_prefill_attend": ([CP, CP, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
+        "tq_prefill_attend_workspace": ([I32, I32, I32, I32, I64, I32], SZ),
         "tq_topk": ([P, I64, I64, I64, I32, P, P, P, SZ, P], I32),
         "tq_topk_workspace": ([I64, I64, I32], SZ),
         "tq_status_string": ([I32], ctypes.c_char_p),
@@ -95,7 +97,8 @@ def load():
 
 EXPORTED = ("tq_make_codebook", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
             "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_decode_attend", "tq_decode_attend_workspace",
-            "tq_append_decode_attend", "tq_append_decode_attend_workspace",
+            "tq_append_decode_attend", "tq_append_decode_attend_workspace", "tq_prefill_attend",
+            "tq_prefill_attend_workspace",
             "tq_topk", "tq_topk_workspace", "tq_status_string", "tq_last_error")
 
 
@@ -315,6 +318,39 @@ def append_decode_attend(kc: Codec, vc: Codec, q: torch.Tensor, k_new: torch.Ten
                                      float(sm_scale), _ptr(out), ot, _ptr(workspace), workspace.numel(),
                                      _stream(stream))
     _check(st, "tq_append_decode_attend")
+    return out
+
+
+def prefill_attend_workspace(batch: int, chunk: int, n_kv_heads: int, group: int, max_ctx: int, d: int) -> int:
+    return int(lib.tq_prefill_attend_workspace(batch, chunk, n_kv_heads, group, max_ctx, d))
+
+
+def prefill_attend(kc: Codec, vc: Codec, q: torch.Tensor, kcodes, kscalars, vcodes, vscalars, pos0: torch.Tensor,
+                   n_kv_heads: int, group: int, max_ctx: Optional[int] = None, sm_scale: Optional[float] = None,
+                   out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal attention of a prefill chunk q [batch, chunk, n_q, d] over the coded cache, whose slots
+    [pos0[b], pos0[b] + chunk) already hold the chunk's keys and values: position i of row b attends to
+    the tokens t <= pos0[b] + i. Returns [batch, chunk, n_q, d] in out_dtype."""
+    q = q.contiguous()
+    batch, chunk = q.shape[0], q.shape[1]
+    cap = kscalars.shape[1]
+    if max_ctx is None:
+        max_ctx = cap
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(kc.d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    need = prefill_attend_workspace(batch, chunk, n_kv_heads, group, max_ctx, kc.d)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    ks, vs = kc.struct(), vc.struct()
+    ot = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[out.dtype]
+    st = lib.tq_prefill_attend(ctypes.byref(ks), ctypes.byref(vs), _ptr(q), _DTYPE[q.dtype], batch, chunk, n_kv_heads,
+                               group, _ptr(kcodes), _ptr(kscalars), _ptr(vcodes), _ptr(vscalars), cap, _ptr(pos0),
+                               max_ctx, float(sm_scale), _ptr(out), ot, _ptr(workspace), workspace.numel(),
+                               _stream(stream))
+    _check(st, "tq_prefill_attend")
     return out
 
 

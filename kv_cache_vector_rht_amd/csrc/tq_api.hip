@@ -113,16 +113,22 @@ tq::ScanParams scan_params(const tq_codec *kc, const void *q, tq_dtype qt, int32
                                   split == tq::kLogitSplit ? 256 : tq::kDecodeMaxBlocks);
   sp.sm_scale = 1.0f;
   sp.qjl = 1;
+  sp.chunk = 1;
+  sp.qgroup = group;
   return sp;
 }
 
-// Shared argument checks and parameter block of the two decode calls.
-tq_status decode_common(const char *fn, bool append, const tq_codec *kc, const tq_codec *vc, const void *q,
-                        tq_dtype qt, int32_t batch, int32_t n_kv_heads, int32_t group, const uint8_t *kcodes,
-                        const uint16_t *kscalars, const uint32_t *vcodes, const uint16_t *vscalars, int64_t cap,
-                        const int32_t *ctx_lens, int64_t max_ctx, float sm_scale, void *out, tq_dtype out_t,
-                        void *workspace, size_t ws_bytes, tq::ScanParams &sp, bool &nothing) {
+// Shared argument checks and parameter block of the decode calls. mode 0:
+// decode, 1: append + decode, 2: prefill (chunk query positions per batch
+// row, ctx_lens holding their first positions).
+tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_codec *vc, const void *q,
+                        tq_dtype qt, int32_t batch, int32_t chunk, int32_t n_kv_heads, int32_t group,
+                        const uint8_t *kcodes, const uint16_t *kscalars, const uint32_t *vcodes,
+                        const uint16_t *vscalars, int64_t cap, const int32_t *ctx_lens, int64_t max_ctx,
+                        float sm_scale, void *out, tq_dtype out_t, void *workspace, size_t ws_bytes,
+                        tq::ScanParams &sp, bool &nothing) {
   nothing = false;
+  const bool append = mode == 1;
   tq_status s = check_codec(kc, 1, fn);
   if (s != TQ_OK) return s;
   s = check_codec(vc, 0, fn);
@@ -134,30 +140,38 @@ tq_status decode_common(const char *fn, bool append, const tq_codec *kc, const t
   if (max_ctx > cap) return fail(TQ_EINVAL, "%s: max_ctx > cap", fn);
   if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (chunk < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (static_cast<int64_t>(chunk) * group > tq::kPrefillMaxHeads)
+    return fail(TQ_EUNSUPPORTED, "%s: chunk*group=%lld > %d", fn, static_cast<long long>(chunk) * group,
+                tq::kPrefillMaxHeads);
   if (!seq_offsets_fit(cap, std::max((kc->lm_bits + 1) * kc->d / 8, vc->lm_bits * kc->d / 8)))
     return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (!std::isfinite(sm_scale)) return fail(TQ_EINVAL, "%s: sm_scale is not finite", fn);
-  if (batch == 0 || n_kv_heads == 0 || group == 0) {
+  if (batch == 0 || n_kv_heads == 0 || group == 0 || chunk == 0) {
     nothing = true;
     return TQ_OK;
   }
   if (!q || !out || !ctx_lens || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
   if ((max_ctx > 0 || append) && (!kcodes || !kscalars || !vcodes || !vscalars))
     return fail(TQ_EINVAL, "%s: NULL cache pointer", fn);
-  const size_t need = append ? tq_append_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, kc->d)
-                             : tq_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, kc->d);
+  const size_t need = mode == 1 ? tq_append_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, kc->d)
+                     : mode == 2 ? tq_prefill_attend_workspace(batch, chunk, n_kv_heads, group, max_ctx, kc->d)
+                                 : tq_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, kc->d);
   if (ws_bytes < need) return fail(TQ_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(TQ_EINVAL, "%s: workspace not 256-byte aligned", fn);
   if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 16 ||
       reinterpret_cast<uintptr_t>(vcodes) % 16 || reinterpret_cast<uintptr_t>(vscalars) % 16)
     return fail(TQ_EINVAL, "%s: cache arrays must be 16-byte aligned", fn);
   if (!staged_inputs_aligned(kc, q)) return fail(TQ_EINVAL, "%s: q, signs and sketch must be 16-byte aligned", fn);
-  sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, max_ctx, tq::kAttendSplit);
+  sp = scan_params(kc, q, qt, batch, n_kv_heads, chunk * group, kcodes, kscalars, cap, max_ctx, tq::kAttendSplit);
+  sp.chunk = chunk;
+  sp.qgroup = group;
   sp.vcodes = vcodes;
   sp.vscalars = vscalars;
   sp.vcent = vc->centroids;
   sp.vsigns = vc->signs;
-  sp.ctx_lens = ctx_lens;
+  if (mode == 2) sp.pos0 = ctx_lens;
+  else sp.ctx_lens = ctx_lens;
   sp.sm_scale = sm_scale;
   sp.partials = static_cast<float *>(workspace);
   sp.out = out;
@@ -343,6 +357,31 @@ size_t tq_append_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int3
   return align_up(static_cast<size_t>(batch) * n_kv_heads * nb * group * (d + 2) * sizeof(float));
 }
 
+size_t tq_prefill_attend_workspace(int32_t batch, int32_t chunk, int32_t n_kv_heads, int32_t group,
+                                   int64_t max_ctx, int32_t d) {
+  if (batch < 0 || chunk < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
+  const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, tq::kAttendSplit);
+  return align_up(static_cast<size_t>(batch) * n_kv_heads * nb * chunk * group * (d + 2) * sizeof(float));
+}
+
+tq_status tq_prefill_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
+                            int32_t chunk, int32_t n_kv_heads, int32_t group, const uint8_t *kcodes,
+                            const uint16_t *kscalars, const uint32_t *vcodes, const uint16_t *vscalars, int64_t cap,
+                            const int32_t *pos0, int64_t max_ctx, float sm_scale, void *out, tq_dtype out_t,
+                            void *workspace, size_t ws_bytes, void *stream) {
+  const char *fn = "tq_prefill_attend";
+  tq::ScanParams sp;
+  bool nothing = false;
+  tq_status s = decode_common(fn, 2, kc, vc, q, qt, batch, chunk, n_kv_heads, group, kcodes, kscalars, vcodes,
+                              vscalars, cap, pos0, max_ctx, sm_scale, out, out_t, workspace, ws_bytes, sp, nothing);
+  if (s != TQ_OK) return s;
+  if (nothing) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, kc->lm_bits, vc->lm_bits, st)
+                             : tq::launch_decode_d<128>(sp, kc->lm_bits, vc->lm_bits, st);
+  return hip_status(e, fn);
+}
+
 tq_status tq_append_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt,
                                   const void *k_new, const void *v_new, tq_dtype kvt, int32_t batch,
                                   int32_t n_kv_heads, int32_t group, uint8_t *kcodes, uint16_t *kscalars,
@@ -352,8 +391,8 @@ tq_status tq_append_decode_attend(const tq_codec *kc, const tq_codec *vc, const 
   const char *fn = "tq_append_decode_attend";
   tq::ScanParams sp;
   bool nothing = false;
-  tq_status s = decode_common(fn, true, kc, vc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, vcodes, vscalars,
-                              cap, ctx_lens, max_ctx, sm_scale, out, out_t, workspace, ws_bytes, sp, nothing);
+  tq_status s = decode_common(fn, 1, kc, vc, q, qt, batch, 1, n_kv_heads, group, kcodes, kscalars, vcodes,
+                              vscalars, cap, ctx_lens, max_ctx, sm_scale, out, out_t, workspace, ws_bytes, sp, nothing);
   if (s != TQ_OK) return s;
   if (!dtype_ok(kvt)) return fail(TQ_EINVAL, "%s: bad k_new/v_new dtype", fn);
   if (nothing) return ok();
@@ -382,8 +421,8 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   const char *fn = "tq_decode_attend";
   tq::ScanParams sp;
   bool nothing = false;
-  tq_status s = decode_common(fn, false, kc, vc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, vcodes, vscalars,
-                              cap, ctx_lens, max_ctx, sm_scale, out, out_t, workspace, ws_bytes, sp, nothing);
+  tq_status s = decode_common(fn, 0, kc, vc, q, qt, batch, 1, n_kv_heads, group, kcodes, kscalars, vcodes,
+                              vscalars, cap, ctx_lens, max_ctx, sm_scale, out, out_t, workspace, ws_bytes, sp, nothing);
   if (s != TQ_OK) return s;
   if (nothing) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);

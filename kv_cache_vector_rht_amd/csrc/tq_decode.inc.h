@@ -291,6 +291,12 @@ constexpr int attend_split() {
   return ring + NRG * (512 / 64) * 1024 <= 160 * 1024 - 4096 ? 512 : 256;
 }
 
+// Row of q holding head v of the group of (b, kv-head kvh).
+__device__ __forceinline__ int64_t query_row(const ScanParams &p, int64_t b, int64_t kvh, int v) {
+  const int gq = p.qgroup;
+  return (b * p.chunk + v / gq) * (static_cast<int64_t>(p.n_kv) * gq) + kvh * gq + v % gq;
+}
+
 // Stage the preparation's inputs into the scratch: the sketch (every wave
 // an equal share) and the query rows of heads [h0, h0 + GE) plus the signs
 // (one load per wave; lanes past the end idle).
@@ -308,12 +314,12 @@ __device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int 
     dma16(p.sketch, static_cast<uint32_t>((j * (D / 8) + c) * 16), scratch + PS::SK + chunk * 1024);
   }
   const int es = (p.xt == 0) ? 4 : 2;
-  const int q_units = GE * D * es / 16;
+  const int upr = D * es / 16;                           // 16-byte units per query row
+  const int q_units = GE * upr;
   const int unit = wave * kWave + lane;
-  const int G = p.group, n_q = p.n_kv * G;
-  const int64_t row0 = (bh / p.n_kv) * n_q + (bh % p.n_kv) * G + p.h0;
   if (unit < q_units) {
-    dma16_at(static_cast<const uint8_t *>(p.q) + row0 * D * es + unit * 16, scratch + PS::QIN + wave * 1024);
+    const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, p.h0 + unit / upr);
+    dma16_at(static_cast<const uint8_t *>(p.q) + row * D * es + (unit % upr) * 16, scratch + PS::QIN + wave * 1024);
   } else if (unit < q_units + D / 4) {
     dma16_at(p.ksigns + (unit - q_units) * 4, scratch + PS::QIN + wave * 1024);
   }
@@ -876,7 +882,9 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   const int64_t bh = APPEND ? blockIdx.x : blockIdx.y;
   const int64_t b = bh / p.n_kv;
   const int64_t kvh = bh % p.n_kv;
-  int64_t ctx64 = p.ctx_lens ? static_cast<int64_t>(p.ctx_lens[b]) : p.max_ctx;
+  // prefill: the launch's last head sees the most tokens
+  int64_t ctx64 = p.pos0 ? static_cast<int64_t>(p.pos0[b]) + (p.h0 + GE - 1) / p.qgroup + 1
+                         : (p.ctx_lens ? static_cast<int64_t>(p.ctx_lens[b]) : p.max_ctx);
   ctx64 = ctx64 < 0 ? 0 : (ctx64 > p.max_ctx ? p.max_ctx : ctx64);
   // append: one block per group encodes the new token (the last slot of the
   // context) and the others scan the context before it
@@ -906,6 +914,13 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   float m_run[NRG], l_run[NRG], accf[NRG];
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) { m_run[rg] = -INFINITY; l_run[rg] = 0.f; accf[rg] = 0.f; }
+  // tokens t < lim[rg] for the lane's head 4 rg + kg (causal in prefill)
+  int lim[NRG];
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) {
+    int64_t l = p.pos0 ? static_cast<int64_t>(p.pos0[b]) + (p.h0 + 4 * rg + kg) / p.qgroup + 1 : ctx64;
+    lim[rg] = static_cast<int>(l < 0 ? 0 : (l > ctx64 ? ctx64 : l));
+  }
 
   SeqArrays sa;
   sa.cap = static_cast<int32_t>(p.cap);
@@ -976,7 +991,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg) {
           const float l = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa) * p.sm_scale;
-          lg[u][rg] = valid ? l : -INFINITY;
+          lg[u][rg] = (valid && sp * S + tl < lim[rg]) ? l : -INFINITY;
           mx[rg] = fmaxf(mx[rg], lg[u][rg]);
         }
         const uint16_t nvb = *reinterpret_cast<const uint16_t *>(wb + SH::OFF_S + 64 * KT + 32 * u + 2 * col);
@@ -1013,6 +1028,10 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
         m_run[rg] = mn;
         l_run[rg] *= alpha[rg];
       }
+      // (a head with no token yet keeps m = -inf: its weights are exp(-inf) = 0)
+      float msub[NRG];
+#pragma unroll
+      for (int rg = 0; rg < NRG; ++rg) msub[rg] = (m_run[rg] == -INFINITY) ? 0.f : m_run[rg];
       float sw[NRG];
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg) sw[rg] = 0.f;
@@ -1025,7 +1044,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
         const int jb = (t64 >> 3) & 3, r = t64 & 3;
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg) {
-          const float e = __expf(lg[u][rg] - m_run[rg]);
+          const float e = __expf(lg[u][rg] - msub[rg]);
           l_run[rg] += e;
           const int fx = __float2int_rn(ldexpf(e * nvv[u], 7 - k + ew));
           sw[rg] = fmaf(static_cast<float>(fx), static_cast<float>(1 << k), sw[rg]);
@@ -1214,7 +1233,7 @@ __global__ __launch_bounds__(256) void merge_kernel(ScanParams p) {
   for (int e = tid; e < GE * D; e += 256) {
     const int hl = e / D, j = e % D;
     const float o = ob[hl][j] * p.vsigns[j] * (1.0f / sqrtf(static_cast<float>(D)));
-    const int64_t row = b * n_q + kvh * G + h0 + hl;
+    const int64_t row = query_row(p, b, kvh, h0 + hl);
     if (p.out_t == 0) static_cast<float *>(p.out)[row * D + j] = o;
     else static_cast<uint16_t *>(p.out)[row * D + j] = float_to_bf16_bits(o);
   }

@@ -55,6 +55,13 @@ struct ScanParams {
   // ctx_lens[b] - 1 of the caches and attends over it; the partials then
   // hold nb + 1 splits per group, the last one that token's
   int32_t append;
+  // query rows: head v of the launch's group of (b, kv-head) is row
+  // (b chunk + v / qgroup) n_kv qgroup + kv-head qgroup + v % qgroup of q
+  // (decode and logits: chunk 1, qgroup = group). Prefill (pos0 set): group
+  // = chunk qgroup heads, the queries of chunk positions, and head v attends
+  // to the tokens t <= pos0[b] + v / qgroup
+  int32_t chunk, qgroup;
+  const int32_t *pos0;
   int kv_t;
   const void *k_new, *v_new;
   const float *kthr, *vthr;
@@ -76,6 +83,8 @@ hipError_t launch_append_decode_d(const ScanParams &p, int kw, int vw, hipStream
 constexpr int kLogitSplit = 256;
 constexpr int kAttendSplit = 512;
 constexpr int kDecodeMaxBlocks = 128;
+// Prefill: most query heads (chunk positions x heads per KV head) per call.
+constexpr int kPrefillMaxHeads = 1024;
 
 // Row-wise top-k: columns per first-stage block, largest k.
 constexpr int kTopkChunk = 4096;

@@ -62,7 +62,7 @@ __all__ = [
     "make_codebook", "hadamard", "rotate", "rotate_inverse",
     "encode", "pack_key_codes", "unpack_key_codes", "pack_value_codes",
     "unpack_value_codes", "prepare_query", "key_logits", "key_logits_mse", "pair_logits", "decode_attend",
-    "append_decode_attend", "top_k", "search",
+    "append_decode_attend", "prefill_attend", "top_k", "search",
     "QJL_CONST",
 ]
 
@@ -444,6 +444,32 @@ def decode_attend(q, k_signs, k_centroids, sketch, kidx, ksigma, knhat, kghat,
             vr = value_rows(vidx[s, :T], vnhat[s, :T], v_centroids)   # [T, d]
             acc = a @ vr                                       # [G, d] rotated domain
             out[b, hk * group:(hk + 1) * group] = rotate_inverse(acc, v_signs)
+    return out
+
+
+def prefill_attend(q, k_signs, k_centroids, sketch, kidx, ksigma, knhat, kghat, v_signs, v_centroids, vidx,
+                   vnhat, pos0, sm_scale, group: int):
+    """Causal attention of a prefill chunk over the coded cache (whose slots
+    already hold the chunk's own tokens): q [B, C, Hq, d]; query position i
+    of batch row b attends to the tokens t <= pos0[b] + i (clamped to the
+    cache arrays' length). Long prefills sit at the high end of the pages'
+    measured throughput range ("TurboQuantとは？仕組み・実測精度・2026年7月
+    時点の実装状況", section 「精度劣化ゼロ」の出所と、マージ後に判明した実測値).
+    Returns fp64 [B, C, Hq, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, C, Hq, d = q.shape
+    T = np.asarray(kidx).shape[1]
+    out = np.zeros((B, C, Hq, d))
+    for b in range(B):
+        for i in range(C):
+            n = min(int(pos0[b]) + i + 1, T)
+            out[b, i] = decode_attend(q[b, i][None], k_signs, k_centroids, sketch,
+                                      kidx[b * (Hq // group):(b + 1) * (Hq // group)],
+                                      ksigma[b * (Hq // group):(b + 1) * (Hq // group)],
+                                      knhat[b * (Hq // group):(b + 1) * (Hq // group)],
+                                      kghat[b * (Hq // group):(b + 1) * (Hq // group)], v_signs, v_centroids,
+                                      vidx[b * (Hq // group):(b + 1) * (Hq // group)],
+                                      vnhat[b * (Hq // group):(b + 1) * (Hq // group)], [n], sm_scale, group)[0]
     return out
 
 

@@ -1,0 +1,77 @@
+"""GPU parity of causal prefill-chunk attention over the coded cache
+(tq_prefill_attend): given the oracle's codes for every cached token
+(including the chunk's own), outputs against the oracle's masked softmax
+attention within the logit tolerance; a one-position chunk against
+tq_decode_attend bit for bit (the same kernels)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_vector_rht_amd as tq
+import oracle as O
+from gpu_common import bf16_rne, key_codec, pack_keys_into, pack_values_into, say, to_f64, value_codec
+from tq_parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _cache(d, kw, vw, batch, n_kv, T, seed):
+    kc, vc = key_codec(1400 + d + kw, d, kw), value_codec(1401 + d + vw, d, vw)
+    cap = ((T + 31) // 32) * 32
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    k = torch.randn((batch * n_kv, T, d), generator=g, dtype=torch.float64)
+    k *= torch.exp(torch.randn((d,), generator=g, dtype=torch.float64))
+    v = torch.randn((batch * n_kv, T, d), generator=g, dtype=torch.float64)
+    ek, ev = kc.encode(k.numpy()), vc.encode(v.numpy())
+    kcodes, kscal = tq.alloc_key_cache(batch * n_kv, cap, kc.gpu)
+    vcodes, vscal = tq.alloc_value_cache(batch * n_kv, cap, vc.gpu)
+    pack_keys_into(ek, kw, kcodes, kscal)
+    pack_values_into(ev, vw, vcodes, vscal)
+    return kc, vc, ek, ev, (kcodes, kscal, vcodes, vscal), g
+
+
+@pytest.mark.parametrize("d,kw,vw,group,batch,n_kv,T,chunk,pos0", [
+    (128, 3, 4, 4, 2, 2, 700, 16, [600, 100]),      # 64 (position, head) pairs: 8 launches
+    (128, 2, 4, 8, 1, 2, 1100, 7, [1000]),          # 56 pairs: a ragged last launch
+    (64, 2, 4, 4, 2, 2, 300, 5, [0, 250]),          # a sequence's first chunk
+    (128, 2, 3, 1, 3, 1, 96, 33, [0, 40, 63]),      # one head per KV head
+    (128, 4, 4, 2, 1, 1, 1300, 12, [1200]),         # 5-bit keys: 256-token splits
+    (64, 3, 4, 8, 2, 1, 1600, 9, [1591, 513]),
+])
+def test_prefill_attend_given_oracle_codes(d, kw, vw, group, batch, n_kv, T, chunk, pos0):
+    say(f"prefill d={d} kw={kw} vw={vw} G={group} batch={batch} n_kv={n_kv} T={T} chunk={chunk} pos0={pos0}")
+    kc, vc, ek, ev, cache, g = _cache(d, kw, vw, batch, n_kv, T, seed=d + kw + 10 * chunk)
+    q = torch.randn((batch, chunk, n_kv * group, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    p0 = torch.tensor(pos0, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    qd = q.to("cuda")
+    out32 = tq.prefill_attend(kc.gpu, vc.gpu, qd, *cache, p0, n_kv_heads=n_kv, group=group, max_ctx=T,
+                              sm_scale=scale, out_dtype=torch.float32)
+    outb = tq.prefill_attend(kc.gpu, vc.gpu, qd, *cache, p0, n_kv_heads=n_kv, group=group, max_ctx=T,
+                             sm_scale=scale, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = O.prefill_attend(to_f64(q), kc.signs, kc.centroids, kc.sketch, ek["idx"], ek["sigma"], ek["nhat"],
+                           ek["ghat"], vc.signs, vc.centroids, ev["idx"], ev["nhat"], pos0, scale, group)
+    worst = assert_close(out32.cpu().numpy(), ref, "prefill f32")
+    say("   worst err/tol", worst)
+    np.testing.assert_array_equal(outb.to(torch.float64).cpu().numpy(), bf16_rne(out32.cpu().numpy()))
+
+
+def test_one_position_chunk_is_decode():
+    """chunk = 1 runs the decode kernels with the same heads and context
+    (ctx_lens = pos0 + 1): outputs identical bit for bit."""
+    d, kw, vw, group, batch, n_kv, T = 128, 3, 4, 4, 4, 2, 900
+    pos0 = [899, 0, 511, 300]
+    say(f"prefill chunk=1 vs decode: pos0={pos0}")
+    kc, vc, ek, ev, cache, g = _cache(d, kw, vw, batch, n_kv, T, seed=3)
+    q = torch.randn((batch, 1, n_kv * group, d), generator=g, dtype=torch.float32).to(torch.bfloat16).to("cuda")
+    pre = tq.prefill_attend(kc.gpu, vc.gpu, q, *cache, torch.tensor(pos0, dtype=torch.int32, device="cuda"),
+                            n_kv_heads=n_kv, group=group, max_ctx=T)
+    dec = tq.decode_attend(kc.gpu, vc.gpu, q[:, 0], *cache,
+                           torch.tensor([p + 1 for p in pos0], dtype=torch.int32, device="cuda"), n_kv_heads=n_kv,
+                           group=group, max_ctx=T)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pre[:, 0].cpu().numpy(), dec.cpu().numpy())

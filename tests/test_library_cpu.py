@@ -197,6 +197,29 @@ def test_append_decode_validation():
     assert _append(k, v, batch=0) == tq.TQ_OK
 
 
+def _prefill(kc, vc, batch=2, chunk=8, n_kv=2, group=4, cap=256, max_ctx=256, ws=None, pos0=FAKE):
+    if ws is None:
+        ws = tq.prefill_attend_workspace(batch, chunk, n_kv, group, max_ctx, 128)
+    return tq.lib.tq_prefill_attend(ctypes.byref(kc), ctypes.byref(vc), _p(), tq.TQ_BF16, batch, chunk, n_kv, group,
+                                    _p(), _p(), _p(), _p(), cap, _p(pos0), max_ctx, 0.1, _p(), tq.TQ_F32, _p(), ws,
+                                    None)
+
+
+def test_prefill_validation():
+    k, v = _codec(), _codec(w=4, key=0, sketch=False)
+    assert _prefill(v, v) == tq.TQ_EINVAL
+    assert _prefill(k, v, chunk=-1) == tq.TQ_EINVAL
+    assert _prefill(k, v, chunk=257, group=4) == tq.TQ_EUNSUPPORTED      # more than 1024 (position, head) pairs
+    assert _prefill(k, v, group=33) == tq.TQ_EUNSUPPORTED
+    assert _prefill(k, v, pos0=0) == tq.TQ_EINVAL
+    assert _prefill(k, v, max_ctx=512) == tq.TQ_EINVAL
+    # the partials of every (position, head) pair
+    assert tq.prefill_attend_workspace(2, 8, 2, 4, 256, 128) == 2 * 2 * 1 * (8 * 4) * (128 + 2) * 4
+    assert _prefill(k, v, ws=tq.decode_attend_workspace(2, 2, 4, 256, 128)) == tq.TQ_EINVAL
+    assert _prefill(k, v, chunk=0) == tq.TQ_OK
+    assert _prefill(k, v, batch=0) == tq.TQ_OK
+
+
 def _topk(n_rows=4, n_cols=5000, ld=5000, k=10, ws=None, scores=FAKE, out=FAKE):
     if ws is None:
         ws = tq.topk_workspace(n_rows, n_cols, k)

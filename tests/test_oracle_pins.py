@@ -639,6 +639,33 @@ def test_append_decode_attend_places_the_new_token():
     np.testing.assert_array_equal(cache1["vnhat"][Hkv:], args[12][Hkv:])
 
 
+def test_prefill_attend_is_masked_softmax_attention():
+    """Causal chunk attention against an explicit mask matrix and scipy's
+    softmax over the full logit matrix, values rebuilt with an explicit
+    rotation matrix; chunk position i equals decode_attend with
+    pos0 + i + 1 tokens."""
+    B, Hkv, G, T, d, C = 2, 2, 3, 40, 64, 6
+    rng, (s, c, S), (sv, cv), ek, ev = _toy_cache(B, Hkv, T, d, 2, 3, 13)
+    q = rng.standard_normal((B, C, Hkv * G, d))
+    pos0 = [20, 34]
+    scale = 0.37
+    args = (s, c, S, ek["idx"], ek["sigma"], ek["nhat"], ek["ghat"], sv, cv, ev["idx"], ev["nhat"])
+    out = O.prefill_attend(q, *args, pos0=pos0, sm_scale=scale, group=G)
+    Rv = scipy.linalg.hadamard(d) @ np.diag(sv) / math.sqrt(d)
+    Vhat = ev["nhat"].astype(np.float64)[..., None] * (cv.astype(np.float64)[ev["idx"]] @ Rv)
+    for b in range(B):
+        for h in range(Hkv * G):
+            sq = b * Hkv + h // G
+            lg = O.key_logits(q[b, :, h], s, c, S, ek["idx"][sq], ek["sigma"][sq], ek["nhat"][sq],
+                              ek["ghat"][sq])                                  # [C, T]
+            mask = np.arange(T)[None, :] <= (pos0[b] + np.arange(C))[:, None]
+            a = scipy.special.softmax(np.where(mask, scale * lg, -np.inf), axis=1)
+            np.testing.assert_allclose(out[b, :, h], a @ Vhat[sq], rtol=1e-10, atol=1e-12)
+    for i in (0, C - 1):
+        dec = O.decode_attend(q[:, i], *args, ctx_lens=[p + i + 1 for p in pos0], sm_scale=scale, group=G)
+        np.testing.assert_allclose(out[:, i], dec, rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- search
 
 
