@@ -413,6 +413,33 @@ def encode_full_cache(torch, tq, syn, steps):
     out = dict(workload=w.name, keys_avg_us=tk * 1e6, values_avg_us=tv * 1e6,
                tokens_per_s=(2 * w.n_vec) / (tk + tv), bytes_per_pass=bk + bv,
                hbm_frac=hbm(bk + bv, tk + tv), keys_hbm_frac=hbm(bk, tk), values_hbm_frac=hbm(bv, tv))
+    del kcodes, kscal, vcodes, vscal, gk, gv
+    torch.cuda.empty_cache()
+    # fractional rates: per-layer widths from tq_rate_plan, one cache per layer
+    per_layer = w.batch * w.n_kv
+    s, S = syn.key_codec_randoms(w.cfg, w.d)
+    sv = syn.value_codec_randoms(w.cfg, w.d)
+    out["fractional"] = []
+    for rate in (2.5, 3.5):
+        kplan, vplan = tq.rate_plan(rate, w.layers, True), tq.rate_plan(rate, w.layers, False)
+        calls, nbytes = [], 0
+        for layer in range(w.layers):
+            kcl = tq.Codec.make(w.d, kplan[layer], True, s, S, device=dev)
+            vcl = tq.Codec.make(w.d, vplan[layer], False, sv, device=dev)
+            kc_l, ks_l = tq.alloc_key_cache(per_layer, w.n_tok, kcl)
+            vc_l, vs_l = tq.alloc_value_cache(per_layer, w.n_tok, vcl)
+            sl = slice(layer * per_layer, (layer + 1) * per_layer)
+            calls.append(lambda a=kcl, x=xk[sl], c=kc_l, sc=ks_l: tq.encode_kv(a, x, c, sc))
+            calls.append(lambda a=vcl, x=xv[sl], c=vc_l, sc=vs_l: tq.encode_kv(a, x, c, sc))
+            nbytes += per_layer * w.n_tok * (2 * w.d * 2 + kcl.record_bytes + 4 + vcl.lm_bits * w.d // 8 + 2)
+        gf = capture(torch, calls)
+        tf = time_replays(torch, [gf], steps)
+        out["fractional"].append(dict(
+            bits_per_channel=rate, key_lm_bits=kplan, value_lm_bits=vplan,
+            key_bits_achieved=sum(b + 1 for b in kplan) / w.layers, value_bits_achieved=sum(vplan) / w.layers,
+            avg_us=tf * 1e6, tokens_per_s=(2 * w.n_vec) / tf, bytes_per_pass=nbytes, hbm_frac=hbm(nbytes, tf)))
+        del calls, gf
+        torch.cuda.empty_cache()
     del xk, xv
     return out
 

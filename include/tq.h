@@ -109,6 +109,26 @@ typedef struct {
  */
 tq_status tq_make_codebook(int32_t d, int32_t lm_bits, float *centroids, float *thresholds);
 
+/*
+ * Fractional rates: per-layer Lloyd-Max widths whose average gives `bits`
+ * per channel (keys: including the QJL sign bit, so the Lloyd-Max average is
+ * bits - 1; values: bits). The pages name 2.5- and 3.5-bit operating points
+ * (quality-neutral at 3.5, slight loss at 2.5: "TurboQuantとは？…", section
+ * 「精度劣化ゼロ」の出所と、マージ後に判明した実測値) and describe a serving
+ * fork offering those two presets with the quantization parameters set per
+ * layer in metadata ("TurboQuant と RotorQuant を DGX Spark で試してみた",
+ * section DGX Spark 専用の vLLM フォーク). Here a rate is a mix of the two
+ * neighbouring integer widths over the layers: with avg the Lloyd-Max
+ * average, w = floor(avg) and n_hi = round((avg - w) * n_layers) layers take
+ * w + 1, spread evenly over the depth (layer l when floor((l+1) n_hi / n)
+ * > floor(l n_hi / n)); each layer's cache is then an ordinary cache of its
+ * width. The achieved average is w + n_hi / n_layers.
+ *   lm_bits  host int32 [n_layers] out
+ * TQ_EINVAL for n_layers <= 0, a non-positive or non-finite rate or is_key
+ * outside {0, 1}; TQ_EUNSUPPORTED when a width would leave 1..4. Host only.
+ */
+tq_status tq_rate_plan(double bits, int32_t n_layers, int32_t is_key, int32_t *lm_bits);
+
 /* Bytes of one key record's codes, (w+1)*d/8; 0 if the arguments are invalid. */
 size_t tq_key_record_bytes(int32_t d, int32_t lm_bits);
 /* Bytes of one 32-token value block, 4*w*d; 0 if the arguments are invalid. */

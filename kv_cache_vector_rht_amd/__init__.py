@@ -52,6 +52,7 @@ def _load():
     CP = ctypes.POINTER(_Codec)
     sig = {
         "tq_make_codebook": ([I32, I32, P, P], I32),
+        "tq_rate_plan": ([ctypes.c_double, I32, I32, P], I32),
         "tq_key_record_bytes": ([I32, I32], SZ),
         "tq_value_block_bytes": ([I32, I32], SZ),
         "tq_encode_kv": ([CP, P, I32, I64, I64, I64, I64, P, P, I64, I64, P], I32),
@@ -95,7 +96,7 @@ def load():
     """Load libtq now (raises ImportError if it is not built)."""
     return lib.tq_status_string
 
-EXPORTED = ("tq_make_codebook", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
+EXPORTED = ("tq_make_codebook", "tq_rate_plan", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
             "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_decode_attend", "tq_decode_attend_workspace",
             "tq_append_decode_attend", "tq_append_decode_attend_workspace", "tq_prefill_attend",
             "tq_prefill_attend_workspace",
@@ -181,6 +182,14 @@ class Codec:
     @property
     def record_bytes(self) -> int:
         return key_record_bytes(self.d, self.lm_bits)
+
+
+def rate_plan(bits: float, n_layers: int, is_key: bool) -> list:
+    """Per-layer Lloyd-Max widths for a fractional rate of `bits` per channel (keys: QJL bit
+    included): the two neighbouring integer widths spread evenly over the layers."""
+    out = (ctypes.c_int32 * n_layers)() if n_layers > 0 else None
+    _check(lib.tq_rate_plan(float(bits), n_layers, int(bool(is_key)), out), "tq_rate_plan")
+    return list(out)
 
 
 def alloc_key_cache(n_seq: int, cap: int, codec: Codec, device=None):

@@ -225,6 +225,30 @@ size_t tq_value_block_bytes(int32_t d, int32_t lm_bits) {
   return static_cast<size_t>(4) * lm_bits * d;
 }
 
+tq_status tq_rate_plan(double bits, int32_t n_layers, int32_t is_key, int32_t *lm_bits) {
+  const char *fn = "tq_rate_plan";
+  if (!lm_bits) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  if (n_layers <= 0) return fail(TQ_EINVAL, "%s: n_layers=%d", fn, n_layers);
+  if (is_key != 0 && is_key != 1) return fail(TQ_EINVAL, "%s: is_key=%d", fn, is_key);
+  if (!std::isfinite(bits) || bits <= 0.0) return fail(TQ_EINVAL, "%s: bits is not a positive number", fn);
+  // Lloyd-Max bits per coordinate on average: keys spend one bit on the QJL sign
+  const double avg = bits - (is_key ? 1.0 : 0.0);
+  const int w_lo = static_cast<int>(std::floor(avg));
+  const int n_hi = static_cast<int>(std::floor((avg - w_lo) * n_layers + 0.5));
+  // the widths used: w_lo on n_layers - n_hi layers, w_lo + 1 on n_hi
+  const int used_lo = (n_hi < n_layers) ? w_lo : w_lo + 1, used_hi = (n_hi > 0) ? w_lo + 1 : w_lo;
+  if (used_lo < 1 || used_hi > 4)
+    return fail(TQ_EUNSUPPORTED, "%s: %.3f bits per channel needs Lloyd-Max widths outside 1..4", fn, bits);
+  // layer l takes the wider codebook when the running count of wide layers,
+  // floor(l * n_hi / n_layers), steps up at l + 1: the n_hi wide layers are
+  // spread evenly over the depth
+  for (int l = 0; l < n_layers; ++l) {
+    const int64_t a = static_cast<int64_t>(l) * n_hi / n_layers, b = static_cast<int64_t>(l + 1) * n_hi / n_layers;
+    lm_bits[l] = w_lo + ((b > a) ? 1 : 0);
+  }
+  return ok();
+}
+
 tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_t n_seq, int64_t n_tok,
                        int64_t x_seq_stride, int64_t x_tok_stride, void *codes, uint16_t *scalars, int64_t cap,
                        int64_t t0, void *stream) {

@@ -62,7 +62,7 @@ __all__ = [
     "make_codebook", "hadamard", "rotate", "rotate_inverse",
     "encode", "pack_key_codes", "unpack_key_codes", "pack_value_codes",
     "unpack_value_codes", "prepare_query", "key_logits", "key_logits_mse", "pair_logits", "decode_attend",
-    "append_decode_attend", "prefill_attend", "top_k", "search",
+    "append_decode_attend", "prefill_attend", "rate_plan", "top_k", "search",
     "QJL_CONST",
 ]
 
@@ -510,6 +510,31 @@ def append_decode_attend(q, k_new, v_new, k_signs, k_centroids, k_thresholds, sk
                         group)
     shape = lambda e: {k: v.reshape((B, Hkv) + v.shape[1:]) for k, v in e.items()}
     return out, cache, shape(ek), shape(ev)
+
+
+# --------------------------------------------------------------------------
+# fractional rates
+# --------------------------------------------------------------------------
+
+def rate_plan(bits: float, n_layers: int, is_key: bool):
+    """Per-layer Lloyd-Max widths for an average of `bits` per channel (keys:
+    the QJL sign bit included). The pages name 2.5- and 3.5-bit operating
+    points ("TurboQuantとは？仕組み・実測精度・2026年7月時点の実装状況",
+    section 「精度劣化ゼロ」の出所と、マージ後に判明した実測値) and a serving
+    fork that sets the quantization parameters per layer for those presets
+    ("TurboQuant と RotorQuant を DGX Spark で試してみた", section DGX Spark
+    専用の vLLM フォーク); how the bits are allocated is not stated. Reading
+    taken: the two neighbouring integer widths, the wider one on
+    round(frac * n_layers) layers spread evenly over the depth (layer l when
+    the proportional count floor(l * n_hi / n_layers) steps up at l + 1).
+    Returns a list of ints, or raises ValueError outside widths 1..4."""
+    avg = bits - (1.0 if is_key else 0.0)
+    w = math.floor(avg)
+    n_hi = math.floor((avg - w) * n_layers + 0.5)
+    plan = [w + (1 if (l + 1) * n_hi // n_layers > l * n_hi // n_layers else 0) for l in range(n_layers)]
+    if min(plan) < 1 or max(plan) > 4:
+        raise ValueError("widths outside 1..4")
+    return plan
 
 
 # --------------------------------------------------------------------------

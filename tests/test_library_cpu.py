@@ -220,6 +220,26 @@ def test_prefill_validation():
     assert _prefill(k, v, batch=0) == tq.TQ_OK
 
 
+def test_rate_plan_matches_oracle():
+    for n in (1, 3, 22, 64):
+        for bits in (1.0, 1.5, 2.5, 3.25, 3.5, 4.0, 4.5):
+            for is_key in (False, True):
+                try:
+                    ref = O.rate_plan(bits, n, is_key)
+                except ValueError:
+                    with pytest.raises(tq.TQError):
+                        tq.rate_plan(bits, n, is_key)
+                    continue
+                assert tq.rate_plan(bits, n, is_key) == ref
+    out = (ctypes.c_int32 * 4)()
+    assert tq.lib.tq_rate_plan(3.5, 0, 1, out) == tq.TQ_EINVAL
+    assert tq.lib.tq_rate_plan(float("nan"), 4, 1, out) == tq.TQ_EINVAL
+    assert tq.lib.tq_rate_plan(3.5, 4, 2, out) == tq.TQ_EINVAL
+    assert tq.lib.tq_rate_plan(3.5, 4, 1, None) == tq.TQ_EINVAL
+    assert tq.lib.tq_rate_plan(1.5, 4, 1, out) == tq.TQ_EUNSUPPORTED     # 0.5 Lloyd-Max bits
+    assert tq.lib.tq_rate_plan(5.5, 4, 0, out) == tq.TQ_EUNSUPPORTED
+
+
 def _topk(n_rows=4, n_cols=5000, ld=5000, k=10, ws=None, scores=FAKE, out=FAKE):
     if ws is None:
         ws = tq.topk_workspace(n_rows, n_cols, k)

@@ -666,6 +666,32 @@ def test_prefill_attend_is_masked_softmax_attention():
         np.testing.assert_allclose(out[:, i], dec, rtol=1e-13, atol=1e-15)
 
 
+def test_rate_plan_mixes_neighbouring_widths_evenly():
+    """The plan's average is the nearest achievable to the target, its widths
+    are the two integers around the Lloyd-Max average, and every prefix of
+    layers holds the proportional count of wide layers up to one (checked
+    directly, for many rates and depths); 3.5-bit keys over an even depth
+    alternate 2 and 3 Lloyd-Max bits."""
+    for n in (1, 2, 3, 7, 22, 32, 80):
+        for bits in (1.0, 1.5, 2.0, 2.25, 2.5, 3.0, 3.3, 3.5, 3.75, 4.0):
+            for is_key in (False, True):
+                avg = bits - (1 if is_key else 0)
+                if avg < 1 or avg > 4:
+                    continue
+                plan = O.rate_plan(bits, n, is_key)
+                lo = math.floor(avg)
+                assert set(plan) <= {lo, lo + 1}
+                n_hi = sum(w - lo for w in plan)
+                # nearest achievable average
+                assert all(abs(n_hi / n - (avg - lo)) <= abs(k / n - (avg - lo)) + 1e-12 for k in range(n + 1))
+                for m in range(n + 1):
+                    assert abs(sum(w - lo for w in plan[:m]) - m * n_hi / n) < 1.0
+    assert O.rate_plan(3.5, 22, True) == [2, 3] * 11
+    assert O.rate_plan(2.5, 4, False) == [2, 3, 2, 3]
+    with pytest.raises(ValueError):
+        O.rate_plan(5.5, 4, True)
+
+
 # ---------------------------------------------------------------- search
 
 
