@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,app3,pre3,dec5,enc4,search,ablation")
+    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,app3,pre3,k8v4,dec5,enc4,search,ablation")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each timed kernel a few times eagerly, after a 1 GiB calibration copy, "
                          "for hardware-counter runs; prints no JSON line")
@@ -392,6 +392,69 @@ def prefill_chunk_workload(torch, tq, syn, cfg, chunk, copies, steps):
                 launches=(chunk * w.group + 7) // 8, copies=copies)
 
 
+def k8v4_ablation(torch, tq, syn, copies, steps):
+    """Workload 3 with fp8 keys (the k8v4 shape) beside its own TurboQuant
+    keys (3-bit, the k3v4 shape), both with the same 4-bit values: decode
+    time, bytes per token-head, and the attention output's relative RMS
+    error against exact attention over the unquantized bf16 keys and values
+    (first two batch rows, all heads)."""
+    w = syn.WORKLOADS[3]
+    dev = "cuda"
+    kc, vc, _ = setup_codecs(torch, tq, syn, w, dev)
+    log(f"[k8v4] encoding {copies} cache copies of {w.name} (TurboQuant and fp8 keys)")
+    tqc, k8c, exact = [], [], None
+    for c in range(copies):
+        kcodes, kscal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+        vcodes, vscal = tq.alloc_value_cache(w.n_seq, w.n_tok, vc)
+        k8 = tq.alloc_fp8_key_cache(w.n_seq, w.n_tok, w.d)
+        xk = syn.keys(w, device=dev, copy=c)
+        tq.encode_kv(kc, xk, kcodes, kscal)
+        tq.encode_fp8_keys(xk, k8)
+        xv = syn.values(w, device=dev, copy=c)
+        tq.encode_kv(vc, xv, vcodes, vscal)
+        if c == 0:
+            exact = (xk[:2 * w.n_kv].float(), xv[:2 * w.n_kv].float())
+        del xk, xv
+        tqc.append((kcodes, kscal, vcodes, vscal))
+        k8c.append(k8)
+    qs = [syn.queries(w, device=dev, copy=c) for c in range(copies)]
+    ctx = torch.full((w.batch,), w.n_tok, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.decode_attend_workspace(w.batch, w.n_kv, w.group, w.n_tok, w.d), dtype=torch.uint8,
+                     device=dev)
+    outs = [torch.empty((w.batch, w.n_q, w.d), dtype=torch.float32, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    def dec_tq(c):
+        kcodes, kscal, vcodes, vscal = tqc[c]
+        return lambda: tq.decode_attend(kc, vc, qs[c], kcodes, kscal, vcodes, vscal, ctx, n_kv_heads=w.n_kv,
+                                        group=w.group, max_ctx=w.n_tok, out=outs[c], workspace=ws)
+
+    def dec_k8(c):
+        _, _, vcodes, vscal = tqc[c]
+        return lambda: tq.decode_attend_k8(vc, qs[c], k8c[c], vcodes, vscal, ctx, n_kv_heads=w.n_kv,
+                                           group=w.group, max_ctx=w.n_tok, out=outs[c], workspace=ws)
+
+    res = {}
+    scale = 1.0 / math.sqrt(w.d)
+    K, V = exact
+    q0 = qs[0][:2].float().reshape(2, w.n_kv, w.group, w.d)
+    Kb, Vb = K.reshape(2, w.n_kv, w.n_tok, w.d), V.reshape(2, w.n_kv, w.n_tok, w.d)
+    ref = torch.softmax(torch.matmul(q0, Kb.transpose(-1, -2).contiguous()) * scale, dim=-1)
+    ref = torch.matmul(ref, Vb).reshape(2, w.n_q, w.d)
+    for name, mk, key_bytes in (("k3v4", dec_tq, kc.record_bytes + 4), ("k8v4", dec_k8, w.d)):
+        mk(0)()
+        torch.cuda.synchronize()
+        err = (outs[0][:2] - ref).pow(2).mean().sqrt() / ref.pow(2).mean().sqrt()
+        g = capture(torch, [mk(c) for c in range(copies)])
+        g.replay()
+        t = time_replays(torch, [g], max(1, steps // copies)) / copies
+        bytes_ = w.n_seq * w.n_tok * (key_bytes + vc.lm_bits * w.d // 8 + 2) + w.batch * w.n_q * w.d * 4
+        res[name] = dict(avg_us=t * 1e6, bytes_per_token_head=key_bytes + vc.lm_bits * w.d // 8 + 2,
+                         hbm_frac=hbm(bytes_, t), rel_rms_error_vs_exact=float(err))
+        del g
+    return dict(workload=w.name, copies=copies, **res)
+
+
 def encode_full_cache(torch, tq, syn, steps):
     """Workload 4: encode every K and V vector of the 22-layer prefill."""
     w = syn.WORKLOADS[4]
@@ -661,6 +724,9 @@ def main():
         torch.cuda.empty_cache()
         if not only or "pre3" in only:
             extras["prefill_chunk"] = prefill_chunk_workload(torch, tq, syn, 3, chunk=16, copies=4, steps=8)
+        torch.cuda.empty_cache()
+        if not only or "k8v4" in only:
+            extras["k8v4_ablation"] = k8v4_ablation(torch, tq, syn, copies=4, steps=20)
         torch.cuda.empty_cache()
         if not only or "dec5" in only:
             extras["decode_attend_long_context"] = decode_workload(torch, tq, syn, 5, copies=2, steps=10)

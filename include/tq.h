@@ -283,6 +283,39 @@ size_t tq_prefill_attend_workspace(int32_t batch, int32_t chunk, int32_t n_kv_he
                                    int32_t group, int64_t max_ctx, int32_t d);
 
 /*
+ * The k8v4 cache shape: fp8 keys with 4-bit (any 1..4-bit) TurboQuant values,
+ * the most conservative of the serving presets the pages list
+ * ("TurboQuantとは？…", sections 「精度劣化ゼロ」の出所と、マージ後に判明した
+ * 実測値 and vLLM：–kv-cache-dtypeの切り替えだけで利用可能), kept here as an
+ * ablation of the key codec: keys store no rotation, no Lloyd-Max codes and
+ * no QJL bits, only each coordinate as an OCP e4m3fn byte.
+ *
+ * tq_encode_fp8_keys: codes uint8 [n_seq][cap][d], byte i of slot t0 + t of
+ * sequence s = e4m3fn(x_i / scale) for input row t of sequence s, the
+ * quotient taken in fp32 (correctly rounded), rounded to nearest even; finite
+ * quotients beyond +-448 saturate to +-448, NaN stays NaN (0x7f / 0xff).
+ *   x, xt, strides, n_seq, n_tok, cap, t0  as tq_encode_kv; d a multiple of 8
+ *   scale   positive finite per-tensor scale (1.0: a plain cast)
+ *   codes   device, 8-byte aligned; slots outside [t0, t0 + n_tok) untouched
+ *
+ * tq_decode_attend_k8: tq_decode_attend with the key cache replaced by fp8
+ * keys: logit = k_scale * sum_i q_i e4m3(k_i) (q as given, fp32-grade sums),
+ * exact softmax of sm_scale * logit, values decoded as in tq_decode_attend.
+ *   vc       the value codec (d from it); kcodes the fp8 key cache
+ *            [batch*n_kv_heads][cap][d], 16-byte aligned; k_scale > 0
+ *   workspace  >= tq_decode_attend_workspace(...) bytes, 256-byte aligned
+ * Other arguments and errors as tq_decode_attend (q needs 16-byte alignment).
+ */
+tq_status tq_encode_fp8_keys(const void *x, tq_dtype xt, int32_t d, int64_t n_seq, int64_t n_tok,
+                             int64_t x_seq_stride, int64_t x_tok_stride, float scale, uint8_t *codes,
+                             int64_t cap, int64_t t0, void *stream);
+tq_status tq_decode_attend_k8(const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
+                              int32_t n_kv_heads, int32_t group, const uint8_t *kcodes, float k_scale,
+                              const uint32_t *vcodes, const uint16_t *vscalars, int64_t cap,
+                              const int32_t *ctx_lens, int64_t max_ctx, float sm_scale, void *out,
+                              tq_dtype out_t, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Row-wise top-k of a score matrix: the ranking step of inner-product search
  * over a coded database (the pages name vector-search indexes as a target of
  * the same codes and estimator: "メモリの壁を砕く圧縮革命、TurboQuant始動",

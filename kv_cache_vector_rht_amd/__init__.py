@@ -66,6 +66,8 @@ def _load():
         "tq_append_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
         "tq_prefill_attend": ([CP, CP, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
         "tq_prefill_attend_workspace": ([I32, I32, I32, I32, I64, I32], SZ),
+        "tq_encode_fp8_keys": ([P, I32, I32, I64, I64, I64, I64, F, P, I64, I64, P], I32),
+        "tq_decode_attend_k8": ([CP, P, I32, I32, I32, I32, P, F, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
         "tq_topk": ([P, I64, I64, I64, I32, P, P, P, SZ, P], I32),
         "tq_topk_workspace": ([I64, I64, I32], SZ),
         "tq_status_string": ([I32], ctypes.c_char_p),
@@ -99,7 +101,7 @@ def load():
 EXPORTED = ("tq_make_codebook", "tq_rate_plan", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
             "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_decode_attend", "tq_decode_attend_workspace",
             "tq_append_decode_attend", "tq_append_decode_attend_workspace", "tq_prefill_attend",
-            "tq_prefill_attend_workspace",
+            "tq_prefill_attend_workspace", "tq_encode_fp8_keys", "tq_decode_attend_k8",
             "tq_topk", "tq_topk_workspace", "tq_status_string", "tq_last_error")
 
 
@@ -360,6 +362,47 @@ def prefill_attend(kc: Codec, vc: Codec, q: torch.Tensor, kcodes, kscalars, vcod
                                max_ctx, float(sm_scale), _ptr(out), ot, _ptr(workspace), workspace.numel(),
                                _stream(stream))
     _check(st, "tq_prefill_attend")
+    return out
+
+
+def alloc_fp8_key_cache(n_seq: int, cap: int, d: int, device="cuda") -> torch.Tensor:
+    """fp8 key cache: uint8 [n_seq, cap, d] of OCP e4m3fn bytes."""
+    return torch.zeros((n_seq, cap, d), dtype=torch.uint8, device=device)
+
+
+def encode_fp8_keys(x: torch.Tensor, codes: torch.Tensor, scale: float = 1.0, t0: int = 0, stream=None):
+    """Encode keys x [n_seq, n_tok, d] (rows contiguous) as e4m3fn(x / scale) into slots [t0, t0 + n_tok)."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [n_seq, n_tok, d] with contiguous rows")
+    n_seq, n_tok, d = x.shape
+    st = lib.tq_encode_fp8_keys(_ptr(x), _DTYPE[x.dtype], d, n_seq, n_tok, x.stride(0), x.stride(1), float(scale),
+                                _ptr(codes), codes.shape[1], t0, _stream(stream))
+    _check(st, "tq_encode_fp8_keys")
+
+
+def decode_attend_k8(vc: Codec, q: torch.Tensor, kcodes: torch.Tensor, vcodes, vscalars, ctx_lens: torch.Tensor,
+                     n_kv_heads: int, group: int, k_scale: float = 1.0, max_ctx: Optional[int] = None,
+                     sm_scale: Optional[float] = None, out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention over fp8 keys and TurboQuant values (the k8v4 shape): [batch, n_q, d]."""
+    q = q.contiguous()
+    batch = q.shape[0]
+    cap = kcodes.shape[1]
+    if max_ctx is None:
+        max_ctx = cap
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(vc.d)
+    if out is None:
+        out = torch.empty((batch, n_kv_heads * group, vc.d), dtype=out_dtype, device=q.device)
+    need = decode_attend_workspace(batch, n_kv_heads, group, max_ctx, vc.d)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    vs = vc.struct()
+    ot = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}[out.dtype]
+    st = lib.tq_decode_attend_k8(ctypes.byref(vs), _ptr(q), _DTYPE[q.dtype], batch, n_kv_heads, group, _ptr(kcodes),
+                                 float(k_scale), _ptr(vcodes), _ptr(vscalars), cap, _ptr(ctx_lens), max_ctx,
+                                 float(sm_scale), _ptr(out), ot, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "tq_decode_attend_k8")
     return out
 
 

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["tq_decode_d128.hip", "tq_append_d128.hip", "tq_encode_d128.hip", "tq_decode_d64.hip",
            "tq_append_d64.hip", "tq_encode_d64.hip",
-           "tq_topk.hip", "tq_api.hip", "tq_codebook.cpp"]
+           "tq_fp8.hip", "tq_topk.hip", "tq_api.hip", "tq_codebook.cpp"]
 
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 

@@ -120,7 +120,8 @@ tq::ScanParams scan_params(const tq_codec *kc, const void *q, tq_dtype qt, int32
 
 // Shared argument checks and parameter block of the decode calls. mode 0:
 // decode, 1: append + decode, 2: prefill (chunk query positions per batch
-// row, ctx_lens holding their first positions).
+// row, ctx_lens holding their first positions), 3: decode over fp8 keys (no
+// key codec: kc is ignored, d comes from the value codec).
 tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_codec *vc, const void *q,
                         tq_dtype qt, int32_t batch, int32_t chunk, int32_t n_kv_heads, int32_t group,
                         const uint8_t *kcodes, const uint16_t *kscalars, const uint32_t *vcodes,
@@ -129,8 +130,13 @@ tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_c
                         tq::ScanParams &sp, bool &nothing) {
   nothing = false;
   const bool append = mode == 1;
-  tq_status s = check_codec(kc, 1, fn);
-  if (s != TQ_OK) return s;
+  tq_status s = TQ_OK;
+  if (mode == 3) {
+    kc = vc;                                       // fp8 keys: no key codec (d from the value codec)
+  } else {
+    s = check_codec(kc, 1, fn);
+    if (s != TQ_OK) return s;
+  }
   s = check_codec(vc, 0, fn);
   if (s != TQ_OK) return s;
   if (kc->d != vc->d) return fail(TQ_EINVAL, "%s: key d=%d and value d=%d differ", fn, kc->d, vc->d);
@@ -144,7 +150,8 @@ tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_c
   if (static_cast<int64_t>(chunk) * group > tq::kPrefillMaxHeads)
     return fail(TQ_EUNSUPPORTED, "%s: chunk*group=%lld > %d", fn, static_cast<long long>(chunk) * group,
                 tq::kPrefillMaxHeads);
-  if (!seq_offsets_fit(cap, std::max((kc->lm_bits + 1) * kc->d / 8, vc->lm_bits * kc->d / 8)))
+  const int key_rec = (mode == 3) ? kc->d : (kc->lm_bits + 1) * kc->d / 8;
+  if (!seq_offsets_fit(cap, std::max(key_rec, vc->lm_bits * kc->d / 8)))
     return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (!std::isfinite(sm_scale)) return fail(TQ_EINVAL, "%s: sm_scale is not finite", fn);
   if (batch == 0 || n_kv_heads == 0 || group == 0 || chunk == 0) {
@@ -152,7 +159,7 @@ tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_c
     return TQ_OK;
   }
   if (!q || !out || !ctx_lens || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
-  if ((max_ctx > 0 || append) && (!kcodes || !kscalars || !vcodes || !vscalars))
+  if ((max_ctx > 0 || append) && (!kcodes || (mode != 3 && !kscalars) || !vcodes || !vscalars))
     return fail(TQ_EINVAL, "%s: NULL cache pointer", fn);
   const size_t need = mode == 1 ? tq_append_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, kc->d)
                      : mode == 2 ? tq_prefill_attend_workspace(batch, chunk, n_kv_heads, group, max_ctx, kc->d)
@@ -162,7 +169,8 @@ tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_c
   if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 16 ||
       reinterpret_cast<uintptr_t>(vcodes) % 16 || reinterpret_cast<uintptr_t>(vscalars) % 16)
     return fail(TQ_EINVAL, "%s: cache arrays must be 16-byte aligned", fn);
-  if (!staged_inputs_aligned(kc, q)) return fail(TQ_EINVAL, "%s: q, signs and sketch must be 16-byte aligned", fn);
+  if (mode == 3 ? reinterpret_cast<uintptr_t>(q) % 16 != 0 : !staged_inputs_aligned(kc, q))
+    return fail(TQ_EINVAL, "%s: q, signs and sketch must be 16-byte aligned", fn);
   sp = scan_params(kc, q, qt, batch, n_kv_heads, chunk * group, kcodes, kscalars, cap, max_ctx, tq::kAttendSplit);
   sp.chunk = chunk;
   sp.qgroup = group;
@@ -379,6 +387,56 @@ size_t tq_append_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int3
   if (batch < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
   const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, tq::kAttendSplit) + 1;
   return align_up(static_cast<size_t>(batch) * n_kv_heads * nb * group * (d + 2) * sizeof(float));
+}
+
+tq_status tq_encode_fp8_keys(const void *x, tq_dtype xt, int32_t d, int64_t n_seq, int64_t n_tok,
+                             int64_t x_seq_stride, int64_t x_tok_stride, float scale, uint8_t *codes, int64_t cap,
+                             int64_t t0, void *stream) {
+  const char *fn = "tq_encode_fp8_keys";
+  if (!dtype_ok(xt)) return fail(TQ_EINVAL, "%s: bad input dtype", fn);
+  if (d <= 0 || d % 8) return fail(TQ_EINVAL, "%s: d=%d must be a positive multiple of 8", fn, d);
+  if (n_seq < 0 || n_tok < 0 || cap < 0 || t0 < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (t0 + n_tok > cap) return fail(TQ_EINVAL, "%s: t0 + n_tok > cap", fn);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(TQ_EINVAL, "%s: scale must be positive and finite", fn);
+  if (n_seq == 0 || n_tok == 0) return ok();
+  if (!x || !codes) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  if (x_tok_stride < d || x_seq_stride < 0) return fail(TQ_EINVAL, "%s: bad strides", fn);
+  if (reinterpret_cast<uintptr_t>(codes) % 8) return fail(TQ_EINVAL, "%s: codes must be 8-byte aligned", fn);
+  tq::EncodeParams ep{};
+  ep.x = x;
+  ep.x_seq_stride = x_seq_stride;
+  ep.x_tok_stride = x_tok_stride;
+  ep.n_tok = n_tok;
+  ep.t0 = t0;
+  ep.cap = cap;
+  ep.n_waves = n_seq;
+  ep.xt = static_cast<int>(xt);
+  ep.codes = codes;
+  return hip_status(tq::launch_encode_fp8(ep, d, scale, static_cast<hipStream_t>(stream)), fn);
+}
+
+tq_status tq_decode_attend_k8(const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
+                              int32_t group, const uint8_t *kcodes, float k_scale, const uint32_t *vcodes,
+                              const uint16_t *vscalars, int64_t cap, const int32_t *ctx_lens, int64_t max_ctx,
+                              float sm_scale, void *out, tq_dtype out_t, void *workspace, size_t ws_bytes,
+                              void *stream) {
+  const char *fn = "tq_decode_attend_k8";
+  if (!vc) return fail(TQ_EINVAL, "%s: codec is NULL", fn);
+  if (!(k_scale > 0.f) || !std::isfinite(k_scale)) return fail(TQ_EINVAL, "%s: k_scale must be positive and finite", fn);
+  tq::ScanParams sp;
+  bool nothing = false;
+  tq_status s = decode_common(fn, 3, nullptr, vc, q, qt, batch, 1, n_kv_heads, group, kcodes, nullptr, vcodes,
+                              vscalars, cap, ctx_lens, max_ctx, sm_scale, out, out_t, workspace, ws_bytes, sp, nothing);
+  if (s != TQ_OK) return s;
+  if (nothing) return ok();
+  sp.k_scale = k_scale;
+  sp.ksigns = nullptr;
+  sp.kcent = nullptr;
+  sp.sketch = nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = vc->d == 64 ? tq::launch_decode_d<64>(sp, tq::kKeyFp8, vc->lm_bits, st)
+                             : tq::launch_decode_d<128>(sp, tq::kKeyFp8, vc->lm_bits, st);
+  return hip_status(e, fn);
 }
 
 size_t tq_prefill_attend_workspace(int32_t batch, int32_t chunk, int32_t n_kv_heads, int32_t group,

@@ -94,20 +94,25 @@ constexpr int kStages = 3;
 // share of a split is staged in a region of LDS that only it reads, so no
 // barrier guards the staging:
 //   [0, OFF_S)         key tiles, 16 x REC bytes each; for d = 128 plane-major
-//                      (the 16 keys' words of plane 0, then of plane 1, ...)
-//   [OFF_S, OFF_V)     the tiles' key scalar pairs (64 B per tile), then
-//                      (decode) their value norms (32 B per tile)
+//                      (the 16 keys' words of plane 0, then of plane 1, ...),
+//                      for fp8 keys chunk-major (16-byte chunk q of key i at
+//                      16-byte unit 16 q + i)
+//   [OFF_S, OFF_V)     the tiles' key scalar pairs (64 B per tile; none for
+//                      fp8 keys), then (decode) their value norms (32 B per
+//                      tile)
 //   [OFF_V, ...)       (decode) value words: [32-token block][plane][16 coords]
 template <int D, int KW, int VW, bool LOGITS, int SPLIT>
 struct ScanShape {
+  static constexpr bool K8 = KW == kKeyFp8;          // fp8 key records
   static constexpr int S = SPLIT;
   static constexpr int NW = D / 16;
   static constexpr int THREADS = NW * kWave;
   static constexpr int KT = S / 16 / NW;             // key tiles per wave
   static constexpr int VT = S / 64;                  // 64-token value tiles
-  static constexpr int REC = (KW + 1) * D / 8;       // record bytes = 16-byte units per key tile
+  static constexpr int REC = K8 ? D : (KW + 1) * D / 8;   // record bytes = 16-byte units per key tile
   static constexpr int KI = (REC + 63) / 64;         // loads per key tile
-  static constexpr int SU = (LOGITS ? 4 : 6) * KT;   // scalar units
+  static constexpr int KSU = K8 ? 0 : 4;             // key scalar units per tile
+  static constexpr int SU = (KSU + (LOGITS ? 0 : 2)) * KT;   // scalar units
   static constexpr int VU = LOGITS ? 0 : (S / 32) * VW * 4;   // value units
   static constexpr int VI = (VU + 63) / 64;
   static constexpr int P = KT * KI + 1 + VI;         // loads per wave per split
@@ -186,17 +191,19 @@ __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t
     for (int ki = 0; ki < SH::KI; ++ki) {
       const int unit = ki * 64 + lane;
       if (unit < REC) {
-        // d = 128: LDS unit 16 q + i <- plane q of key i; d = 64: a plain copy
-        const uint32_t lo = (D == 128) ? (unit % 16) * REC + (unit / 16) * 16 : unit * 16;
+        // d = 128 and fp8 keys: LDS unit 16 q + i <- 16-byte unit q (a plane,
+        // or 16 fp8 coordinates) of key i; d = 64: a plain copy
+        const uint32_t lo = (D == 128 || SH::K8) ? (unit % 16) * REC + (unit / 16) * 16 : unit * 16;
         dma16(sa.kcodes, tile0[u] * REC + lo, wb + u * REC * 16 + ki * 1024);
       }
     }
   }
   if (lane < SH::SU) {
-    // lanes [0, 4 KT): key scalar pairs of tile lane/4; then value norms
-    const bool key = lane < 4 * SH::KT;
-    const int u = key ? lane / 4 : (lane - 4 * SH::KT) / 2;
-    const int m = key ? lane % 4 : (lane - 4 * SH::KT) % 2;
+    // lanes [0, 4 KT): key scalar pairs of tile lane/4 (none for fp8 keys);
+    // then value norms
+    const bool key = lane < SH::KSU * SH::KT;
+    const int u = key ? lane / 4 : (lane - SH::KSU * SH::KT) / 2;
+    const int m = key ? lane % 4 : (lane - SH::KSU * SH::KT) % 2;
     uint32_t t0 = 0;
 #pragma unroll
     for (int v = 0; v < SH::KT; ++v) t0 = (u == v) ? tile0[v] : t0;
@@ -286,8 +293,9 @@ struct PrepShape {
 template <int D, int KW, int VW, int NRG>
 constexpr int attend_split() {
   using S5 = ScanShape<D, KW, VW, false, 512>;
-  using PS = PrepShape<D, KW, NRG>;
-  constexpr int ring = S5::STAGE_BYTES + (S5::STAGE_BYTES > PS::BYTES ? S5::STAGE_BYTES : PS::BYTES);
+  using PS = PrepShape<D, KW == kKeyFp8 ? 1 : KW, NRG>;
+  constexpr int PSB = KW == kKeyFp8 ? 4096 : PS::BYTES;
+  constexpr int ring = S5::STAGE_BYTES + (S5::STAGE_BYTES > PSB ? S5::STAGE_BYTES : PSB);
   return ring + NRG * (512 / 64) * 1024 <= 160 * 1024 - 4096 ? 512 : 256;
 }
 
@@ -543,6 +551,95 @@ __device__ __forceinline__ void wait_splits(int n_after) {
     case 5: wait_vm<5 * P < 63 ? 5 * P : 63>(); break;
     default: wait_vm<6 * P < 63 ? 6 * P : 63>(); break;
   }
+}
+
+// ------------------------------------------------------------------ fp8 keys
+
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+union BF8 {
+  uint4 u;
+  v8bf16 v;
+};
+
+// Stage the raw query rows of heads [h0, h0 + GE) at scratch (one 16-byte
+// load per lane; lanes past the end idle).
+template <int D>
+__device__ __forceinline__ void issue_q_rows(const ScanParams &p, int64_t bh, int GE, uint8_t *scratch, int wave) {
+  const int es = (p.xt == 0) ? 4 : 2;
+  const int upr = D * es / 16;
+  const int unit = wave * kWave + lane_id();
+  if (unit < GE * upr) {
+    const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, p.h0 + unit / upr);
+    dma16_at(static_cast<const uint8_t *>(p.q) + row * D * es + (unit % upr) * 16, scratch + unit * 16);
+  }
+}
+
+// A operands of the fp8-key logits, v_mfma_f32_16x16x32_bf16 over 32
+// coordinates per product: row i = 4 u + part of row group rg is head
+// 4 rg + u's query split exactly into bf16 parts q = hi + mid + lo (part 3
+// zero); lane (i, kg) holds coordinates 32 s + 8 kg .. + 7 of its row.
+template <int D, int NRG>
+__device__ __forceinline__ void k8_operands(const ScanParams &p, int GE, const uint8_t *qrows,
+                                            v8bf16 (&a8)[NRG][D / 32]) {
+  const int lane = lane_id(), i = lane % 16, kg = lane / 16;
+  const int part = i % 4;
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) {
+    const int hl = 4 * rg + i / 4;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      BF8 o;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (hl < GE && part < 3) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int at = hl * D + 32 * s + 8 * kg + e;
+          float x;
+          if (p.xt == 0) x = reinterpret_cast<const float *>(qrows)[at];
+          else if (p.xt == 1) x = bf16_bits_to_float(reinterpret_cast<const uint16_t *>(qrows)[at]);
+          else x = f16_bits_to_float(reinterpret_cast<const uint16_t *>(qrows)[at]);
+          uint16_t b = float_to_bf16_bits(x);
+          for (int k = 0; k < part; ++k) {             // the remainders are exact in fp32
+            x -= bf16_bits_to_float(b);
+            b = float_to_bf16_bits(x);
+          }
+          w[e / 2] |= static_cast<uint32_t>(b) << (16 * (e % 2));
+        }
+      }
+      o.u = make_uint4(w[0], w[1], w[2], w[3]);
+      a8[rg][s] = o.v;
+    }
+  }
+}
+
+// Logits of one 16-key tile of fp8 keys (chunk-major in LDS at kb): lane
+// (kg, n) converts key n's coordinates 32 s + 8 kg .. + 7 to bf16 (exact)
+// as the B operand; the sum of the C rows of the lane's head is q . key.
+template <int D, int NRG>
+__device__ __forceinline__ void k8_tile_logits(const uint8_t *kb, const v8bf16 (&a8)[NRG][D / 32], int nrg,
+                                               float (&dot)[NRG]) {
+  const int lane = lane_id(), col = lane % 16, kg = lane / 16;
+  v4f c[NRG];
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) c[rg] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    const uint2 raw = *reinterpret_cast<const uint2 *>(kb + (16 * (2 * s + (kg >> 1)) + col) * 16 + 8 * (kg & 1));
+    const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
+    const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);
+    const auto b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false);
+    const auto b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, true);
+    BF8 bo;
+    bo.u = make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
+                      __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3));
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg)
+      if (rg < nrg) c[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8[rg][s], bo.v, c[rg], 0, 0, 0);
+  }
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) dot[rg] = (c[rg][0] + c[rg][1]) + (c[rg][2] + c[rg][3]);
 }
 
 // ------------------------------------------------------------------ append
@@ -845,7 +942,10 @@ template <int D, int KW, int VW, int NRG, bool LOGITS, bool APPEND = false>
 __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int SPLIT = LOGITS ? kLogitSplit : attend_split<D, KW, VW, NRG>();
   using SH = ScanShape<D, KW, VW, LOGITS, SPLIT>;
-  using PS = PrepShape<D, KW, NRG>;
+  constexpr bool K8 = SH::K8;
+  static_assert(!(K8 && (LOGITS || APPEND)), "fp8 keys: decode attention only");
+  using PS = PrepShape<D, K8 ? 1 : KW, NRG>;
+  constexpr int PS_BYTES = K8 ? 4096 : PS::BYTES;   // fp8 keys: the raw query rows only
   constexpr int S = SH::S, NW = SH::NW, KT = SH::KT, VT = SH::VT, REC = SH::REC, P = SH::P;
   constexpr int NMF = PS::NMF;
   constexpr int NBV = Basis<VW>::N;
@@ -856,11 +956,11 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   // splits per block) keeps up to 6 in flight, its query preparation in a
   // region of its own so that every stage can be filled before it
   constexpr int LDS_BUDGET = 160 * 1024 - 2048;
-  constexpr int NST_L = (LDS_BUDGET - PS::BYTES) / SB < 6 ? (LDS_BUDGET - PS::BYTES) / SB : 6;
+  constexpr int NST_L = (LDS_BUDGET - PS_BYTES) / SB < 6 ? (LDS_BUDGET - PS_BYTES) / SB : 6;
   constexpr bool SEP = LOGITS && NST_L >= 3;
   constexpr int NST = SEP ? NST_L : (SPLIT == 512 ? 2 : kStages);
   constexpr int PREP_AT = SEP ? NST * SB : SB;
-  constexpr int RING = (NST * SB > PREP_AT + PS::BYTES) ? NST * SB : PREP_AT + PS::BYTES;
+  constexpr int RING = (NST * SB > PREP_AT + PS_BYTES) ? NST * SB : PREP_AT + PS_BYTES;
   static_assert(RING <= LDS_BUDGET - (LOGITS ? 0 : NRG * VT * 1024), "LDS budget");
   static_assert(!APPEND || RING >= (21 * D + 128) * 4 + 4 * 9 * D * 8, "append scratch");
   static_assert(P * (NST - 1) < 64, "vmcnt range");
@@ -931,19 +1031,33 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   sa.vscal = LOGITS ? nullptr : reinterpret_cast<const uint8_t *>(p.vscalars) + bh * p.cap * 2;
   v4i a[NRG][NMF];
   float4 fh[NRG];
-  if (ns > 0) {
-    // the preparation's inputs first, alone; the splits that do not
-    // overlap its scratch are issued once the queries are rotated
-    issue_prep<D, KW, NRG>(p, bh, GE, ring + PREP_AT, wave);
-    const int first = SEP ? min(ns, NST) : 1;
-    wait_vm<0>();
-    lds_barrier();
-    group_prep<D, KW, NRG>(p, GE, ring + PREP_AT, [&] {
-      for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
-    });
-    load_prepared<D, KW, NRG>(ring + PREP_AT, GE, a, fh);
-    lds_barrier();                                 // every wave holds its operands
-    for (int k = first; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+  v8bf16 a8[NRG][K8 ? D / 32 : 1];
+  if constexpr (K8) {
+    if (ns > 0) {
+      // fp8 keys: the raw query rows, then the bf16 operands from them
+      issue_q_rows<D>(p, bh, GE, ring + PREP_AT, wave);
+      wait_vm<0>();
+      lds_barrier();
+      issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx, ring, wave);
+      k8_operands<D, NRG>(p, GE, ring + PREP_AT, a8);
+      lds_barrier();                               // every wave holds its operands
+      for (int k = 1; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+    }
+  } else {
+    if (ns > 0) {
+      // the preparation's inputs first, alone; the splits that do not
+      // overlap its scratch are issued once the queries are rotated
+      issue_prep<D, KW, NRG>(p, bh, GE, ring + PREP_AT, wave);
+      const int first = SEP ? min(ns, NST) : 1;
+      wait_vm<0>();
+      lds_barrier();
+      group_prep<D, KW, NRG>(p, GE, ring + PREP_AT, [&] {
+        for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+      });
+      load_prepared<D, KW, NRG>(ring + PREP_AT, GE, a, fh);
+      lds_barrier();                               // every wave holds its operands
+      for (int k = first; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+    }
   }
 
   for (int it = 0; it < ns; ++it) {
@@ -963,38 +1077,47 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
     for (int u = 0; u < KT; ++u) {
       const int tl = 16 * (wave + NW * u) + col;
       const uint8_t *kb = wb + u * REC * 16;
-      KeyTile<D, KW> kt;
-#pragma unroll
-      for (int q = 0; q <= KW; ++q) {
-        if constexpr (D == 128) {
-          const uint2 v = *reinterpret_cast<const uint2 *>(kb + (16 * q + col) * 16 + 8 * (kg >> 1));
-          kt.w[q][0] = v.x;
-          kt.w[q][D == 128 ? 1 : 0] = v.y;
-        } else {
-          kt.w[q][0] = *reinterpret_cast<const uint32_t *>(kb + col * REC + q * 8 + 4 * (kg >> 1));
-        }
-      }
-      kt.sc = *reinterpret_cast<const uint32_t *>(wb + SH::OFF_S + 64 * u + 4 * col);
-      v4i clm[NRG], cqj[NRG];
-      key_tile_mfma<D, KW, NRG>(kt, a, mask, NRG, clm, cqj);
       const bool valid = tl < n;
-      const float kn = kt.norm(), kgm = kt.gamma();
+      float lr[NRG];                               // the lane's heads' logits of key tl
+      if constexpr (K8) {
+        k8_tile_logits<D, NRG>(kb, a8, NRG, lr);
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg) lr[rg] *= p.k_scale;
+      } else {
+        KeyTile<D, KW> kt;
+#pragma unroll
+        for (int q = 0; q <= KW; ++q) {
+          if constexpr (D == 128) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(kb + (16 * q + col) * 16 + 8 * (kg >> 1));
+            kt.w[q][0] = v.x;
+            kt.w[q][D == 128 ? 1 : 0] = v.y;
+          } else {
+            kt.w[q][0] = *reinterpret_cast<const uint32_t *>(kb + col * REC + q * 8 + 4 * (kg >> 1));
+          }
+        }
+        kt.sc = *reinterpret_cast<const uint32_t *>(wb + SH::OFF_S + 64 * u + 4 * col);
+        v4i clm[NRG], cqj[NRG];
+        key_tile_mfma<D, KW, NRG>(kt, a, mask, NRG, clm, cqj);
+        const float kn = kt.norm(), kgm = kt.gamma();
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg) lr[rg] = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa);
+      }
       if constexpr (LOGITS) {
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg) {
           const int hl = 4 * rg + kg;
-          const float l = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa);
-          if (valid && hl < GE) p.logits[(b * n_q + kvh * G + p.h0 + hl) * p.max_ctx + sp * S + tl] = l;
+          if (valid && hl < GE) p.logits[(b * n_q + kvh * G + p.h0 + hl) * p.max_ctx + sp * S + tl] = lr[rg];
         }
         (void)lg; (void)nvv;
       } else {
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg) {
-          const float l = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa) * p.sm_scale;
+          const float l = lr[rg] * p.sm_scale;
           lg[u][rg] = (valid && sp * S + tl < lim[rg]) ? l : -INFINITY;
           mx[rg] = fmaxf(mx[rg], lg[u][rg]);
         }
-        const uint16_t nvb = *reinterpret_cast<const uint16_t *>(wb + SH::OFF_S + 64 * KT + 32 * u + 2 * col);
+        const uint16_t nvb =
+            *reinterpret_cast<const uint16_t *>(wb + SH::OFF_S + 16 * SH::KSU * KT + 32 * u + 2 * col);
         const float nvf = f16_bits_to_float(nvb);
         nvv[u] = valid ? nvf : 0.f;
         nvm = fmaxf(nvm, nvv[u]);
@@ -1303,6 +1426,9 @@ hipError_t launch_decode_da(const ScanParams &p0, int kw, int vw, hipStream_t st
       case 1: TQ_DS_V(1); break;
       case 2: TQ_DS_V(2); break;
       case 3: TQ_DS_V(3); break;
+      case kKeyFp8:
+        if constexpr (!APPEND) TQ_DS_V(kKeyFp8);
+        break;
       default: TQ_DS_V(4);
     }
 #undef TQ_DS_V

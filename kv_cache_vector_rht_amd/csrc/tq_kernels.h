@@ -22,6 +22,8 @@ struct EncodeParams {
 
 template <int D>
 hipError_t launch_encode_d(const EncodeParams &p, int w, bool key, hipStream_t st);
+// fp8 keys: codes[s][t][i] = e4m3fn(sat(x / scale)) for slots [t0, t0 + n_tok)
+hipError_t launch_encode_fp8(const EncodeParams &p, int d, float scale, hipStream_t st);
 
 // Logit scan and decode attention over the coded cache (one parameter block
 // for both; the logit scan leaves the value fields unset).
@@ -62,6 +64,8 @@ struct ScanParams {
   // to the tokens t <= pos0[b] + v / qgroup
   int32_t chunk, qgroup;
   const int32_t *pos0;
+  // fp8 keys (key width kKeyFp8): logit = k_scale * q . e4m3(k)
+  float k_scale;
   int kv_t;
   const void *k_new, *v_new;
   const float *kthr, *vthr;
@@ -83,6 +87,9 @@ hipError_t launch_append_decode_d(const ScanParams &p, int kw, int vw, hipStream
 constexpr int kLogitSplit = 256;
 constexpr int kAttendSplit = 512;
 constexpr int kDecodeMaxBlocks = 128;
+// Key width selecting fp8 key records (d bytes of OCP e4m3fn per key, no
+// scalars) in the decode kernels.
+constexpr int kKeyFp8 = 8;
 // Prefill: most query heads (chunk positions x heads per KV head) per call.
 constexpr int kPrefillMaxHeads = 1024;
 

@@ -62,7 +62,8 @@ __all__ = [
     "make_codebook", "hadamard", "rotate", "rotate_inverse",
     "encode", "pack_key_codes", "unpack_key_codes", "pack_value_codes",
     "unpack_value_codes", "prepare_query", "key_logits", "key_logits_mse", "pair_logits", "decode_attend",
-    "append_decode_attend", "prefill_attend", "rate_plan", "top_k", "search",
+    "append_decode_attend", "prefill_attend", "rate_plan", "e4m3_value", "e4m3_encode", "decode_attend_k8",
+    "top_k", "search",
     "QJL_CONST",
 ]
 
@@ -510,6 +511,78 @@ def append_decode_attend(q, k_new, v_new, k_signs, k_centroids, k_thresholds, sk
                         group)
     shape = lambda e: {k: v.reshape((B, Hkv) + v.shape[1:]) for k, v in e.items()}
     return out, cache, shape(ek), shape(ev)
+
+
+# --------------------------------------------------------------------------
+# fp8 keys (the k8v4 cache shape)
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """Value of OCP e4m3fn byte(s): sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent field 0 is subnormal (m/8 * 2^-6), the two
+    codes with all exponent and mantissa bits set are NaN, there is no
+    infinity."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def e4m3_encode(x, scale=1.0):
+    """e4m3fn bytes of x / scale: the quotient in float32 (both operands as
+    float32, correctly rounded), finite values beyond +-448 saturated, then
+    rounded to the nearest e4m3 value with ties to an even mantissa; NaN gives
+    0xff. Reading for the k8v4 preset the pages name (fp8 keys with 4-bit
+    values, "TurboQuantとは？仕組み・実測精度・2026年7月時点の実装状況", section
+    vLLM：–kv-cache-dtypeの切り替えだけで利用可能): the pages do not give the
+    fp8 format or its scaling; OCP e4m3fn with one per-tensor scale is the
+    common fp8 KV-cache form."""
+    y = (np.asarray(x, dtype=np.float32) / np.float32(scale)).astype(np.float64)
+    nan = np.isnan(y)
+    y = np.where(nan, 0.0, np.clip(y, -E4M3_MAX, E4M3_MAX))
+    sign = np.signbit(y)
+    a = np.abs(y)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)                          # subnormals share the quantum 2^-9
+    q = 2.0 ** (e - 3.0)
+    r = np.rint(a / q) * q                           # round half to even on the mantissa
+    # fields of the rounded magnitude
+    normal = r >= 2.0 ** -6
+    er = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    ef = np.where(normal, er + 7.0, 0.0)
+    mf = np.where(normal, (r / 2.0 ** er - 1.0) * 8.0, r / 2.0 ** -9)
+    code = (sign.astype(np.int64) << 7) | (ef.astype(np.int64) << 3) | mf.astype(np.int64)
+    return np.where(nan, 0xFF, code).astype(np.uint8)
+
+
+def decode_attend_k8(q, kcodes, k_scale, v_signs, v_centroids, vidx, vnhat, ctx_lens, sm_scale, group: int):
+    """Decode attention over fp8 keys and coded values: logit = k_scale *
+    q . e4m3(k) (no rotation on the key side), softmax, values as in
+    decode_attend. q [B, Hq, d]; kcodes uint8 [B*Hkv, T, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv = Hq // group
+    K = e4m3_value(kcodes) * float(k_scale)
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        T = int(ctx_lens[b])
+        if T <= 0:
+            continue
+        for hk in range(Hkv):
+            s = b * Hkv + hk
+            lg = q[b, hk * group:(hk + 1) * group] @ K[s, :T].T
+            z = sm_scale * lg
+            z = z - z.max(axis=1, keepdims=True)
+            a = np.exp(z)
+            a = a / a.sum(axis=1, keepdims=True)
+            out[b, hk * group:(hk + 1) * group] = rotate_inverse(a @ value_rows(vidx[s, :T], vnhat[s, :T],
+                                                                                v_centroids), v_signs)
+    return out
 
 
 # --------------------------------------------------------------------------

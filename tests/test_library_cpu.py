@@ -220,6 +220,32 @@ def test_prefill_validation():
     assert _prefill(k, v, batch=0) == tq.TQ_OK
 
 
+def test_fp8_key_calls_validation():
+    x = _p(FAKE)
+    enc = lambda **kw: tq.lib.tq_encode_fp8_keys(kw.get("x", x), kw.get("xt", tq.TQ_BF16), kw.get("d", 128), 2, 10,
+                                                 10 * 128, 128, kw.get("scale", 1.0), kw.get("codes", x),
+                                                 kw.get("cap", 32), kw.get("t0", 0), None)
+    assert enc(d=60) == tq.TQ_EINVAL
+    assert enc(scale=0.0) == tq.TQ_EINVAL
+    assert enc(scale=float("inf")) == tq.TQ_EINVAL
+    assert enc(t0=30) == tq.TQ_EINVAL                              # t0 + n_tok > cap
+    assert enc(xt=5) == tq.TQ_EINVAL
+    assert enc(codes=None) == tq.TQ_EINVAL
+    v = _codec(w=4, key=0, sketch=False)
+    ws = tq.decode_attend_workspace(2, 2, 4, 256, 128)
+    dec = lambda **kw: tq.lib.tq_decode_attend_k8(ctypes.byref(kw.get("vc", v)), _p(), tq.TQ_BF16, 2, 2,
+                                                  kw.get("group", 4), _p(), kw.get("ks", 1.0), _p(), _p(), 256, _p(),
+                                                  kw.get("max_ctx", 256), 0.1, _p(), tq.TQ_F32, _p(),
+                                                  kw.get("ws", ws), None)
+    assert dec(ks=-1.0) == tq.TQ_EINVAL
+    assert dec(vc=_codec()) == tq.TQ_EINVAL                        # a key codec where values are expected
+    assert dec(max_ctx=512) == tq.TQ_EINVAL
+    assert dec(group=33) == tq.TQ_EUNSUPPORTED
+    assert dec(ws=64) == tq.TQ_EINVAL
+    assert tq.lib.tq_decode_attend_k8(None, _p(), tq.TQ_BF16, 2, 2, 4, _p(), 1.0, _p(), _p(), 256, _p(), 256, 0.1,
+                                      _p(), tq.TQ_F32, _p(), ws, None) == tq.TQ_EINVAL
+
+
 def test_rate_plan_matches_oracle():
     for n in (1, 3, 22, 64):
         for bits in (1.0, 1.5, 2.5, 3.25, 3.5, 4.0, 4.5):

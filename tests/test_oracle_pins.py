@@ -692,6 +692,69 @@ def test_rate_plan_mixes_neighbouring_widths_evenly():
         O.rate_plan(5.5, 4, True)
 
 
+def test_e4m3_format_against_torch_and_brute_force():
+    """The e4m3fn decode table from its bit fields against torch's
+    float8_e4m3fn (all 256 codes, NaN at 0x7f and 0xff); encoding against
+    brute-force nearest-value search with ties to an even mantissa (every
+    midpoint between neighbouring values, random values across the range)
+    and against torch's cast, saturation at +-448, the scale applied to the
+    float32 quotient."""
+    import torch
+    codes = np.arange(256)
+    v = O.e4m3_value(codes)
+    t = torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(t)) and np.all(np.isnan(v) == np.isin(codes, [0x7F, 0xFF]))
+    np.testing.assert_array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+    finite = [(v[c], c) for c in range(256) if not np.isnan(v[c])]
+    pos = sorted({val for val, _ in finite if val >= 0})
+    mids = [(a + b) / 2 for a, b in zip(pos[:-1], pos[1:])]
+    rng = np.random.default_rng(3)
+    xs = np.array(mids + [-m for m in mids] + list(rng.standard_normal(3000) * 30) + [0.0, -0.0, 1e-9, -1e-9],
+                  dtype=np.float32)
+    got = O.e4m3_encode(xs)
+    for x, c in zip(xs.astype(np.float64), got):
+        # nearest value (a zero keeps the input's sign); among equal distances the even mantissa
+        cands = [(val, cc) for val, cc in finite if val != 0 or np.signbit(val) == np.signbit(x)]
+        dist = min(abs(val - x) for val, _ in cands)
+        ties = [cc for val, cc in cands if abs(val - x) == dist]
+        expect = min(ties, key=lambda cc: (cc & 1, cc))
+        assert int(c) == int(expect), (x, c, expect)
+    tc = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, tc)
+    np.testing.assert_array_equal(O.e4m3_encode(np.array([500.0, -1e30, 448.0], dtype=np.float32)), [0x7E, 0xFE, 0x7E])
+    assert O.e4m3_encode(np.array([np.nan], dtype=np.float32))[0] == 0xFF
+    # x / scale taken in float32
+    x = np.array([1.3, -7.7, 200.0], dtype=np.float32)
+    np.testing.assert_array_equal(O.e4m3_encode(x, 0.6), O.e4m3_encode(x / np.float32(0.6)))
+
+
+def test_decode_attend_k8_is_softmax_attention_over_decoded_keys():
+    """fp8-key attention against scipy's softmax over logits from the explicit
+    decoded key matrix; one token gives the value itself."""
+    B, Hkv, G, T, d = 2, 2, 3, 33, 64
+    rng = np.random.default_rng(21)
+    sv = rng.choice([-1.0, 1.0], size=d)
+    cv, tv = O.make_codebook(d, 4)
+    V = rng.standard_normal((B * Hkv, T, d))
+    ev = O.encode(V, sv, cv, tv)
+    K = rng.standard_normal((B * Hkv, T, d)) * 5
+    kc = O.e4m3_encode(K.astype(np.float32), 0.5)
+    q = rng.standard_normal((B, Hkv * G, d))
+    out = O.decode_attend_k8(q, kc, 0.5, sv, cv, ev["idx"], ev["nhat"], [T, 9], 0.3, G)
+    Rv = scipy.linalg.hadamard(d) @ np.diag(sv) / math.sqrt(d)
+    Vhat = ev["nhat"].astype(np.float64)[..., None] * (cv.astype(np.float64)[ev["idx"]] @ Rv)
+    Kd = O.e4m3_value(kc) * 0.5
+    for b, Tb in enumerate([T, 9]):
+        for h in range(Hkv * G):
+            sq = b * Hkv + h // G
+            a = scipy.special.softmax(0.3 * (Kd[sq, :Tb] @ q[b, h]))
+            np.testing.assert_allclose(out[b, h], a @ Vhat[sq, :Tb], rtol=1e-10, atol=1e-12)
+    out1 = O.decode_attend_k8(q, kc, 0.5, sv, cv, ev["idx"], ev["nhat"], [1, 1], 0.3, G)
+    for b in range(B):
+        for h in range(Hkv * G):
+            np.testing.assert_allclose(out1[b, h], Vhat[b * Hkv + h // G, 0], atol=1e-12)
+
+
 # ---------------------------------------------------------------- search
 
 
