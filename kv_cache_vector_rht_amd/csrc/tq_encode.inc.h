@@ -157,8 +157,13 @@ __host__ __device__ constexpr int mfma_row_coord(int r) { return 16 * ((r >> 2) 
 // 32 b + 16 h + i (b < D / 32, i < 16) of token 32 T + t in
 // v[(D / 2) T + 16 b + i]: 64 values per lane, each token split over the two
 // half-waves.
+// Threads per encode block: the block stages the codec once for its waves.
+// (Blocks of 512 threads, at 3 or 4 waves per SIMD, measured slower: fewer
+// resident waves per CU, or spills at 128 registers.)
+constexpr int kEncThreads = 256;
+
 template <int D, int W, bool KEY, int XT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void encode_kernel(EncodeParams p) {
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void encode_kernel(EncodeParams p) {
   constexpr int L = 1 << W;
   constexpr int NT = 128 / D;                // 32-token tiles per wave (1 or 2)
   constexpr int TPW = 32 * NT;               // tokens per wave
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       s_ha[idx] = w;
     }
   }
-  if (KEY) stage_sketch<D>(p.sketch, s_sk);
+  if (KEY) stage_sketch<D, kEncThreads>(p.sketch, s_sk);
   __syncthreads();
 
   const int lane = lane_id();
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 
 // ---------------------------------------------------------------- dispatch
 
-// Blocks of 256 threads of `kernel` that fit on the current device at once:
+// Blocks of kEncThreads threads of `kernel` that fit on the current device at once:
 // the grid is capped at that so that every block stages the codec once and
 // its waves loop over the token groups. `cached` belongs to one kernel.
 template <typename K>
@@ -475,7 +480,7 @@ static int64_t resident_blocks(K kernel, int (&cached)[64]) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 30;
   if (cached[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kEncThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 || cus <= 0)
       return 1 << 30;
     cached[dev] = per_cu * cus;
@@ -487,10 +492,11 @@ template <int D, int W, bool KEY, int XT>
 static void launch_encode_x(const EncodeParams &p, hipStream_t st) {
   static int cached[64] = {};
   const auto kernel = encode_kernel<D, W, KEY, XT>;
-  int64_t blocks = (p.n_waves + 3) / 4;
+  constexpr int wpb = kEncThreads / kWave;
+  int64_t blocks = (p.n_waves + wpb - 1) / wpb;
   const int64_t cap = resident_blocks(kernel, cached);
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kEncThreads), 0, st, p);
 }
 
 template <int D, int W, bool KEY>

@@ -62,17 +62,18 @@ __device__ __forceinline__ uint32_t nonneg_bits(const v16f &c) {
 }
 
 // Stage the fp16 sketch [D][D] in LDS with rows padded by 8 halves. The
-// block has 256 threads; all loads are issued before the first store.
-template <int D>
+// block has THREADS threads; all loads are issued before the first store.
+template <int D, int THREADS>
 __device__ __forceinline__ void stage_sketch(const uint16_t *__restrict__ sketch, uint16_t *s_sk) {
   constexpr int RP = D + 8;
-  constexpr int N = D * D / 8 / 256;         // 16-byte pieces per thread (8 or 2)
+  constexpr int N = D * D / 8 / THREADS;     // 16-byte pieces per thread
+  static_assert(N * THREADS == D * D / 8, "sketch pieces per thread");
   uint4 v[N];
 #pragma unroll
-  for (int k = 0; k < N; ++k) v[k] = reinterpret_cast<const uint4 *>(sketch)[k * 256 + threadIdx.x];
+  for (int k = 0; k < N; ++k) v[k] = reinterpret_cast<const uint4 *>(sketch)[k * THREADS + threadIdx.x];
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    const int e = k * 256 + threadIdx.x;
+    const int e = k * THREADS + threadIdx.x;
     const int row = e / (D / 8), c8 = e % (D / 8);
     // column unit 4 a + 2 h + b (coordinates 32 a + 16 h + 8 b ..) goes to
     // position (D / 16) h + 2 a + b, the K order of the encoder's lanes
