@@ -178,6 +178,31 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
 size_t tq_logits_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d);
 
 /*
+ * tq_logits in two calls, for callers that can run the query preparation
+ * beside other work (e.g. on a second stream while the step's keys are
+ * encoded): tq_prepare_queries does the preparation that every scan block
+ * of tq_logits otherwise does itself (q' = R q, p = S q', their fixed-point
+ * MFMA operands and per-head constants) once per (batch, kv-head, chunk of 8
+ * heads) and stores it in `prepared`; tq_logits_prepared then scans the keys
+ * with it and writes the same logits, bit for bit, as tq_logits.
+ *   prepared  device, >= tq_prepared_queries_bytes(...) bytes, 16-byte
+ *             aligned; an opaque record per (batch, kv-head, head chunk),
+ *             valid for the codec and the queries it was prepared from
+ * The other arguments and errors are those of tq_logits (the queries are
+ * read by tq_prepare_queries only). tq_prepared_queries_bytes returns 0 for
+ * invalid arguments.
+ */
+size_t tq_prepared_queries_bytes(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d,
+                                 int32_t lm_bits);
+tq_status tq_prepare_queries(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch,
+                             int32_t n_kv_heads, int32_t group, void *prepared, size_t bytes,
+                             void *stream);
+tq_status tq_logits_prepared(const tq_codec *kc, const void *prepared, size_t bytes, int32_t batch,
+                             int32_t n_kv_heads, int32_t group, const uint8_t *kcodes,
+                             const uint16_t *kscalars, int64_t cap, int64_t n_keys, float *logits,
+                             void *stream);
+
+/*
  * The MSE-only ablation of tq_logits: the estimator's first term alone,
  *   logit = n * sum_i q'_i c[idx_i],
  * from the same key records (their sign plane and residual norm are read

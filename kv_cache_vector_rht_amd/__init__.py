@@ -59,6 +59,9 @@ def _load():
         "tq_logits": ([CP, P, I32, I32, I32, I32, P, P, I64, I64, P, P, SZ, P], I32),
         "tq_logits_workspace": ([I32, I32, I32, I32], SZ),
         "tq_logits_mse": ([CP, P, I32, I32, I32, I32, P, P, I64, I64, P, P, SZ, P], I32),
+        "tq_prepared_queries_bytes": ([I32, I32, I32, I32, I32], SZ),
+        "tq_prepare_queries": ([CP, P, I32, I32, I32, I32, P, SZ, P], I32),
+        "tq_logits_prepared": ([CP, P, SZ, I32, I32, I32, P, P, I64, I64, P, P], I32),
         "tq_decode_attend": ([CP, CP, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
         "tq_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
         "tq_append_decode_attend": ([CP, CP, P, I32, P, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P,
@@ -99,7 +102,8 @@ def load():
     return lib.tq_status_string
 
 EXPORTED = ("tq_make_codebook", "tq_rate_plan", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
-            "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_decode_attend", "tq_decode_attend_workspace",
+            "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_prepared_queries_bytes", "tq_prepare_queries",
+            "tq_logits_prepared", "tq_decode_attend", "tq_decode_attend_workspace",
             "tq_append_decode_attend", "tq_append_decode_attend_workspace", "tq_prefill_attend",
             "tq_prefill_attend_workspace", "tq_encode_fp8_keys", "tq_decode_attend_k8",
             "tq_topk", "tq_topk_workspace", "tq_status_string", "tq_last_error")
@@ -290,6 +294,39 @@ def decode_attend(kc: Codec, vc: Codec, q: torch.Tensor, kcodes, kscalars, vcode
                               _ptr(ctx_lens), max_ctx, float(sm_scale), _ptr(out), ot, _ptr(workspace),
                               workspace.numel(), _stream(stream))
     _check(st, "tq_decode_attend")
+    return out
+
+
+def prepared_queries_bytes(batch: int, n_kv_heads: int, group: int, d: int, lm_bits: int) -> int:
+    return int(lib.tq_prepared_queries_bytes(batch, n_kv_heads, group, d, lm_bits))
+
+
+def prepare_queries(codec: Codec, q: torch.Tensor, n_kv_heads: int, group: int,
+                    prepared: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The query preparation of tq_logits alone: an opaque uint8 buffer for logits_prepared."""
+    q = q.contiguous()
+    batch = q.shape[0]
+    need = prepared_queries_bytes(batch, n_kv_heads, group, codec.d, codec.lm_bits)
+    if prepared is None:
+        prepared = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    cs = codec.struct()
+    st = lib.tq_prepare_queries(ctypes.byref(cs), _ptr(q), _DTYPE[q.dtype], batch, n_kv_heads, group, _ptr(prepared),
+                                prepared.numel(), _stream(stream))
+    _check(st, "tq_prepare_queries")
+    return prepared
+
+
+def logits_prepared(codec: Codec, prepared: torch.Tensor, batch: int, codes: torch.Tensor, scalars: torch.Tensor,
+                    n_kv_heads: int, group: int, n_keys: int, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """tq_logits from prepared queries: float32 [batch, n_kv_heads*group, n_keys]."""
+    cap = scalars.shape[1]
+    if out is None:
+        out = torch.empty((batch, n_kv_heads * group, n_keys), dtype=torch.float32, device=codes.device)
+    cs = codec.struct()
+    st = lib.tq_logits_prepared(ctypes.byref(cs), _ptr(prepared), prepared.numel(), batch, n_kv_heads, group,
+                                _ptr(codes), _ptr(scalars), cap, n_keys, _ptr(out), _stream(stream))
+    _check(st, "tq_logits_prepared")
     return out
 
 

@@ -336,6 +336,62 @@ static tq_status logits_call(const char *fn, int qjl, const tq_codec *kc, const 
   return hip_status(e, fn);
 }
 
+size_t tq_prepared_queries_bytes(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d, int32_t lm_bits) {
+  if (batch < 0 || n_kv_heads < 0 || group < 0 || (d != 64 && d != 128) || lm_bits < 1 || lm_bits > 4) return 0;
+  return align_up(static_cast<size_t>(batch) * n_kv_heads * ((group + 7) / 8) *
+                  static_cast<size_t>(tq::prepared_stride(d, lm_bits)));
+}
+
+tq_status tq_prepare_queries(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
+                             int32_t group, void *prepared, size_t bytes, void *stream) {
+  const char *fn = "tq_prepare_queries";
+  tq_status s = check_codec(kc, 1, fn);
+  if (s != TQ_OK) return s;
+  if (!dtype_ok(qt)) return fail(TQ_EINVAL, "%s: bad query dtype", fn);
+  if (batch < 0 || n_kv_heads < 0 || group < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (batch == 0 || n_kv_heads == 0 || group == 0) return ok();
+  if (!q || !prepared) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  const size_t need = tq_prepared_queries_bytes(batch, n_kv_heads, group, kc->d, kc->lm_bits);
+  if (bytes < need) return fail(TQ_EINVAL, "%s: prepared buffer %zu < %zu bytes", fn, bytes, need);
+  if (reinterpret_cast<uintptr_t>(prepared) % 16) return fail(TQ_EINVAL, "%s: prepared buffer not 16-byte aligned", fn);
+  if (!staged_inputs_aligned(kc, q)) return fail(TQ_EINVAL, "%s: q, signs and sketch must be 16-byte aligned", fn);
+  tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, nullptr, nullptr, 0, 0, tq::kLogitSplit);
+  sp.prepared_w = static_cast<uint8_t *>(prepared);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = kc->d == 64 ? tq::launch_prepare_d<64>(sp, kc->lm_bits, st) : tq::launch_prepare_d<128>(sp, kc->lm_bits, st);
+  return hip_status(e, fn);
+}
+
+tq_status tq_logits_prepared(const tq_codec *kc, const void *prepared, size_t bytes, int32_t batch,
+                             int32_t n_kv_heads, int32_t group, const uint8_t *kcodes, const uint16_t *kscalars,
+                             int64_t cap, int64_t n_keys, float *logits, void *stream) {
+  const char *fn = "tq_logits_prepared";
+  tq_status s = check_codec(kc, 1, fn);
+  if (s != TQ_OK) return s;
+  if (batch < 0 || n_kv_heads < 0 || group < 0 || n_keys < 0 || cap < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (n_keys > cap) return fail(TQ_EINVAL, "%s: n_keys > cap", fn);
+  if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
+  if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!seq_offsets_fit(cap, (kc->lm_bits + 1) * kc->d / 8))
+    return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
+  if (batch == 0 || n_kv_heads == 0 || group == 0 || n_keys == 0) return ok();
+  if (!prepared || !kcodes || !kscalars || !logits) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  const size_t need = tq_prepared_queries_bytes(batch, n_kv_heads, group, kc->d, kc->lm_bits);
+  if (bytes < need) return fail(TQ_EINVAL, "%s: prepared buffer %zu < %zu bytes", fn, bytes, need);
+  if (reinterpret_cast<uintptr_t>(prepared) % 16) return fail(TQ_EINVAL, "%s: prepared buffer not 16-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(kcodes) % 16 || reinterpret_cast<uintptr_t>(kscalars) % 16)
+    return fail(TQ_EINVAL, "%s: kcodes and kscalars must be 16-byte aligned", fn);
+  tq::ScanParams sp = scan_params(kc, nullptr, TQ_F32, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys,
+                                  tq::kLogitSplit);
+  sp.logits = logits;
+  sp.prepared = static_cast<const uint8_t *>(prepared);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = kc->d == 64 ? tq::launch_logits_prepared_d<64>(sp, kc->lm_bits, st)
+                             : tq::launch_logits_prepared_d<128>(sp, kc->lm_bits, st);
+  return hip_status(e, fn);
+}
+
 tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
                     int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap, int64_t n_keys,
                     float *logits, void *workspace, size_t ws_bytes, void *stream) {

@@ -938,7 +938,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
 //  4. refills the stage buffer with the split NST (ring depth) ahead.
 // Decode writes the block's partial {m, l, acc} to the workspace;
 // merge_kernel combines them.
-template <int D, int KW, int VW, int NRG, bool LOGITS, bool APPEND = false>
+template <int D, int KW, int VW, int NRG, bool LOGITS, bool APPEND = false, bool PREPARED = false>
 __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int SPLIT = LOGITS ? kLogitSplit : attend_split<D, KW, VW, NRG>();
   using SH = ScanShape<D, KW, VW, LOGITS, SPLIT>;
@@ -958,6 +958,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int LDS_BUDGET = 160 * 1024 - 2048;
   constexpr int NST_L = (LDS_BUDGET - PS_BYTES) / SB < 6 ? (LDS_BUDGET - PS_BYTES) / SB : 6;
   constexpr bool SEP = LOGITS && NST_L >= 3;
+  static_assert(!PREPARED || (LOGITS && SEP), "prepared queries: the logit scan with its own preparation region");
   constexpr int NST = SEP ? NST_L : (SPLIT == 512 ? 2 : kStages);
   constexpr int PREP_AT = SEP ? NST * SB : SB;
   constexpr int RING = (NST * SB > PREP_AT + PS_BYTES) ? NST * SB : PREP_AT + PS_BYTES;
@@ -1042,6 +1043,20 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
       k8_operands<D, NRG>(p, GE, ring + PREP_AT, a8);
       lds_barrier();                               // every wave holds its operands
       for (int k = 1; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+    }
+  } else if constexpr (PREPARED) {
+    if (ns > 0) {
+      // the prepared operand fragments and head constants into the
+      // preparation's region (separate from the stages), then every stage
+      const uint8_t *src = p.prepared + (bh * p.n_hchunks + p.h0 / 8) * prepared_stride(D, KW);
+      constexpr int FW = NRG * NMF;                  // 1 KB fragments: 64 lanes x 16 bytes
+      for (int f = wave; f < FW; f += NW) dma16_at(src + (f * kWave + lane) * 16, ring + PREP_AT + f * 1024);
+      if (wave == 0 && lane < 8)
+        dma16_at(src + prepared_stride(D, KW) - 128 + 16 * lane, ring + PREP_AT + PS::SCON);
+      wait_vm<0>();
+      lds_barrier();
+      for (int k = 0; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+      load_prepared<D, KW, NRG>(ring + PREP_AT, GE, a, fh);
     }
   } else {
     if (ns > 0) {
@@ -1289,6 +1304,35 @@ __global__ __launch_bounds__(4 * D) void logits_kernel(ScanParams p) {
   scan_block<D, KW, 1, NRG, true>(p);
 }
 
+// The logit scan from prepared queries (tq_prepare_queries).
+template <int D, int KW, int NRG>
+__global__ __launch_bounds__(4 * D) void logits_prepared_kernel(ScanParams p) {
+  scan_block<D, KW, 1, NRG, true, false, true>(p);
+}
+
+// The query preparation of one (group, head chunk) alone, as a scan block
+// does it, written out as a record of prepared_stride bytes: the operand
+// fragments (as the scan blocks hold them in LDS) and the heads' constants.
+template <int D, int KW, int NRG>
+__global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
+  using PS = PrepShape<D, KW, NRG>;
+  __shared__ __attribute__((aligned(1024))) uint8_t scratch[PS::BYTES];
+  const int GE = min(4 * NRG, p.group - p.h0);
+  const int64_t bh = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  issue_prep<D, KW, NRG>(p, bh, GE, scratch, wave);
+  wait_vm<0>();
+  lds_barrier();
+  group_prep<D, KW, NRG>(p, GE, scratch, [] {});   // ends with a barrier
+  uint8_t *dst = p.prepared_w + (bh * p.n_hchunks + p.h0 / 8) * prepared_stride(D, KW);
+  constexpr int FB = NRG * PS::NMF * 1024;
+  for (int off = static_cast<int>(threadIdx.x) * 16; off < FB; off += 4 * D * 16)
+    *reinterpret_cast<uint4 *>(dst + off) = *reinterpret_cast<const uint4 *>(scratch + off);
+  if (threadIdx.x < 8)
+    *reinterpret_cast<uint4 *>(dst + prepared_stride(D, KW) - 128 + 16 * threadIdx.x) =
+        *reinterpret_cast<const uint4 *>(scratch + PS::SCON + 16 * threadIdx.x);
+}
+
 // Merge of the split partials of one (batch, kv-head) group and head chunk
 // (8 heads): log-sum-exp weights over the blocks, division by the softmax
 // sum, inverse rotation out = diag(s_v) H acc / sqrt(D), store. A kernel of
@@ -1376,32 +1420,58 @@ static void launch_decode_kv(const ScanParams &p, dim3 grid, hipStream_t st) {
   }
 }
 
-template <int D, int KW>
+// MODE 0: the logit scan, 1: from prepared queries, 2: the preparation alone.
+template <int D, int KW, int MODE>
 static void launch_logits_k(const ScanParams &p, dim3 grid, hipStream_t st) {
   dim3 block(4 * D);
-  if (p.group - p.h0 > 4) hipLaunchKernelGGL((logits_kernel<D, KW, 2>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((logits_kernel<D, KW, 1>), grid, block, 0, st, p);
+  const bool two = p.group - p.h0 > 4;
+  if constexpr (MODE == 0) {
+    if (two) hipLaunchKernelGGL((logits_kernel<D, KW, 2>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((logits_kernel<D, KW, 1>), grid, block, 0, st, p);
+  } else if constexpr (MODE == 1) {
+    if (two) hipLaunchKernelGGL((logits_prepared_kernel<D, KW, 2>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((logits_prepared_kernel<D, KW, 1>), grid, block, 0, st, p);
+  } else {
+    dim3 g1(1, grid.y);
+    if (two) hipLaunchKernelGGL((prep_kernel<D, KW, 2>), g1, block, 0, st, p);
+    else hipLaunchKernelGGL((prep_kernel<D, KW, 1>), g1, block, 0, st, p);
+  }
 }
 
 // Head chunks of 8 heads: every launch reads the keys (and values) once for
 // its chunk.
-template <int D>
-hipError_t launch_logits_d(const ScanParams &p0, int kw, hipStream_t st) {
-  if (p0.batch == 0 || p0.n_kv == 0 || p0.max_ctx == 0) return hipSuccess;
+template <int D, int MODE>
+hipError_t launch_logits_m(const ScanParams &p0, int kw, hipStream_t st) {
+  if (p0.batch == 0 || p0.n_kv == 0 || (MODE != 2 && p0.max_ctx == 0)) return hipSuccess;
   dim3 grid(static_cast<uint32_t>(p0.nb), static_cast<uint32_t>(p0.batch) * p0.n_kv);
   for (int hc = 0; hc < p0.n_hchunks; ++hc) {
     ScanParams p = p0;
     p.h0 = 8 * hc;
     switch (kw) {
-      case 1: launch_logits_k<D, 1>(p, grid, st); break;
-      case 2: launch_logits_k<D, 2>(p, grid, st); break;
-      case 3: launch_logits_k<D, 3>(p, grid, st); break;
-      default: launch_logits_k<D, 4>(p, grid, st);
+      case 1: launch_logits_k<D, 1, MODE>(p, grid, st); break;
+      case 2: launch_logits_k<D, 2, MODE>(p, grid, st); break;
+      case 3: launch_logits_k<D, 3, MODE>(p, grid, st); break;
+      default: launch_logits_k<D, 4, MODE>(p, grid, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_logits_d(const ScanParams &p, int kw, hipStream_t st) {
+  return launch_logits_m<D, 0>(p, kw, st);
+}
+
+template <int D>
+hipError_t launch_logits_prepared_d(const ScanParams &p, int kw, hipStream_t st) {
+  return launch_logits_m<D, 1>(p, kw, st);
+}
+
+template <int D>
+hipError_t launch_prepare_d(const ScanParams &p, int kw, hipStream_t st) {
+  return launch_logits_m<D, 2>(p, kw, st);
 }
 
 // Head chunks of 8 heads, then the merge. APPEND: nb + 1 blocks per group,

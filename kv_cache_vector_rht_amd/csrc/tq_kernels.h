@@ -66,6 +66,10 @@ struct ScanParams {
   const int32_t *pos0;
   // fp8 keys (key width kKeyFp8): logit = k_scale * q . e4m3(k)
   float k_scale;
+  // prepared queries: one record of prepared_stride bytes per (group, head
+  // chunk), written by the preparation kernel, read by the prepared scan
+  const uint8_t *prepared;
+  uint8_t *prepared_w;
   int kv_t;
   const void *k_new, *v_new;
   const float *kthr, *vthr;
@@ -77,6 +81,11 @@ struct ScanParams {
 
 template <int D>
 hipError_t launch_logits_d(const ScanParams &p, int kw, hipStream_t st);
+// the query preparation alone (into p.prepared_w), and the logit scan from it
+template <int D>
+hipError_t launch_prepare_d(const ScanParams &p, int kw, hipStream_t st);
+template <int D>
+hipError_t launch_logits_prepared_d(const ScanParams &p, int kw, hipStream_t st);
 template <int D>
 hipError_t launch_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st);
 template <int D>

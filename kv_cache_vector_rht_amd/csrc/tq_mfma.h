@@ -51,6 +51,13 @@ template <> struct Basis<4> {
 
 __host__ __device__ constexpr int basis_size(int w) { return w == 1 ? 1 : w == 2 ? 2 : w == 3 ? 4 : 8; }
 
+// Bytes of one (group, head chunk) record of prepared queries: the MFMA
+// operand fragments of up to two row groups of 4 heads ((basis + sign plane)
+// x D/64 fragments of 64 lanes x 16 bytes each) and 8 heads' constants.
+__host__ __device__ constexpr int64_t prepared_stride(int d, int w) {
+  return 2LL * (basis_size(w) + 1) * (d / 64) * 1024 + 128;
+}
+
 __device__ __forceinline__ int basis_mask(int w, int s) {
   // same tables as Basis<W>::M, for runtime use
   if (w <= 2) return 1 << s;

@@ -246,6 +246,27 @@ def test_fp8_key_calls_validation():
                                       _p(), tq.TQ_F32, _p(), ws, None) == tq.TQ_EINVAL
 
 
+def test_prepared_logits_validation():
+    k = _codec()
+    cs = ctypes.byref(k)
+    need = tq.prepared_queries_bytes(2, 8, 4, 128, 2)
+    assert need == 2 * 8 * 1 * (2 * (2 + 1) * 2 * 1024 + 128)
+    assert tq.prepared_queries_bytes(2, 8, 4, 96, 2) == 0
+    prep = lambda **kw: tq.lib.tq_prepare_queries(cs, _p(), kw.get("qt", tq.TQ_BF16), 2, 8, kw.get("group", 4),
+                                                  kw.get("buf", _p()), kw.get("bytes", need), None)
+    assert prep(bytes=need - 1) == tq.TQ_EINVAL
+    assert prep(buf=None) == tq.TQ_EINVAL
+    assert prep(qt=9) == tq.TQ_EINVAL
+    assert prep(group=33) == tq.TQ_EUNSUPPORTED
+    assert prep(group=0) == tq.TQ_OK
+    lg = lambda **kw: tq.lib.tq_logits_prepared(cs, kw.get("buf", _p()), kw.get("bytes", need), 2, 8, 4, _p(), _p(),
+                                                kw.get("cap", 256), kw.get("n", 256), _p(), None)
+    assert lg(bytes=need - 1) == tq.TQ_EINVAL
+    assert lg(n=300) == tq.TQ_EINVAL                                    # n_keys > cap
+    assert lg(cap=250, n=200) == tq.TQ_EINVAL
+    assert lg(n=0) == tq.TQ_OK
+
+
 def test_rate_plan_matches_oracle():
     for n in (1, 3, 22, 64):
         for bits in (1.0, 1.5, 2.5, 3.25, 3.5, 4.0, 4.5):
