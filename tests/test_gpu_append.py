@@ -218,3 +218,56 @@ def test_append_steps_replayed_in_a_hip_graph():
         say(f"   step {it}: lens {lens} worst err/tol {worst}")
         ctx.add_(1)
         lens = [x + 1 for x in lens]
+
+
+def test_prompt_chunks_then_decode_steps():
+    """A serving sequence end to end: a prompt written by chunks
+    (tq_encode_kv of each chunk's keys and values, then tq_prefill_attend of
+    its queries), then decode steps that append one token each; every
+    output against the oracle over the cache the GPU holds at that point."""
+    d, kw, vw, group, batch, n_kv = 128, 3, 4, 4, 2, 2
+    chunks, C, steps = 3, 24, 3
+    cap = 128
+    n_q = n_kv * group
+    say(f"prompt of {chunks} chunks of {C} tokens, then {steps} decode steps (batch {batch})")
+    kc, vc = key_codec(2100, d, kw), value_codec(2101, d, vw)
+    kcodes, kscal = tq.alloc_key_cache(batch * n_kv, cap, kc.gpu)
+    vcodes, vscal = tq.alloc_value_cache(batch * n_kv, cap, vc.gpu)
+    scale = 1.0 / math.sqrt(d)
+    T = chunks * C + steps
+
+    def oracle_cache():
+        c = _snapshot(kcodes, kscal, vcodes, vscal)
+        kidx, ksig = O.unpack_key_codes(c["kcodes"], d, kw)
+        ks = c["kscal"].view(np.float16)
+        vidx = O.unpack_value_codes(c["vcodes"].view(np.uint32), cap)
+        return (kidx, ksig, ks[..., 0], ks[..., 1], vidx, c["vscal"].view(np.float16))
+
+    for ch in range(chunks):
+        t0 = ch * C
+        k = _randn((batch * n_kv, C, d), 300 + ch, scale_channels=True).to(torch.bfloat16)
+        v = _randn((batch * n_kv, C, d), 400 + ch).to(torch.bfloat16)
+        q = _randn((batch, C, n_q, d), 500 + ch).to(torch.bfloat16)
+        tq.encode_kv(kc.gpu, k.to("cuda"), kcodes, kscal, t0=t0)
+        tq.encode_kv(vc.gpu, v.to("cuda"), vcodes, vscal, t0=t0)
+        pos0 = torch.full((batch,), t0, dtype=torch.int32, device="cuda")
+        out = tq.prefill_attend(kc.gpu, vc.gpu, q.to("cuda"), kcodes, kscal, vcodes, vscal, pos0, n_kv_heads=n_kv,
+                                group=group, max_ctx=T, sm_scale=scale)
+        torch.cuda.synchronize()
+        kidx, ksig, kn, kg, vidx, vn = oracle_cache()
+        ref = O.prefill_attend(to_f64(q), kc.signs, kc.centroids, kc.sketch, kidx, ksig, kn, kg, vc.signs,
+                               vc.centroids, vidx, vn, [t0] * batch, scale, group)
+        say(f"   chunk {ch}: worst err/tol {assert_close(out.cpu().numpy(), ref, 'prefill chunk')}")
+    for st in range(steps):
+        lens = [chunks * C + st + 1] * batch
+        q = _randn((batch, n_q, d), 600 + st).to(torch.bfloat16)
+        k_new = _randn((batch, n_kv, d), 700 + st, scale_channels=True).to(torch.bfloat16)
+        v_new = _randn((batch, n_kv, d), 800 + st).to(torch.bfloat16)
+        before = _snapshot(kcodes, kscal, vcodes, vscal)
+        out = tq.append_decode_attend(kc.gpu, vc.gpu, q.to("cuda"), k_new.to("cuda"), v_new.to("cuda"), kcodes, kscal,
+                                      vcodes, vscal, torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                                      n_kv_heads=n_kv, group=group, max_ctx=T, sm_scale=scale)
+        torch.cuda.synchronize()
+        after = _snapshot(kcodes, kscal, vcodes, vscal)
+        worst = _check_step(kc, vc, kw, vw, d, n_kv, group, q, k_new, v_new, lens, before, after, out, scale)
+        say(f"   step {st}: worst err/tol {worst}")
