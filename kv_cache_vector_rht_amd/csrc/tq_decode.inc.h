@@ -1334,73 +1334,54 @@ __global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
 }
 
 // Merge of the split partials of one (batch, kv-head) group and head chunk
-// (8 heads): log-sum-exp weights over the blocks, division by the softmax
-// sum, inverse rotation out = diag(s_v) H acc / sqrt(D), store. A kernel of
+// (8 heads), one wave per head: log-sum-exp weights over the blocks, division
+// by the softmax sum, inverse rotation out = diag(s_v) H acc / sqrt(D) (the
+// wave butterflies, lane l holding coordinates l + 64 e), store. A kernel of
 // its own: the partials are visible to it without any device-wide fence
 // (inside one kernel that fence writes back every XCD's L2 per block).
+constexpr int kMergeThreads = 8 * kWave;
+
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(ScanParams p) {
-  __shared__ float ob[8][D];
-  __shared__ float se[8][kDecodeMaxBlocks + 1];
-  __shared__ float sL[8];
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(ScanParams p) {
+  constexpr int E = D / kWave;
   const int G = p.group;
-  const int n_q = p.n_kv * G;
+  const int hl = static_cast<int>(threadIdx.x) / kWave;   // head of the chunk
   const int h0 = 8 * blockIdx.x;
-  const int GE = min(8, G - h0);
+  if (hl >= min(8, G - h0)) return;                        // (no block barrier below)
+  const int lane = lane_id();
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.n_kv;
   const int64_t kvh = bh % p.n_kv;
-  const int nb = p.nb + p.append;                  // partials per group
-  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  const float *pbase = p.partials + bh * nb * G * (D + 2);
+  const int nb = p.nb + p.append;                          // partials per group
   const int64_t pstride = static_cast<int64_t>(G) * (D + 2);
-  for (int hl = wave; hl < GE; hl += 4) {
-    float M = -INFINITY;
-    for (int j = lane; j < nb; j += kWave) M = fmaxf(M, pbase[j * pstride + (h0 + hl) * (D + 2)]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int j = lane; j < nb; j += kWave) {
-      const float m = pbase[j * pstride + (h0 + hl) * (D + 2)];
-      const float e = (m == -INFINITY) ? 0.f : __expf(m - M);
-      se[hl][j] = e;
-      L = fmaf(pbase[j * pstride + (h0 + hl) * (D + 2) + 1], e, L);
-    }
-    L = wave_sum(L);
-    if (lane == 0) sL[hl] = L;
-  }
-  __syncthreads();
-  for (int e = tid; e < GE * D; e += 256) {
-    const int hl = e / D, i = e % D;
-    const float *src = pbase + (h0 + hl) * (D + 2) + 2 + i;
-    float acc = 0.f;
-    int j = 0;
-    for (; j + 8 <= nb; j += 8) {
-      float v[8];
+  const float *ph = p.partials + bh * nb * pstride + (h0 + hl) * (D + 2);
+  float M = -INFINITY;
+  for (int j = lane; j < nb; j += kWave) M = fmaxf(M, ph[j * pstride]);
+  M = wave_max(M);
+  float L = 0.f;
+  float acc[E];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = src[(j + k) * pstride];
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int j = 0; j < nb; ++j) {
+    const float m = ph[j * pstride];
+    const float w = (m == -INFINITY) ? 0.f : __expf(m - M);
+    L = fmaf(ph[j * pstride + 1], w, L);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc = fmaf(v[k], se[hl][j + k], acc);
-    }
-    for (; j < nb; ++j) acc = fmaf(src[j * pstride], se[hl][j], acc);
-    ob[hl][i] = (sL[hl] > 0.f) ? acc / sL[hl] : 0.f;
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(ph[j * pstride + 2 + lane + kWave * e], w, acc[e]);
   }
-  __syncthreads();
-  for (int hs = 1; hs < D; hs <<= 1) {
-    for (int e = tid; e < GE * D / 2; e += 256) {
-      const int hl = e / (D / 2);
-      const int r = e % (D / 2);
-      const int j = (r / hs) * 2 * hs + (r % hs);
-      const float x = ob[hl][j];
-      const float y = ob[hl][j + hs];
-      ob[hl][j] = x + y;
-      ob[hl][j + hs] = x - y;
-    }
-    __syncthreads();
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = (L > 0.f) ? acc[e] / L : 0.f;
+  if constexpr (E == 2) {
+    const float a0 = x[0] + x[1], a1 = x[0] - x[1];
+    x[0] = a0;
+    x[1] = a1;
   }
-  for (int e = tid; e < GE * D; e += 256) {
-    const int hl = e / D, j = e % D;
-    const float o = ob[hl][j] * p.vsigns[j] * (1.0f / sqrtf(static_cast<float>(D)));
-    const int64_t row = query_row(p, b, kvh, h0 + hl);
+  const int64_t row = query_row(p, b, kvh, h0 + hl);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + kWave * e;
+    const float o = wave_fwht(x[e], lane) * p.vsigns[j] * (1.0f / sqrtf(static_cast<float>(D)));
     if (p.out_t == 0) static_cast<float *>(p.out)[row * D + j] = o;
     else static_cast<uint16_t *>(p.out)[row * D + j] = float_to_bf16_bits(o);
   }
@@ -1505,7 +1486,8 @@ hipError_t launch_decode_da(const ScanParams &p0, int kw, int vw, hipStream_t st
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(static_cast<uint32_t>(p0.n_hchunks), groups), dim3(256), 0, st, p0);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(static_cast<uint32_t>(p0.n_hchunks), groups), dim3(kMergeThreads), 0, st,
+                     p0);
   return hipGetLastError();
 }
 
