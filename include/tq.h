@@ -22,7 +22,8 @@
  *     TQ_EINVAL for a malformed argument (null pointer, negative size,
  *     workspace too small, inconsistent shapes), TQ_EUNSUPPORTED for a
  *     well-formed request this build does not implement (a head dimension
- *     other than 64 or 128, more than 4 Lloyd-Max bits, ...). A failed
+ *     other than 64 or 128, more than 4 Lloyd-Max bits, more than 65535
+ *     (batch, kv-head) sequences in one logit or attention call, ...). A failed
  *     launch returns TQ_EHIP. tq_last_error() then describes the failure.
  *   - Data values are not inspected: NaN/Inf in inputs propagate, and a norm
  *     above 65504 is stored as fp16 infinity.

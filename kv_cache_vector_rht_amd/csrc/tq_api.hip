@@ -83,6 +83,13 @@ bool seq_offsets_fit(int64_t cap, int bytes_per_token) {
   return cap * static_cast<int64_t>(bytes_per_token) < (static_cast<int64_t>(1) << 32);
 }
 
+// The scan, merge and preparation launches put the (batch, kv-head)
+// sequences on the grid's y dimension.
+constexpr int64_t kMaxSequences = 65535;
+bool sequences_fit(int32_t batch, int32_t n_kv_heads) {
+  return static_cast<int64_t>(batch) * n_kv_heads <= kMaxSequences;
+}
+
 // The scan kernels stage the queries, signs and sketch with 16-byte loads.
 bool staged_inputs_aligned(const tq_codec *kc, const void *q) {
   return reinterpret_cast<uintptr_t>(q) % 16 == 0 && reinterpret_cast<uintptr_t>(kc->signs) % 16 == 0 &&
@@ -146,6 +153,8 @@ tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_c
   if (max_ctx > cap) return fail(TQ_EINVAL, "%s: max_ctx > cap", fn);
   if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!sequences_fit(batch, n_kv_heads))
+    return fail(TQ_EUNSUPPORTED, "%s: batch*n_kv_heads above %lld", fn, static_cast<long long>(kMaxSequences));
   if (chunk < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (static_cast<int64_t>(chunk) * group > tq::kPrefillMaxHeads)
     return fail(TQ_EUNSUPPORTED, "%s: chunk*group=%lld > %d", fn, static_cast<long long>(chunk) * group,
@@ -321,6 +330,8 @@ static tq_status logits_call(const char *fn, int qjl, const tq_codec *kc, const 
   if (n_keys > cap) return fail(TQ_EINVAL, "%s: n_keys > cap", fn);
   if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!sequences_fit(batch, n_kv_heads))
+    return fail(TQ_EUNSUPPORTED, "%s: batch*n_kv_heads above %lld", fn, static_cast<long long>(kMaxSequences));
   if (!seq_offsets_fit(cap, (kc->lm_bits + 1) * kc->d / 8))
     return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (batch == 0 || n_kv_heads == 0 || group == 0 || n_keys == 0) return ok();
@@ -350,6 +361,8 @@ tq_status tq_prepare_queries(const tq_codec *kc, const void *q, tq_dtype qt, int
   if (!dtype_ok(qt)) return fail(TQ_EINVAL, "%s: bad query dtype", fn);
   if (batch < 0 || n_kv_heads < 0 || group < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!sequences_fit(batch, n_kv_heads))
+    return fail(TQ_EUNSUPPORTED, "%s: batch*n_kv_heads above %lld", fn, static_cast<long long>(kMaxSequences));
   if (batch == 0 || n_kv_heads == 0 || group == 0) return ok();
   if (!q || !prepared) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
   const size_t need = tq_prepared_queries_bytes(batch, n_kv_heads, group, kc->d, kc->lm_bits);
@@ -373,6 +386,8 @@ tq_status tq_logits_prepared(const tq_codec *kc, const void *prepared, size_t by
   if (n_keys > cap) return fail(TQ_EINVAL, "%s: n_keys > cap", fn);
   if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!sequences_fit(batch, n_kv_heads))
+    return fail(TQ_EUNSUPPORTED, "%s: batch*n_kv_heads above %lld", fn, static_cast<long long>(kMaxSequences));
   if (!seq_offsets_fit(cap, (kc->lm_bits + 1) * kc->d / 8))
     return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (batch == 0 || n_kv_heads == 0 || group == 0 || n_keys == 0) return ok();

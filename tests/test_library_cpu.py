@@ -246,6 +246,16 @@ def test_fp8_key_calls_validation():
                                       _p(), tq.TQ_F32, _p(), ws, None) == tq.TQ_EINVAL
 
 
+def test_sequence_count_limit():
+    """(batch, kv-head) sequences ride on the grid's y dimension: above 65535
+    per call is rejected before any launch."""
+    k, v = _codec(), _codec(w=4, key=0, sketch=False)
+    assert _logits(k, batch=65536, n_kv=1) == tq.TQ_EUNSUPPORTED
+    assert _decode(k, v, batch=65536, n_kv=1, ws=1 << 40) == tq.TQ_EUNSUPPORTED
+    assert _append(k, v, batch=32768, n_kv=2, ws=1 << 40) == tq.TQ_EUNSUPPORTED
+    assert _prefill(k, v, batch=70000, n_kv=1, ws=1 << 40) == tq.TQ_EUNSUPPORTED
+
+
 def test_prepared_logits_validation():
     k = _codec()
     cs = ctypes.byref(k)
