@@ -844,13 +844,15 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
   }
   __syncthreads();
 
-  // 2. projections PZ[c] = S ROT[c], c <= GE (c = GE: z = S r) in fp64:
-  //    thread (j, kq) sums its quarter of row j for every column, then the
-  //    four quarters are added
+  // 2. projections PZ[c] = S ROT[c], c <= GE: thread (j, kq) sums its
+  //    quarter of row j for every column, then the four quarters are added.
+  //    The key's z = S r (c = GE), whose signs are the record's, in fp64;
+  //    the heads' p (for the token's logit) in fp32
   {
-    double acc[9];
+    double acck = 0.0;
+    float acc[8];
 #pragma unroll
-    for (int c = 0; c < 9; ++c) acc[c] = 0.0;
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
 #pragma unroll
     for (int u = 0; u < KQ / 8; ++u) {
       const uint32_t wv[4] = {sk[u].x, sk[u].y, sk[u].z, sk[u].w};
@@ -860,20 +862,26 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
         sv[2 * k] = f16_bits_to_float(static_cast<uint16_t>(wv[k] & 0xffffu));
         sv[2 * k + 1] = f16_bits_to_float(static_cast<uint16_t>(wv[k] >> 16));
       }
+      const float4 k0 = *reinterpret_cast<const float4 *>(rot + GE * D + KQ * kq + 8 * u);
+      const float4 k1 = *reinterpret_cast<const float4 *>(rot + GE * D + KQ * kq + 8 * u + 4);
+      const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        if (c <= GE) {
+      for (int k = 0; k < 8; ++k) acck = fma(static_cast<double>(sv[k]), static_cast<double>(kv[k]), acck);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (c < GE) {
           const float4 r0 = *reinterpret_cast<const float4 *>(rot + c * D + KQ * kq + 8 * u);
           const float4 r1 = *reinterpret_cast<const float4 *>(rot + c * D + KQ * kq + 8 * u + 4);
           const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc[c] = fma(static_cast<double>(sv[k]), static_cast<double>(rv[k]), acc[c]);
+          for (int k = 0; k < 8; ++k) acc[c] = fmaf(sv[k], rv[k], acc[c]);
         }
       }
     }
 #pragma unroll
-    for (int c = 0; c < 9; ++c)
-      if (c <= GE) part_s[(kq * 9 + c) * D + j] = acc[c];
+    for (int c = 0; c < 8; ++c)
+      if (c < GE) part_s[(kq * 9 + c) * D + j] = static_cast<double>(acc[c]);
+    part_s[(kq * 9 + GE) * D + j] = acck;
   }
   __syncthreads();
   for (int e = tid; e < (GE + 1) * D; e += 4 * D) {
@@ -884,19 +892,24 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
   }
   __syncthreads();
 
-  // 3. the sign plane and the key record
+  // 3. the sign plane and the key record, by wave 0 alone (the other waves
+  //    go on to the heads' logits, which read the signs from PZ themselves)
   if (wave == 0) {
+    uint32_t sw[2 * E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint64_t m = __ballot(pz[GE * D + lane + kWave * e] >= 0.f);
-      if (lane == 0) {
-        rec[KW * (D / 32) + 2 * e] = static_cast<uint32_t>(m);
-        rec[KW * (D / 32) + 2 * e + 1] = static_cast<uint32_t>(m >> 32);
-      }
+      sw[2 * e] = static_cast<uint32_t>(m);
+      sw[2 * e + 1] = static_cast<uint32_t>(m >> 32);
+    }
+    if (lane < REC / 4) {
+      const int k = lane - KW * (D / 32);                // sign-plane word, or < 0: an index-plane word
+      uint32_t w = (k < 0) ? rec[lane] : sw[0];
+#pragma unroll
+      for (int i = 1; i < 2 * E; ++i) w = (k == i) ? sw[i] : w;
+      reinterpret_cast<uint32_t *>(p.kcodes_w + slot * REC)[lane] = w;
     }
   }
-  __syncthreads();
-  if (tid < REC / 4) reinterpret_cast<uint32_t *>(p.kcodes_w + slot * REC)[tid] = rec[tid];
 
   // 4. the token's logit for each head and its partial
   const float kappa = kSqrtHalfPi / static_cast<float>(D);
