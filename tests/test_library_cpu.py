@@ -246,6 +246,33 @@ def test_fp8_key_calls_validation():
                                       _p(), tq.TQ_F32, _p(), ws, None) == tq.TQ_EINVAL
 
 
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/tq.h compiles as strict C99 and a C program links against
+    libtq and calls its host entry points (no GPU needed)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "use_tq.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "tq.h"\n'
+        "int main(void) {\n"
+        "  float c[4], t[3];\n"
+        "  if (tq_make_codebook(128, 2, c, t) != TQ_OK) return 1;\n"
+        "  if (!(c[0] < c[1] && c[1] < 0 && t[1] == 0.0f)) return 2;\n"
+        "  if (tq_key_record_bytes(128, 3) != 64) return 3;\n"
+        "  int32_t w[4];\n"
+        "  if (tq_rate_plan(3.5, 4, 1, w) != TQ_OK || w[0] + w[1] + w[2] + w[3] != 10) return 4;\n"
+        "  printf(\"%s\\n\", tq_status_string(TQ_EINVAL));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "use_tq"
+    lib_dir = os.path.join(root, "kv_cache_vector_rht_amd")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(root, "include"),
+                        str(src), "-o", str(exe), "-L", lib_dir, "-ltq", f"-Wl,-rpath,{lib_dir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.startswith("TQ_EINVAL")
+
+
 def test_sequence_count_limit():
     """(batch, kv-head) sequences ride on the grid's y dimension: above 65535
     per call is rejected before any launch."""
