@@ -297,6 +297,59 @@ def test_zero_vector_encodes_to_zero_norm():
     assert np.all(lg == 0)
 
 
+@pytest.mark.parametrize("d,bits", [(16, 2), (64, 3), (128, 2)])
+def test_requantize_key_with_the_encoders_indices_reproduces_encode(d, bits):
+    """Given the indices encode() chose, requantize_key recomputes the key's
+    residual, its norm, the projection and the sign bits exactly as encode()
+    did (the second stage applied to the same first-stage codes)."""
+    rng = np.random.default_rng(1000 + d + bits)
+    c, t = O.make_codebook(d, bits)
+    s = rng.choice([-1.0, 1.0], size=d)
+    S = rng.standard_normal((d, d)).astype(np.float16)
+    x = rng.standard_normal((40, d)) * np.exp(rng.standard_normal(d))
+    enc = O.encode(x, s, c, t, S)
+    rq = O.requantize_key(enc["y"], enc["idx"], c, S)
+    for k in ("r", "gamma", "z"):
+        np.testing.assert_array_equal(rq[k], enc[k])
+    np.testing.assert_array_equal(rq["sigma"], enc["sigma"])
+    np.testing.assert_array_equal(rq["ghat"].view(np.uint16), enc["ghat"].view(np.uint16))
+
+
+def test_requantize_key_with_a_moved_index_is_the_explicit_residual_projection():
+    """After one index is moved to a neighbouring cell (what the parity rule
+    does when the GPU crossed a threshold the oracle did not), the residual is
+    y - c[idx'] coordinate by coordinate, gamma its Euclidean norm and z_j the
+    sum over k of S[j][k] r_k, written out here as plain Python loops with
+    exactly rounded sums; sigma_j = [fp32(z_j) >= 0]."""
+    d, bits = 16, 3
+    rng = np.random.default_rng(77)
+    c, t = O.make_codebook(d, bits)
+    s = rng.choice([-1.0, 1.0], size=d)
+    S = rng.standard_normal((d, d)).astype(np.float16)
+    x = rng.standard_normal((6, d))
+    enc = O.encode(x, s, c, t, S)
+    idx = enc["idx"].copy()
+    L = 1 << bits
+    for row in range(idx.shape[0]):
+        col = (3 * row + 1) % d
+        idx[row, col] = idx[row, col] + 1 if idx[row, col] < L - 1 else idx[row, col] - 1
+    rq = O.requantize_key(enc["y"], idx, c, S)
+    c32 = [float(np.float32(v)) for v in c]
+    for row in range(idx.shape[0]):
+        y = [float(v) for v in enc["y"][row]]
+        r = [y[k] - c32[int(idx[row, k])] for k in range(d)]
+        gamma = math.sqrt(math.fsum(v * v for v in r))
+        z = [math.fsum(float(S[j, k]) * r[k] for k in range(d)) for j in range(d)]
+        np.testing.assert_allclose(rq["r"][row], r, rtol=0, atol=0)
+        assert abs(rq["gamma"][row] - gamma) <= 1e-15 * max(gamma, 1.0)
+        np.testing.assert_allclose(rq["z"][row], z, rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(rq["sigma"][row], [1 if np.float32(v) >= 0 else 0 for v in z])
+        assert rq["ghat"][row] == np.float16(gamma)
+        # the moved coordinate really changed the residual: the old one differs there
+        col = (3 * row + 1) % d
+        assert rq["r"][row, col] != enc["r"][row, col]
+
+
 # --------------------------------------------------------------------------
 # QJL estimator: unbiasedness, test power, variance, d = 4 brute force
 # --------------------------------------------------------------------------
