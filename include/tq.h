@@ -42,9 +42,15 @@
  *                  coordinate i) holds bit p of the index of token 32B+j at
  *                  bit j. `cap` must be a multiple of 32.
  *          scalars fp16   [n_seq][cap]  {norm}
- *   Index idx_i of coordinate i is the number of thresholds t_j <= y_i
- *   (exact ties go to the upper cell); a sign bit is 1 when its projection
- *   is >= 0.
+ *   Index idx_i of coordinate i is the number of thresholds t_j <= y_i,
+ *   taken with the codebook's symmetry: the sign of y_i gives the top index
+ *   bit (y_i = +0 or -0 counts as positive) and |y_i| is compared with the
+ *   upper half's thresholds. A positive y_i equal to a threshold therefore
+ *   takes the upper cell and a negative one the lower cell (the cell further
+ *   from zero); every encoding entry point (tq_encode_kv and the append of
+ *   tq_append_decode_attend) follows this rule. The comparison itself is
+ *   made on the rotated, unnormalised vector against the thresholds scaled
+ *   by its norm, in fp32. A sign bit is 1 when its projection is >= 0.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -138,7 +144,14 @@ size_t tq_value_block_bytes(int32_t d, int32_t lm_bits);
 /*
  * Encode n_tok tokens of each of n_seq sequences into cache slots
  * [t0, t0 + n_tok) (steps: store the norm, rotate, Lloyd-Max quantize; keys
- * also take the residual, its norm and the QJL sign bits; pack).
+ * also take the residual, its norm and the QJL sign bits; pack). The two
+ * stages are those of "TurboQuant と RotorQuant を DGX Spark で試してみた",
+ * section "PolarQuant + QJL の 2 段階圧縮" (rotate and scalar-quantize, then
+ * one bit per coordinate for the remaining error), with stage 1 as the
+ * randomized Hadamard rotation and per-coordinate Lloyd-Max quantizer of
+ * "TurboQuantとは？…", section 第1段, and stage 2 as the 1-bit sign of a
+ * Gaussian random projection of the residual of its section 第2段; the
+ * stored norms replace any per-block scale (section 第1段).
  *   x        device, dtype xt (TQ_F32 / TQ_BF16 / TQ_F16); element i of token
  *            t of sequence s at x[s*x_seq_stride + t*x_tok_stride + i]
  *            (strides in elements; rows are contiguous)
@@ -221,7 +234,14 @@ tq_status tq_logits_mse(const tq_codec *kc, const void *q, tq_dtype qt, int32_t 
  * Fused decode attention over the coded cache: logits as tq_logits, exact
  * softmax of sm_scale*logit over tokens t < ctx_lens[b], and the weighted sum
  * of the decoded values n_t R_v^T c_v[idx_t] (accumulated in the rotated
- * domain, rotated back once per output row).
+ * domain, rotated back once per output row). This is the decode step the
+ * pages measure: attention reads the keys and values of the past tokens
+ * from the compressed cache ("TurboQuant と RotorQuant を DGX Spark で試して
+ * みた", section TurboQuant とは: the KV cache holds the past tokens' keys
+ * and values), with values quantized MSE-only to their own width (the k/v
+ * widths of the presets in "TurboQuantとは？…", section 「精度劣化ゼロ」の
+ * 出所と、マージ後に判明した実測値), and decode-heavy serving is where the
+ * pages place the codec's cost (same section).
  *   q        device [batch][n_kv_heads*group][d], dtype qt, 16-byte aligned
  *            (as are the key codec's signs and sketch)
  *   kcodes, kscalars, vcodes, vscalars  key and value caches, `cap` slots

@@ -652,19 +652,22 @@ __device__ __forceinline__ float load_elem(const void *base, int64_t i, int xt) 
 }
 
 // Lloyd-Max decision of one rotated coordinate v against the thresholds
-// scaled by ||v|| (th, cent: the codebook in LDS): idx = #{j : v >= t_j ||v||}
-// and c = cent[idx].
+// scaled by ||v|| (th, cent: the codebook in LDS), by the same rule as the
+// encode kernels: the sign of v gives the top index bit (v = -0 counts as
+// positive) and j = #{k : |v| >= t_{L/2+k} ||v||} over the upper half's
+// nonzero thresholds, idx = L/2 + j (v >= 0) or L/2 - 1 - j (v < 0), so that
+// a negative v equal to a scaled threshold takes the cell further from zero
+// exactly as there; c = cent[idx].
 template <int W>
 __device__ __forceinline__ void decide_scaled(float v, float vn, const float *th, const float *cent, int &idx,
                                               float &c) {
-  idx = 0;
-  c = cent[0];
+  constexpr int H = (1 << W) / 2;
+  const float a = fabsf(v);
+  int j = 0;
 #pragma unroll
-  for (int j = 0; j < (1 << W) - 1; ++j) {
-    const bool up = v >= th[j] * vn;
-    idx += up ? 1 : 0;
-    c = up ? cent[j + 1] : c;
-  }
+  for (int k = 0; k < H - 1; ++k) j += (a >= th[H + k] * vn) ? 1 : 0;
+  idx = (v >= 0.f) ? H + j : H - 1 - j;
+  c = cent[idx];
 }
 
 // The new token of group bh, encoded by the one extra block of an append
