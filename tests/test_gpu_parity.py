@@ -33,7 +33,7 @@ def _inputs(n_seq, n_tok, d, dtype, seed, stream=1, scale_channels=False):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("w", [1, 2, 3])
+@pytest.mark.parametrize("w", [1, 2, 3, 4])
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_encode_keys(d, w, dt):
     say(f"encode keys d={d} w={w} dtype={dt} n_seq=3 n_tok=300 t0=37")
@@ -268,3 +268,37 @@ def test_calls_replay_in_a_hip_graph():
         torch.cuda.synchronize()
         for a, b in zip((kcodes, kscal, vcodes, vscal, lg, out), ref):
             assert torch.equal(a, b), f"replay {rep} differs"
+
+
+def test_explicit_side_stream_owns_the_temporaries():
+    """A call given an explicit stream (not the current one) with no
+    workspace, no output and a non-contiguous query: the binding's copy,
+    output and workspace belong to that stream, so work allocated and
+    written on the current stream right after the call cannot reuse them
+    while the kernels still run. The result equals the same call on the
+    current stream, bit for bit."""
+    say("side stream: decode with workspace=None, then allocations on the current stream")
+    d, kw, vw, batch, n_kv, group, T = 128, 3, 4, 4, 8, 4, 4096
+    kc, vc = key_codec(811, d, kw), value_codec(812, d, vw)
+    k = _inputs(batch * n_kv, T, d, torch.bfloat16, seed=21, stream=1)
+    v = _inputs(batch * n_kv, T, d, torch.bfloat16, seed=22, stream=2)
+    qt = _inputs(n_kv * group, batch, d, torch.bfloat16, seed=23, stream=3).transpose(0, 1)   # not contiguous
+    kcodes, kscal = tq.alloc_key_cache(batch * n_kv, T, kc.gpu)
+    vcodes, vscal = tq.alloc_value_cache(batch * n_kv, T, vc.gpu)
+    tq.encode_kv(kc.gpu, k, kcodes, kscal)
+    tq.encode_kv(vc.gpu, v, vcodes, vscal)
+    ctx = torch.full((batch,), T, dtype=torch.int32, device="cuda")
+    ref = tq.decode_attend(kc.gpu, vc.gpu, qt, kcodes, kscal, vcodes, vscal, ctx, n_kv_heads=n_kv, group=group)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(tq.decode_attend(kc.gpu, vc.gpu, qt, kcodes, kscal, vcodes, vscal, ctx, n_kv_heads=n_kv,
+                                     group=group, stream=side))
+        junk = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        junk.fill_(0xA5)
+        del junk
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)

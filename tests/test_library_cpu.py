@@ -349,3 +349,49 @@ def test_topk_validation():
 def test_status_strings():
     for s in (tq.TQ_OK, tq.TQ_EINVAL, tq.TQ_EUNSUPPORTED, tq.TQ_EHIP):
         assert tq.lib.tq_status_string(s).decode().startswith("TQ_")
+
+
+def _cpu_codecs(d=64):
+    """Codecs whose arrays live on the host: every device call must refuse them."""
+    rng = np.random.default_rng(3)
+    s = rng.choice([-1.0, 1.0], size=d)
+    S = rng.standard_normal((d, d)).astype(np.float16)
+    return tq.Codec.make(d, 2, True, s, S, device="cpu"), tq.Codec.make(d, 4, False, s, device="cpu")
+
+
+def test_binding_rejects_bad_tensors_before_any_launch():
+    """The binding checks dtypes, shapes and devices before a pointer reaches
+    the library: int64 context lengths (which the kernels would read as
+    interleaved low and high words), queries of the wrong head size or head
+    count, and host tensors."""
+    import torch
+    kc, vc = _cpu_codecs()
+    batch, n_kv, group, cap, d = 2, 2, 4, 64, 64
+    kcodes, kscal = tq.alloc_key_cache(batch * n_kv, cap, kc)
+    vcodes, vscal = tq.alloc_value_cache(batch * n_kv, cap, vc)
+    q = torch.zeros((batch, n_kv * group, d), dtype=torch.bfloat16)
+    call = lambda **kw: tq.decode_attend(kc, vc, kw.get("q", q), kcodes, kscal, vcodes, vscal,
+                                         kw.get("lens", torch.tensor([5, 7], dtype=torch.int32)),
+                                         n_kv_heads=n_kv, group=group, max_ctx=cap)
+    with pytest.raises(ValueError, match="int32"):
+        call(lens=torch.tensor([5, 7]))                       # int64
+    with pytest.raises(ValueError, match="at least 2"):
+        call(lens=torch.tensor([5], dtype=torch.int32))
+    with pytest.raises(ValueError, match="CUDA"):
+        call()                                                # every tensor on the host
+    with pytest.raises(ValueError, match="shape"):
+        tq.logits(kc, torch.zeros((batch, n_kv * group, d // 2)), kcodes, kscal, n_kv_heads=n_kv, group=group,
+                  n_keys=cap)
+    with pytest.raises(ValueError, match="shape"):
+        tq.logits(kc, torch.zeros((batch, n_kv * group + 1, d)), kcodes, kscal, n_kv_heads=n_kv, group=group,
+                  n_keys=cap)
+    with pytest.raises(ValueError, match="int32"):
+        tq.prefill_attend(kc, vc, torch.zeros((batch, 3, n_kv * group, d)), kcodes, kscal, vcodes, vscal,
+                          torch.zeros(batch, dtype=torch.int64), n_kv_heads=n_kv, group=group)
+    with pytest.raises(ValueError, match="int32"):
+        tq.append_decode_attend(kc, vc, q, torch.zeros((batch, n_kv, d)), torch.zeros((batch, n_kv, d)), kcodes,
+                                kscal, vcodes, vscal, torch.tensor([5, 7]), n_kv_heads=n_kv, group=group)
+    with pytest.raises(ValueError, match=f"\\[n_seq, n_tok, {d}\\]"):
+        tq.encode_kv(kc, torch.zeros((n_kv, 10, d + 8)), kcodes, kscal)
+    with pytest.raises(ValueError, match="CUDA"):
+        tq.encode_kv(kc, torch.zeros((n_kv, 10, d)), kcodes, kscal)
