@@ -266,6 +266,31 @@ size_t tq_decode_attend_workspace(int32_t batch, int32_t n_kv_heads, int32_t gro
                                   int64_t max_ctx, int32_t d);
 
 /*
+ * tq_decode_attend without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the split partials go to a fixed scratch array
+ * that the library holds in device memory, one copy per GPU, for the life of
+ * the process. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks up that
+ * device's copy. The caller still provides q, the caches, ctx_lens and out.
+ * Results are those of tq_decode_attend, bit for bit (the same kernels).
+ * Calls that overlap on one GPU (several streams, or several host threads)
+ * share the scratch and race: serialize them. Every call overwrites the
+ * partials it uses, so nothing needs clearing between calls.
+ *   Arguments, output and errors as tq_decode_attend; in addition
+ *   TQ_EUNSUPPORTED when tq_decode_attend_workspace(batch, n_kv_heads, group,
+ *   max_ctx, d) exceeds tq_decode_attend_noalloc_max_workspace() (16 MiB:
+ *   e.g. up to 256 (batch, kv-head) groups of 32 query heads at d = 128).
+ */
+tq_status tq_decode_attend_noalloc(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt,
+                                   int32_t batch, int32_t n_kv_heads, int32_t group,
+                                   const uint8_t *kcodes, const uint16_t *kscalars,
+                                   const uint32_t *vcodes, const uint16_t *vscalars, int64_t cap,
+                                   const int32_t *ctx_lens, int64_t max_ctx, float sm_scale,
+                                   void *out, tq_dtype out_t, void *stream);
+size_t tq_decode_attend_noalloc_max_workspace(void);
+
+/*
  * One decoding step in one launch: the new token's key and value of every
  * (batch, kv-head) sequence are encoded into the caches (as tq_encode_kv
  * would, into slot ctx_lens[b] - 1) and the query heads attend over the

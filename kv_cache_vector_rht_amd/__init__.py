@@ -64,6 +64,8 @@ def _load():
         "tq_logits_prepared": ([CP, P, SZ, I32, I32, I32, P, P, I64, I64, P, P], I32),
         "tq_decode_attend": ([CP, CP, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
         "tq_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
+        "tq_decode_attend_noalloc": ([CP, CP, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P], I32),
+        "tq_decode_attend_noalloc_max_workspace": ([], SZ),
         "tq_append_decode_attend": ([CP, CP, P, I32, P, P, I32, I32, I32, I32, P, P, P, P, I64, P, I64, F, P, I32, P,
                                      SZ, P], I32),
         "tq_append_decode_attend_workspace": ([I32, I32, I32, I64, I32], SZ),
@@ -103,7 +105,8 @@ def load():
 
 EXPORTED = ("tq_make_codebook", "tq_rate_plan", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
             "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_prepared_queries_bytes", "tq_prepare_queries",
-            "tq_logits_prepared", "tq_decode_attend", "tq_decode_attend_workspace",
+            "tq_logits_prepared", "tq_decode_attend", "tq_decode_attend_workspace", "tq_decode_attend_noalloc",
+            "tq_decode_attend_noalloc_max_workspace",
             "tq_append_decode_attend", "tq_append_decode_attend_workspace", "tq_prefill_attend",
             "tq_prefill_attend_workspace", "tq_encode_fp8_keys", "tq_decode_attend_k8",
             "tq_topk", "tq_topk_workspace", "tq_status_string", "tq_last_error")
@@ -473,6 +476,33 @@ def decode_attend(kc: Codec, vc: Codec, q: torch.Tensor, kcodes, kscalars, vcode
                               workspace.numel(), _stream(stream))
     _check(st, "tq_decode_attend")
     return out
+
+
+@_on_stream
+def decode_attend_noalloc(kc: Codec, vc: Codec, q: torch.Tensor, kcodes, kscalars, vcodes, vscalars,
+                          ctx_lens: torch.Tensor, n_kv_heads: int, group: int, out: torch.Tensor,
+                          max_ctx: Optional[int] = None, sm_scale: Optional[float] = None,
+                          stream=None) -> torch.Tensor:
+    """decode_attend with the split partials in the library's fixed device scratch (no workspace):
+    q must be contiguous and `out` given, so that the call allocates nothing. Calls that overlap on
+    one GPU share the scratch and must be serialized."""
+    batch = _batch_of(q, 3, "[batch, n_kv_heads*group, d]")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous (the call makes no copies)")
+    n_q = n_kv_heads * group
+    q, cap, max_ctx, sm_scale, out, ot = _attend_common(kc, vc, q, (batch, n_q), kcodes, kscalars, vcodes, vscalars,
+                                                        ctx_lens, "ctx_lens", batch, n_kv_heads, max_ctx, sm_scale,
+                                                        out, out.dtype if torch.is_tensor(out) else None)
+    ks, vs = kc.struct(), vc.struct()
+    st = lib.tq_decode_attend_noalloc(ctypes.byref(ks), ctypes.byref(vs), _ptr(q), _DTYPE[q.dtype], batch,
+                                      n_kv_heads, group, _ptr(kcodes), _ptr(kscalars), _ptr(vcodes), _ptr(vscalars),
+                                      cap, _ptr(ctx_lens), max_ctx, float(sm_scale), _ptr(out), ot, _stream(stream))
+    _check(st, "tq_decode_attend_noalloc")
+    return out
+
+
+def decode_attend_noalloc_max_workspace() -> int:
+    return int(lib.tq_decode_attend_noalloc_max_workspace())
 
 
 def prepared_queries_bytes(batch: int, n_kv_heads: int, group: int, d: int, lm_bits: int) -> int:

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/tq.h"
@@ -194,6 +195,45 @@ tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_c
   sp.out = out;
   sp.out_t = static_cast<int>(out_t);
   return TQ_OK;
+}
+
+// Fixed device scratch of tq_decode_attend_noalloc: the split partials live
+// in this file-scope array instead of a caller workspace. Every GPU the
+// library runs on holds its own copy for the life of the process. Host code
+// must use the address hipGetSymbolAddress returns for the current device
+// (the array's name is a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = static_cast<size_t>(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up once per device, with
+// that device current); nullptr with the failure recorded otherwise.
+void *device_scratch(const char *fn, tq_status &st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    st = fail(TQ_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    st = fail(TQ_EUNSUPPORTED, "%s: device %d beyond the %d the scratch table holds", fn, dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      st = fail(TQ_EHIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  st = TQ_OK;
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -578,6 +618,40 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
                               vscalars, cap, ctx_lens, max_ctx, sm_scale, out, out_t, workspace, ws_bytes, sp, nothing);
   if (s != TQ_OK) return s;
   if (nothing) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, kc->lm_bits, vc->lm_bits, st)
+                             : tq::launch_decode_d<128>(sp, kc->lm_bits, vc->lm_bits, st);
+  return hip_status(e, fn);
+}
+
+size_t tq_decode_attend_noalloc_max_workspace(void) { return kScratchBytes; }
+
+tq_status tq_decode_attend_noalloc(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
+                                   int32_t n_kv_heads, int32_t group, const uint8_t *kcodes, const uint16_t *kscalars,
+                                   const uint32_t *vcodes, const uint16_t *vscalars, int64_t cap,
+                                   const int32_t *ctx_lens, int64_t max_ctx, float sm_scale, void *out,
+                                   tq_dtype out_t, void *stream) {
+  const char *fn = "tq_decode_attend_noalloc";
+  // the partials this call needs, checked against the fixed scratch before
+  // anything else touches the device (0 for arguments the checks below reject)
+  const int32_t d = kc ? kc->d : 0;
+  const size_t need = tq_decode_attend_workspace(batch, n_kv_heads, group, max_ctx, d);
+  if (need > kScratchBytes)
+    return fail(TQ_EUNSUPPORTED, "%s: the call needs %zu bytes of split partials, above the fixed %zu-byte scratch "
+                                 "(use tq_decode_attend with a workspace)", fn, need, kScratchBytes);
+  // the arguments are validated as tq_decode_attend's, against a stand-in
+  // for the workspace (the scratch is aligned and large enough); the
+  // scratch's device address is looked up only for a call that launches
+  tq::ScanParams sp;
+  bool nothing = false;
+  tq_status s = decode_common(fn, 0, kc, vc, q, qt, batch, 1, n_kv_heads, group, kcodes, kscalars, vcodes, vscalars,
+                              cap, ctx_lens, max_ctx, sm_scale, out, out_t, reinterpret_cast<void *>(kAlign),
+                              kScratchBytes, sp, nothing);
+  if (s != TQ_OK) return s;
+  if (nothing) return ok();
+  void *ws = device_scratch(fn, s);
+  if (!ws) return s;
+  sp.partials = static_cast<float *>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, kc->lm_bits, vc->lm_bits, st)
                              : tq::launch_decode_d<128>(sp, kc->lm_bits, vc->lm_bits, st);
