@@ -89,7 +89,8 @@ __device__ __forceinline__ void lane_masks(uint32_t (&mask)[4]) {
 // barriers and per-split steps per token), else 256 tokens in kStages.
 constexpr int kStages = 3;
 
-// Block layout: D/16 waves. Wave w owns the 16-key tiles w, w + NW, ... of
+// Block layout: NW waves (D/16 for decode; the logit scan may take more).
+// Wave w owns the 16-key tiles w, w + NW, ... of
 // every split and (decode) the value coordinates [16 w, 16 w + 16). Its
 // share of a split is staged in a region of LDS that only it reads, so no
 // barrier guards the staging:
@@ -101,11 +102,11 @@ constexpr int kStages = 3;
 //                      fp8 keys), then (decode) their value norms (32 B per
 //                      tile)
 //   [OFF_V, ...)       (decode) value words: [32-token block][plane][16 coords]
-template <int D, int KW, int VW, bool LOGITS, int SPLIT>
+template <int D, int KW, int VW, bool LOGITS, int SPLIT, int NWAVE = D / 16>
 struct ScanShape {
   static constexpr bool K8 = KW == kKeyFp8;          // fp8 key records
   static constexpr int S = SPLIT;
-  static constexpr int NW = D / 16;
+  static constexpr int NW = NWAVE;
   static constexpr int THREADS = NW * kWave;
   static constexpr int KT = S / 16 / NW;             // key tiles per wave
   static constexpr int VT = S / 64;                  // 64-token value tiles
@@ -143,6 +144,10 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint8_t *l
 __device__ __forceinline__ void dma16_at(const void *src, uint8_t *lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_m0(lds)) : "memory");
 }
+// 4 bytes per lane from this lane's address into LDS at lds + 4 * lane.
+__device__ __forceinline__ void dma4_at(const void *src, uint8_t *lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_m0(lds)) : "memory");
+}
 
 // Wait until at most N vector memory operations of this wave are in flight.
 template <int N>
@@ -172,9 +177,9 @@ struct SeqArrays {
 // Every wave issues exactly P loads. Tiles past the cache capacity load the
 // sequence's first tile instead (their keys are past the context and are
 // never used), so every address stays inside the caller's arrays.
-template <int D, int KW, int VW, bool LOGITS, int SPLIT>
+template <int D, int KW, int VW, bool LOGITS, int SPLIT, int NWAVE = D / 16>
 __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t *stage, int wave) {
-  using SH = ScanShape<D, KW, VW, LOGITS, SPLIT>;
+  using SH = ScanShape<D, KW, VW, LOGITS, SPLIT, NWAVE>;
   constexpr int REC = SH::REC;
   const int lane = lane_id();
   uint8_t *wb = stage + wave * SH::WAVE_BYTES;
@@ -257,35 +262,50 @@ __device__ __forceinline__ float wave_fwht(float x, int lane) {
 }
 
 // Scratch of the in-block query preparation (byte offsets):
-//   FRAG   int8 digit operands [NRG][NMF][64 lanes][16]
-//   SQ, SP q' and p, [8][D] float
-//   SST    per head: max |q'| and sum q' [8][4]; SCON per-head constants [8][4];
-//   SB     key basis coefficients [8]
-//   SPS    per 32-row tile of S and head: max |p| and sum p over the tile
-//   SK     the sketch [D][D] fp16, staged by direct-to-LDS loads; the 16-byte
-//          chunk c of row j sits at chunk position c ^ (j % (D/8)), so that
-//          32 lanes reading the same columns of 32 rows hit distinct banks
-//   QIN    the raw query rows [8][D] (input dtype) then the signs [D] float,
-//          staged by direct-to-LDS loads
-//   TAB    (over SK and QIN once those are consumed) the digit words of the
-//          operands, [head][operand][coordinate]
+//   SQ, SP  q' and p, [8][D] float
+//   SQH,SQL q' of each head scaled by a power of two (its max |q'| below
+//           2^14) and split into fp16 hi + lo, [8][D] halves each: the B
+//           operands of the sketch product
+//   SST     per head: max |q'| and sum q' [8][4]; SCON per-head constants [8][4]
+//   SB      key basis coefficients [8]
+//   SPS     per 32-row tile of S and head: max |p| and sum p over the tile
+//   CENT    the centroids [2^KW] float, staged by a direct-to-LDS load
+//   FRAG    the operand bytes in the MFMA A layout, [NRG][NMF][64 lanes][16]
+// Prepared-query records (tq_prepare_queries) hold the operand fragments
+// [NRG][NMF][64 lanes][16 bytes] (REC_FRAG bytes), then the 8 heads'
+// constants (128 bytes); a scan block copies one to the start of its
+// scratch.
 template <int D, int KW, int NRG>
 struct PrepShape {
   static constexpr int NB = Basis<KW>::N;
   static constexpr int NMF = (NB + 1) * (D / 64);
-  static constexpr int FRAG = NRG * NMF * 1024;
-  static constexpr int SQ = FRAG;
+  static constexpr int SQ = 0;
   static constexpr int SP = SQ + 8 * D * 4;
-  static constexpr int SST = SP + 8 * D * 4;
+  static constexpr int SQH = SP + 8 * D * 4;
+  static constexpr int SQL = SQH + 8 * D * 2;
+  static constexpr int SST = SQL + 8 * D * 2;
   static constexpr int SCON = SST + 8 * 4 * 4;
   static constexpr int SB = SCON + 8 * 4 * 4;
   static constexpr int SPS = SB + 64;                 // per row tile and head: max |p|, sum p
-  static constexpr int SK = SPS + (D / 32) * 8 * 2 * 4;
-  static constexpr int QIN = SK + D * D * 2;
-  static constexpr int QIN_BYTES = (D / 16) * 1024;  // one load per wave
-  static constexpr int TAB = SK;                      // after the GEMV: [4 NRG][NB + 1][D] digit words
-  static constexpr int TAB_BYTES = 4 * NRG * (NB + 1) * D * 4;
-  static constexpr int BYTES = (QIN + QIN_BYTES > TAB + TAB_BYTES) ? QIN + QIN_BYTES : TAB + TAB_BYTES;
+  static constexpr int CENT = SPS + (D / 32) * 8 * 2 * 4;
+  static constexpr int FRAG = (CENT + 64 + 1023) / 1024 * 1024;
+  static constexpr int REC_FRAG = NRG * NMF * 1024;
+  static constexpr int BYTES = FRAG + REC_FRAG;
+  static_assert(REC_FRAG + 128 <= BYTES, "a prepared record fits in the scratch");
+};
+
+// Inputs of the query preparation, loaded straight into the registers of the
+// waves that use them: the query rows of the heads a wave rotates (head
+// wave + NW k, lane l holding elements E l .. E l + E - 1, E = D / 64) with
+// their signs, and for the waves of the sketch product their 32-row tile of
+// the sketch as MFMA A operands, 16 bytes per K step.
+template <int D, int NW>
+struct PrepIn {
+  static constexpr int E = D / kWave;
+  static constexpr int HPW = (8 + NW - 1) / NW;        // heads per wave (at most 8 heads)
+  float q[HPW][E];
+  float s[E];
+  uint4 sk[D / 16];
 };
 
 // Tokens per decode split: 512 (two stages) if those stages, the query
@@ -305,124 +325,157 @@ __device__ __forceinline__ int64_t query_row(const ScanParams &p, int64_t b, int
   return (b * p.chunk + v / gq) * (static_cast<int64_t>(p.n_kv) * gq) + kvh * gq + v % gq;
 }
 
-// Stage the preparation's inputs into the scratch: the sketch (every wave
-// an equal share) and the query rows of heads [h0, h0 + GE) plus the signs
-// (one load per wave; lanes past the end idle).
-template <int D, int KW, int NRG>
-__device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int GE, uint8_t *scratch, int wave) {
+// Load the preparation's inputs (a block of NW waves): the query rows and
+// signs into the registers of the waves that rotate them, the sketch tiles
+// into those of the waves of the sketch product (ordinary loads: these waves
+// issue no direct-to-LDS load before they have consumed them), and the
+// centroids into the scratch by one direct-to-LDS load of the last wave.
+template <int D, int KW, int NRG, int NW = D / 16>
+__device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int GE, uint8_t *scratch, int wave,
+                                           PrepIn<D, NW> &in) {
   using PS = PrepShape<D, KW, NRG>;
-  constexpr int NW = D / 16;
-  constexpr int SKI = D * D * 2 / 1024 / NW;           // sketch loads per wave (4 or 2)
+  using PI = PrepIn<D, NW>;
+  constexpr int E = PI::E;
   const int lane = lane_id();
+  if (wave < GE) {
 #pragma unroll
-  for (int i = 0; i < SKI; ++i) {
-    const int chunk = wave * SKI + i;
-    const int unit = chunk * kWave + lane;                 // LDS chunk position
-    const int j = unit / (D / 8), c = (unit % (D / 8)) ^ (j % (D / 8));
-    dma16(p.sketch, static_cast<uint32_t>((j * (D / 8) + c) * 16), scratch + PS::SK + chunk * 1024);
+    for (int e = 0; e < E; ++e) in.s[e] = p.ksigns[E * lane + e];
+#pragma unroll
+    for (int k = 0; k < PI::HPW; ++k) {
+      const int h = wave + NW * k;
+      if (h < GE) {
+        const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, p.h0 + h);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int64_t i = row * D + E * lane + e;
+          in.q[k][e] = (p.xt == 0) ? static_cast<const float *>(p.q)[i]
+                       : (p.xt == 1) ? bf16_bits_to_float(static_cast<const uint16_t *>(p.q)[i])
+                                     : f16_bits_to_float(static_cast<const uint16_t *>(p.q)[i]);
+        }
+      }
+    }
   }
-  const int es = (p.xt == 0) ? 4 : 2;
-  const int upr = D * es / 16;                           // 16-byte units per query row
-  const int q_units = GE * upr;
-  const int unit = wave * kWave + lane;
-  if (unit < q_units) {
-    const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, p.h0 + unit / upr);
-    dma16_at(static_cast<const uint8_t *>(p.q) + row * D * es + (unit % upr) * 16, scratch + PS::QIN + wave * 1024);
-  } else if (unit < q_units + D / 4) {
-    dma16_at(p.ksigns + (unit - q_units) * 4, scratch + PS::QIN + wave * 1024);
+  if (wave < D / 32) {
+    const int r = 32 * wave + lane % 32, half = lane / 32;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      in.sk[ks] = *reinterpret_cast<const uint4 *>(p.sketch + static_cast<int64_t>(r) * D + 16 * ks + 8 * half);
   }
+  if (wave == NW - 1 && lane < (1 << KW)) dma4_at(p.kcent + lane, scratch + PS::CENT);
 }
 
 // Query preparation of the heads [h0, h0 + GE) (GE <= 4 NRG) of group bh by
-// one block of 4 D threads, from the staged inputs: q' = R q, p = S q', the
+// one block of NW waves, from the staged inputs: q' = R q, p = S q', the
 // digit operands of the key planes (2 beta_s q') and of the sign plane
 // (2 p), one fixed-point exponent per head for each, and the per-head
-// constants {2^-(7+e_lm), c[L-1] sum q', 2^-(7+e_qj), sum p}. Rows of absent
-// heads stay zero. after_rotation() runs once q' is in LDS (the caller issues
-// its first key loads there: issued earlier, their traffic slows the
-// preparation's own input loads and instruction fetch).
-template <int D, int KW, int NRG, class AfterRotation>
-__device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t *scratch, AfterRotation after_rotation) {
+// constants {2^-(7+e_lm), c[L-1] sum q', 2^-(7+e_qj), sum p}. Every wave
+// ends holding all operand fragments of the chunk in a[][] and its heads'
+// constants in fh[] (rows of absent heads zero).
+// Phases, each closed by a block barrier: (1) one wave per head rotates it
+// (q' = H diag(s) q / sqrt(D) in registers) and writes q', its statistics
+// and its scaled fp16 hi + lo split; (2) the waves of the sketch's 32-row
+// tiles form p = S q' on the matrix cores; (3) every thread writes the
+// digits of one (head, coordinate) for every operand, straight into the
+// fragment layout; (4) every wave loads the fragments. late_loads(): the
+// waves of phase 2 call it right after their products, the other waves at
+// the start of phase 2 (the caller issues there the first key loads of the
+// waves that had preparation work to do first).
+template <int D, int KW, int NRG, int NW = D / 16, class LateLoads>
+__device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t *scratch, const PrepIn<D, NW> &in,
+                                           LateLoads late_loads, v4i (&a)[NRG][PrepShape<D, KW, NRG>::NMF],
+                                           float4 (&fh)[NRG]) {
   using PS = PrepShape<D, KW, NRG>;
-  constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64;
-  constexpr int NW = D / 16;
+  constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64, NK = NB + 1;
+  constexpr int E = D / kWave;
+  constexpr int L = 1 << KW;
   float *sq = reinterpret_cast<float *>(scratch + PS::SQ);      // [8][D]
   float *sp = reinterpret_cast<float *>(scratch + PS::SP);      // [8][D]
+  uint16_t *sqh = reinterpret_cast<uint16_t *>(scratch + PS::SQH);   // [8][D]
+  uint16_t *sql = reinterpret_cast<uint16_t *>(scratch + PS::SQL);   // [8][D]
   float *sst = reinterpret_cast<float *>(scratch + PS::SST);    // [8][4]
   float *scon = reinterpret_cast<float *>(scratch + PS::SCON);  // [8][4]
   float *sb = reinterpret_cast<float *>(scratch + PS::SB);      // [8]
-  const uint8_t *qin = scratch + PS::QIN;
-  const float *sgn = reinterpret_cast<const float *>(qin + GE * D * ((p.xt == 0) ? 4 : 2));
+  float *sps = reinterpret_cast<float *>(scratch + PS::SPS);    // [D/32][8][2]
+  const float *cent = reinterpret_cast<const float *>(scratch + PS::CENT);
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  if (tid < NB) sb[tid] = basis_coeff(p.kcent, KW, basis_mask(KW, tid));
 
-  // q' = H (s q) / sqrt(D): one wave per head, in registers (lane l holds
-  // elements l and l + 64 for D = 128, element l for D = 64)
-  constexpr int E = D / kWave;
-  for (int h = wave; h < GE; h += NW) {
+  // (1) q' = H (s q) / sqrt(D): one wave per head, lane l holding elements
+  //     E l .. E l + E - 1 (index bit 0 in registers for D = 128, the others
+  //     across the lanes)
+#pragma unroll
+  for (int kh = 0; kh < PrepIn<D, NW>::HPW; ++kh) {
+    const int h = wave + NW * kh;
+    if (h >= GE) break;
     float x[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = lane + kWave * e, at = h * D + i;
-      float v;
-      if (p.xt == 0) v = reinterpret_cast<const float *>(qin)[at];
-      else if (p.xt == 1) v = bf16_bits_to_float(reinterpret_cast<const uint16_t *>(qin)[at]);
-      else v = f16_bits_to_float(reinterpret_cast<const uint16_t *>(qin)[at]);
-      x[e] = v * sgn[i];
-    }
+    for (int e = 0; e < E; ++e) x[e] = in.q[kh][e] * in.s[e];
     if constexpr (E == 2) {
       const float a0 = x[0] + x[1], a1 = x[0] - x[1];
       x[0] = a0;
       x[1] = a1;
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = wave_fwht(x[e], lane);
+    for (int e = 0; e < E; ++e) x[e] = wave_fwht(x[e], lane) * (1.0f / sqrtf(static_cast<float>(D)));
     float mq = 0.f, s1 = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      x[e] *= 1.0f / sqrtf(static_cast<float>(D));
-      sq[h * D + lane + kWave * e] = x[e];
       mq = fmaxf(mq, fabsf(x[e]));
       s1 += x[e];
     }
     mq = wave_max(mq);
     s1 = wave_sum(s1);
     if (lane == 0) { sst[4 * h] = mq; sst[4 * h + 1] = s1; }
+    // the GEMV's B operand: q' times 2^sexp (max |q'| below 2^14), as fp16
+    // hi + lo (22 significant bits)
+    int ex = 0;
+    (void)frexpf(mq, &ex);
+    const float up = ldexpf(1.0f, min(14 - ex, 100));
+    if constexpr (E == 2) {
+      *reinterpret_cast<float2 *>(sq + h * D + 2 * lane) = make_float2(x[0], x[1]);
+      uint32_t hi, lo;
+      split_pair(x[0] * up, x[1] * up, hi, lo);
+      reinterpret_cast<uint32_t *>(sqh + h * D)[lane] = hi;
+      reinterpret_cast<uint32_t *>(sql + h * D)[lane] = lo;
+    } else {
+      sq[h * D + lane] = x[0];
+      const float nb = __shfl_xor(x[0], 1);     // the pair (2 m, 2 m + 1) in the even lane
+      uint32_t hi, lo;
+      split_pair(x[0] * up, nb * up, hi, lo);
+      if ((lane & 1) == 0) {
+        reinterpret_cast<uint32_t *>(sqh + h * D)[lane / 2] = hi;
+        reinterpret_cast<uint32_t *>(sql + h * D)[lane / 2] = lo;
+      }
+    }
   }
   lds_barrier();
-  after_rotation();
-  // p = S q' on the matrix cores (v_mfma_f32_32x32x16_f16), one 32-row tile
-  // of S per wave: A = 32 sketch rows x 16 columns (fp16, exact), B = 16
-  // entries of q' for the columns = heads (lanes of absent heads zero), each
-  // head scaled by a power of two (its max |q'| below 2^14) and split into
-  // fp16 hi + lo, two MFMAs per K step: fp32-grade sums.
-  // The epilogue also leaves the tile's max |p| and sum p per head.
-  float *sps = reinterpret_cast<float *>(scratch + PS::SPS);    // [D/32][8][2]
+
+  // (2) p = S q' on the matrix cores (v_mfma_f32_32x32x16_f16), one 32-row
+  //     tile of S per wave: A = 32 sketch rows x 16 columns (fp16, exact),
+  //     B = 16 entries of q' for the columns = heads (lanes of absent heads
+  //     zero) as fp16 hi + lo, two MFMAs per K step: fp32-grade sums. The
+  //     epilogue also leaves the tile's max |p| and sum p per head. The
+  //     other waves compute the basis coefficients. (The centroids are in
+  //     the scratch from here on.)
   if (wave < D / 32) {
-    constexpr int U = D / 8;
     const int h = lane % 32, half = lane / 32;
     const bool live = h < GE;
-    int ex = 0;
-    if (live) (void)frexpf(sst[4 * h], &ex);
-    const int sexp = min(14 - ex, 100);
-    const float up = live ? ldexpf(1.0f, sexp) : 0.f;
-    const int r = 32 * wave + h;                          // sketch row of this lane's A entries
     v16f c = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const int cl = 2 * ks + half;                       // logical 16-byte chunk of the row
-      const uint4 au = *reinterpret_cast<const uint4 *>(scratch + PS::SK + (r * U + (cl ^ (r % U))) * 16);
-      V8H a, bh, bl;
-      a.u[0] = au.x; a.u[1] = au.y; a.u[2] = au.z; a.u[3] = au.w;
-      const float *qx = sq + (live ? h : 0) * D + 16 * ks + 8 * half;
-      const float4 x0 = *reinterpret_cast<const float4 *>(qx), x1 = *reinterpret_cast<const float4 *>(qx + 4);
-      split_pair(x0.x * up, x0.y * up, bh.u[0], bl.u[0]);
-      split_pair(x0.z * up, x0.w * up, bh.u[1], bl.u[1]);
-      split_pair(x1.x * up, x1.y * up, bh.u[2], bl.u[2]);
-      split_pair(x1.z * up, x1.w * up, bh.u[3], bl.u[3]);
-      c = mfma_f16_32x32x16(a.h, bh.h, c);
-      c = mfma_f16_32x32x16(a.h, bl.h, c);
+      const uint4 au = in.sk[ks];                         // sketch row 32 wave + h, columns 16 ks + 8 half ..
+      V8H av, bh, bl;
+      av.u[0] = au.x; av.u[1] = au.y; av.u[2] = au.z; av.u[3] = au.w;
+      const uint4 uh = live ? *reinterpret_cast<const uint4 *>(sqh + h * D + 16 * ks + 8 * half) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 ul = live ? *reinterpret_cast<const uint4 *>(sql + h * D + 16 * ks + 8 * half) : make_uint4(0u, 0u, 0u, 0u);
+      bh.u[0] = uh.x; bh.u[1] = uh.y; bh.u[2] = uh.z; bh.u[3] = uh.w;
+      bl.u[0] = ul.x; bl.u[1] = ul.y; bl.u[2] = ul.z; bl.u[3] = ul.w;
+      c = mfma_f16_32x32x16(av.h, bh.h, c);
+      c = mfma_f16_32x32x16(av.h, bl.h, c);
     }
+    late_loads();
+    int ex = 0;
+    if (live) (void)frexpf(sst[4 * h], &ex);
+    const int sexp = min(14 - ex, 100);
     // lane holds rows 8 (q / 4) + 4 half + q % 4 of the tile, column h
     float mp = 0.f, s2 = 0.f;
 #pragma unroll
@@ -435,97 +488,87 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
     mp = fmaxf(mp, swap_half_f(mp));
     s2 += swap_half_f(s2);
     if (live && half == 0) { sps[(wave * 8 + h) * 2] = mp; sps[(wave * 8 + h) * 2 + 1] = s2; }
+  } else {
+    late_loads();
+    if (tid - (D / 32) * kWave < NB) {
+      const int s = tid - (D / 32) * kWave;
+      sb[s] = basis_coeff(cent, KW, basis_mask(KW, s));
+    }
   }
   lds_barrier();
 
-  // Per head: exponents and constants {2^-(7+e_lm), c[L-1] sum q',
-  // 2^-(7+e_qj), sum p} (every wave derives the ones it needs from the
-  // statistics; wave 0 also records them). Then one wave per operand slot
-  // group (rg, mf): lane slot l = row l%16 (head 4 rg + (l%16)/4, digit
-  // l%4), K slots 16 (l/16) + 4 r + jb <-> coordinate
-  // 32 word + 8 jb + 4 (kg & 1) + r (slot_coord). The wave first writes the
-  // digit words of exactly the entries it reads -- the operand value in
-  // fixed point, 2 beta_s q'_c or 2 p_c times 2^(7 + e - c % 8) (c % 8 is the
-  // bit of the plane word whose expanded byte weighs 2^(c % 8) in the MFMA;
-  // the top bit's byte is negative), as four signed 8-bit digits -- then
-  // gathers the digit bytes with byte permutes: no block barrier between.
+  // (3) per (head, coordinate): the exponents and the digits of every
+  //     operand -- the operand value in fixed point, 2 beta_s q'_c or 2 p_c
+  //     times 2^(7 + e - c % 8) (c % 8 is the bit of the plane word whose
+  //     expanded byte weighs 2^(c % 8) in the MFMA; the top bit's byte is
+  //     negative), as four signed 8-bit digits -- each byte written straight
+  //     into the fragment layout (FRAG, over the consumed sketch): lane slot
+  //     l = row l%16 (head 4 rg + (l%16)/4, digit l%4), K slots 16 (l/16) +
+  //     4 r + jb <-> coordinate 32 word + 8 jb + 4 (kg & 1) + r
+  //     (slot_coord); coordinate 0's thread also records the head's
+  //     constants
+  uint8_t *frag = scratch + PS::FRAG;
+  const float cmax = cent[L - 1];
   float mb = 0.f;
 #pragma unroll
   for (int s = 0; s < NB; ++s) mb = fmaxf(mb, fabsf(sb[s]));
-  auto head_exps = [&](int hl, int &el, int &eq, float &sp_sum) {
+  for (int e = tid; e < GE * D; e += NW * kWave) {
+    const int hl = e / D, coord = e % D;
     float mp = 0.f, s2 = 0.f;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) { mp = fmaxf(mp, sps[(t * 8 + hl) * 2]); s2 += sps[(t * 8 + hl) * 2 + 1]; }
-    el = fixed_exponent(2.0f * mb * sst[4 * hl]);
-    eq = fixed_exponent(2.0f * mp);
-    sp_sum = s2;
-  };
-  if (wave == 0 && lane < GE) {
-    int el, eq;
-    float s2;
-    head_exps(lane, el, eq, s2);
-    scon[4 * lane] = ldexpf(1.0f, -7 - el);
-    scon[4 * lane + 1] = p.kcent[(1 << KW) - 1] * sst[4 * lane + 1];
-    scon[4 * lane + 2] = ldexpf(1.0f, -7 - eq);
-    scon[4 * lane + 3] = s2;
-  }
-  constexpr int NK = NB + 1;
-  uint32_t *tab = reinterpret_cast<uint32_t *>(scratch + PS::TAB);
-  for (int grp = wave; grp < NRG * NMF; grp += NW) {
-    const int mf = grp % NMF, rg = grp / NMF;
-    const bool qjl = mf >= NB * NH;
-    const int m = qjl ? NB : mf / NH, half = mf % NH;
-    const float coef = qjl ? 2.0f : 2.0f * sb[m];
-    // entries: head 4 rg + u (u < 4), this half's coordinate ci = lane:
-    // word 2 (ci / 32) + half (d = 128) or ci / 32 (d = 64)
-    const int ci = lane;
-    const int word = (D == 128) ? (2 * (ci / 32) + half) : (ci / 32);
-    const int coord = 32 * word + (ci % 32);
-    const int k = coord & 7;
+    const int el = fixed_exponent(2.0f * mb * sst[4 * hl]);
+    const int eq = fixed_exponent(2.0f * mp);
+    const int k = coord & 7, word = coord >> 5;
+    const int half = (D == 128) ? (word & 1) : 0;
+    const int kg = 2 * ((D == 128) ? (word >> 1) : word) + (k >> 2);
+    const int j = 4 * (k & 3) + ((coord >> 3) & 3);
+    const int rg = hl >> 2, u = hl & 3;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int hl = 4 * rg + u;
-      if (hl < GE) {
-        int el, eq;
-        float s2;
-        head_exps(hl, el, eq, s2);
-        float v = ldexpf(coef * (qjl ? sp : sq)[hl * D + coord], 7 - k + (qjl ? eq : el));
-        if (k == 7) v = -v;
-        tab[(hl * NK + m) * D + coord] = signed_digits(__float2int_rn(v));
-      }
-    }
-    wait_lds();                                   // this wave's table writes before its reads
-    const int l = lane, hl = 4 * rg + (l % 16) / 4, sd = l % 4, kg = l / 16;
-    uint4 out = make_uint4(0u, 0u, 0u, 0u);
-    if (hl < GE) {
-      const int w2 = (D == 128) ? (2 * (kg >> 1) + half) : (kg >> 1);
-      const uint32_t *row = tab + (hl * NK + m) * D + 32 * w2 + 4 * (kg & 1);
-      uint4 q4[4];
+    for (int m = 0; m < NK; ++m) {
+      const bool qjl = m == NB;
+      const float coef = qjl ? 2.0f : 2.0f * sb[m];
+      float v = ldexpf(coef * (qjl ? sp : sq)[hl * D + coord], 7 - k + (qjl ? eq : el));
+      if (k == 7) v = -v;
+      const uint32_t dig = signed_digits(__float2int_rn(v));
+      uint8_t *dst = frag + (rg * NMF + m * NH + half) * 1024 + (16 * kg + 4 * u) * 16 + j;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) q4[jb] = *reinterpret_cast<const uint4 *>(row + 8 * jb);
-      const uint32_t sel = 0x0c0c0000u | (static_cast<uint32_t>(4 + sd) << 8) | static_cast<uint32_t>(sd);
-      auto gather = [&](uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3) {
-        const uint32_t t01 = __builtin_amdgcn_perm(e1, e0, sel);
-        const uint32_t t23 = __builtin_amdgcn_perm(e3, e2, sel);
-        return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-      };
-      out.x = gather(q4[0].x, q4[1].x, q4[2].x, q4[3].x);
-      out.y = gather(q4[0].y, q4[1].y, q4[2].y, q4[3].y);
-      out.z = gather(q4[0].z, q4[1].z, q4[2].z, q4[3].z);
-      out.w = gather(q4[0].w, q4[1].w, q4[2].w, q4[3].w);
+      for (int sd = 0; sd < 4; ++sd) dst[16 * sd] = static_cast<uint8_t>(dig >> (8 * sd));
     }
-    *reinterpret_cast<uint4 *>(scratch + (grp * kWave + l) * 16) = out;
+    if (coord == 0) {
+      scon[4 * hl] = ldexpf(1.0f, -7 - el);
+      scon[4 * hl + 1] = cmax * sst[4 * hl + 1];
+      scon[4 * hl + 2] = ldexpf(1.0f, -7 - eq);
+      scon[4 * hl + 3] = s2;
+    }
   }
   lds_barrier();
+
+  // (4) every wave loads every fragment; rows of absent heads (never
+  //     written above) are zeroed
+  const int kgl = lane / 16;
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg) {
+    const bool live = 4 * rg + (lane % 16) / 4 < GE;
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(frag + ((rg * NMF + mf) * kWave + lane) * 16);
+      a[rg][mf] = live ? v4i{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)}
+                       : v4i{0, 0, 0, 0};
+    }
+    const int h = 4 * rg + kgl;
+    fh[rg] = (h < GE) ? *reinterpret_cast<const float4 *>(scon + 4 * h) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 }
 
-// The lane's operands and head constants from the prepared scratch.
+// The lane's operands and head constants from a prepared record copied to
+// the start of the scratch (fragments, then the constants).
 template <int D, int KW, int NRG>
 __device__ __forceinline__ void load_prepared(const uint8_t *scratch, int GE, v4i (&a)[NRG][PrepShape<D, KW, NRG>::NMF],
                                               float4 (&fh)[NRG]) {
   using PS = PrepShape<D, KW, NRG>;
   const int lane = lane_id(), kg = lane / 16;
-  const float *scon = reinterpret_cast<const float *>(scratch + PS::SCON);
+  const float *scon = reinterpret_cast<const float *>(scratch + PS::REC_FRAG);
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
 #pragma unroll
@@ -954,10 +997,11 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
 //  4. refills the stage buffer with the split NST (ring depth) ahead.
 // Decode writes the block's partial {m, l, acc} to the workspace;
 // merge_kernel combines them.
-template <int D, int KW, int VW, int NRG, bool LOGITS, bool APPEND = false, bool PREPARED = false>
+template <int D, int KW, int VW, int NRG, bool LOGITS, bool APPEND = false, bool PREPARED = false, int NWAVE = D / 16>
 __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int SPLIT = LOGITS ? kLogitSplit : attend_split<D, KW, VW, NRG>();
-  using SH = ScanShape<D, KW, VW, LOGITS, SPLIT>;
+  static_assert(LOGITS || NWAVE == D / 16, "decode: one wave per 16 value coordinates");
+  using SH = ScanShape<D, KW, VW, LOGITS, SPLIT, NWAVE>;
   constexpr bool K8 = SH::K8;
   static_assert(!(K8 && (LOGITS || APPEND)), "fp8 keys: decode attention only");
   using PS = PrepShape<D, K8 ? 1 : KW, NRG>;
@@ -1055,10 +1099,10 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
       issue_q_rows<D>(p, bh, GE, ring + PREP_AT, wave);
       wait_vm<0>();
       lds_barrier();
-      issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx, ring, wave);
+      issue_split<D, KW, VW, LOGITS, SPLIT, NWAVE>(sa, bx, ring, wave);
       k8_operands<D, NRG>(p, GE, ring + PREP_AT, a8);
       lds_barrier();                               // every wave holds its operands
-      for (int k = 1; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+      for (int k = 1; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT, NWAVE>(sa, bx + k * nb, ring + k * SB, wave);
     }
   } else if constexpr (PREPARED) {
     if (ns > 0) {
@@ -1068,26 +1112,44 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
       constexpr int FW = NRG * NMF;                  // 1 KB fragments: 64 lanes x 16 bytes
       for (int f = wave; f < FW; f += NW) dma16_at(src + (f * kWave + lane) * 16, ring + PREP_AT + f * 1024);
       if (wave == 0 && lane < 8)
-        dma16_at(src + prepared_stride(D, KW) - 128 + 16 * lane, ring + PREP_AT + PS::SCON);
-      wait_vm<0>();
+        dma16_at(src + prepared_stride(D, KW) - 128 + 16 * lane, ring + PREP_AT + PS::REC_FRAG);
+      // every stage's key loads behind the record's, then a wait for the
+      // record alone
+      const int first = min(ns, NST);
+      for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT, NWAVE>(sa, bx + k * nb, ring + k * SB, wave);
+      wait_splits<P>(first);
       lds_barrier();
-      for (int k = 0; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
       load_prepared<D, KW, NRG>(ring + PREP_AT, GE, a, fh);
     }
   } else {
     if (ns > 0) {
-      // the preparation's inputs first, alone; the splits that do not
-      // overlap its scratch are issued once the queries are rotated
-      issue_prep<D, KW, NRG>(p, bh, GE, ring + PREP_AT, wave);
+      // the preparation's inputs first, then the first splits that do not
+      // overlap its scratch (all of them for the logit scan, the first one
+      // for decode): their loads stream in during the preparation
+      PrepIn<D, NWAVE> pin;
+      issue_prep<D, KW, NRG, NWAVE>(p, bh, GE, ring + PREP_AT, wave, pin);
       const int first = SEP ? min(ns, NST) : 1;
-      wait_vm<0>();
-      lds_barrier();
-      group_prep<D, KW, NRG>(p, GE, ring + PREP_AT, [&] {
-        for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
-      });
-      load_prepared<D, KW, NRG>(ring + PREP_AT, GE, a, fh);
-      lds_barrier();                               // every wave holds its operands
-      for (int k = first; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT>(sa, bx + k * nb, ring + k * SB, wave);
+      // waves with no part in the rotation or the sketch product issue their
+      // key loads at once, behind their preparation loads; the others (the
+      // preparation's critical path: issuing a split holds a wave for a
+      // while) once their part is done
+      const bool early = wave >= D / 32 && wave >= GE;
+      // every wave's preparation loads go out before the first key load
+      __builtin_amdgcn_s_barrier();
+      if (early) {
+        for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT, NWAVE>(sa, bx + k * nb, ring + k * SB, wave);
+        wait_splits<P>(first);                     // this wave's preparation load, issued before
+      } else {
+        wait_vm<0>();
+      }
+      group_prep<D, KW, NRG, NWAVE>(p, GE, ring + PREP_AT, pin, [&] {
+        if (!early)
+          for (int k = 0; k < first; ++k) issue_split<D, KW, VW, LOGITS, SPLIT, NWAVE>(sa, bx + k * nb, ring + k * SB, wave);
+      }, a, fh);
+      if constexpr (!SEP) {
+        lds_barrier();                             // every wave holds its operands; the scratch is free
+        for (int k = first; k < min(ns, NST); ++k) issue_split<D, KW, VW, LOGITS, SPLIT, NWAVE>(sa, bx + k * nb, ring + k * SB, wave);
+      }
     }
   }
 
@@ -1271,7 +1333,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
     // 4. refill this stage (this wave's region only; its reads are done)
     if (it + NST < ns) {
       wait_lds();
-      issue_split<D, KW, VW, LOGITS, SPLIT>(sa, sp + NST * nb, buf, wave);
+      issue_split<D, KW, VW, LOGITS, SPLIT, NWAVE>(sa, sp + NST * nb, buf, wave);
     }
   }
   if constexpr (LOGITS) return;
@@ -1315,15 +1377,25 @@ __global__ __launch_bounds__(4 * D) void append_decode_kernel(ScanParams p) {
   scan_block<D, KW, VW, NRG, false, true>(p);
 }
 
+// Waves per logit-scan block: twice the decode block's for chunks of up to 4
+// heads (the A operands then fit in the registers of four waves per SIMD),
+// so that the matrix and vector pipes of each SIMD can overlap across waves.
+template <int D, int NRG>
+struct LogitWaves {
+  static constexpr int value = NRG == 1 ? D / 8 : D / 16;
+};
+
 template <int D, int KW, int NRG>
-__global__ __launch_bounds__(4 * D) void logits_kernel(ScanParams p) {
-  scan_block<D, KW, 1, NRG, true>(p);
+__global__ __launch_bounds__(kWave * (NRG == 1 ? D / 8 : D / 16)) void logits_kernel(ScanParams p) {
+  constexpr int NWL = LogitWaves<D, NRG>::value;
+  scan_block<D, KW, 1, NRG, true, false, false, NWL>(p);
 }
 
 // The logit scan from prepared queries (tq_prepare_queries).
 template <int D, int KW, int NRG>
-__global__ __launch_bounds__(4 * D) void logits_prepared_kernel(ScanParams p) {
-  scan_block<D, KW, 1, NRG, true, false, true>(p);
+__global__ __launch_bounds__(kWave * (NRG == 1 ? D / 8 : D / 16)) void logits_prepared_kernel(ScanParams p) {
+  constexpr int NWL = LogitWaves<D, NRG>::value;
+  scan_block<D, KW, 1, NRG, true, false, true, NWL>(p);
 }
 
 // The query preparation of one (group, head chunk) alone, as a scan block
@@ -1336,14 +1408,30 @@ __global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
   const int GE = min(4 * NRG, p.group - p.h0);
   const int64_t bh = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-  issue_prep<D, KW, NRG>(p, bh, GE, scratch, wave);
+  PrepIn<D, D / 16> pin;
+  issue_prep<D, KW, NRG>(p, bh, GE, scratch, wave, pin);
   wait_vm<0>();
-  lds_barrier();
-  group_prep<D, KW, NRG>(p, GE, scratch, [] {});   // ends with a barrier
+  v4i a[NRG][PS::NMF];
+  float4 fh[NRG];
+  group_prep<D, KW, NRG>(p, GE, scratch, pin, [] {}, a, fh);
+  // fragment f = rg NMF + mf (as the scan blocks hold it) is written by
+  // wave f % NW from its registers; the constants from the scratch
   uint8_t *dst = p.prepared_w + (bh * p.n_hchunks + p.h0 / 8) * prepared_stride(D, KW);
-  constexpr int FB = NRG * PS::NMF * 1024;
-  for (int off = static_cast<int>(threadIdx.x) * 16; off < FB; off += 4 * D * 16)
-    *reinterpret_cast<uint4 *>(dst + off) = *reinterpret_cast<const uint4 *>(scratch + off);
+  constexpr int NW = D / 16;
+  const int lane = lane_id();
+#pragma unroll
+  for (int rg = 0; rg < NRG; ++rg)
+#pragma unroll
+    for (int mf = 0; mf < PS::NMF; ++mf) {
+      const int f = rg * PS::NMF + mf;
+      if (f % NW == wave) {
+        const v4i &v = a[rg][mf];
+        *reinterpret_cast<uint4 *>(dst + (f * kWave + lane) * 16) =
+            make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
+                       static_cast<uint32_t>(v[3]));
+      }
+    }
+  (void)fh;
   if (threadIdx.x < 8)
     *reinterpret_cast<uint4 *>(dst + prepared_stride(D, KW) - 128 + 16 * threadIdx.x) =
         *reinterpret_cast<const uint4 *>(scratch + PS::SCON + 16 * threadIdx.x);
@@ -1421,13 +1509,14 @@ static void launch_decode_kv(const ScanParams &p, dim3 grid, hipStream_t st) {
 template <int D, int KW, int MODE>
 static void launch_logits_k(const ScanParams &p, dim3 grid, hipStream_t st) {
   dim3 block(4 * D);
+  const dim3 b1(kWave * LogitWaves<D, 1>::value), b2(kWave * LogitWaves<D, 2>::value);
   const bool two = p.group - p.h0 > 4;
   if constexpr (MODE == 0) {
-    if (two) hipLaunchKernelGGL((logits_kernel<D, KW, 2>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((logits_kernel<D, KW, 1>), grid, block, 0, st, p);
+    if (two) hipLaunchKernelGGL((logits_kernel<D, KW, 2>), grid, b2, 0, st, p);
+    else hipLaunchKernelGGL((logits_kernel<D, KW, 1>), grid, b1, 0, st, p);
   } else if constexpr (MODE == 1) {
-    if (two) hipLaunchKernelGGL((logits_prepared_kernel<D, KW, 2>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((logits_prepared_kernel<D, KW, 1>), grid, block, 0, st, p);
+    if (two) hipLaunchKernelGGL((logits_prepared_kernel<D, KW, 2>), grid, b2, 0, st, p);
+    else hipLaunchKernelGGL((logits_prepared_kernel<D, KW, 1>), grid, b1, 0, st, p);
   } else {
     dim3 g1(1, grid.y);
     if (two) hipLaunchKernelGGL((prep_kernel<D, KW, 2>), g1, block, 0, st, p);
