@@ -319,6 +319,10 @@ constexpr int attend_split() {
   return ring + NRG * (512 / 64) * 1024 <= 160 * 1024 - 4096 ? 512 : 256;
 }
 
+// First head of this block's chunk of 8 heads: the chunks of a group are
+// the launch grid's z dimension.
+__device__ __forceinline__ int head_chunk0() { return 8 * static_cast<int>(blockIdx.z); }
+
 // Row of q holding head v of the group of (b, kv-head kvh).
 __device__ __forceinline__ int64_t query_row(const ScanParams &p, int64_t b, int64_t kvh, int v) {
   const int gq = p.qgroup;
@@ -344,7 +348,7 @@ __device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int 
     for (int k = 0; k < PI::HPW; ++k) {
       const int h = wave + NW * k;
       if (h < GE) {
-        const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, p.h0 + h);
+        const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, head_chunk0() + h);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int64_t i = row * D + E * lane + e;
@@ -614,7 +618,7 @@ __device__ __forceinline__ void issue_q_rows(const ScanParams &p, int64_t bh, in
   const int upr = D * es / 16;
   const int unit = wave * kWave + lane_id();
   if (unit < GE * upr) {
-    const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, p.h0 + unit / upr);
+    const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, head_chunk0() + unit / upr);
     dma16_at(static_cast<const uint8_t *>(p.q) + row * D * es + (unit % upr) * 16, scratch + unit * 16);
   }
 }
@@ -756,7 +760,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
   if (ctx < 1) {                                   // nothing to append: an empty partial
     for (int e = tid; e < GE * (D + 2); e += 4 * D) {
       const int hl = e / (D + 2), i = e % (D + 2);
-      part[(p.h0 + hl) * (D + 2) + i] = (i == 0) ? -INFINITY : 0.f;
+      part[(head_chunk0() + hl) * (D + 2) + i] = (i == 0) ? -INFINITY : 0.f;
     }
     return;
   }
@@ -791,7 +795,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int i = lane + kWave * e;
-        x[k][e] = isq ? load_elem(p.q, (b * n_q + kvh * G + p.h0 + r) * D + i, p.xt)
+        x[k][e] = isq ? load_elem(p.q, (b * n_q + kvh * G + head_chunk0() + r) * D + i, p.xt)
                       : load_elem(r == GE ? p.k_new : p.v_new, bh * D + i, p.kv_t);
         sgn[k][e] = sg[i];
       }
@@ -970,7 +974,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
     slm = wave_sum(slm);
     sqj = wave_sum(sqj);
     const float logit = shat[0] * fmaf(kappa * shat[1], sqj, slm);
-    float *ph = part + (p.h0 + hl) * (D + 2);
+    float *ph = part + (head_chunk0() + hl) * (D + 2);
     if (lane == 0) { ph[0] = logit * p.sm_scale; ph[1] = 1.0f; }
 #pragma unroll
     for (int e = 0; e < E; ++e) ph[2 + lane + kWave * e] = vh[lane + kWave * e];
@@ -1036,7 +1040,8 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
 
   const int G = p.group;
   const int n_q = p.n_kv * G;
-  const int GE = min(GMAX, G - p.h0);
+  const int h0 = head_chunk0();
+  const int GE = min(GMAX, G - h0);
   // append launches: grid (groups, nb + 1) with the append blocks at y = 0,
   // so that they are dispatched before every scan block (interleaved with
   // the scan blocks, each finishing one would start another scan block late)
@@ -1044,7 +1049,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   const int64_t b = bh / p.n_kv;
   const int64_t kvh = bh % p.n_kv;
   // prefill: the launch's last head sees the most tokens
-  int64_t ctx64 = p.pos0 ? static_cast<int64_t>(p.pos0[b]) + (p.h0 + GE - 1) / p.qgroup + 1
+  int64_t ctx64 = p.pos0 ? static_cast<int64_t>(p.pos0[b]) + (h0 + GE - 1) / p.qgroup + 1
                          : (p.ctx_lens ? static_cast<int64_t>(p.ctx_lens[b]) : p.max_ctx);
   ctx64 = ctx64 < 0 ? 0 : (ctx64 > p.max_ctx ? p.max_ctx : ctx64);
   // append: one block per group encodes the new token (the last slot of the
@@ -1079,7 +1084,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   int lim[NRG];
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
-    int64_t l = p.pos0 ? static_cast<int64_t>(p.pos0[b]) + (p.h0 + 4 * rg + kg) / p.qgroup + 1 : ctx64;
+    int64_t l = p.pos0 ? static_cast<int64_t>(p.pos0[b]) + (h0 + 4 * rg + kg) / p.qgroup + 1 : ctx64;
     lim[rg] = static_cast<int>(l < 0 ? 0 : (l > ctx64 ? ctx64 : l));
   }
 
@@ -1108,7 +1113,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
     if (ns > 0) {
       // the prepared operand fragments and head constants into the
       // preparation's region (separate from the stages), then every stage
-      const uint8_t *src = p.prepared + (bh * p.n_hchunks + p.h0 / 8) * prepared_stride(D, KW);
+      const uint8_t *src = p.prepared + (bh * p.n_hchunks + h0 / 8) * prepared_stride(D, KW);
       constexpr int FW = NRG * NMF;                  // 1 KB fragments: 64 lanes x 16 bytes
       for (int f = wave; f < FW; f += NW) dma16_at(src + (f * kWave + lane) * 16, ring + PREP_AT + f * 1024);
       if (wave == 0 && lane < 8)
@@ -1199,7 +1204,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
 #pragma unroll
         for (int rg = 0; rg < NRG; ++rg) {
           const int hl = 4 * rg + kg;
-          if (valid && hl < GE) p.logits[(b * n_q + kvh * G + p.h0 + hl) * p.max_ctx + sp * S + tl] = lr[rg];
+          if (valid && hl < GE) p.logits[(b * n_q + kvh * G + h0 + hl) * p.max_ctx + sp * S + tl] = lr[rg];
         }
         (void)lg; (void)nvv;
       } else {
@@ -1349,7 +1354,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) {
     const int hl = 4 * rg + kg;
-    if (hl < GE) part[(p.h0 + hl) * (D + 2) + 2 + 16 * wave + col] = accf[rg];
+    if (hl < GE) part[(h0 + hl) * (D + 2) + 2 + 16 * wave + col] = accf[rg];
   }
   if (wave == 0 && col == 0) {
 #pragma unroll
@@ -1358,8 +1363,8 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
       if (hl < GE) {
         float l = 0.f;
         for (int w = 0; w < NW; ++w) l += spm[w][hl];
-        part[(p.h0 + hl) * (D + 2)] = m_run[rg];
-        part[(p.h0 + hl) * (D + 2) + 1] = l;
+        part[(h0 + hl) * (D + 2)] = m_run[rg];
+        part[(h0 + hl) * (D + 2) + 1] = l;
       }
     }
   }
@@ -1405,7 +1410,7 @@ template <int D, int KW, int NRG>
 __global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
   using PS = PrepShape<D, KW, NRG>;
   __shared__ __attribute__((aligned(1024))) uint8_t scratch[PS::BYTES];
-  const int GE = min(4 * NRG, p.group - p.h0);
+  const int GE = min(4 * NRG, p.group - head_chunk0());
   const int64_t bh = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   PrepIn<D, D / 16> pin;
@@ -1416,7 +1421,7 @@ __global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
   group_prep<D, KW, NRG>(p, GE, scratch, pin, [] {}, a, fh);
   // fragment f = rg NMF + mf (as the scan blocks hold it) is written by
   // wave f % NW from its registers; the constants from the scratch
-  uint8_t *dst = p.prepared_w + (bh * p.n_hchunks + p.h0 / 8) * prepared_stride(D, KW);
+  uint8_t *dst = p.prepared_w + (bh * p.n_hchunks + head_chunk0() / 8) * prepared_stride(D, KW);
   constexpr int NW = D / 16;
   const int lane = lane_id();
 #pragma unroll
@@ -1497,10 +1502,10 @@ template <int D, int KW, int VW, bool APPEND>
 static void launch_decode_kv(const ScanParams &p, dim3 grid, hipStream_t st) {
   dim3 block(4 * D);
   if constexpr (APPEND) {
-    if (p.group - p.h0 > 4) hipLaunchKernelGGL((append_decode_kernel<D, KW, VW, 2>), grid, block, 0, st, p);
+    if (p.group > 4) hipLaunchKernelGGL((append_decode_kernel<D, KW, VW, 2>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((append_decode_kernel<D, KW, VW, 1>), grid, block, 0, st, p);
   } else {
-    if (p.group - p.h0 > 4) hipLaunchKernelGGL((decode_kernel<D, KW, VW, 2>), grid, block, 0, st, p);
+    if (p.group > 4) hipLaunchKernelGGL((decode_kernel<D, KW, VW, 2>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((decode_kernel<D, KW, VW, 1>), grid, block, 0, st, p);
   }
 }
@@ -1510,7 +1515,7 @@ template <int D, int KW, int MODE>
 static void launch_logits_k(const ScanParams &p, dim3 grid, hipStream_t st) {
   dim3 block(4 * D);
   const dim3 b1(kWave * LogitWaves<D, 1>::value), b2(kWave * LogitWaves<D, 2>::value);
-  const bool two = p.group - p.h0 > 4;
+  const bool two = p.group > 4;
   if constexpr (MODE == 0) {
     if (two) hipLaunchKernelGGL((logits_kernel<D, KW, 2>), grid, b2, 0, st, p);
     else hipLaunchKernelGGL((logits_kernel<D, KW, 1>), grid, b1, 0, st, p);
@@ -1518,31 +1523,27 @@ static void launch_logits_k(const ScanParams &p, dim3 grid, hipStream_t st) {
     if (two) hipLaunchKernelGGL((logits_prepared_kernel<D, KW, 2>), grid, b2, 0, st, p);
     else hipLaunchKernelGGL((logits_prepared_kernel<D, KW, 1>), grid, b1, 0, st, p);
   } else {
-    dim3 g1(1, grid.y);
+    dim3 g1(1, grid.y, grid.z);
     if (two) hipLaunchKernelGGL((prep_kernel<D, KW, 2>), g1, block, 0, st, p);
     else hipLaunchKernelGGL((prep_kernel<D, KW, 1>), g1, block, 0, st, p);
   }
 }
 
-// Head chunks of 8 heads: every launch reads the keys (and values) once for
-// its chunk.
+// One launch per call: grid (blocks per group, groups, head chunks of 8
+// heads); every block reads its keys once for its chunk. (A chunk of up to
+// 4 heads is taken by the single-row-group kernel only when the whole group
+// has at most 4 heads.)
 template <int D, int MODE>
-hipError_t launch_logits_m(const ScanParams &p0, int kw, hipStream_t st) {
-  if (p0.batch == 0 || p0.n_kv == 0 || (MODE != 2 && p0.max_ctx == 0)) return hipSuccess;
-  dim3 grid(static_cast<uint32_t>(p0.nb), static_cast<uint32_t>(p0.batch) * p0.n_kv);
-  for (int hc = 0; hc < p0.n_hchunks; ++hc) {
-    ScanParams p = p0;
-    p.h0 = 8 * hc;
-    switch (kw) {
-      case 1: launch_logits_k<D, 1, MODE>(p, grid, st); break;
-      case 2: launch_logits_k<D, 2, MODE>(p, grid, st); break;
-      case 3: launch_logits_k<D, 3, MODE>(p, grid, st); break;
-      default: launch_logits_k<D, 4, MODE>(p, grid, st);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_logits_m(const ScanParams &p, int kw, hipStream_t st) {
+  if (p.batch == 0 || p.n_kv == 0 || (MODE != 2 && p.max_ctx == 0)) return hipSuccess;
+  dim3 grid(static_cast<uint32_t>(p.nb), static_cast<uint32_t>(p.batch) * p.n_kv, static_cast<uint32_t>(p.n_hchunks));
+  switch (kw) {
+    case 1: launch_logits_k<D, 1, MODE>(p, grid, st); break;
+    case 2: launch_logits_k<D, 2, MODE>(p, grid, st); break;
+    case 3: launch_logits_k<D, 3, MODE>(p, grid, st); break;
+    default: launch_logits_k<D, 4, MODE>(p, grid, st);
   }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 template <int D>
@@ -1560,39 +1561,37 @@ hipError_t launch_prepare_d(const ScanParams &p, int kw, hipStream_t st) {
   return launch_logits_m<D, 2>(p, kw, st);
 }
 
-// Head chunks of 8 heads, then the merge. APPEND: nb + 1 blocks per group,
-// one of them encoding the group's new token (every head chunk's launch
-// encodes it again, to the same bytes, for that chunk's partials).
+// One launch over (blocks, groups, head chunks of 8 heads), then the merge.
+// APPEND: nb + 1 blocks per group, one of them encoding the group's new
+// token (the append block of every head chunk encodes it, to the same
+// bytes, for that chunk's partials).
 template <int D, bool APPEND>
-hipError_t launch_decode_da(const ScanParams &p0, int kw, int vw, hipStream_t st) {
-  if (p0.batch == 0 || p0.n_kv == 0) return hipSuccess;
-  const uint32_t groups = static_cast<uint32_t>(p0.batch) * p0.n_kv;
-  dim3 grid = APPEND ? dim3(groups, static_cast<uint32_t>(p0.nb + 1)) : dim3(static_cast<uint32_t>(p0.nb), groups);
-  for (int hc = 0; hc < p0.n_hchunks; ++hc) {
-    ScanParams p = p0;
-    p.h0 = 8 * hc;
+hipError_t launch_decode_da(const ScanParams &p, int kw, int vw, hipStream_t st) {
+  if (p.batch == 0 || p.n_kv == 0) return hipSuccess;
+  const uint32_t groups = static_cast<uint32_t>(p.batch) * p.n_kv;
+  const uint32_t chunks = static_cast<uint32_t>(p.n_hchunks);
+  dim3 grid = APPEND ? dim3(groups, static_cast<uint32_t>(p.nb + 1), chunks)
+                     : dim3(static_cast<uint32_t>(p.nb), groups, chunks);
 #define TQ_DS_V(KK)                                                   \
-    switch (vw) {                                                     \
-      case 1: launch_decode_kv<D, KK, 1, APPEND>(p, grid, st); break; \
-      case 2: launch_decode_kv<D, KK, 2, APPEND>(p, grid, st); break; \
-      case 3: launch_decode_kv<D, KK, 3, APPEND>(p, grid, st); break; \
-      default: launch_decode_kv<D, KK, 4, APPEND>(p, grid, st);       \
-    }
-    switch (kw) {
-      case 1: TQ_DS_V(1); break;
-      case 2: TQ_DS_V(2); break;
-      case 3: TQ_DS_V(3); break;
-      case kKeyFp8:
-        if constexpr (!APPEND) TQ_DS_V(kKeyFp8);
-        break;
-      default: TQ_DS_V(4);
-    }
-#undef TQ_DS_V
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  switch (vw) {                                                       \
+    case 1: launch_decode_kv<D, KK, 1, APPEND>(p, grid, st); break;   \
+    case 2: launch_decode_kv<D, KK, 2, APPEND>(p, grid, st); break;   \
+    case 3: launch_decode_kv<D, KK, 3, APPEND>(p, grid, st); break;   \
+    default: launch_decode_kv<D, KK, 4, APPEND>(p, grid, st);         \
   }
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(static_cast<uint32_t>(p0.n_hchunks), groups), dim3(kMergeThreads), 0, st,
-                     p0);
+  switch (kw) {
+    case 1: TQ_DS_V(1); break;
+    case 2: TQ_DS_V(2); break;
+    case 3: TQ_DS_V(3); break;
+    case kKeyFp8:
+      if constexpr (!APPEND) TQ_DS_V(kKeyFp8);
+      break;
+    default: TQ_DS_V(4);
+  }
+#undef TQ_DS_V
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(chunks, groups), dim3(kMergeThreads), 0, st, p);
   return hipGetLastError();
 }
 
