@@ -12,6 +12,12 @@ Inputs are resident in HBM before timing starts; each step uses a different
 one of `--copies` independent input/cache sets (together > 1 GiB) so that
 the 256 MB Infinity Cache cannot hold the working set.
 
+The step's logit scan reads codes its own encode has just written; at 17.8
+MB they are resident in the 256 MB Infinity Cache, so the step is partly
+served from cache, and the per-kernel roofline figures (graphs of
+back-to-back calls of one kind over the rotated copies) are the ones to
+price against HBM.
+
 Printed: one JSON line. `value` is q.k logits per second over whole steps
 (encode + logit scan with its query preparation); the K timed steps (the
 two library calls per step, each step on a fresh input copy) are captured
@@ -25,8 +31,11 @@ committed profile summary while the kernel sources are unchanged. The extras tim
 fused decode attention on the batched (16 x 8192) and long-context
 (4 x 131072) decode workloads and the full-cache encode of the 22-layer
 TinyLlama-shaped prefill, the search scan (32 queries over 1,048,576
-coded vectors, then the top 100 of each), and the MSE-only ablation of the
-logit scan (the estimator without its QJL term, against exact q.k).
+coded vectors, then the top 100 of each), the MSE-only ablation of the
+logit scan (the estimator without its QJL term, against exact q.k), and the
+single-head workload (4096 fp32 keys, 16 queries; launch-latency bound,
+absolute numbers only). Every scan's HBM fraction is also given against a
+read-only stream measured on the same part (`tq_probe_read`, 4 GiB).
 """
 from __future__ import annotations
 
@@ -41,6 +50,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # B/s, MI355X datasheet
+# VALU issue: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 instruction per 4 cycles
+# per SIMD (16 lanes per cycle; the packed fp32 forms that double it are not
+# used by this library)
+VALU_PEAK = 256 * 4 * 2.4e9 / 4        # wave instructions per second (614.4 G)
+MFMA_F16_PEAK = 2.5e15                 # dense fp16 FLOP/s
 METRIC = "q·k logits/s + encode tokens/s over packed TurboQuant KV; % of HBM roofline"
 
 
@@ -52,7 +66,11 @@ def parse():
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extra sections: dec3,app3,pre3,k8v4,dec5,enc4,search,ablation")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle on the batched and long-context decode workloads in full (minutes) "
+                         "and on the 22-layer encode's layer {0, 21} x row {0, 63} slices")
+    ap.add_argument("--only", default="", help="comma list of extra sections: "
+                                               "dec3,app3,pre3,k8v4,dec5,enc4,search,ablation,single")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each timed kernel a few times eagerly, after a 1 GiB calibration copy, "
                          "for hardware-counter runs; prints no JSON line")
@@ -128,9 +146,10 @@ PROFILE_OF = {
 }
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel's sources changed since it was taken."""
+def profile_field(kernel, name):
+    """A figure (first number of the line `name: ...`) from the committed
+    counter summary of `kernel`, or None when there is none or the kernel's
+    sources changed since it was taken."""
     path = os.path.join(ROOT, PROFILE_OF.get(kernel, ""))
     if not os.path.isfile(path):
         return None
@@ -142,9 +161,14 @@ def measured_traffic(kernel):
     try:
         if fields.get("kernel_sources_sha256") != kernel_sources_digest(kernel):
             return None
-        return float(fields["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return float(fields[name].split()[0])
+    except (KeyError, ValueError, IndexError):
         return None
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary (None if stale)."""
+    return profile_field(kernel, "traffic_bytes_per_launch")
 
 
 def copy_probe(torch, gib=4, reps=5):
@@ -169,8 +193,40 @@ def copy_probe(torch, gib=4, reps=5):
     return {"bytes": 2 * n, "GBps": 2 * n / sec / 1e9, "what": f"{gib} GiB device-to-device copy, torch copy kernel"}
 
 
+def read_probe(torch, tq, gib=4, reps=5):
+    """Read-only stream over `gib` GiB (tq_probe_read): bytes per second a
+    kernel that only reads gets from HBM on this part."""
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    tq.probe_read(src, sink)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        tq.probe_read(src, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src
+    torch.cuda.empty_cache()
+    return {"bytes": n, "GBps": n / sec / 1e9, "what": f"{gib} GiB read-and-reduce stream (tq_probe_read)"}
+
+
+PROBE_GBPS = None   # set by main() once the read probe has run
+
+
 def hbm(bytes_, seconds):
     return bytes_ / seconds / HBM_PEAK if seconds > 0 else 0.0
+
+
+def of_probe(bytes_, seconds):
+    """Fraction of the measured read-only stream (None before the probe ran)."""
+    if PROBE_GBPS is None or seconds <= 0:
+        return None
+    return bytes_ / seconds / (PROBE_GBPS * 1e9)
 
 
 # ------------------------------------------------------------------ workloads
@@ -241,11 +297,13 @@ def main_decode_layer(args, torch, tq, syn):
         "encode": dict(avg_us=ks["encode"]["avg_s"] * 1e6, bytes_per_launch=bytes_encode,
                        unit="key vectors", units_per_launch=n_vec,
                        tokens_per_s=n_vec / ks["encode"]["avg_s"],
-                       hbm_frac=hbm(bytes_encode, ks["encode"]["avg_s"])),
+                       hbm_frac=hbm(bytes_encode, ks["encode"]["avg_s"]),
+                       mfma_flops_per_launch=n_vec * 2 * w.d * w.d),
         "logits": dict(avg_us=ks["logits"]["avg_s"] * 1e6, bytes_per_launch=bytes_logits,
                        unit="keys (x32 query heads)", units_per_launch=n_vec,
                        logits_per_s=logits_per_step / ks["logits"]["avg_s"],
-                       hbm_frac=hbm(bytes_logits, ks["logits"]["avg_s"])),
+                       hbm_frac=hbm(bytes_logits, ks["logits"]["avg_s"]),
+                       frac_of_read_probe=of_probe(bytes_logits, ks["logits"]["avg_s"])),
     }
     return dict(w=w, total_s=total, wall_s=wall, steps=args.steps, kernels=kern,
                 value=logits_per_step * args.steps / total, unit="logits/s",
@@ -289,7 +347,7 @@ def decode_workload(torch, tq, syn, cfg, copies, steps):
     bytes_ = th * (kc.record_bytes + 4 + vc.lm_bits * w.d // 8 + 2) + w.batch * w.n_q * w.d * 4
     return dict(workload=w.name, avg_us=avg * 1e6, bytes_per_launch=bytes_, unit="token-heads",
                 units_per_launch=th, attended_logits_per_s=w.batch * w.n_q * w.n_tok / avg,
-                hbm_frac=hbm(bytes_, avg), copies=copies)
+                hbm_frac=hbm(bytes_, avg), frac_of_read_probe=of_probe(bytes_, avg), copies=copies)
 
 
 def append_step_workload(torch, tq, syn, cfg, copies, steps):
@@ -450,7 +508,8 @@ def k8v4_ablation(torch, tq, syn, copies, steps):
         t = time_replays(torch, [g], max(1, steps // copies)) / copies
         bytes_ = w.n_seq * w.n_tok * (key_bytes + vc.lm_bits * w.d // 8 + 2) + w.batch * w.n_q * w.d * 4
         res[name] = dict(avg_us=t * 1e6, bytes_per_token_head=key_bytes + vc.lm_bits * w.d // 8 + 2,
-                         hbm_frac=hbm(bytes_, t), rel_rms_error_vs_exact=float(err))
+                         hbm_frac=hbm(bytes_, t), frac_of_read_probe=of_probe(bytes_, t),
+                         rel_rms_error_vs_exact=float(err))
         del g
     return dict(workload=w.name, copies=copies, **res)
 
@@ -556,7 +615,9 @@ def search_workload(torch, tq, syn, copies, steps):
     return dict(workload=w.name, search_avg_us=t_all * 1e6, scan_avg_us=t_scan * 1e6, topk_avg_us=t_rank * 1e6,
                 scores_per_s=w.n_q * w.n_db / t_all, queries_per_s=w.n_q / t_all,
                 scan_bytes_per_launch=b_scan, scan_hbm_frac=hbm(b_scan, t_scan),
-                topk_bytes_per_launch=b_rank, topk_hbm_frac=hbm(b_rank, t_rank), k=w.k, copies=copies)
+                scan_frac_of_read_probe=of_probe(b_scan, t_scan),
+                topk_bytes_per_launch=b_rank, topk_hbm_frac=hbm(b_rank, t_rank),
+                topk_frac_of_read_probe=of_probe(b_rank, t_rank), k=w.k, copies=copies)
 
 
 def mse_keys_ablation(torch, tq, syn, steps):
@@ -594,51 +655,179 @@ def mse_keys_ablation(torch, tq, syn, steps):
     return out
 
 
+def single_head_workload(torch, tq, syn, reps=50):
+    """The single-head workload: encode of 4096 fp32 keys (d 128, 2 Lloyd-Max
+    bits + QJL) and all 16 x 4096 logits. Its 2.8 MB fit any cache and a call
+    is a few microseconds of launch latency, so the figures are absolute
+    rates (graphs of back-to-back calls, HIP events), not HBM fractions."""
+    w = syn.WORKLOADS[1]
+    dev = "cuda"
+    kc, _, _ = setup_codecs(torch, tq, syn, w, dev)
+    x = syn.keys(w, device=dev)
+    q = syn.queries(w, device=dev)
+    codes, scal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+    out = torch.empty((w.batch, w.n_q, w.n_tok), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    enc = lambda: tq.encode_kv(kc, x, codes, scal)
+    lgt = lambda: tq.logits(kc, q, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok, out=out)
+    n = 16
+    t_enc = time_replays(torch, [capture(torch, [enc] * n)], reps) / n
+    t_lgt = time_replays(torch, [capture(torch, [lgt] * n)], reps) / n
+    t_step = time_replays(torch, [capture(torch, [f for _ in range(n) for f in (enc, lgt)])], reps) / n
+    return dict(workload=w.name, encode_us=t_enc * 1e6, logits_us=t_lgt * 1e6, step_us=t_step * 1e6,
+                encode_tokens_per_s=w.n_vec / t_enc, logits_per_s=w.n_q * w.n_tok / t_lgt,
+                step_logits_per_s=w.n_q * w.n_tok / t_step)
+
+
 # ------------------------------------------------------------------ CPU baseline
 
 
-def cpu_baseline(w, syn, torch):
-    """The oracle (numpy fp64) on the host cores, on a bounded sample of the
-    headline step: the prefill of 2 KV heads encoded, then the logits of
-    their query heads; scaled to the step's mix (encode of all keys + all
-    logits)."""
-    import numpy as np
-    import oracle as O
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
-    s, S = syn.key_codec_randoms(w.cfg, w.d)
-    c, t = O.make_codebook(w.d, w.key_lm_bits)
-    kv_heads = w.n_kv                          # all KV heads: the whole step, no extrapolation
+        return 1
+
+
+def _oracle_decode(O, np, syn, torch, w, kvs, q, lens, s, S, sv, ck, tk, cv, tv):
+    """Encode a sample's keys and values with the oracle, then its decode attention."""
+    k, v = kvs
+    ek = O.encode(k, s, ck, tk, S)
+    ev = O.encode(v, sv, cv, tv)
+    return O.decode_attend(q, s, ck, S, ek["idx"], ek["sigma"], ek["nhat"], ek["ghat"], sv, cv, ev["idx"],
+                           ev["nhat"], lens, 1.0 / math.sqrt(w.d), w.group)
+
+
+def cpu_baseline(w, syn, torch, full=False):
+    """The oracle (numpy fp64) on the host cores.
+
+    Headline (`value`): the decode-layer step (encode of the 262144-key
+    prefill + all 1,048,576 logits), median of 3 runs with every thread
+    numpy's BLAS has. Beside it: the single-head workload at 1 thread and at
+    all threads (median of 3), and one run per sample of the batched-decode
+    and long-context workloads (encode of the sample's K and V + its decode
+    attention) and of the 22-layer encode, each scaled linearly to its
+    whole workload and labelled extrapolated unless it is the whole workload
+    (`full`: the two decode workloads in full, chunked by batch row, and the
+    22-layer encode on layers {0, 21} x batch rows {0, 63})."""
     import dataclasses
-    ws = dataclasses.replace(w, n_kv=kv_heads, batch=1)
-    x = syn.keys(ws).double().numpy()          # [kv_heads, n_tok, d]
-    q = syn.queries(ws).double().numpy()[0]    # [kv_heads * group, d]
-    n = kv_heads * w.n_tok
-    reps = []
-    for _ in range(3):
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    threads = blas_threads()
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[1]
+
+    # headline: the decode-layer step, all 8 KV heads
+    s, S = syn.key_codec_randoms(w.cfg, w.d)
+    sn, Sn = s.numpy(), S.numpy()
+    c, t = O.make_codebook(w.d, w.key_lm_bits)
+    ws = dataclasses.replace(w, batch=1)
+    x = syn.keys(ws).double().numpy()          # [n_kv, n_tok, d]
+    q = syn.queries(ws).double().numpy()[0]    # [n_q, d]
+    encs = {}
+
+    def enc_all():
+        encs["e"] = [O.encode(x[h], sn, c, t, Sn) for h in range(w.n_kv)]
+
+    def lg_all():
+        for h, e in enumerate(encs["e"]):
+            O.key_logits(q[h * w.group:(h + 1) * w.group], sn, c, Sn, e["idx"], e["sigma"], e["nhat"], e["ghat"])
+    enc_s = med3(enc_all)
+    lg_s = med3(lg_all)
+    step_s = enc_s + lg_s
+    del x, encs
+    out = {"value": w.batch * w.n_q * w.n_tok / step_s, "unit": "logits/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"numpy fp64 oracle, median of 3 runs, {threads} BLAS threads: the whole decode-layer step "
+                     f"(encode of {w.n_vec} keys + {w.batch * w.n_q * w.n_tok} logits)",
+           "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": threads,
+           "step_s": step_s, "encode_keys_per_s": w.n_vec / enc_s, "logits_per_s": w.batch * w.n_q * w.n_tok / lg_s}
+
+    # the single-head workload, 1 thread and all threads
+    w1 = syn.WORKLOADS[1]
+    s1, S1 = syn.key_codec_randoms(w1.cfg, w1.d)
+    c1, t1 = O.make_codebook(w1.d, w1.key_lm_bits)
+    x1 = syn.keys(w1).double().numpy()[0]
+    q1 = syn.queries(w1).double().numpy()[0]
+
+    def step1():
+        e = O.encode(x1, s1.numpy(), c1, t1, S1.numpy())
+        O.key_logits(q1, s1.numpy(), c1, S1.numpy(), e["idx"], e["sigma"], e["nhat"], e["ghat"])
+    single = {}
+    for label, lim in (("1_thread", 1), ("all_threads", threads)):
+        with threadpool_limits(limits=lim):
+            sec = med3(step1)
+        single[label] = {"threads": lim, "step_s": sec, "encode_tokens_per_s_incl_logits": w1.n_vec / sec,
+                         "logits_per_s": w1.n_q * w1.n_tok / sec}
+    out["single_head"] = single
+
+    # decode-attention workloads: samples (or, full, every batch row)
+    work = {}
+    for cfg in (3, 5):
+        wc = syn.WORKLOADS[cfg]
+        sk, Sk = syn.key_codec_randoms(cfg, wc.d)
+        sv = syn.value_codec_randoms(cfg, wc.d).numpy()
+        ck, tk = O.make_codebook(wc.d, wc.key_lm_bits)
+        cv, tv = O.make_codebook(wc.d, wc.val_bits)
+        rows = list(range(wc.batch)) if full else [0]
+        n_kv_sample = wc.n_kv if (full or cfg == 3) else 1
+        ws1 = dataclasses.replace(wc, batch=1, n_kv=n_kv_sample)
+        qa = syn.queries(wc).double().numpy()
+        sec = 0.0
+        for b in rows:
+            kv = (syn.kv_slice(ws1, 0, 0, b).double().numpy(), syn.kv_slice(ws1, 1, 0, b).double().numpy())
+            qb = qa[b:b + 1, :n_kv_sample * wc.group]
+            t0 = time.perf_counter()
+            _oracle_decode(O, np, syn, torch, ws1, kv, qb, [wc.n_tok], sk.numpy(), Sk.numpy(), sv, ck, tk, cv, tv)
+            sec += time.perf_counter() - t0
+            del kv
+        done = len(rows) * n_kv_sample
+        whole = wc.batch * wc.n_kv
+        work[f"decode_attend_cfg{cfg}"] = {
+            "workload": wc.name, "sample": f"{len(rows)} batch row(s) x {n_kv_sample} KV head(s) of "
+                                           f"{wc.batch} x {wc.n_kv}: encode of K and V + decode attention",
+            "sample_s": sec, "extrapolated": done < whole, "whole_s": sec * whole / done,
+            "attended_logits_per_s": wc.batch * wc.n_q * wc.n_tok / (sec * whole / done)}
+    # 22-layer encode: (layer, batch row) slices of 32 heads x 4096 tokens, K and V
+    w4 = syn.WORKLOADS[4]
+    sk4, Sk4 = syn.key_codec_randoms(4, w4.d)
+    sv4 = syn.value_codec_randoms(4, w4.d).numpy()
+    ck4, tk4 = O.make_codebook(w4.d, w4.key_lm_bits)
+    cv4, tv4 = O.make_codebook(w4.d, w4.val_bits)
+    slices = [(0, 0), (0, 63), (21, 0), (21, 63)] if full else [(0, 0)]
+    sec = 0.0
+    for layer, b in slices:
+        k = syn.kv_slice(w4, 0, layer, b).double().numpy()
+        v = syn.kv_slice(w4, 1, layer, b).double().numpy()
         t0 = time.perf_counter()
-        encs = [O.encode(x[h], s.numpy(), c, t, S.numpy()) for h in range(kv_heads)]
-        t1 = time.perf_counter()
-        for h, enc in enumerate(encs):
-            O.key_logits(q[h * w.group:(h + 1) * w.group], s.numpy(), c, S.numpy(), enc["idx"], enc["sigma"],
-                         enc["nhat"], enc["ghat"])
-        t2 = time.perf_counter()
-        reps.append((t1 - t0, t2 - t1))
-    enc_s = sorted(r[0] for r in reps)[1]
-    lg_s = sorted(r[1] for r in reps)[1]
-    # whole step: encode all n_vec keys, compute all n_q * n_tok logits
-    step_s = enc_s * (w.n_vec / n) + lg_s * (w.batch * w.n_q * w.n_tok) / (kv_heads * w.group * w.n_tok)
-    return {"value": w.batch * w.n_q * w.n_tok / step_s, "unit": "logits/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"numpy fp64 oracle, median of 3 runs: encode of the {w.n_tok}-token prefill of "
-                      f"{kv_heads} of the {w.n_kv} KV heads ({n} keys) + all logits of their "
-                      f"{kv_heads * w.group} query heads; scaled linearly to the whole step (encode "
-                      f"{w.n_vec} keys + {w.batch * w.n_q * w.n_tok} logits)",
-            "host_cpus": len(os.sched_getaffinity(0)), "encode_keys_per_s": n / enc_s,
-            "logits_per_s": kv_heads * w.group * w.n_tok / lg_s}
+        O.encode(k, sk4.numpy(), ck4, tk4, Sk4.numpy())
+        O.encode(v, sv4, cv4, tv4)
+        sec += time.perf_counter() - t0
+        del k, v
+    per_vec = sec / (2 * len(slices) * w4.n_kv * w4.n_tok)
+    work["encode_cfg4"] = {"workload": w4.name, "sample": f"(layer, batch row) slices {slices}: 32 heads x 4096 "
+                                                          f"tokens each, K and V (same-law stand-in draws)",
+                           "sample_s": sec, "extrapolated": True, "whole_s": per_vec * 2 * w4.n_vec,
+                           "vectors_per_s": 1.0 / per_vec}
+    out["workloads"] = work
+    return out
 
 
 # ------------------------------------------------------------------ counters
@@ -701,6 +890,10 @@ def main():
         pmc_pass(torch, tq, syn)
         return
 
+    global PROBE_GBPS
+    log("[probe] read-only stream")
+    rp = read_probe(torch, tq)
+    PROBE_GBPS = rp["GBps"]
     res = main_decode_layer(args, torch, tq, syn)
     w = res["w"]
     kern = res["kernels"]
@@ -708,14 +901,40 @@ def main():
     kd = kern[dom]
     log("[copy] device copy bandwidth probe")
     cp = copy_probe(torch)
-    achieved = kd["bytes_per_launch"] / (kd["avg_us"] * 1e-6) / 1e9
-    roof = {"kernel": dom, "bound": "hbm", "achieved": achieved,
-            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": kd["hbm_frac"], "traffic": measured_traffic(dom),
+    t_dom = kd["avg_us"] * 1e-6
+    # the roofs of the dominant kernel: HBM (algorithmic bytes), the matrix
+    # cores (algorithmic flops of its dense products, fp16 peak) and VALU
+    # issue (wave instructions the counters saw per launch, while the
+    # committed counter summary is current); the binding roof is the one the
+    # kernel comes closest to
+    roofs = {"hbm": {"achieved": kd["bytes_per_launch"] / t_dom / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": kd["hbm_frac"], "per_unit": kd["bytes_per_launch"] / kd["units_per_launch"],
+                     "per_unit_what": "algorithmic bytes per " + kd["unit"].rstrip("s").split(" (")[0]}}
+    if kd.get("mfma_flops_per_launch"):
+        f = kd["mfma_flops_per_launch"] / t_dom
+        roofs["mfma"] = {"achieved": f / 1e12, "peak": MFMA_F16_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": f / MFMA_F16_PEAK,
+                         "per_unit": kd["mfma_flops_per_launch"] / kd["units_per_launch"],
+                         "per_unit_what": "algorithmic flops per key (the d x d QJL projection)"}
+    valu = profile_field(dom, "valu_instructions_per_launch")
+    if valu:
+        roofs["valu"] = {"achieved": valu / t_dom / 1e9, "peak": VALU_PEAK / 1e9, "unit": "G wave-instructions/s",
+                         "frac": valu / t_dom / VALU_PEAK, "per_unit": valu / kd["units_per_launch"],
+                         "per_unit_what": "VALU wave instructions per key (counter SQ_INSTS_VALU)"}
+    bound = max(roofs, key=lambda r: roofs[r]["frac"])
+    rb = roofs[bound]
+    roof = {"kernel": dom, "bound": bound, "achieved": rb["achieved"], "peak": rb["peak"], "unit": rb["unit"],
+            "frac": rb["frac"], "traffic": measured_traffic(dom),
             "bytes_per_unit": kd["bytes_per_launch"] / kd["units_per_launch"],
-            "units_per_launch": kd["units_per_launch"],
-            "copy_probe_GBps": cp["GBps"], "frac_of_copy": achieved / cp["GBps"]}
+            "units_per_launch": kd["units_per_launch"], "roofs": roofs,
+            "copy_probe_GBps": cp["GBps"], "read_probe_GBps": rp["GBps"],
+            "hbm_frac_of_copy": roofs["hbm"]["achieved"] / cp["GBps"],
+            "hbm_frac_of_read_probe": roofs["hbm"]["achieved"] / rp["GBps"]}
     extras = {}
     if not args.no_extras:
+        if not only or "single" in only:
+            extras["single_head"] = single_head_workload(torch, tq, syn)
+        torch.cuda.empty_cache()
         if not only or "dec3" in only:
             extras["decode_attend_batched"] = decode_workload(torch, tq, syn, 3, copies=9, steps=20)
         torch.cuda.empty_cache()
@@ -742,8 +961,8 @@ def main():
         torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
-        log("[cpu] timing the oracle on a sample")
-        cpu = cpu_baseline(w, syn, torch)
+        log("[cpu] timing the oracle" + (" in full (minutes)" if args.cpu_full else " on samples"))
+        cpu = cpu_baseline(w, syn, torch, full=args.cpu_full)
     line = {
         "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["total_s"] / res["steps"] * 1e3, "higher_is_better": True,
@@ -751,8 +970,10 @@ def main():
         "config": {"workload": "Llama-3.1-8B-shaped decode layer: encode 32768-token key prefill + all q.k "
                                "logits", "kv_heads": w.n_kv, "q_heads": w.n_q, "head_dim": w.d, "batch": w.batch,
                    "context": w.n_tok, "key_bits": w.key_bits, "input_dtype": "bf16",
+                   "compute": "fp32 vector arithmetic, int8/fp16/bf16 matrix cores with exact operands",
                    "copies_rotated": args.copies},
-        "encode_tokens_per_s": res["encode_tokens_per_s"],
+        "encode_tokens_per_s": kern["encode"]["tokens_per_s"],
+        "step_encode_tokens_per_s": res["encode_tokens_per_s"],
         "roofline": roof, "cpu_baseline": cpu, "kernels": kern, "extras": extras,
     }
     print(json.dumps(line))

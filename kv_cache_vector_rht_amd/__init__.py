@@ -75,6 +75,7 @@ def _load():
         "tq_decode_attend_k8": ([CP, P, I32, I32, I32, I32, P, F, P, P, I64, P, I64, F, P, I32, P, SZ, P], I32),
         "tq_topk": ([P, I64, I64, I64, I32, P, P, P, SZ, P], I32),
         "tq_topk_workspace": ([I64, I64, I32], SZ),
+        "tq_probe_read": ([P, SZ, P, P], I32),
         "tq_status_string": ([I32], ctypes.c_char_p),
         "tq_last_error": ([], ctypes.c_char_p),
     }
@@ -109,7 +110,7 @@ EXPORTED = ("tq_make_codebook", "tq_rate_plan", "tq_key_record_bytes", "tq_value
             "tq_decode_attend_noalloc_max_workspace",
             "tq_append_decode_attend", "tq_append_decode_attend_workspace", "tq_prefill_attend",
             "tq_prefill_attend_workspace", "tq_encode_fp8_keys", "tq_decode_attend_k8",
-            "tq_topk", "tq_topk_workspace", "tq_status_string", "tq_last_error")
+            "tq_topk", "tq_topk_workspace", "tq_probe_read", "tq_status_string", "tq_last_error")
 
 
 def _check(status: int, what: str):
@@ -705,6 +706,16 @@ def topk(scores: torch.Tensor, k: int, n_cols: Optional[int] = None, workspace: 
                      workspace.numel(), _stream(stream))
     _check(st, "tq_topk")
     return vals, idx
+
+
+@_on_stream
+def probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Measurement only: one read-and-reduce pass over the bytes of a contiguous CUDA tensor
+    (tq_probe_read); sink is a CUDA int32/uint32 tensor of at least one element."""
+    if not (src.is_cuda and src.is_contiguous() and sink.is_cuda):
+        raise ValueError("src must be a contiguous CUDA tensor and sink a CUDA tensor")
+    st = lib.tq_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream))
+    _check(st, "tq_probe_read")
 
 
 @_on_stream

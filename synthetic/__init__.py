@@ -217,6 +217,35 @@ def _kv(w: Workload, stream: int, which: int, device, copy: int) -> torch.Tensor
     return _randn_into(out, g, scale_fn)
 
 
+def kv_slice(w: Workload, which: int, layer: int = 0, b: int = 0, device="cpu") -> torch.Tensor:
+    """The n_kv sequences of one (layer, batch row) of a workload, [n_kv, n_tok, d]
+    in its input dtype, drawn from a generator of their own (copy 1000 + the
+    slice's index) with the same law as ``keys``/``values`` (which = 0 / 1):
+    the layer's outlier mask, the channel scales, the outlier channels. The
+    draws differ from those of the full cache; a stand-in of the same law for
+    timing samples of caches too large to draw whole."""
+    g = generator(w.cfg, STREAM_K if which == 0 else STREAM_V, 1000 + layer * w.batch + b, device=device)
+    out = torch.empty((w.n_kv, w.n_tok, w.d), dtype=w.in_dtype, device=device)
+    scale_fn = None
+    if w.cfg == 1:
+        ch = outlier_channels_cfg1(w.d).to(device)
+
+        def scale_fn(r0, r1, x):
+            x[:, :, ch] *= 20.0
+    elif w.cfg in (2, 5):
+        sc = channel_scales(w.cfg, w.n_kv, w.d, which).to(device)
+
+        def scale_fn(r0, r1, x):
+            x.mul_(sc[r0:r1][:, None, :])
+    elif w.cfg == 4:
+        m = outlier_mask_cfg4(which, w.layers, w.n_kv, w.d)[layer].to(device)   # [H, d]
+        sc = torch.where(m, 10.0, 1.0).to(torch.float32)
+
+        def scale_fn(r0, r1, x):
+            x.mul_(sc[r0:r1][:, None, :])
+    return _randn_into(out, g, scale_fn)
+
+
 def queries(w: Workload, device="cpu", copy: int = 0) -> torch.Tensor:
     """Query input [batch, n_q, d] N(0, 1) in the workload's input dtype."""
     g = generator(w.cfg, STREAM_Q, copy, device=device)

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    import glob
+    src = "".join(open(f).read() for f in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", src)))
 
@@ -26,7 +27,7 @@ def test_library_exports_every_declared_symbol():
                          check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines()}
     declared = _declared()
-    assert declared, "no declarations found in include/tq.h"
+    assert declared, "no declarations found in include/*.h"
     missing = [s for s in declared if s not in exported]
     assert not missing, missing
     assert set(declared) == set(tq.EXPORTED)
