@@ -45,6 +45,10 @@ is named in the function that relies on it:
                 head h // G; a query attends to t < ctx_len tokens.
   value decode  acc = sum_t a_t n_t c_v[idx_t] in the rotated domain, then
                 out = R_v^T acc.
+  MSE-only keys the ablation without the QJL stage (same page, 第2段: the
+                MSE-optimal quantizer alone biases inner products): a key
+                keeps its index planes and norm only, and its logit is the
+                estimator's first term n sum_i q'_i c[idx_i].
 
 Parity of the estimator itself (logits given codes) is unpinned beyond its
 special cases: the pages print no logit values.
@@ -60,7 +64,7 @@ from scipy import special
 __all__ = [
     "sphere_coord_density", "coord_cdf", "interval_mass", "interval_moment",
     "make_codebook", "hadamard", "rotate", "rotate_inverse",
-    "encode", "pack_key_codes", "unpack_key_codes", "pack_value_codes",
+    "encode", "pack_key_codes", "unpack_key_codes", "pack_mse_key_codes", "unpack_mse_key_codes", "pack_value_codes",
     "unpack_value_codes", "prepare_query", "key_logits", "key_logits_mse", "pair_logits", "decode_attend",
     "append_decode_attend", "prefill_attend", "rate_plan", "e4m3_value", "e4m3_encode", "decode_attend_k8",
     "top_k", "search",
@@ -314,6 +318,24 @@ def unpack_key_codes(codes, d: int, lm_bits: int):
     return idx, sigma
 
 
+def pack_mse_key_codes(idx, lm_bits: int):
+    """MSE-only key record (the ablation without the QJL stage): the lm_bits
+    index planes of a key record and nothing else, plane p holding bit p of
+    idx, coordinate i at byte i//8, bit i%8. Returns uint8 [..., lm_bits*d/8]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    return np.concatenate([_plane_bytes((idx >> p) & 1) for p in range(lm_bits)], axis=-1)
+
+
+def unpack_mse_key_codes(codes, d: int, lm_bits: int):
+    codes = np.asarray(codes, dtype=np.uint8)
+    assert codes.shape[-1] == lm_bits * (d // 8)
+    bits = np.unpackbits(codes, axis=-1, bitorder="little").astype(np.int64)
+    idx = np.zeros(codes.shape[:-1] + (d,), dtype=np.int64)
+    for p in range(lm_bits):
+        idx |= bits[..., p * d:(p + 1) * d] << p
+    return idx
+
+
 VALUE_BLOCK = 32   # tokens per value-code block
 
 
@@ -424,6 +446,8 @@ def decode_attend(q, k_signs, k_centroids, sketch, kidx, ksigma, knhat, kghat,
     q: [B, Hq, d]; key/value arrays indexed [B*Hkv, T, ...]; ctx_lens [B].
     Query head h of batch b reads KV sequence b*Hkv + h // group, tokens
     t < ctx_lens[b]. Returns fp64 [B, Hq, d]; rows with ctx_len <= 0 are 0.
+    sketch None: MSE-only keys (no QJL stage; ksigma and kghat unused), whose
+    logits are the estimator's first term (key_logits_mse).
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
@@ -436,8 +460,11 @@ def decode_attend(q, k_signs, k_centroids, sketch, kidx, ksigma, knhat, kghat,
         for hk in range(Hkv):
             s = b * Hkv + hk
             qs = q[b, hk * group:(hk + 1) * group]
-            lg = key_logits(qs, k_signs, k_centroids, sketch, kidx[s, :T], ksigma[s, :T],
-                            knhat[s, :T], kghat[s, :T])        # [G, T]
+            if sketch is None:
+                lg = key_logits_mse(qs, k_signs, k_centroids, kidx[s, :T], knhat[s, :T])
+            else:
+                lg = key_logits(qs, k_signs, k_centroids, sketch, kidx[s, :T], ksigma[s, :T],
+                                knhat[s, :T], kghat[s, :T])    # [G, T]
             z = sm_scale * lg
             z = z - z.max(axis=1, keepdims=True)
             a = np.exp(z)
@@ -456,21 +483,19 @@ def prefill_attend(q, k_signs, k_centroids, sketch, kidx, ksigma, knhat, kghat, 
     cache arrays' length). Long prefills sit at the high end of the pages'
     measured throughput range ("TurboQuantとは？仕組み・実測精度・2026年7月
     時点の実装状況", section 「精度劣化ゼロ」の出所と、マージ後に判明した実測値).
-    Returns fp64 [B, C, Hq, d]."""
+    sketch None: MSE-only keys, as in decode_attend. Returns fp64 [B, C, Hq, d]."""
     q = np.asarray(q, dtype=np.float64)
     B, C, Hq, d = q.shape
     T = np.asarray(kidx).shape[1]
     out = np.zeros((B, C, Hq, d))
+    Hkv = Hq // group
     for b in range(B):
+        rows = lambda a: None if a is None else a[b * Hkv:(b + 1) * Hkv]
         for i in range(C):
             n = min(int(pos0[b]) + i + 1, T)
-            out[b, i] = decode_attend(q[b, i][None], k_signs, k_centroids, sketch,
-                                      kidx[b * (Hq // group):(b + 1) * (Hq // group)],
-                                      ksigma[b * (Hq // group):(b + 1) * (Hq // group)],
-                                      knhat[b * (Hq // group):(b + 1) * (Hq // group)],
-                                      kghat[b * (Hq // group):(b + 1) * (Hq // group)], v_signs, v_centroids,
-                                      vidx[b * (Hq // group):(b + 1) * (Hq // group)],
-                                      vnhat[b * (Hq // group):(b + 1) * (Hq // group)], [n], sm_scale, group)[0]
+            out[b, i] = decode_attend(q[b, i][None], k_signs, k_centroids, sketch, rows(kidx), rows(ksigma),
+                                      rows(knhat), rows(kghat), v_signs, v_centroids, rows(vidx), rows(vnhat),
+                                      [n], sm_scale, group)[0]
     return out
 
 
@@ -487,13 +512,15 @@ def append_decode_attend(q, k_new, v_new, k_signs, k_centroids, k_thresholds, sk
 
     The cache arrays are [B*Hkv, T, ...] as in decode_attend and are not
     modified; returns (out [B, Hq, d], updated cache dict, key encoding and
-    value encoding of the new rows, each [B, Hkv, ...])."""
+    value encoding of the new rows, each [B, Hkv, ...]). sketch None:
+    MSE-only keys (ksigma and kghat unused and returned as None)."""
     k_new = np.asarray(k_new, dtype=np.float64)
     B, Hkv, d = k_new.shape
     ek = encode(k_new.reshape(B * Hkv, d), k_signs, k_centroids, k_thresholds, sketch)
     ev = encode(np.asarray(v_new, dtype=np.float64).reshape(B * Hkv, d), v_signs, v_centroids, v_thresholds)
-    cache = {"kidx": np.array(kidx), "ksigma": np.array(ksigma), "knhat": np.array(knhat),
-             "kghat": np.array(kghat), "vidx": np.array(vidx), "vnhat": np.array(vnhat)}
+    qjl = sketch is not None
+    cache = {"kidx": np.array(kidx), "ksigma": np.array(ksigma) if qjl else None, "knhat": np.array(knhat),
+             "kghat": np.array(kghat) if qjl else None, "vidx": np.array(vidx), "vnhat": np.array(vnhat)}
     for b in range(B):
         t = int(ctx_lens[b]) - 1
         if t < 0:
@@ -501,9 +528,10 @@ def append_decode_attend(q, k_new, v_new, k_signs, k_centroids, k_thresholds, sk
         for hk in range(Hkv):
             s = b * Hkv + hk
             cache["kidx"][s, t] = ek["idx"][s]
-            cache["ksigma"][s, t] = ek["sigma"][s]
             cache["knhat"][s, t] = ek["nhat"][s]
-            cache["kghat"][s, t] = ek["ghat"][s]
+            if qjl:
+                cache["ksigma"][s, t] = ek["sigma"][s]
+                cache["kghat"][s, t] = ek["ghat"][s]
             cache["vidx"][s, t] = ev["idx"][s]
             cache["vnhat"][s, t] = ev["nhat"][s]
     out = decode_attend(q, k_signs, k_centroids, sketch, cache["kidx"], cache["ksigma"], cache["knhat"],

@@ -719,6 +719,76 @@ def test_prefill_attend_is_masked_softmax_attention():
         np.testing.assert_allclose(out[:, i], dec, rtol=1e-13, atol=1e-15)
 
 
+def test_mse_key_record_is_the_key_record_without_its_sign_plane():
+    """MSE-only key records against the hand-derived key records (their first
+    w planes) and a round trip."""
+    n = 0
+    for row in _golden_lines("pack_d8.txt"):
+        kv = dict(x.split("=", 1) for x in row[1:])
+        if row[0] != "key":
+            continue
+        w = int(kv["lm_bits"])
+        idx = np.array([int(v) for v in kv["idx"].split(",")])[None]
+        want = [int(v, 16) for v in kv["bytes"].split(",")][:w]          # d = 8: one byte per plane
+        rec = O.pack_mse_key_codes(idx, w)[0]
+        assert [int(b) for b in rec] == want
+        np.testing.assert_array_equal(O.unpack_mse_key_codes(rec[None], 8, w), idx)
+        n += 1
+    assert n > 0
+    rng = np.random.default_rng(5)
+    for w in (1, 2, 3, 4):
+        idx = rng.integers(0, 1 << w, size=(2, 33, 128))
+        rec = O.pack_mse_key_codes(idx, w)
+        assert rec.shape == (2, 33, w * 16)
+        np.testing.assert_array_equal(O.unpack_mse_key_codes(rec, 128, w), idx)
+
+
+def test_attention_over_mse_only_keys_is_the_zero_residual_case():
+    """With sketch None (MSE-only keys) decode, prefill and append attention
+    equal the full estimator's with every residual norm 0 (which drops the
+    QJL term), and decode equals scipy's softmax over key_logits_mse."""
+    B, Hkv, G, T, d = 2, 2, 3, 29, 64
+    rng, (s, c, S), (sv, cv), ek, ev = _toy_cache(B, Hkv, T, d, 3, 2, 21)
+    q = rng.standard_normal((B, Hkv * G, d))
+    scale = 0.29
+    zg = np.zeros_like(ek["ghat"])
+    lens = [T, 11]
+    mse = O.decode_attend(q, s, c, None, ek["idx"], None, ek["nhat"], None, sv, cv, ev["idx"], ev["nhat"],
+                          lens, scale, G)
+    full0 = O.decode_attend(q, s, c, S, ek["idx"], ek["sigma"], ek["nhat"], zg, sv, cv, ev["idx"], ev["nhat"],
+                            lens, scale, G)
+    np.testing.assert_allclose(mse, full0, rtol=1e-12, atol=1e-14)
+    Rv = scipy.linalg.hadamard(d) @ np.diag(sv) / math.sqrt(d)
+    Vhat = ev["nhat"].astype(np.float64)[..., None] * (cv.astype(np.float64)[ev["idx"]] @ Rv)
+    for b in range(B):
+        for h in range(Hkv * G):
+            sq = b * Hkv + h // G
+            lg = O.key_logits_mse(q[b, h:h + 1], s, c, ek["idx"][sq, :lens[b]], ek["nhat"][sq, :lens[b]])[0]
+            a = scipy.special.softmax(scale * lg)
+            np.testing.assert_allclose(mse[b, h], a @ Vhat[sq, :lens[b]], rtol=1e-10, atol=1e-12)
+    C = 4
+    qc = rng.standard_normal((B, C, Hkv * G, d))
+    pm = O.prefill_attend(qc, s, c, None, ek["idx"], None, ek["nhat"], None, sv, cv, ev["idx"], ev["nhat"],
+                          [3, 20], scale, G)
+    pf = O.prefill_attend(qc, s, c, S, ek["idx"], ek["sigma"], ek["nhat"], zg, sv, cv, ev["idx"], ev["nhat"],
+                          [3, 20], scale, G)
+    np.testing.assert_allclose(pm, pf, rtol=1e-12, atol=1e-14)
+    # append: the new token lands in slot T-1 and is attended like the rest
+    t = O.make_codebook(d, 3)[1]
+    tv = O.make_codebook(d, 2)[1]
+    K = rng.standard_normal((B * Hkv, d))
+    V = rng.standard_normal((B * Hkv, d))
+    out, cache, nk, _ = O.append_decode_attend(q, K.reshape(B, Hkv, d), V.reshape(B, Hkv, d), s, c, t, None,
+                                               ek["idx"], None, ek["nhat"], None, sv, cv, tv, ev["idx"],
+                                               ev["nhat"], [T, T], scale, G)
+    assert cache["ksigma"] is None and cache["kghat"] is None and "sigma" not in nk
+    e_new = O.encode(K, s, c, t)
+    np.testing.assert_array_equal(cache["kidx"][:, T - 1], e_new["idx"])
+    ref = O.decode_attend(q, s, c, None, cache["kidx"], None, cache["knhat"], None, sv, cv, cache["vidx"],
+                          cache["vnhat"], [T, T], scale, G)
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-15)
+
+
 def test_rate_plan_mixes_neighbouring_widths_evenly():
     """The plan's average is the nearest achievable to the target, its widths
     are the two integers around the Lloyd-Max average, and every prefix of
