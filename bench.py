@@ -31,8 +31,10 @@ committed profile summary while the kernel sources are unchanged. The extras tim
 fused decode attention on the batched (16 x 8192) and long-context
 (4 x 131072) decode workloads and the full-cache encode of the 22-layer
 TinyLlama-shaped prefill, the search scan (32 queries over 1,048,576
-coded vectors, then the top 100 of each), the MSE-only ablation of the
-logit scan (the estimator without its QJL term, against exact q.k), and the
+coded vectors, then the top 100 of each), the MSE-only key ablation (the
+logit scan over 68 B TurboQuant records, 50 B and 66 B MSE-only records, and
+the estimator's first term alone on the 68 B records: time, bytes and error
+against exact q.k), and the
 single-head workload (4096 fp32 keys, 16 queries; launch-latency bound,
 absolute numbers only). Every scan's HBM fraction is also given against a
 read-only stream measured on the same part (`tq_probe_read`, 4 GiB).
@@ -620,39 +622,65 @@ def search_workload(torch, tq, syn, copies, steps):
                 topk_frac_of_read_probe=of_probe(b_rank, t_rank), k=w.k, copies=copies)
 
 
-def mse_keys_ablation(torch, tq, syn, steps):
-    """The MSE-only ablation on the decode-layer workload (8 KV / 32 Q heads,
-    32768 keys, 4-bit keys): the logit scan with and without the QJL term on
-    the same records (times), and both estimates against the exact q.k of
-    the unquantized keys: least-squares slope (the shrinkage the QJL bit
-    removes) and RMS error relative to the exact logits' RMS."""
+def mse_keys_ablation(torch, tq, syn, copies, steps):
+    """The MSE-only key ablation on the decode-layer workload (8 KV / 32 Q
+    heads, 32768 keys, bf16 keys with lognormal channel scales), one logit
+    scan per key cache format, each over `copies` cache copies rotated so
+    that the working set exceeds the Infinity Cache:
+      tq_b4        4-bit TurboQuant keys (3 Lloyd-Max bits + QJL), 68 B/key
+      mse_b3       MSE-only keys, 3 Lloyd-Max bits (codec is_key = 2), 50 B/key
+      mse_b4       MSE-only keys, 4 Lloyd-Max bits, 66 B/key (the same bits
+                   per channel as tq_b4)
+      tq_b4_first_term  the estimator's first term alone over the 68 B records
+                   (tq_logits_mse: the bias on identical codes)
+    For each: time per call, algorithmic bytes, HBM fractions, and the logits
+    against the exact q.k of the unquantized keys: least-squares slope (the
+    shrinkage the QJL bit removes) and RMS error relative to the exact
+    logits' RMS."""
     w = syn.WORKLOADS[2]
     dev = "cuda"
-    kc, _, _ = setup_codecs(torch, tq, syn, w, dev)
+    s, S = syn.key_codec_randoms(w.cfg, w.d)
+    codecs = {
+        "tq_b4": (tq.Codec.make(w.d, w.key_lm_bits, True, s, S, device=dev), False),
+        "mse_b3": (tq.Codec.make(w.d, w.key_lm_bits, True, s, device=dev, mse_only=True), False),
+        "mse_b4": (tq.Codec.make(w.d, w.key_lm_bits + 1, True, s, device=dev, mse_only=True), False),
+    }
+    codecs["tq_b4_first_term"] = (codecs["tq_b4"][0], True)
     x = syn.keys(w, device=dev)
     q = syn.queries(w, device=dev)
-    codes, scal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
-    tq.encode_kv(kc, x, codes, scal)
-    full = torch.empty((w.batch, w.n_q, w.n_tok), dtype=torch.float32, device=dev)
-    mse = torch.empty_like(full)
-    f_full = lambda: tq.logits(kc, q, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok, out=full)
-    f_mse = lambda: tq.logits(kc, q, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok, out=mse,
-                              mse_only=True)
-    # 8 back-to-back calls per graph (no launch gaps between them)
-    t_full = time_replays(torch, [capture(torch, [f_full] * 8)], steps) / 8
-    t_mse = time_replays(torch, [capture(torch, [f_mse] * 8)], steps) / 8
+    log(f"[ablation] encoding {copies} copies of {w.name} in three key formats")
+    caches = {}
+    for name in ("tq_b4", "mse_b3", "mse_b4"):
+        kc = codecs[name][0]
+        caches[name] = []
+        for _ in range(copies):
+            codes, scal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+            tq.encode_kv(kc, x, codes, scal)
+            caches[name].append((codes, scal))
+    caches["tq_b4_first_term"] = caches["tq_b4"]
+    outs = [torch.empty((w.batch, w.n_q, w.n_tok), dtype=torch.float32, device=dev) for _ in range(copies)]
     # exact logits: query head h against the keys of KV head h // group
     qf = q[0].float().view(w.n_kv, w.group, w.d)
-    exact = torch.bmm(qf, x.float().transpose(1, 2).contiguous()).view(1, w.n_q, w.n_tok)
-    ex = exact.double()
-    out = dict(workload=w.name, logits_us=t_full * 1e6, logits_mse_us=t_mse * 1e6,
-               record_bytes=kc.record_bytes + 4, mse_only_record_bytes=w.key_lm_bits * w.d // 8 + 2)
-    for name, est in (("full", full), ("mse_only", mse)):
-        e = est.double()
-        out[f"slope_{name}"] = float((e * ex).sum() / (ex * ex).sum())
-        out[f"rel_rms_err_{name}"] = float(((e - ex) ** 2).mean().sqrt() / (ex ** 2).mean().sqrt())
-    del x
-    return out
+    ex = torch.bmm(qf, x.float().transpose(1, 2).contiguous()).view(1, w.n_q, w.n_tok).double()
+    torch.cuda.synchronize()
+    res = dict(workload=w.name, copies=copies)
+    for name, (kc, first_term) in codecs.items():
+        def call(c, kc=kc, first_term=first_term, name=name):
+            codes, scal = caches[name][c]
+            return lambda: tq.logits(kc, q, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok,
+                                     out=outs[c], mse_only=first_term)
+        t = time_replays(torch, [capture(torch, [call(c) for c in range(copies)])], max(1, steps // copies)) / copies
+        rec = kc.record_bytes + 2 * kc.key_scalars
+        nbytes = w.n_vec * rec + w.batch * w.n_q * w.n_tok * 4
+        call(0)()
+        e = outs[0].double()
+        res[name] = dict(avg_us=t * 1e6, record_bytes=rec, bytes_per_call=nbytes, hbm_frac=hbm(nbytes, t),
+                         frac_of_read_probe=of_probe(nbytes, t), logits_per_s=w.batch * w.n_q * w.n_tok / t,
+                         slope=float((e * ex).sum() / (ex * ex).sum()),
+                         rel_rms_err=float(((e - ex) ** 2).mean().sqrt() / (ex ** 2).mean().sqrt()))
+    del x, caches
+    torch.cuda.empty_cache()
+    return res
 
 
 def single_head_workload(torch, tq, syn, reps=50):
@@ -957,7 +985,7 @@ def main():
             extras["search_scan"] = search_workload(torch, tq, syn, copies=4, steps=20)
         torch.cuda.empty_cache()
         if not only or "ablation" in only:
-            extras["mse_keys_ablation"] = mse_keys_ablation(torch, tq, syn, steps=20)
+            extras["mse_keys_ablation"] = mse_keys_ablation(torch, tq, syn, copies=16, steps=32)
         torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:

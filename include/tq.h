@@ -37,6 +37,10 @@
  *                  QJL sign plane; each plane is d/8 bytes, coordinate i at
  *                  byte i/8, bit i%8 (LSB first).
  *          scalars fp16   [n_seq][cap][2]  {norm, residual norm}
+ *   MSE-only keys (the ablation without the QJL stage: codec is_key = 2)
+ *          codes   uint8  [n_seq][cap][w*d/8]  the w index planes of a key
+ *                  record, without the sign plane
+ *          scalars fp16   [n_seq][cap]  {norm}
  *   Values codes   uint32 [n_seq][cap/32][w][d]  token-major: tokens are
  *                  grouped in blocks of 32; the word for (block B, plane p,
  *                  coordinate i) holds bit p of the index of token 32B+j at
@@ -77,7 +81,10 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
  *   d           head dimension (a power of two)
  *   lm_bits     w, Lloyd-Max bits per coordinate: keys use b-1 of their b
  *               bits (the last bit is the QJL sign), values use all b
- *   is_key      1: keys (QJL sign plane + residual norm), 0: values
+ *   is_key      1: keys (QJL sign plane + residual norm), 0: values,
+ *               2: MSE-only keys (key records without the QJL part: every
+ *               call that reads keys then computes the estimator's first
+ *               term alone, logit = n sum_i q'_i c[idx_i])
  *   signs       device float [d], +1/-1: the rotation R = H diag(signs)/sqrt(d),
  *               H the Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i&j)
  *   centroids   device float [L], ascending and symmetric (c[L-1-k] = -c[k]),
@@ -86,8 +93,9 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
  *               (t[L-2-k] = -t[k], middle one 0) as tq_make_codebook makes
  *               them: the kernels use the upper halves of both arrays (the
  *               sign of a rotated coordinate gives its top index bit)
- *   sketch      device fp16 bit patterns [d][d] (keys only, else NULL): the
- *               QJL projection S, row j = the j-th projection direction
+ *   sketch      device fp16 bit patterns [d][d] (is_key = 1 only; ignored
+ *               otherwise, may be NULL): the QJL projection S, row j = the
+ *               j-th projection direction
  * The arrays are read, never written, and must stay alive while any call
  * that uses the codec is in flight.
  */
@@ -138,6 +146,8 @@ tq_status tq_rate_plan(double bits, int32_t n_layers, int32_t is_key, int32_t *l
 
 /* Bytes of one key record's codes, (w+1)*d/8; 0 if the arguments are invalid. */
 size_t tq_key_record_bytes(int32_t d, int32_t lm_bits);
+/* Bytes of one MSE-only key record's codes (is_key = 2), w*d/8; 0 if invalid. */
+size_t tq_mse_key_record_bytes(int32_t d, int32_t lm_bits);
 /* Bytes of one 32-token value block, 4*w*d; 0 if the arguments are invalid. */
 size_t tq_value_block_bytes(int32_t d, int32_t lm_bits);
 
@@ -217,13 +227,18 @@ tq_status tq_logits_prepared(const tq_codec *kc, const void *prepared, size_t by
                              void *stream);
 
 /*
- * The MSE-only ablation of tq_logits: the estimator's first term alone,
+ * The MSE-only estimator over full key records: the estimator's first term
+ * alone,
  *   logit = n * sum_i q'_i c[idx_i],
  * from the same key records (their sign plane and residual norm are read
- * and left out). It is the biased estimate that the QJL bit corrects: the
- * MSE-optimal codebook shrinks inner products by about the per-coordinate
- * distortion ("TurboQuantとは？…", 第2段: the 1-bit residual removes the
- * inner-product bias). Arguments and errors as tq_logits.
+ * and left out), so that the bias can be measured on identical codes. It is
+ * the biased estimate that the QJL bit corrects: the MSE-optimal codebook
+ * shrinks inner products by about the per-coordinate distortion
+ * ("TurboQuantとは？…", 第2段: the 1-bit residual removes the inner-product
+ * bias). The MSE-only cache format, which also saves the sign plane's and
+ * the residual norm's bytes, is the codec with is_key = 2 (any call that
+ * reads keys). Arguments and errors as tq_logits (an is_key = 2 codec gives
+ * the logits of tq_logits).
  */
 tq_status tq_logits_mse(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch,
                         int32_t n_kv_heads, int32_t group, const uint8_t *kcodes,

@@ -54,6 +54,7 @@ def _load():
         "tq_make_codebook": ([I32, I32, P, P], I32),
         "tq_rate_plan": ([ctypes.c_double, I32, I32, P], I32),
         "tq_key_record_bytes": ([I32, I32], SZ),
+        "tq_mse_key_record_bytes": ([I32, I32], SZ),
         "tq_value_block_bytes": ([I32, I32], SZ),
         "tq_encode_kv": ([CP, P, I32, I64, I64, I64, I64, P, P, I64, I64, P], I32),
         "tq_logits": ([CP, P, I32, I32, I32, I32, P, P, I64, I64, P, P, SZ, P], I32),
@@ -104,7 +105,8 @@ def load():
     """Load libtq now (raises ImportError if it is not built)."""
     return lib.tq_status_string
 
-EXPORTED = ("tq_make_codebook", "tq_rate_plan", "tq_key_record_bytes", "tq_value_block_bytes", "tq_encode_kv",
+EXPORTED = ("tq_make_codebook", "tq_rate_plan", "tq_key_record_bytes", "tq_mse_key_record_bytes",
+            "tq_value_block_bytes", "tq_encode_kv",
             "tq_logits", "tq_logits_workspace", "tq_logits_mse", "tq_prepared_queries_bytes", "tq_prepare_queries",
             "tq_logits_prepared", "tq_decode_attend", "tq_decode_attend_workspace", "tq_decode_attend_noalloc",
             "tq_decode_attend_noalloc_max_workspace",
@@ -195,13 +197,15 @@ def _check_out(out, shape, dtypes, device):
 
 
 def _check_key_cache(codec, codes, scal, n_seq, device):
-    """Key cache of at least n_seq sequences: codes uint8 [S, cap, rec], scalars int16 [S, cap, 2]."""
+    """Key cache of at least n_seq sequences: codes uint8 [S, cap, rec], scalars int16 [S, cap, 2]
+    ([S, cap, 1] for MSE-only keys)."""
     _tensor("key codes", codes)
     _tensor("key scalars", scal)
     if codes.dtype != torch.uint8 or scal.dtype != torch.int16:
         raise ValueError("key codes must be uint8 and key scalars int16 (fp16 bits)")
-    if codes.dim() != 3 or scal.dim() != 3 or scal.shape[2] != 2:
-        raise ValueError("key cache must be codes [n_seq, cap, rec] and scalars [n_seq, cap, 2]")
+    ns = codec.key_scalars
+    if codes.dim() != 3 or scal.dim() != 3 or scal.shape[2] != ns:
+        raise ValueError(f"key cache must be codes [n_seq, cap, rec] and scalars [n_seq, cap, {ns}]")
     if codes.shape[2] != codec.record_bytes:
         raise ValueError(f"key records must be {codec.record_bytes} bytes (got {codes.shape[2]})")
     if codes.shape[:2] != scal.shape[:2]:
@@ -259,6 +263,10 @@ def key_record_bytes(d: int, lm_bits: int) -> int:
     return int(lib.tq_key_record_bytes(d, lm_bits))
 
 
+def mse_key_record_bytes(d: int, lm_bits: int) -> int:
+    return int(lib.tq_mse_key_record_bytes(d, lm_bits))
+
+
 def value_block_bytes(d: int, lm_bits: int) -> int:
     return int(lib.tq_value_block_bytes(d, lm_bits))
 
@@ -268,35 +276,42 @@ def value_block_bytes(d: int, lm_bits: int) -> int:
 
 @dataclass
 class Codec:
-    """Device-resident codec parameters (see tq_codec in include/tq.h)."""
+    """Device-resident codec parameters (see tq_codec in include/tq.h).
+    mse_only: key records without the QJL part (is_key = 2 in the C ABI)."""
     d: int
     lm_bits: int
     is_key: bool
     signs: torch.Tensor          # float32 [d]
     centroids: torch.Tensor      # float32 [2^w]
     thresholds: torch.Tensor     # float32 [2^w - 1]
-    sketch: Optional[torch.Tensor] = None   # float16 [d, d] (keys)
+    sketch: Optional[torch.Tensor] = None   # float16 [d, d] (keys with the QJL stage)
+    mse_only: bool = False
 
     @staticmethod
-    def make(d, lm_bits, is_key, signs, sketch=None, device="cuda", centroids=None, thresholds=None):
-        """Codec from rotation signs (+ sketch for keys); the codebook comes
-        from tq_make_codebook unless given."""
+    def make(d, lm_bits, is_key, signs, sketch=None, device="cuda", centroids=None, thresholds=None,
+             mse_only=False):
+        """Codec from rotation signs (+ sketch for keys with the QJL stage); the
+        codebook comes from tq_make_codebook unless given."""
         if centroids is None or thresholds is None:
             centroids, thresholds = make_codebook(d, lm_bits)
+        if mse_only and not is_key:
+            raise ValueError("mse_only applies to key codecs")
         dev = torch.device(device)
         sk = None
-        if is_key:
+        if is_key and not mse_only:
             if sketch is None:
                 raise ValueError("a key codec needs a sketch")
             sk = torch.as_tensor(sketch).to(torch.float16).contiguous().to(dev)
         return Codec(d, lm_bits, bool(is_key),
                      torch.as_tensor(signs, dtype=torch.float32).contiguous().to(dev),
                      torch.as_tensor(centroids, dtype=torch.float32).contiguous().to(dev),
-                     torch.as_tensor(thresholds, dtype=torch.float32).contiguous().to(dev), sk)
+                     torch.as_tensor(thresholds, dtype=torch.float32).contiguous().to(dev), sk,
+                     bool(mse_only))
 
     def struct(self) -> _Codec:
         s = _Codec()
-        s.d, s.lm_bits, s.is_key, s.reserved = self.d, self.lm_bits, int(self.is_key), 0
+        kind = (2 if self.mse_only else 1) if self.is_key else 0
+        s.d, s.lm_bits, s.is_key, s.reserved = self.d, self.lm_bits, kind, 0
         s.signs = self.signs.data_ptr()
         s.centroids = self.centroids.data_ptr()
         s.thresholds = self.thresholds.data_ptr()
@@ -305,7 +320,14 @@ class Codec:
 
     @property
     def record_bytes(self) -> int:
+        if self.mse_only:
+            return mse_key_record_bytes(self.d, self.lm_bits)
         return key_record_bytes(self.d, self.lm_bits)
+
+    @property
+    def key_scalars(self) -> int:
+        """fp16 scalars stored per key token: {norm, residual norm}, or {norm} (MSE-only)."""
+        return 1 if self.mse_only else 2
 
 
 def rate_plan(bits: float, n_layers: int, is_key: bool) -> list:
@@ -317,10 +339,11 @@ def rate_plan(bits: float, n_layers: int, is_key: bool) -> list:
 
 
 def alloc_key_cache(n_seq: int, cap: int, codec: Codec, device=None):
-    """(codes uint8 [n_seq, cap, (w+1)d/8], scalars int16 [n_seq, cap, 2] holding fp16 bits)."""
+    """(codes uint8 [n_seq, cap, (w+1)d/8], scalars int16 [n_seq, cap, 2] holding fp16 bits);
+    MSE-only keys: codes [n_seq, cap, w d/8], scalars [n_seq, cap, 1]."""
     dev = device or codec.signs.device
     codes = torch.zeros((n_seq, cap, codec.record_bytes), dtype=torch.uint8, device=dev)
-    scal = torch.zeros((n_seq, cap, 2), dtype=torch.int16, device=dev)
+    scal = torch.zeros((n_seq, cap, codec.key_scalars), dtype=torch.int16, device=dev)
     return codes, scal
 
 

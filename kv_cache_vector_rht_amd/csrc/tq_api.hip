@@ -52,20 +52,25 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Codec checks shared by the device calls. `need_key` = 1 requires a key
-// codec, 0 a value codec, -1 either.
+// codec (full or MSE-only records), 0 a value codec, -1 any.
 tq_status check_codec(const tq_codec *c, int need_key, const char *name) {
   if (!c) return fail(TQ_EINVAL, "%s: codec is NULL", name);
   if (!pow2(c->d) || c->d < 8) return fail(TQ_EINVAL, "%s: d=%d is not a power of two >= 8", name, c->d);
   if (c->d != 64 && c->d != 128) return fail(TQ_EUNSUPPORTED, "%s: d=%d (this build supports 64 and 128)", name, c->d);
   if (c->lm_bits < 1) return fail(TQ_EINVAL, "%s: lm_bits=%d", name, c->lm_bits);
   if (c->lm_bits > 4) return fail(TQ_EUNSUPPORTED, "%s: lm_bits=%d (this build supports 1..4)", name, c->lm_bits);
-  if (c->is_key != 0 && c->is_key != 1) return fail(TQ_EINVAL, "%s: is_key=%d", name, c->is_key);
-  if (need_key >= 0 && c->is_key != need_key)
+  if (c->is_key < 0 || c->is_key > 2) return fail(TQ_EINVAL, "%s: is_key=%d", name, c->is_key);
+  if (need_key >= 0 && (c->is_key != 0) != (need_key != 0))
     return fail(TQ_EINVAL, "%s: expected a %s codec", name, need_key ? "key" : "value");
   if (!c->signs || !c->centroids || !c->thresholds) return fail(TQ_EINVAL, "%s: codec array is NULL", name);
-  if (c->is_key && !c->sketch) return fail(TQ_EINVAL, "%s: key codec without a sketch", name);
+  if (c->is_key == 1 && !c->sketch) return fail(TQ_EINVAL, "%s: key codec without a sketch", name);
   return TQ_OK;
 }
+
+// Key width for the scan kernels: w for full key records, kKeyMse + w for
+// MSE-only ones; and the bytes of one key record's codes.
+int key_width(const tq_codec *kc) { return kc->is_key == 2 ? tq::kKeyMse + kc->lm_bits : kc->lm_bits; }
+int key_rec_bytes(const tq_codec *kc) { return tq::key_planes(key_width(kc)) * kc->d / 8; }
 
 // Scan blocks per (batch, kv-head) group: each block walks every blocks-th
 // split of `split` tokens. One block fills a CU's LDS, so aim for one block
@@ -160,7 +165,7 @@ tq_status decode_common(const char *fn, int mode, const tq_codec *kc, const tq_c
   if (static_cast<int64_t>(chunk) * group > tq::kPrefillMaxHeads)
     return fail(TQ_EUNSUPPORTED, "%s: chunk*group=%lld > %d", fn, static_cast<long long>(chunk) * group,
                 tq::kPrefillMaxHeads);
-  const int key_rec = (mode == 3) ? kc->d : (kc->lm_bits + 1) * kc->d / 8;
+  const int key_rec = (mode == 3) ? kc->d : key_rec_bytes(kc);
   if (!seq_offsets_fit(cap, std::max(key_rec, vc->lm_bits * kc->d / 8)))
     return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (!std::isfinite(sm_scale)) return fail(TQ_EINVAL, "%s: sm_scale is not finite", fn);
@@ -277,6 +282,11 @@ size_t tq_key_record_bytes(int32_t d, int32_t lm_bits) {
   return static_cast<size_t>(lm_bits + 1) * d / 8;
 }
 
+size_t tq_mse_key_record_bytes(int32_t d, int32_t lm_bits) {
+  if (!pow2(d) || d < 8 || lm_bits < 1 || lm_bits > 8) return 0;
+  return static_cast<size_t>(lm_bits) * d / 8;
+}
+
 size_t tq_value_block_bytes(int32_t d, int32_t lm_bits) {
   if (!pow2(d) || d < 8 || lm_bits < 1 || lm_bits > 8) return 0;
   return static_cast<size_t>(4) * lm_bits * d;
@@ -347,9 +357,8 @@ tq_status tq_encode_kv(const tq_codec *codec, const void *x, tq_dtype xt, int64_
   if (reinterpret_cast<uintptr_t>(codes) % 16 != 0 || reinterpret_cast<uintptr_t>(scalars) % 4 != 0)
     return fail(TQ_EINVAL, "%s: codes must be 16-byte and scalars 4-byte aligned", fn);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool key = codec->is_key != 0;
-  hipError_t e = codec->d == 64 ? tq::launch_encode_d<64>(p, codec->lm_bits, key, st)
-                                : tq::launch_encode_d<128>(p, codec->lm_bits, key, st);
+  hipError_t e = codec->d == 64 ? tq::launch_encode_d<64>(p, codec->lm_bits, codec->is_key, st)
+                                : tq::launch_encode_d<128>(p, codec->lm_bits, codec->is_key, st);
   return hip_status(e, fn);
 }
 
@@ -372,7 +381,7 @@ static tq_status logits_call(const char *fn, int qjl, const tq_codec *kc, const 
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
   if (!sequences_fit(batch, n_kv_heads))
     return fail(TQ_EUNSUPPORTED, "%s: batch*n_kv_heads above %lld", fn, static_cast<long long>(kMaxSequences));
-  if (!seq_offsets_fit(cap, (kc->lm_bits + 1) * kc->d / 8))
+  if (!seq_offsets_fit(cap, key_rec_bytes(kc)))
     return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (batch == 0 || n_kv_heads == 0 || group == 0 || n_keys == 0) return ok();
   if (!q || !kcodes || !kscalars || !logits) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
@@ -383,7 +392,7 @@ static tq_status logits_call(const char *fn, int qjl, const tq_codec *kc, const 
   tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys, tq::kLogitSplit);
   sp.logits = logits;
   sp.qjl = qjl;
-  hipError_t e = kc->d == 64 ? tq::launch_logits_d<64>(sp, kc->lm_bits, st) : tq::launch_logits_d<128>(sp, kc->lm_bits, st);
+  hipError_t e = kc->d == 64 ? tq::launch_logits_d<64>(sp, key_width(kc), st) : tq::launch_logits_d<128>(sp, key_width(kc), st);
   return hip_status(e, fn);
 }
 
@@ -412,7 +421,7 @@ tq_status tq_prepare_queries(const tq_codec *kc, const void *q, tq_dtype qt, int
   tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, nullptr, nullptr, 0, 0, tq::kLogitSplit);
   sp.prepared_w = static_cast<uint8_t *>(prepared);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kc->d == 64 ? tq::launch_prepare_d<64>(sp, kc->lm_bits, st) : tq::launch_prepare_d<128>(sp, kc->lm_bits, st);
+  hipError_t e = kc->d == 64 ? tq::launch_prepare_d<64>(sp, key_width(kc), st) : tq::launch_prepare_d<128>(sp, key_width(kc), st);
   return hip_status(e, fn);
 }
 
@@ -428,7 +437,7 @@ tq_status tq_logits_prepared(const tq_codec *kc, const void *prepared, size_t by
   if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
   if (!sequences_fit(batch, n_kv_heads))
     return fail(TQ_EUNSUPPORTED, "%s: batch*n_kv_heads above %lld", fn, static_cast<long long>(kMaxSequences));
-  if (!seq_offsets_fit(cap, (kc->lm_bits + 1) * kc->d / 8))
+  if (!seq_offsets_fit(cap, key_rec_bytes(kc)))
     return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
   if (batch == 0 || n_kv_heads == 0 || group == 0 || n_keys == 0) return ok();
   if (!prepared || !kcodes || !kscalars || !logits) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
@@ -442,8 +451,8 @@ tq_status tq_logits_prepared(const tq_codec *kc, const void *prepared, size_t by
   sp.logits = logits;
   sp.prepared = static_cast<const uint8_t *>(prepared);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kc->d == 64 ? tq::launch_logits_prepared_d<64>(sp, kc->lm_bits, st)
-                             : tq::launch_logits_prepared_d<128>(sp, kc->lm_bits, st);
+  hipError_t e = kc->d == 64 ? tq::launch_logits_prepared_d<64>(sp, key_width(kc), st)
+                             : tq::launch_logits_prepared_d<128>(sp, key_width(kc), st);
   return hip_status(e, fn);
 }
 
@@ -570,8 +579,8 @@ tq_status tq_prefill_attend(const tq_codec *kc, const tq_codec *vc, const void *
   if (s != TQ_OK) return s;
   if (nothing) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, kc->lm_bits, vc->lm_bits, st)
-                             : tq::launch_decode_d<128>(sp, kc->lm_bits, vc->lm_bits, st);
+  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, key_width(kc), vc->lm_bits, st)
+                             : tq::launch_decode_d<128>(sp, key_width(kc), vc->lm_bits, st);
   return hip_status(e, fn);
 }
 
@@ -601,8 +610,8 @@ tq_status tq_append_decode_attend(const tq_codec *kc, const tq_codec *vc, const 
   sp.vcodes_w = vcodes;
   sp.vscal_w = vscalars;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kc->d == 64 ? tq::launch_append_decode_d<64>(sp, kc->lm_bits, vc->lm_bits, st)
-                             : tq::launch_append_decode_d<128>(sp, kc->lm_bits, vc->lm_bits, st);
+  hipError_t e = kc->d == 64 ? tq::launch_append_decode_d<64>(sp, key_width(kc), vc->lm_bits, st)
+                             : tq::launch_append_decode_d<128>(sp, key_width(kc), vc->lm_bits, st);
   return hip_status(e, fn);
 }
 
@@ -619,8 +628,8 @@ tq_status tq_decode_attend(const tq_codec *kc, const tq_codec *vc, const void *q
   if (s != TQ_OK) return s;
   if (nothing) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, kc->lm_bits, vc->lm_bits, st)
-                             : tq::launch_decode_d<128>(sp, kc->lm_bits, vc->lm_bits, st);
+  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, key_width(kc), vc->lm_bits, st)
+                             : tq::launch_decode_d<128>(sp, key_width(kc), vc->lm_bits, st);
   return hip_status(e, fn);
 }
 
@@ -653,8 +662,8 @@ tq_status tq_decode_attend_noalloc(const tq_codec *kc, const tq_codec *vc, const
   if (!ws) return s;
   sp.partials = static_cast<float *>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, kc->lm_bits, vc->lm_bits, st)
-                             : tq::launch_decode_d<128>(sp, kc->lm_bits, vc->lm_bits, st);
+  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, key_width(kc), vc->lm_bits, st)
+                             : tq::launch_decode_d<128>(sp, key_width(kc), vc->lm_bits, st);
   return hip_status(e, fn);
 }
 

@@ -24,22 +24,31 @@ constexpr float kSqrtHalfPi = 1.2533141373155002f;   // sqrt(pi / 2)
 
 // ------------------------------------------------------------ key tiles
 
+// MFMA operand fragments of the query side per row group: one per key basis
+// plane (and the sign plane of full records) and 64-coordinate chunk.
+__host__ __device__ constexpr int key_frags(int d, int kw) {
+  return (basis_size(key_lm(kw)) + (key_qjl(kw) ? 1 : 0)) * (d / 64);
+}
+
 // One 16-key tile of a wave: lane (kg = l/16, n = l%16) holds the plane words
-// of key n that its K slots need, and the key's raw fp16 scalar pair.
+// of key n that its K slots need, and the key's raw fp16 scalars (norm in the
+// low half, residual norm in the high half; MSE-only records: the norm alone).
 template <int D, int KW>
 struct KeyTile {
   static constexpr int NH = D / 64;
-  uint32_t w[KW + 1][NH];
+  uint32_t w[key_planes(KW)][NH];
   uint32_t sc;
   __device__ __forceinline__ float norm() const { return f16_bits_to_float(static_cast<uint16_t>(sc & 0xffffu)); }
   __device__ __forceinline__ float gamma() const { return f16_bits_to_float(static_cast<uint16_t>(sc >> 16)); }
 };
 
-// Accumulate the key planes and the sign plane of one tile for NRG row groups.
+// Accumulate the key planes and (full records) the sign plane of one tile for
+// NRG row groups.
 template <int D, int KW, int NRG>
-__device__ __forceinline__ void key_tile_mfma(const KeyTile<D, KW> &kt, const v4i (&a)[NRG][(Basis<KW>::N + 1) * (D / 64)],
+__device__ __forceinline__ void key_tile_mfma(const KeyTile<D, KW> &kt, const v4i (&a)[NRG][key_frags(D, KW)],
                                               const uint32_t (&mask)[4], int nrg, v4i (&clm)[NRG], v4i (&cqj)[NRG]) {
-  constexpr int NB = Basis<KW>::N;
+  constexpr int KL = key_lm(KW);
+  constexpr int NB = Basis<KL>::N;
   constexpr int NH = D / 64;
 #pragma unroll
   for (int rg = 0; rg < NRG; ++rg) { clm[rg] = v4i{0, 0, 0, 0}; cqj[rg] = v4i{0, 0, 0, 0}; }
@@ -49,27 +58,32 @@ __device__ __forceinline__ void key_tile_mfma(const KeyTile<D, KW> &kt, const v4
     for (int hf = 0; hf < NH; ++hf) {
       uint32_t w = 0u;
 #pragma unroll
-      for (int q = 0; q < KW; ++q)
-        if ((Basis<KW>::M[s] >> q) & 1) w ^= kt.w[q][hf];
+      for (int q = 0; q < KL; ++q)
+        if ((Basis<KL>::M[s] >> q) & 1) w ^= kt.w[q][hf];
       const v4i bv = expand_bits(w, mask);
 #pragma unroll
       for (int rg = 0; rg < NRG; ++rg)
         if (rg < nrg) clm[rg] = mfma_i8(a[rg][s * NH + hf], bv, clm[rg]);
     }
   }
+  if constexpr (key_qjl(KW)) {
 #pragma unroll
-  for (int hf = 0; hf < NH; ++hf) {
-    const v4i bv = expand_bits(kt.w[KW][hf], mask);
+    for (int hf = 0; hf < NH; ++hf) {
+      const v4i bv = expand_bits(kt.w[KL][hf], mask);
 #pragma unroll
-    for (int rg = 0; rg < NRG; ++rg)
-      if (rg < nrg) cqj[rg] = mfma_i8(a[rg][NB * NH + hf], bv, cqj[rg]);
+      for (int rg = 0; rg < NRG; ++rg)
+        if (rg < nrg) cqj[rg] = mfma_i8(a[rg][NB * NH + hf], bv, cqj[rg]);
+    }
   }
 }
 
-// fl = {inv_lm, cst_lm, inv_qj, cst_qj} of the lane's head.
+// fl = {inv_lm, cst_lm, inv_qj, cst_qj} of the lane's head. QJ: the full
+// estimator; else its first term alone (MSE-only records).
+template <bool QJ>
 __device__ __forceinline__ float tile_logit(const v4i &clm, const v4i &cqj, const float4 &fl, float n, float g,
                                             float kappa) {
   const float lm = fmaf(combine_digits(clm), fl.x, -fl.y);
+  if constexpr (!QJ) return n * lm;
   const float qj = fmaf(combine_digits(cqj), fl.z, -fl.w);
   return n * fmaf(kappa * g, qj, lm);
 }
@@ -98,9 +112,9 @@ constexpr int kStages = 3;
 //                      (the 16 keys' words of plane 0, then of plane 1, ...),
 //                      for fp8 keys chunk-major (16-byte chunk q of key i at
 //                      16-byte unit 16 q + i)
-//   [OFF_S, OFF_V)     the tiles' key scalar pairs (64 B per tile; none for
-//                      fp8 keys), then (decode) their value norms (32 B per
-//                      tile)
+//   [OFF_S, OFF_V)     the tiles' key scalars (64 B per tile, 32 B for
+//                      MSE-only records, none for fp8 keys), then (decode)
+//                      their value norms (32 B per tile)
 //   [OFF_V, ...)       (decode) value words: [32-token block][plane][16 coords]
 template <int D, int KW, int VW, bool LOGITS, int SPLIT, int NWAVE = D / 16>
 struct ScanShape {
@@ -110,9 +124,9 @@ struct ScanShape {
   static constexpr int THREADS = NW * kWave;
   static constexpr int KT = S / 16 / NW;             // key tiles per wave
   static constexpr int VT = S / 64;                  // 64-token value tiles
-  static constexpr int REC = K8 ? D : (KW + 1) * D / 8;   // record bytes = 16-byte units per key tile
+  static constexpr int REC = K8 ? D : key_planes(KW) * D / 8;   // record bytes = 16-byte units per key tile
   static constexpr int KI = (REC + 63) / 64;         // loads per key tile
-  static constexpr int KSU = K8 ? 0 : 4;             // key scalar units per tile
+  static constexpr int KSU = K8 ? 0 : key_scalar_bytes(KW);   // key scalar units per tile (16 keys' scalars)
   static constexpr int SU = (KSU + (LOGITS ? 0 : 2)) * KT;   // scalar units
   static constexpr int VU = LOGITS ? 0 : (S / 32) * VW * 4;   // value units
   static constexpr int VI = (VU + 63) / 64;
@@ -204,15 +218,17 @@ __device__ __forceinline__ void issue_split(const SeqArrays &sa, int sp, uint8_t
     }
   }
   if (lane < SH::SU) {
-    // lanes [0, 4 KT): key scalar pairs of tile lane/4 (none for fp8 keys);
+    // lanes [0, KSU KT): unit m of the key scalars of tile lane / KSU (KSU
+    // units of 16 bytes per tile: 16 / KSU keys each; none for fp8 keys);
     // then value norms
+    constexpr int KSD = SH::KSU > 0 ? SH::KSU : 1;
     const bool key = lane < SH::KSU * SH::KT;
-    const int u = key ? lane / 4 : (lane - SH::KSU * SH::KT) / 2;
-    const int m = key ? lane % 4 : (lane - SH::KSU * SH::KT) % 2;
+    const int u = key ? lane / KSD : (lane - SH::KSU * SH::KT) / 2;
+    const int m = key ? lane % KSD : (lane - SH::KSU * SH::KT) % 2;
     uint32_t t0 = 0;
 #pragma unroll
     for (int v = 0; v < SH::KT; ++v) t0 = (u == v) ? tile0[v] : t0;
-    dma16_at(key ? sa.kscal + (t0 + 4 * m) * 4 : sa.vscal + (t0 + 8 * m) * 2, wb + SH::OFF_S);
+    dma16_at(key ? sa.kscal + (t0 + (16 / KSD) * m) * KSD : sa.vscal + (t0 + 8 * m) * 2, wb + SH::OFF_S);
   }
 #pragma unroll
   for (int vi = 0; vi < SH::VI; ++vi) {
@@ -269,7 +285,7 @@ __device__ __forceinline__ float wave_fwht(float x, int lane) {
 //   SST     per head: max |q'| and sum q' [8][4]; SCON per-head constants [8][4]
 //   SB      key basis coefficients [8]
 //   SPS     per 32-row tile of S and head: max |p| and sum p over the tile
-//   CENT    the centroids [2^KW] float, staged by a direct-to-LDS load
+//   CENT    the centroids [2^w] float, staged by a direct-to-LDS load
 //   FRAG    the operand bytes in the MFMA A layout, [NRG][NMF][64 lanes][16]
 // Prepared-query records (tq_prepare_queries) hold the operand fragments
 // [NRG][NMF][64 lanes][16 bytes] (REC_FRAG bytes), then the 8 heads'
@@ -277,8 +293,8 @@ __device__ __forceinline__ float wave_fwht(float x, int lane) {
 // scratch.
 template <int D, int KW, int NRG>
 struct PrepShape {
-  static constexpr int NB = Basis<KW>::N;
-  static constexpr int NMF = (NB + 1) * (D / 64);
+  static constexpr int NB = Basis<key_lm(KW)>::N;
+  static constexpr int NMF = key_frags(D, KW);
   static constexpr int SQ = 0;
   static constexpr int SP = SQ + 8 * D * 4;
   static constexpr int SQH = SP + 8 * D * 4;
@@ -359,20 +375,21 @@ __device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int 
       }
     }
   }
-  if (wave < D / 32) {
+  if (key_qjl(KW) && wave < D / 32) {
     const int r = 32 * wave + lane % 32, half = lane / 32;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       in.sk[ks] = *reinterpret_cast<const uint4 *>(p.sketch + static_cast<int64_t>(r) * D + 16 * ks + 8 * half);
   }
-  if (wave == NW - 1 && lane < (1 << KW)) dma4_at(p.kcent + lane, scratch + PS::CENT);
+  if (wave == NW - 1 && lane < (1 << key_lm(KW))) dma4_at(p.kcent + lane, scratch + PS::CENT);
 }
 
 // Query preparation of the heads [h0, h0 + GE) (GE <= 4 NRG) of group bh by
 // one block of NW waves, from the staged inputs: q' = R q, p = S q', the
 // digit operands of the key planes (2 beta_s q') and of the sign plane
 // (2 p), one fixed-point exponent per head for each, and the per-head
-// constants {2^-(7+e_lm), c[L-1] sum q', 2^-(7+e_qj), sum p}. Every wave
+// constants {2^-(7+e_lm), c[L-1] sum q', 2^-(7+e_qj), sum p}. (MSE-only
+// key records: no p, no sign-plane operand, the last two constants 0.) Every wave
 // ends holding all operand fragments of the chunk in a[][] and its heads'
 // constants in fh[] (rows of absent heads zero).
 // Phases, each closed by a block barrier: (1) one wave per head rotates it
@@ -389,9 +406,11 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
                                            LateLoads late_loads, v4i (&a)[NRG][PrepShape<D, KW, NRG>::NMF],
                                            float4 (&fh)[NRG]) {
   using PS = PrepShape<D, KW, NRG>;
-  constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64, NK = NB + 1;
+  constexpr bool QJ = key_qjl(KW);
+  constexpr int KL = key_lm(KW);
+  constexpr int NB = PS::NB, NMF = PS::NMF, NH = D / 64, NK = NB + (QJ ? 1 : 0);
   constexpr int E = D / kWave;
-  constexpr int L = 1 << KW;
+  constexpr int L = 1 << KL;
   float *sq = reinterpret_cast<float *>(scratch + PS::SQ);      // [8][D]
   float *sp = reinterpret_cast<float *>(scratch + PS::SP);      // [8][D]
   uint16_t *sqh = reinterpret_cast<uint16_t *>(scratch + PS::SQH);   // [8][D]
@@ -429,6 +448,11 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
     mq = wave_max(mq);
     s1 = wave_sum(s1);
     if (lane == 0) { sst[4 * h] = mq; sst[4 * h + 1] = s1; }
+    if constexpr (!QJ) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sq[h * D + E * lane + e] = x[e];
+      continue;
+    }
     // the GEMV's B operand: q' times 2^sexp (max |q'| below 2^14), as fp16
     // hi + lo (22 significant bits)
     int ex = 0;
@@ -460,7 +484,7 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
   //     epilogue also leaves the tile's max |p| and sum p per head. The
   //     other waves compute the basis coefficients. (The centroids are in
   //     the scratch from here on.)
-  if (wave < D / 32) {
+  if (QJ && wave < D / 32) {
     const int h = lane % 32, half = lane / 32;
     const bool live = h < GE;
     v16f c = {};
@@ -494,10 +518,8 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
     if (live && half == 0) { sps[(wave * 8 + h) * 2] = mp; sps[(wave * 8 + h) * 2 + 1] = s2; }
   } else {
     late_loads();
-    if (tid - (D / 32) * kWave < NB) {
-      const int s = tid - (D / 32) * kWave;
-      sb[s] = basis_coeff(cent, KW, basis_mask(KW, s));
-    }
+    const int s = tid - (QJ ? (D / 32) * kWave : 0);
+    if (s >= 0 && s < NB) sb[s] = basis_coeff(cent, KL, basis_mask(KL, s));
   }
   lds_barrier();
 
@@ -519,8 +541,10 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
   for (int e = tid; e < GE * D; e += NW * kWave) {
     const int hl = e / D, coord = e % D;
     float mp = 0.f, s2 = 0.f;
+    if constexpr (QJ) {
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) { mp = fmaxf(mp, sps[(t * 8 + hl) * 2]); s2 += sps[(t * 8 + hl) * 2 + 1]; }
+      for (int t = 0; t < D / 32; ++t) { mp = fmaxf(mp, sps[(t * 8 + hl) * 2]); s2 += sps[(t * 8 + hl) * 2 + 1]; }
+    }
     const int el = fixed_exponent(2.0f * mb * sst[4 * hl]);
     const int eq = fixed_exponent(2.0f * mp);
     const int k = coord & 7, word = coord >> 5;
@@ -542,7 +566,7 @@ __device__ __forceinline__ void group_prep(const ScanParams &p, int GE, uint8_t 
     if (coord == 0) {
       scon[4 * hl] = ldexpf(1.0f, -7 - el);
       scon[4 * hl + 1] = cmax * sst[4 * hl + 1];
-      scon[4 * hl + 2] = ldexpf(1.0f, -7 - eq);
+      scon[4 * hl + 2] = QJ ? ldexpf(1.0f, -7 - eq) : 0.f;
       scon[4 * hl + 3] = s2;
     }
   }
@@ -737,11 +761,15 @@ __device__ __forceinline__ void decide_scaled(float v, float vn, const float *th
 // [D] the decoded value; the key record and stored norms; CB the key and
 // value codebooks [4][16] (thresholds, centroids); PART [4][9][D] doubles,
 // the projections' partial sums over quarters of the columns of S.
+// MSE-only key records: no residual, projections or sign plane; the logit
+// is the estimator's first term.
 template <int D, int KW, int VW>
 __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, int GE, int nb, uint8_t *scratch) {
+  constexpr bool QJ = key_qjl(KW);
+  constexpr int KL = key_lm(KW);
   constexpr int NW = D / 16, E = D / kWave;
   constexpr int RPW = (10 + NW - 1) / NW;                  // rows per wave
-  constexpr int REC = (KW + 1) * D / 8;
+  constexpr int REC = key_planes(KW) * D / 8;
   constexpr int KQ = D / 4;                                 // columns of S per thread
   float *rot = reinterpret_cast<float *>(scratch);
   float *pz = rot + 10 * D;
@@ -775,15 +803,17 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
   //    codebooks (into LDS)
   if (tid < 64) {
     const int which = tid / 16, k = tid % 16;
-    const int lv = 1 << ((which < 2) ? KW : VW);
+    const int lv = 1 << ((which < 2) ? KL : VW);
     const float *src = (which == 0) ? p.kthr : (which == 1) ? p.kcent : (which == 2) ? p.vthr : p.vcent;
     if (k < lv - ((which & 1) ? 0 : 1)) cb[tid] = src[k];
   }
   const int j = tid % D, kq = tid / D;
   uint4 sk[KQ / 8];
+  if constexpr (QJ) {
 #pragma unroll
-  for (int u = 0; u < KQ / 8; ++u)
-    sk[u] = *reinterpret_cast<const uint4 *>(p.sketch + static_cast<int64_t>(j) * D + KQ * kq + 8 * u);
+    for (int u = 0; u < KQ / 8; ++u)
+      sk[u] = *reinterpret_cast<const uint4 *>(p.sketch + static_cast<int64_t>(j) * D + KQ * kq + 8 * u);
+  }
   float x[RPW][E], sgn[RPW][E];
   uint32_t vw_old[E][VW];
 #pragma unroll
@@ -845,7 +875,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (isv) decide_scaled<VW>(y[e], vn, cb + 32, cb + 48, idx[e], cq[e]);
-      else decide_scaled<KW>(y[e], vn, cb, cb + 16, idx[e], cq[e]);
+      else decide_scaled<KL>(y[e], vn, cb, cb + 16, idx[e], cq[e]);
     }
     const uint16_t nh = float_to_f16_bits(nrm);
     if (isv) {
@@ -876,7 +906,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
     }
     const float gamma = sqrtf(wave_sum(g2));
 #pragma unroll
-    for (int q = 0; q < KW; ++q)
+    for (int q = 0; q < KL; ++q)
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const uint64_t m = __ballot((idx[e] >> q) & 1);
@@ -886,13 +916,33 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
         }
       }
     if (lane == 0) {
-      const uint16_t gh = float_to_f16_bits(gamma);
       shat[0] = f16_bits_to_float(nh);
-      shat[1] = f16_bits_to_float(gh);
-      reinterpret_cast<uint32_t *>(p.kscal_w)[slot] = static_cast<uint32_t>(nh) | (static_cast<uint32_t>(gh) << 16);
+      if constexpr (QJ) {
+        const uint16_t gh = float_to_f16_bits(gamma);
+        shat[1] = f16_bits_to_float(gh);
+        reinterpret_cast<uint32_t *>(p.kscal_w)[slot] = static_cast<uint32_t>(nh) | (static_cast<uint32_t>(gh) << 16);
+      } else {
+        shat[1] = 0.f;
+        p.kscal_w[slot] = nh;
+      }
     }
   }
   __syncthreads();
+  if constexpr (!QJ) {
+    // MSE-only record: the index planes, by wave 0; each head's logit
+    if (wave == 0 && lane < REC / 4) reinterpret_cast<uint32_t *>(p.kcodes_w + slot * REC)[lane] = rec[lane];
+    for (int hl = wave; hl < GE; hl += NW) {
+      float slm = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) slm = fmaf(rot[hl * D + lane + kWave * e], ck[lane + kWave * e], slm);
+      slm = wave_sum(slm);
+      float *ph = part + (head_chunk0() + hl) * (D + 2);
+      if (lane == 0) { ph[0] = shat[0] * slm * p.sm_scale; ph[1] = 1.0f; }
+#pragma unroll
+      for (int e = 0; e < E; ++e) ph[2 + lane + kWave * e] = vh[lane + kWave * e];
+    }
+    return;
+  }
 
   // 2. projections PZ[c] = S ROT[c], c <= GE: thread (j, kq) sums its
   //    quarter of row j for every column, then the four quarters are added.
@@ -953,7 +1003,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
       sw[2 * e + 1] = static_cast<uint32_t>(m >> 32);
     }
     if (lane < REC / 4) {
-      const int k = lane - KW * (D / 32);                // sign-plane word, or < 0: an index-plane word
+      const int k = lane - KL * (D / 32);                // sign-plane word, or < 0: an index-plane word
       uint32_t w = (k < 0) ? rec[lane] : sw[0];
 #pragma unroll
       for (int i = 1; i < 2 * E; ++i) w = (k == i) ? sw[i] : w;
@@ -1025,9 +1075,11 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   static_assert(!PREPARED || (LOGITS && SEP), "prepared queries: the logit scan with its own preparation region");
   constexpr int NST = SEP ? NST_L : (SPLIT == 512 ? 2 : kStages);
   constexpr int PREP_AT = SEP ? NST * SB : SB;
-  constexpr int RING = (NST * SB > PREP_AT + PS_BYTES) ? NST * SB : PREP_AT + PS_BYTES;
+  constexpr int RING0 = (NST * SB > PREP_AT + PS_BYTES) ? NST * SB : PREP_AT + PS_BYTES;
+  // (the append block's scratch overlays the ring)
+  constexpr int APPEND_BYTES = APPEND ? (21 * D + 128) * 4 + 4 * 9 * D * 8 : 0;
+  constexpr int RING = RING0 > APPEND_BYTES ? RING0 : APPEND_BYTES;
   static_assert(RING <= LDS_BUDGET - (LOGITS ? 0 : NRG * VT * 1024), "LDS budget");
-  static_assert(!APPEND || RING >= (21 * D + 128) * 4 + 4 * 9 * D * 8, "append scratch");
   static_assert(P * (NST - 1) < 64, "vmcnt range");
   // stage k at ring + k * SB; the query preparation uses [PREP_AT,
   // PREP_AT + PS::BYTES), which (decode) stages 1 and 2 reuse once it is done
@@ -1073,7 +1125,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   const int col = lane % 16;
   uint32_t mask[4];
   lane_masks(mask);
-  const float kappa = p.qjl ? kSqrtHalfPi / static_cast<float>(D) : 0.f;
+  const float kappa = (key_qjl(KW) && p.qjl) ? kSqrtHalfPi / static_cast<float>(D) : 0.f;
   const float cvmax = LOGITS ? 0.f : p.vcent[(1 << VW) - 1];
   if (!LOGITS && tid < NBV) svb[tid] = basis_coeff(p.vcent, VW, basis_mask(VW, tid));
 
@@ -1092,7 +1144,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   sa.cap = static_cast<int32_t>(p.cap);
   sa.nblk = static_cast<int32_t>(p.cap / kValueBlock);
   sa.kcodes = p.kcodes + bh * p.cap * REC;
-  sa.kscal = reinterpret_cast<const uint8_t *>(p.kscalars) + bh * p.cap * 4;
+  sa.kscal = reinterpret_cast<const uint8_t *>(p.kscalars) + bh * p.cap * key_scalar_bytes(KW);
   sa.vcodes = LOGITS ? nullptr : reinterpret_cast<const uint8_t *>(p.vcodes + bh * sa.nblk * VW * D);
   sa.vscal = LOGITS ? nullptr : reinterpret_cast<const uint8_t *>(p.vscalars) + bh * p.cap * 2;
   v4i a[NRG][NMF];
@@ -1113,11 +1165,12 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
     if (ns > 0) {
       // the prepared operand fragments and head constants into the
       // preparation's region (separate from the stages), then every stage
-      const uint8_t *src = p.prepared + (bh * p.n_hchunks + h0 / 8) * prepared_stride(D, KW);
+      constexpr int64_t PSTR = prepared_stride(D, key_lm(KW));
+      const uint8_t *src = p.prepared + (bh * p.n_hchunks + h0 / 8) * PSTR;
       constexpr int FW = NRG * NMF;                  // 1 KB fragments: 64 lanes x 16 bytes
       for (int f = wave; f < FW; f += NW) dma16_at(src + (f * kWave + lane) * 16, ring + PREP_AT + f * 1024);
       if (wave == 0 && lane < 8)
-        dma16_at(src + prepared_stride(D, KW) - 128 + 16 * lane, ring + PREP_AT + PS::REC_FRAG);
+        dma16_at(src + PSTR - 128 + 16 * lane, ring + PREP_AT + PS::REC_FRAG);
       // every stage's key loads behind the record's, then a wait for the
       // record alone
       const int first = min(ns, NST);
@@ -1184,7 +1237,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
       } else {
         KeyTile<D, KW> kt;
 #pragma unroll
-        for (int q = 0; q <= KW; ++q) {
+        for (int q = 0; q < key_planes(KW); ++q) {
           if constexpr (D == 128) {
             const uint2 v = *reinterpret_cast<const uint2 *>(kb + (16 * q + col) * 16 + 8 * (kg >> 1));
             kt.w[q][0] = v.x;
@@ -1193,12 +1246,13 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
             kt.w[q][0] = *reinterpret_cast<const uint32_t *>(kb + col * REC + q * 8 + 4 * (kg >> 1));
           }
         }
-        kt.sc = *reinterpret_cast<const uint32_t *>(wb + SH::OFF_S + 64 * u + 4 * col);
+        if constexpr (key_qjl(KW)) kt.sc = *reinterpret_cast<const uint32_t *>(wb + SH::OFF_S + 64 * u + 4 * col);
+        else kt.sc = *reinterpret_cast<const uint16_t *>(wb + SH::OFF_S + 32 * u + 2 * col);
         v4i clm[NRG], cqj[NRG];
         key_tile_mfma<D, KW, NRG>(kt, a, mask, NRG, clm, cqj);
         const float kn = kt.norm(), kgm = kt.gamma();
 #pragma unroll
-        for (int rg = 0; rg < NRG; ++rg) lr[rg] = tile_logit(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa);
+        for (int rg = 0; rg < NRG; ++rg) lr[rg] = tile_logit<key_qjl(KW)>(clm[rg], cqj[rg], fh[rg], kn, kgm, kappa);
       }
       if constexpr (LOGITS) {
 #pragma unroll
@@ -1421,7 +1475,8 @@ __global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
   group_prep<D, KW, NRG>(p, GE, scratch, pin, [] {}, a, fh);
   // fragment f = rg NMF + mf (as the scan blocks hold it) is written by
   // wave f % NW from its registers; the constants from the scratch
-  uint8_t *dst = p.prepared_w + (bh * p.n_hchunks + head_chunk0() / 8) * prepared_stride(D, KW);
+  constexpr int64_t PSTR = prepared_stride(D, key_lm(KW));
+  uint8_t *dst = p.prepared_w + (bh * p.n_hchunks + head_chunk0() / 8) * PSTR;
   constexpr int NW = D / 16;
   const int lane = lane_id();
 #pragma unroll
@@ -1438,7 +1493,7 @@ __global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
     }
   (void)fh;
   if (threadIdx.x < 8)
-    *reinterpret_cast<uint4 *>(dst + prepared_stride(D, KW) - 128 + 16 * threadIdx.x) =
+    *reinterpret_cast<uint4 *>(dst + PSTR - 128 + 16 * threadIdx.x) =
         *reinterpret_cast<const uint4 *>(scratch + PS::SCON + 16 * threadIdx.x);
 }
 
@@ -1533,38 +1588,70 @@ static void launch_logits_k(const ScanParams &p, dim3 grid, hipStream_t st) {
 // heads); every block reads its keys once for its chunk. (A chunk of up to
 // 4 heads is taken by the single-row-group kernel only when the whole group
 // has at most 4 heads.)
-template <int D, int MODE>
+// K0: 0 for full key records, kKeyMse for MSE-only ones (key width K0 + w).
+template <int D, int MODE, int K0>
 hipError_t launch_logits_m(const ScanParams &p, int kw, hipStream_t st) {
   if (p.batch == 0 || p.n_kv == 0 || (MODE != 2 && p.max_ctx == 0)) return hipSuccess;
   dim3 grid(static_cast<uint32_t>(p.nb), static_cast<uint32_t>(p.batch) * p.n_kv, static_cast<uint32_t>(p.n_hchunks));
-  switch (kw) {
-    case 1: launch_logits_k<D, 1, MODE>(p, grid, st); break;
-    case 2: launch_logits_k<D, 2, MODE>(p, grid, st); break;
-    case 3: launch_logits_k<D, 3, MODE>(p, grid, st); break;
-    default: launch_logits_k<D, 4, MODE>(p, grid, st);
+  switch (key_lm(kw)) {
+    case 1: launch_logits_k<D, K0 + 1, MODE>(p, grid, st); break;
+    case 2: launch_logits_k<D, K0 + 2, MODE>(p, grid, st); break;
+    case 3: launch_logits_k<D, K0 + 3, MODE>(p, grid, st); break;
+    default: launch_logits_k<D, K0 + 4, MODE>(p, grid, st);
   }
   return hipGetLastError();
 }
 
+// MSE-only key records (their kernels are instantiated in a translation
+// unit of their own)
+template <int D>
+hipError_t launch_logits_msek_d(const ScanParams &p, int kw, int mode, hipStream_t st) {
+  if (mode == 0) return launch_logits_m<D, 0, kKeyMse>(p, kw, st);
+  if (mode == 1) return launch_logits_m<D, 1, kKeyMse>(p, kw, st);
+  return launch_logits_m<D, 2, kKeyMse>(p, kw, st);
+}
+
 template <int D>
 hipError_t launch_logits_d(const ScanParams &p, int kw, hipStream_t st) {
-  return launch_logits_m<D, 0>(p, kw, st);
+  return kw > kKeyMse ? launch_logits_msek_d<D>(p, kw, 0, st) : launch_logits_m<D, 0, 0>(p, kw, st);
 }
 
 template <int D>
 hipError_t launch_logits_prepared_d(const ScanParams &p, int kw, hipStream_t st) {
-  return launch_logits_m<D, 1>(p, kw, st);
+  return kw > kKeyMse ? launch_logits_msek_d<D>(p, kw, 1, st) : launch_logits_m<D, 1, 0>(p, kw, st);
 }
 
 template <int D>
 hipError_t launch_prepare_d(const ScanParams &p, int kw, hipStream_t st) {
-  return launch_logits_m<D, 2>(p, kw, st);
+  return kw > kKeyMse ? launch_logits_msek_d<D>(p, kw, 2, st) : launch_logits_m<D, 2, 0>(p, kw, st);
 }
 
 // One launch over (blocks, groups, head chunks of 8 heads), then the merge.
 // APPEND: nb + 1 blocks per group, one of them encoding the group's new
 // token (the append block of every head chunk encodes it, to the same
 // bytes, for that chunk's partials).
+template <int D, int KW, bool APPEND>
+static void launch_decode_v(const ScanParams &p, int vw, dim3 grid, hipStream_t st) {
+  switch (vw) {
+    case 1: launch_decode_kv<D, KW, 1, APPEND>(p, grid, st); break;
+    case 2: launch_decode_kv<D, KW, 2, APPEND>(p, grid, st); break;
+    case 3: launch_decode_kv<D, KW, 3, APPEND>(p, grid, st); break;
+    default: launch_decode_kv<D, KW, 4, APPEND>(p, grid, st);
+  }
+}
+
+// The scan launch of decode attention over MSE-only key records (their
+// kernels are instantiated in translation units of their own).
+template <int D, bool APPEND>
+void launch_decode_msek_d(const ScanParams &p, int kw, int vw, dim3 grid, hipStream_t st) {
+  switch (key_lm(kw)) {
+    case 1: launch_decode_v<D, kKeyMse + 1, APPEND>(p, vw, grid, st); break;
+    case 2: launch_decode_v<D, kKeyMse + 2, APPEND>(p, vw, grid, st); break;
+    case 3: launch_decode_v<D, kKeyMse + 3, APPEND>(p, vw, grid, st); break;
+    default: launch_decode_v<D, kKeyMse + 4, APPEND>(p, vw, grid, st);
+  }
+}
+
 template <int D, bool APPEND>
 hipError_t launch_decode_da(const ScanParams &p, int kw, int vw, hipStream_t st) {
   if (p.batch == 0 || p.n_kv == 0) return hipSuccess;
@@ -1572,23 +1659,16 @@ hipError_t launch_decode_da(const ScanParams &p, int kw, int vw, hipStream_t st)
   const uint32_t chunks = static_cast<uint32_t>(p.n_hchunks);
   dim3 grid = APPEND ? dim3(groups, static_cast<uint32_t>(p.nb + 1), chunks)
                      : dim3(static_cast<uint32_t>(p.nb), groups, chunks);
-#define TQ_DS_V(KK)                                                   \
-  switch (vw) {                                                       \
-    case 1: launch_decode_kv<D, KK, 1, APPEND>(p, grid, st); break;   \
-    case 2: launch_decode_kv<D, KK, 2, APPEND>(p, grid, st); break;   \
-    case 3: launch_decode_kv<D, KK, 3, APPEND>(p, grid, st); break;   \
-    default: launch_decode_kv<D, KK, 4, APPEND>(p, grid, st);         \
-  }
   switch (kw) {
-    case 1: TQ_DS_V(1); break;
-    case 2: TQ_DS_V(2); break;
-    case 3: TQ_DS_V(3); break;
+    case 1: launch_decode_v<D, 1, APPEND>(p, vw, grid, st); break;
+    case 2: launch_decode_v<D, 2, APPEND>(p, vw, grid, st); break;
+    case 3: launch_decode_v<D, 3, APPEND>(p, vw, grid, st); break;
+    case 4: launch_decode_v<D, 4, APPEND>(p, vw, grid, st); break;
     case kKeyFp8:
-      if constexpr (!APPEND) TQ_DS_V(kKeyFp8);
+      if constexpr (!APPEND) launch_decode_v<D, kKeyFp8, false>(p, vw, grid, st);
       break;
-    default: TQ_DS_V(4);
+    default: launch_decode_msek_d<D, APPEND>(p, kw, vw, grid, st);
   }
-#undef TQ_DS_V
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<D>), dim3(chunks, groups), dim3(kMergeThreads), 0, st, p);

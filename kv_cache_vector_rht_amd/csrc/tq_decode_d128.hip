@@ -2,6 +2,10 @@
 #include "tq_decode.inc.h"
 
 namespace tq {
+// the kernels for MSE-only key records are instantiated in tq_msek_d128.hip
+extern template hipError_t launch_logits_msek_d<128>(const ScanParams &p, int kw, int mode, hipStream_t st);
+extern template void launch_decode_msek_d<128, false>(const ScanParams &p, int kw, int vw, dim3 grid, hipStream_t st);
+
 template hipError_t launch_logits_d<128>(const ScanParams &p, int kw, hipStream_t st);
 template hipError_t launch_logits_prepared_d<128>(const ScanParams &p, int kw, hipStream_t st);
 template hipError_t launch_prepare_d<128>(const ScanParams &p, int kw, hipStream_t st);

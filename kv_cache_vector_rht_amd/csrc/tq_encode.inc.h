@@ -17,7 +17,9 @@
 // the half-waves). A ballot over the wave of one value slot's index bit
 // yields two 32-bit value-code words (two coordinates of one 32-token
 // block). Key records are assembled per lane pair; the QJL projection of
-// each 32-token tile runs on the matrix cores (tq_qjl.h).
+// each 32-token tile runs on the matrix cores (tq_qjl.h). MSE-only key
+// records (the ablation without the QJL stage) take the key path's
+// decisions and packing and stop there.
 #include "tq_device.h"
 #include "tq_kernels.h"
 #include "tq_qjl.h"
@@ -162,8 +164,11 @@ __host__ __device__ constexpr int mfma_row_coord(int r) { return 16 * ((r >> 2) 
 // resident waves per CU, or spills at 128 registers.)
 constexpr int kEncThreads = 256;
 
-template <int D, int W, bool KEY, int XT>
+// KIND: 0 values, 1 keys, 2 MSE-only keys (index planes and the norm only).
+template <int D, int W, int KIND, int XT>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void encode_kernel(EncodeParams p) {
+  constexpr bool KEY = KIND != 0;              // key record layout
+  constexpr bool QJ = KIND == 1;               // with the QJL stage
   constexpr int L = 1 << W;
   constexpr int NT = 128 / D;                // 32-token tiles per wave (1 or 2)
   constexpr int TPW = 32 * NT;               // tokens per wave
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ float s_cent[L];
   __shared__ float s_th[L];
   __shared__ __attribute__((aligned(16))) float s_sign[D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_sk[KEY ? D * (D + 8) : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t s_sk[QJ ? D * (D + 8) : 8];
   // 16-bit input: A operands of the rotation's 32-point blocks,
   // [block b][K step e][lane][8 halves]. Lane l holds row l % 32, standing
   // for output coordinate rc = mfma_row_coord(l % 32), and input coordinates
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
       s_ha[idx] = w;
     }
   }
-  if (KEY) stage_sketch<D, kEncThreads>(p.sketch, s_sk);
+  if constexpr (QJ) stage_sketch<D, kEncThreads>(p.sketch, s_sk);
   __syncthreads();
 
   const int lane = lane_id();
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int T = 0; T < NT; ++T) ls[T].load(s_th, vn[T]);
 
-    if (KEY) {
+    if constexpr (KEY) {
       // (a3) indices -> bit planes: each decision's lane mask is added in as
       // the carry of half + half into the 16-bit group of its block
       // (coordinate order reversed, so the first coordinate lands on bit 0);
@@ -345,14 +350,16 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const int T = i / CT;
         uint64_t m[W];
         float cq;
-        decide_masks<W, true>(v[i], ls[T], c_up, m, cq);
+        decide_masks<W, QJ>(v[i], ls[T], c_up, m, cq);
 #pragma unroll
         for (int q = 0; q < W; ++q) {
           uint64_t carry;
           asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(hw[q][i / 16]), "=s"(carry) : "s"(m[q]));
         }
-        v[i] = fmaf(v[i], rs[T], -cq);
-        asm volatile("" : "+v"(v[i]));    // consume the decisions here
+        if constexpr (QJ) {
+          v[i] = fmaf(v[i], rs[T], -cq);
+          asm volatile("" : "+v"(v[i]));  // consume the decisions here
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       // plane words: word b of a token = its group b of lane half 0 | that of
@@ -374,6 +381,24 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
           pw[q][0] = hv ? ((recv & 0xffffu) | (hw[q][1] << 16)) : (hw[q][0] | (recv << 16));
           pw[q][1] = hv ? ((recv >> 16) | (hw[q][3] << 16)) : (hw[q][2] | (recv & 0xffff0000u));
         }
+      }
+      if constexpr (!QJ) {
+        // MSE-only record: the W index planes, D/8 bytes each; scalar {norm}
+        constexpr int REC = W * D / 8;
+        constexpr int PB = D / 8;
+#pragma unroll
+        for (int T = 0; T < NT; ++T) {
+          if (active[T]) {
+            uint8_t *rec = static_cast<uint8_t *>(p.codes) + (seq * p.cap + pos[T]) * REC + (PB / 2) * hv;
+#pragma unroll
+            for (int q = 0; q < W; ++q) {
+              if constexpr (D == 128) *reinterpret_cast<uint2 *>(rec + q * PB) = make_uint2(pw[q][0], pw[q][1]);
+              else *reinterpret_cast<uint32_t *>(rec + q * PB) = pw[q][T];
+            }
+            if (hv == 0) p.scalars[seq * p.cap + pos[T]] = float_to_f16_bits(nrm[T]);
+          }
+        }
+        continue;
       }
       float gamma[NT];
 #pragma unroll
@@ -488,10 +513,10 @@ static int64_t resident_blocks(K kernel, int (&cached)[64]) {
   return cached[dev];
 }
 
-template <int D, int W, bool KEY, int XT>
+template <int D, int W, int KIND, int XT>
 static void launch_encode_x(const EncodeParams &p, hipStream_t st) {
   static int cached[64] = {};
-  const auto kernel = encode_kernel<D, W, KEY, XT>;
+  const auto kernel = encode_kernel<D, W, KIND, XT>;
   constexpr int wpb = kEncThreads / kWave;
   int64_t blocks = (p.n_waves + wpb - 1) / wpb;
   const int64_t cap = resident_blocks(kernel, cached);
@@ -499,32 +524,31 @@ static void launch_encode_x(const EncodeParams &p, hipStream_t st) {
   hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kEncThreads), 0, st, p);
 }
 
-template <int D, int W, bool KEY>
+template <int D, int W, int KIND>
 static hipError_t launch_encode_dw(const EncodeParams &p, hipStream_t st) {
   switch (p.xt) {
-    case 0: launch_encode_x<D, W, KEY, 0>(p, st); break;
-    case 1: launch_encode_x<D, W, KEY, 1>(p, st); break;
-    default: launch_encode_x<D, W, KEY, 2>(p, st); break;
+    case 0: launch_encode_x<D, W, KIND, 0>(p, st); break;
+    case 1: launch_encode_x<D, W, KIND, 1>(p, st); break;
+    default: launch_encode_x<D, W, KIND, 2>(p, st); break;
   }
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_encode_d(const EncodeParams &p, int w, bool key, hipStream_t st) {
-  if (key) {
-    switch (w) {
-      case 1: return launch_encode_dw<D, 1, true>(p, st);
-      case 2: return launch_encode_dw<D, 2, true>(p, st);
-      case 3: return launch_encode_dw<D, 3, true>(p, st);
-      default: return launch_encode_dw<D, 4, true>(p, st);
-    }
-  }
+template <int D, int KIND>
+static hipError_t launch_encode_dk(const EncodeParams &p, int w, hipStream_t st) {
   switch (w) {
-    case 1: return launch_encode_dw<D, 1, false>(p, st);
-    case 2: return launch_encode_dw<D, 2, false>(p, st);
-    case 3: return launch_encode_dw<D, 3, false>(p, st);
-    default: return launch_encode_dw<D, 4, false>(p, st);
+    case 1: return launch_encode_dw<D, 1, KIND>(p, st);
+    case 2: return launch_encode_dw<D, 2, KIND>(p, st);
+    case 3: return launch_encode_dw<D, 3, KIND>(p, st);
+    default: return launch_encode_dw<D, 4, KIND>(p, st);
   }
+}
+
+template <int D>
+hipError_t launch_encode_d(const EncodeParams &p, int w, int kind, hipStream_t st) {
+  if (kind == 1) return launch_encode_dk<D, 1>(p, w, st);
+  if (kind == 2) return launch_encode_dk<D, 2>(p, w, st);
+  return launch_encode_dk<D, 0>(p, w, st);
 }
 
 }  // namespace tq

@@ -2,5 +2,5 @@
 #include "tq_encode.inc.h"
 
 namespace tq {
-template hipError_t launch_encode_d<64>(const EncodeParams &p, int w, bool key, hipStream_t st);
+template hipError_t launch_encode_d<64>(const EncodeParams &p, int w, int kind, hipStream_t st);
 }  // namespace tq

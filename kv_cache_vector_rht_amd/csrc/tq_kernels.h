@@ -20,8 +20,9 @@ struct EncodeParams {
   uint16_t *scalars;
 };
 
+// kind: 0 values, 1 keys, 2 MSE-only keys (key layout without the QJL part)
 template <int D>
-hipError_t launch_encode_d(const EncodeParams &p, int w, bool key, hipStream_t st);
+hipError_t launch_encode_d(const EncodeParams &p, int w, int kind, hipStream_t st);
 // fp8 keys: codes[s][t][i] = e4m3fn(sat(x / scale)) for slots [t0, t0 + n_tok)
 hipError_t launch_encode_fp8(const EncodeParams &p, int d, float scale, hipStream_t st);
 
@@ -99,6 +100,15 @@ constexpr int kDecodeMaxBlocks = 128;
 // Key width selecting fp8 key records (d bytes of OCP e4m3fn per key, no
 // scalars) in the decode kernels.
 constexpr int kKeyFp8 = 8;
+// Key width kKeyMse + w selects MSE-only key records (w index planes, one
+// fp16 norm per token: no sign plane, no residual norm) in the scan and
+// decode kernels; a plain w (1..4) the full records.
+constexpr int kKeyMse = 16;
+__host__ __device__ constexpr int key_lm(int kw) { return kw > kKeyMse ? kw - kKeyMse : kw; }
+__host__ __device__ constexpr bool key_qjl(int kw) { return kw < kKeyMse && kw != kKeyFp8; }
+__host__ __device__ constexpr int key_planes(int kw) { return key_lm(kw) + (key_qjl(kw) ? 1 : 0); }
+// Bytes of the fp16 scalars stored per key token: {norm, residual norm} or {norm}.
+__host__ __device__ constexpr int key_scalar_bytes(int kw) { return key_qjl(kw) ? 4 : 2; }
 // Prefill: most query heads (chunk positions x heads per KV head) per call.
 constexpr int kPrefillMaxHeads = 1024;
 

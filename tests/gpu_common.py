@@ -24,9 +24,9 @@ class CodecPair:
     The GPU side takes its codebook from tq_make_codebook, the oracle side
     from oracle.make_codebook; the two are checked equal elsewhere."""
 
-    def __init__(self, d, lm_bits, is_key, signs, sketch=None, device="cuda"):
+    def __init__(self, d, lm_bits, is_key, signs, sketch=None, device="cuda", mse_only=False):
         self.d, self.lm_bits, self.is_key = d, lm_bits, is_key
-        self.gpu = tq.Codec.make(d, lm_bits, is_key, signs, sketch, device=device)
+        self.gpu = tq.Codec.make(d, lm_bits, is_key, signs, sketch, device=device, mse_only=mse_only)
         self.signs = np.asarray(signs, dtype=np.float64)
         self.sketch = None if sketch is None else np.asarray(sketch.numpy() if torch.is_tensor(sketch) else sketch,
                                                              dtype=np.float16)
@@ -40,6 +40,12 @@ class CodecPair:
 def key_codec(cfg, d, lm_bits, device="cuda"):
     s, S = syn.key_codec_randoms(cfg, d)
     return CodecPair(d, lm_bits, True, s.numpy(), S, device)
+
+
+def mse_key_codec(cfg, d, lm_bits, device="cuda"):
+    """MSE-only keys: the key codec's rotation and codebook, no sketch."""
+    s, _ = syn.key_codec_randoms(cfg, d)
+    return CodecPair(d, lm_bits, True, s.numpy(), None, device, mse_only=True)
 
 
 def value_codec(cfg, d, lm_bits, device="cuda"):
@@ -58,6 +64,15 @@ def pack_keys_into(enc, lm_bits, codes: torch.Tensor, scal: torch.Tensor, seqs=N
     idx = torch.arange(n) if seqs is None else torch.as_tensor(seqs)
     codes[idx.to(codes.device), t0:t0 + T] = torch.from_numpy(rec).to(codes.device)
     scal[idx.to(scal.device), t0:t0 + T] = torch.from_numpy(sc.view(np.int16)).to(scal.device)
+
+
+def pack_mse_keys_into(enc, lm_bits, codes: torch.Tensor, scal: torch.Tensor):
+    """Write oracle MSE-only key codes [n, T, ...] into GPU cache tensors at slots 0.."""
+    rec = O.pack_mse_key_codes(enc["idx"], lm_bits)                           # [n, T, R]
+    n, T = rec.shape[:2]
+    codes[:n, :T] = torch.from_numpy(rec).to(codes.device)
+    sc = np.asarray(enc["nhat"], dtype=np.float16)[..., None]                 # [n, T, 1]
+    scal[:n, :T] = torch.from_numpy(sc.view(np.int16)).to(scal.device)
 
 
 def pack_values_into(enc, lm_bits, codes: torch.Tensor, scal: torch.Tensor, seqs=None):

@@ -62,6 +62,9 @@ def test_record_sizes():
     assert tq.key_record_bytes(64, 2) == 24
     assert tq.value_block_bytes(128, 4) == 2048
     assert tq.key_record_bytes(96, 2) == 0
+    assert tq.mse_key_record_bytes(128, 3) == 48          # + a 2-byte norm: 50 B against 68 B with QJL
+    assert tq.mse_key_record_bytes(64, 4) == 32
+    assert tq.mse_key_record_bytes(96, 2) == 0
 
 
 # ---------------------------------------------------------------- validation
@@ -94,6 +97,8 @@ def _encode(c, xt=tq.TQ_BF16, n_seq=1, n_tok=64, seq_stride=64 * 128, tok_stride
     (dict(c="w0"), tq.TQ_EINVAL),
     (dict(c="w5"), tq.TQ_EUNSUPPORTED),
     (dict(c="nosketch"), tq.TQ_EINVAL),
+    (dict(c="kind3"), tq.TQ_EINVAL),
+    (dict(c="mse", n_tok=-1), tq.TQ_EINVAL),                # an MSE-only key codec needs no sketch
     (dict(xt=7), tq.TQ_EINVAL),
     (dict(n_tok=-1), tq.TQ_EINVAL),
     (dict(t0=32, n_tok=64, cap=64), tq.TQ_EINVAL),
@@ -109,7 +114,7 @@ def test_encode_validation(kwargs, status):
     c = kwargs.pop("c", "key")
     codec = {"key": _codec(), "d96": _codec(d=96), "d256": _codec(d=256), "w0": _codec(w=0),
              "w5": _codec(w=5), "nosketch": _codec(sketch=False), "value": _codec(key=0),
-             None: None}[c]
+             "kind3": _codec(key=3), "mse": _codec(key=2, sketch=False), None: None}[c]
     assert _encode(codec, **kwargs) == status
     assert tq.lib.tq_last_error().decode()
 
@@ -136,6 +141,9 @@ def test_logits_validation():
     assert _logits(_codec(), qt=9) == tq.TQ_EINVAL
     assert _logits(_codec(), batch=-1) == tq.TQ_EINVAL
     assert _logits(_codec(), n_keys=0) == tq.TQ_OK
+    # MSE-only key records: no sketch needed; the 4 GiB bound uses their w d/8 bytes
+    assert _logits(_codec(key=2, sketch=False), n_keys=0) == tq.TQ_OK
+    assert _logits(_codec(key=2, sketch=False, w=4), cap=1 << 27, n_keys=64) == tq.TQ_EUNSUPPORTED
     assert tq.logits_workspace(1, 8, 4, 128) == 0                           # queries are prepared in LDS
     # the MSE-only ablation validates exactly like tq_logits
     cs = _codec()
