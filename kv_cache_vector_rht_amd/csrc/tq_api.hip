@@ -84,6 +84,25 @@ int decode_blocks_per_group(int32_t batch, int32_t n_kv, int64_t max_ctx, int sp
   return static_cast<int>(std::min<int64_t>(splits, want));
 }
 
+// The single-pass prefill: used when a KV head has more (position, head)
+// pairs than one pass of the decode kernels holds (8). Blocks per group:
+// about two per CU over the launch, at most one per split.
+bool prefill_single_pass(int32_t chunk, int32_t group) { return static_cast<int64_t>(chunk) * group > 8; }
+
+int prefill_blocks_per_group(int32_t batch, int32_t n_kv, int32_t pairs, int64_t max_ctx) {
+  const int64_t groups = std::max<int64_t>(1, static_cast<int64_t>(batch) * n_kv) *
+                         ((pairs + tq::kPrefillBlockPairs - 1) / tq::kPrefillBlockPairs);
+  const int64_t splits = std::max<int64_t>(1, (max_ctx + tq::kPrefillSplitTokens - 1) / tq::kPrefillSplitTokens);
+  const int64_t want = std::max<int64_t>(1, (512 + groups - 1) / groups);
+  return static_cast<int>(std::min<int64_t>(std::min<int64_t>(splits, want), tq::kDecodeMaxBlocks));
+}
+
+// Bytes of the prepared query records of the single-pass prefill (one per 8
+// pairs of every group, sized for the widest keys), after the partials.
+size_t prefill_prepared_bytes(int32_t batch, int32_t n_kv, int32_t pairs, int32_t d) {
+  return static_cast<size_t>(batch) * n_kv * ((pairs + 7) / 8) * static_cast<size_t>(tq::prepared_stride(d, 4));
+}
+
 // The scan kernels address one sequence's arrays with 32-bit offsets.
 bool seq_offsets_fit(int64_t cap, int bytes_per_token) {
   return cap * static_cast<int64_t>(bytes_per_token) < (static_cast<int64_t>(1) << 32);
@@ -562,8 +581,15 @@ tq_status tq_decode_attend_k8(const tq_codec *vc, const void *q, tq_dtype qt, in
 size_t tq_prefill_attend_workspace(int32_t batch, int32_t chunk, int32_t n_kv_heads, int32_t group,
                                    int64_t max_ctx, int32_t d) {
   if (batch < 0 || chunk < 0 || n_kv_heads < 0 || group <= 0 || max_ctx < 0 || d <= 0) return 0;
-  const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, tq::kAttendSplit);
-  return align_up(static_cast<size_t>(batch) * n_kv_heads * nb * chunk * group * (d + 2) * sizeof(float));
+  const int64_t pairs = static_cast<int64_t>(chunk) * group;
+  if (pairs > tq::kPrefillMaxHeads) return 0;
+  if (!prefill_single_pass(chunk, group)) {
+    const int nb = decode_blocks_per_group(batch, n_kv_heads, max_ctx, tq::kAttendSplit);
+    return align_up(static_cast<size_t>(batch) * n_kv_heads * nb * pairs * (d + 2) * sizeof(float));
+  }
+  const int nb = prefill_blocks_per_group(batch, n_kv_heads, static_cast<int32_t>(pairs), max_ctx);
+  return align_up(static_cast<size_t>(batch) * n_kv_heads * nb * pairs * (d + 2) * sizeof(float)) +
+         align_up(prefill_prepared_bytes(batch, n_kv_heads, static_cast<int32_t>(pairs), d));
 }
 
 tq_status tq_prefill_attend(const tq_codec *kc, const tq_codec *vc, const void *q, tq_dtype qt, int32_t batch,
@@ -579,8 +605,22 @@ tq_status tq_prefill_attend(const tq_codec *kc, const tq_codec *vc, const void *
   if (s != TQ_OK) return s;
   if (nothing) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = kc->d == 64 ? tq::launch_decode_d<64>(sp, key_width(kc), vc->lm_bits, st)
-                             : tq::launch_decode_d<128>(sp, key_width(kc), vc->lm_bits, st);
+  hipError_t e;
+  if (prefill_single_pass(chunk, group)) {
+    // one scan of the context per 64 pairs; the prepared query records
+    // follow the partials in the workspace
+    const int32_t pairs = chunk * group;
+    sp.nb = prefill_blocks_per_group(batch, n_kv_heads, pairs, max_ctx);
+    const size_t part = align_up(static_cast<size_t>(batch) * n_kv_heads * sp.nb * pairs * (kc->d + 2) * sizeof(float));
+    uint8_t *prep = static_cast<uint8_t *>(workspace) + part;
+    sp.prepared_w = prep;
+    sp.prepared = prep;
+    e = kc->d == 64 ? tq::launch_prefill_d<64>(sp, key_width(kc), vc->lm_bits, st)
+                    : tq::launch_prefill_d<128>(sp, key_width(kc), vc->lm_bits, st);
+  } else {
+    e = kc->d == 64 ? tq::launch_decode_d<64>(sp, key_width(kc), vc->lm_bits, st)
+                    : tq::launch_decode_d<128>(sp, key_width(kc), vc->lm_bits, st);
+  }
   return hip_status(e, fn);
 }
 

@@ -1065,6 +1065,8 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   constexpr int NBV = Basis<VW>::N;
   constexpr int GMAX = 4 * NRG;
   constexpr int NBG = (NRG == 2 && NBV == 8) ? 4 : NBV;
+  // (combine_digits: at most 16 MFMAs accumulate into one digit row)
+  static_assert(VT <= 16 && key_frags(D, K8 ? 1 : KW) <= 18, "digit sums in range");
   constexpr int SB = SH::STAGE_BYTES;
   // ring depth: 3 stages for decode; the logit scan (small stages, few
   // splits per block) keeps up to 6 in flight, its query preparation in a

@@ -91,6 +91,11 @@ template <int D>
 hipError_t launch_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st);
 template <int D>
 hipError_t launch_append_decode_d(const ScanParams &p, int kw, int vw, hipStream_t st);
+// Single-pass prefill attention: the query preparation of every 8 pairs into
+// p.prepared_w (read back through p.prepared), one scan of the context per
+// 64 (position, head) pairs, the merge.
+template <int D>
+hipError_t launch_prefill_d(const ScanParams &p, int kw, int vw, hipStream_t st);
 
 // Tokens per split (one pipeline stage) of the logit scan and of decode
 // attention, and the most blocks one (batch, kv-head) group is spread over.
@@ -109,8 +114,11 @@ __host__ __device__ constexpr bool key_qjl(int kw) { return kw < kKeyMse && kw !
 __host__ __device__ constexpr int key_planes(int kw) { return key_lm(kw) + (key_qjl(kw) ? 1 : 0); }
 // Bytes of the fp16 scalars stored per key token: {norm, residual norm} or {norm}.
 __host__ __device__ constexpr int key_scalar_bytes(int kw) { return key_qjl(kw) ? 4 : 2; }
-// Prefill: most query heads (chunk positions x heads per KV head) per call.
+// Prefill: most query heads (chunk positions x heads per KV head) per call;
+// (position, head) pairs per block of the single-pass prefill and its split.
 constexpr int kPrefillMaxHeads = 1024;
+constexpr int kPrefillBlockPairs = 64;
+constexpr int kPrefillSplitTokens = 128;
 
 // Row-wise top-k: columns per first-stage block, largest k.
 constexpr int kTopkChunk = 4096;

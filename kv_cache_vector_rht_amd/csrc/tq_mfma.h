@@ -94,13 +94,16 @@ __device__ __forceinline__ uint32_t signed_digits(int32_t v) {
   return (static_cast<uint32_t>(v) + 0x00808080u) ^ 0x00808080u;
 }
 
-// sum_s 2^(8 s) C_s for the 4 digit rows a lane holds.
+// sum_s 2^(8 s) C_s for the 4 digit rows a lane holds. A K slot's product is
+// digit (|d| <= 128) x 2^k, and the 64 slots of one MFMA hold each bit k
+// 0..7 eight times (sum of 2^k: 2040), so a row accumulated over at most 16
+// MFMAs (the planes of a 4-bit key, or the value tiles of a split) keeps
+// |C_s| < 128 * 2040 * 16 < 2^22: the digit pairs C_0 + 256 C_1 and
+// C_2 + 256 C_3 stay below 2^31 in int32, and one fma joins them.
 __device__ __forceinline__ float combine_digits(const v4i &c) {
-  float f = static_cast<float>(c[3]);
-  f = fmaf(f, 256.f, static_cast<float>(c[2]));
-  f = fmaf(f, 256.f, static_cast<float>(c[1]));
-  f = fmaf(f, 256.f, static_cast<float>(c[0]));
-  return f;
+  const int lo = c[0] + (c[1] << 8);
+  const int hi = c[2] + (c[3] << 8);
+  return fmaf(static_cast<float>(hi), 65536.f, static_cast<float>(lo));
 }
 
 // K-slot -> coordinate within the 64-coordinate chunk `half`.

@@ -75,3 +75,71 @@ def test_one_position_chunk_is_decode():
                            group=group, max_ctx=T)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(pre[:, 0].cpu().numpy(), dec.cpu().numpy())
+
+
+@pytest.mark.parametrize("d,kw,vw,group,batch,n_kv,T,chunk,pos0", [
+    (128, 2, 4, 4, 2, 2, 1000, 16, [984, 0]),       # 64 pairs; the chunk ends at max_ctx
+    (128, 3, 4, 4, 1, 1, 500, 25, [475]),           # 100 pairs: blocks of 64 and 36 pairs
+    (64, 1, 2, 16, 1, 2, 300, 4, [100]),            # 1-bit keys, 2-bit values
+    (128, 4, 3, 8, 1, 1, 257, 8, [249]),            # 5-bit keys, 3-bit values
+    (64, 4, 1, 2, 2, 1, 130, 11, [0, 119]),         # 1-bit values
+])
+def test_single_pass_prefill_given_oracle_codes(d, kw, vw, group, batch, n_kv, T, chunk, pos0):
+    """More than 8 (position, head) pairs per KV head: one scan of the context
+    per 64 pairs (values on the fp16 matrix cores), against the oracle."""
+    say(f"single-pass prefill d={d} kw={kw} vw={vw} G={group} batch={batch} n_kv={n_kv} T={T} chunk={chunk} "
+        f"pos0={pos0}")
+    kc, vc, ek, ev, cache, g = _cache(d, kw, vw, batch, n_kv, T, seed=7 * d + kw + chunk)
+    q = torch.randn((batch, chunk, n_kv * group, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    p0 = torch.tensor(pos0, dtype=torch.int32, device="cuda")
+    scale = 0.7 / math.sqrt(d)
+    out = tq.prefill_attend(kc.gpu, vc.gpu, q.to("cuda"), *cache, p0, n_kv_heads=n_kv, group=group, max_ctx=T,
+                            sm_scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.prefill_attend(to_f64(q), kc.signs, kc.centroids, kc.sketch, ek["idx"], ek["sigma"], ek["nhat"],
+                           ek["ghat"], vc.signs, vc.centroids, ev["idx"], ev["nhat"], pos0, scale, group)
+    say("   worst err/tol", assert_close(out.cpu().numpy(), ref, "single-pass prefill"))
+
+
+def test_prefill_batched_decode_shape_sampled():
+    """The batched-decode cache shape (16 x 8 KV heads x 8192 tokens, 32 query
+    heads, 3-bit keys, 4-bit values) with a 16-token chunk at its end, caches
+    encoded on the GPU: two sampled (batch row, KV head) groups against the
+    oracle over the GPU's codes."""
+    import synthetic as syn
+    w = syn.WORKLOADS[3]
+    d, chunk = w.d, 16
+    say(f"prefill chunk {chunk} on {w.name}")
+    s, S = syn.key_codec_randoms(w.cfg, d)
+    kc = tq.Codec.make(d, w.key_lm_bits, True, s, S, device="cuda")
+    vc = tq.Codec.make(d, w.val_bits, False, syn.value_codec_randoms(w.cfg, d), device="cuda")
+    kcodes, kscal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+    vcodes, vscal = tq.alloc_value_cache(w.n_seq, w.n_tok, vc)
+    x = syn.keys(w, device="cuda")
+    tq.encode_kv(kc, x, kcodes, kscal)
+    del x
+    x = syn.values(w, device="cuda")
+    tq.encode_kv(vc, x, vcodes, vscal)
+    del x
+    g = torch.Generator(device="cpu")
+    g.manual_seed(33)
+    q = torch.randn((w.batch, chunk, w.n_q, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    pos0 = [w.n_tok - chunk - 37 * b for b in range(w.batch)]
+    p0 = torch.tensor(pos0, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    out = tq.prefill_attend(kc, vc, q.to("cuda"), kcodes, kscal, vcodes, vscal, p0, n_kv_heads=w.n_kv,
+                            group=w.group, max_ctx=w.n_tok, sm_scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cs, cv = O.make_codebook(d, w.key_lm_bits), O.make_codebook(d, w.val_bits)
+    for b, kvh in ((0, 0), (w.batch - 1, w.n_kv - 1)):
+        sq = b * w.n_kv + kvh
+        kidx, ksig = O.unpack_key_codes(kcodes[sq].cpu().numpy(), d, w.key_lm_bits)
+        ks = kscal[sq].cpu().numpy().view(np.float16)
+        vidx = O.unpack_value_codes(vcodes[sq:sq + 1].cpu().numpy().view(np.uint32), w.n_tok)
+        vn = vscal[sq:sq + 1].cpu().numpy().view(np.float16)
+        heads = slice(kvh * w.group, (kvh + 1) * w.group)
+        ref = O.prefill_attend(to_f64(q[b:b + 1, :, heads]), s.numpy(), cs[0], S.numpy(), kidx[None], ksig[None],
+                               ks[None, :, 0], ks[None, :, 1], syn.value_codec_randoms(w.cfg, d).numpy(), cv[0],
+                               vidx, vn, [pos0[b]], scale, w.group)
+        say(f"   group (b={b}, kv={kvh}) worst err/tol",
+            assert_close(out[b:b + 1, :, heads].cpu().numpy(), ref, f"prefill b={b} kv={kvh}"))
