@@ -447,9 +447,13 @@ def prefill_chunk_workload(torch, tq, syn, cfg, chunk, copies, steps):
     gr.replay()
     avg = time_replays(torch, [gr], max(1, steps // copies)) / copies
     pairs = w.batch * w.n_q * sum(w.n_tok - chunk + i + 1 for i in range(chunk))
+    heads = chunk * w.group                               # (position, head) pairs per KV head
+    scans = (heads + 63) // 64 if heads > 8 else (heads + 7) // 8   # passes over each context
+    nbytes = w.n_seq * w.n_tok * ((kc.record_bytes + 4) + (w.val_bits * w.d // 8 + 2))
     return dict(workload=f"{w.name}, causal prefill chunk of {chunk} tokens at the end of the context",
-                avg_us=avg * 1e6, attended_logits_per_s=pairs / avg, chunk=chunk,
-                launches=(chunk * w.group + 7) // 8, copies=copies)
+                avg_us=avg * 1e6, attended_logits_per_s=pairs / avg, chunk=chunk, pairs_per_kv_head=heads,
+                context_scans=scans, cache_bytes=nbytes, hbm_frac=hbm(nbytes * scans, avg),
+                frac_of_read_probe=of_probe(nbytes * scans, avg), copies=copies)
 
 
 def k8v4_ablation(torch, tq, syn, copies, steps):

@@ -14,6 +14,7 @@
 // which turns (1 - x^2)^((d-3)/2) dx into cos(theta)^(d-2) dtheta, a smooth
 // integrand, and composite Gauss-Legendre quadrature. The normalising
 // constant cancels in every conditional mean.
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -58,14 +59,15 @@ const GaussLegendre &gl() {
   return g;
 }
 
-// Integrals over theta in [a, b] of cos^m and sin * cos^m.
+// Integrals over theta in [a, b] of cos^m and sin * cos^m: Gauss-Legendre
+// panels at the resolution of 24 panels over [0, pi/2] (at least one).
 void cell_integrals(double a, double b, int m, double &mass, double &moment) {
   const GaussLegendre &g = gl();
-  constexpr int PANELS = 24;
+  const int panels = std::max(1, static_cast<int>(std::ceil(24.0 * (b - a) / (0.5 * M_PI) - 1e-9)));
   mass = 0.0;
   moment = 0.0;
-  const double h = (b - a) / PANELS;
-  for (int pi = 0; pi < PANELS; ++pi) {
+  const double h = (b - a) / panels;
+  for (int pi = 0; pi < panels; ++pi) {
     const double lo = a + pi * h;
     const double mid = lo + 0.5 * h;
     for (int k = 0; k < GaussLegendre::N; ++k) {
@@ -87,13 +89,19 @@ bool lloyd_max_positive_half(int d, int bits, std::vector<double> &c) {
   const int H = L / 2;
   const int m = d - 2;
   c.assign(H, 0.0);
-  // start: positive-half quantiles of N(0, 1/d), found by bisection on erf
+  // start: the positive half's quantiles of f_d itself, P(0 < X < c_k) =
+  // (k + 1/2) / H of P(X > 0), by bisection on the cell mass: strictly
+  // increasing and inside (0, 1) for every d and width
+  double half_mass, unused;
+  cell_integrals(0.0, 0.5 * M_PI, m, half_mass, unused);
   for (int k = 0; k < H; ++k) {
-    const double target = (k + 0.5) / H;                 // P(0 < X < c) / P(X > 0)
+    const double target = (k + 0.5) / H * half_mass;
     double lo = 0.0, hi = 1.0;
-    for (int it = 0; it < 200; ++it) {
+    for (int it = 0; it < 64; ++it) {
       const double mid = 0.5 * (lo + hi);
-      if (std::erf(mid * std::sqrt(d / 2.0)) < target) lo = mid; else hi = mid;
+      double mass;
+      cell_integrals(0.0, std::asin(mid), m, mass, unused);
+      if (mass < target) lo = mid; else hi = mid;
     }
     c[k] = 0.5 * (lo + hi);
   }
@@ -106,7 +114,7 @@ bool lloyd_max_positive_half(int d, int bits, std::vector<double> &c) {
       const double x1 = (k == H - 1) ? 1.0 : 0.5 * (c[k] + c[k + 1]);
       double mass, moment;
       cell_integrals(std::asin(x0), std::asin(x1), m, mass, moment);
-      nc[k] = moment / mass;
+      nc[k] = (mass > 0.0) ? moment / mass : c[k];      // (an empty cell keeps its centroid)
       delta = std::fmax(delta, std::fabs(nc[k] - c[k]));
     }
     c.swap(nc);

@@ -237,13 +237,14 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(ScanParams p) {
     }
     const int t0 = sp * S;
 
-    // 1. logits of the wave's pairs for every key tile of the split
+    // 1. logits of the wave's pairs for every key tile of the split,
+    //    software-pipelined: tile u + 1's products are issued before tile u's
+    //    epilogue, so that the epilogue's VALU work runs beside them
     float lg[KTL][RGW];
     float mx[RGW];
 #pragma unroll
     for (int r = 0; r < RGW; ++r) mx[r] = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < KTL; ++u) {
+    auto tile_products = [&](int u, v4i (&clm)[RGW], v4i (&cqj)[RGW], uint32_t &sc) {
       const uint8_t *kb = buf + u * PS::REC * 16;
       KeyTile<D, KW> kt;
 #pragma unroll
@@ -259,17 +260,27 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(ScanParams p) {
       const int tok = 16 * u + col;
       if constexpr (key_qjl(KW)) kt.sc = *reinterpret_cast<const uint32_t *>(buf + PS::OFF_KS + 4 * tok);
       else kt.sc = *reinterpret_cast<const uint16_t *>(buf + PS::OFF_KS + 2 * tok);
-      v4i clm[RGW], cqj[RGW];
       key_tile_mfma<D, KW, RGW>(kt, a, mask, RGW, clm, cqj);
-      const float kn = kt.norm(), kgm = kt.gamma();
+      sc = kt.sc;
+    };
+    v4i clm[2][RGW], cqj[2][RGW];
+    uint32_t ksc[2];
+    tile_products(0, clm[0], cqj[0], ksc[0]);
+#pragma unroll
+    for (int u = 0; u < KTL; ++u) {
+      const int cur = u & 1;
+      if (u + 1 < KTL) tile_products(u + 1, clm[cur ^ 1], cqj[cur ^ 1], ksc[cur ^ 1]);
+      const int tok = 16 * u + col;
+      const float kn = f16_bits_to_float(static_cast<uint16_t>(ksc[cur] & 0xffffu));
+      const float kgm = f16_bits_to_float(static_cast<uint16_t>(ksc[cur] >> 16));
 #pragma unroll
       for (int r = 0; r < RGW; ++r) {
-        const float l = tile_logit<key_qjl(KW)>(clm[r], cqj[r], fh[r], kn, kgm, kappa) * sl;
+        const float l = tile_logit<key_qjl(KW)>(clm[cur][r], cqj[cur][r], fh[r], kn, kgm, kappa) * sl;
         lg[u][r] = (t0 + tok < lim[r]) ? l : -INFINITY;
         asm volatile("" : "+v"(lg[u][r]));       // formed here, not at its later uses
         mx[r] = fmaxf(mx[r], lg[u][r]);
       }
-      // one tile's operands and accumulators live at a time
+      // at most two tiles' operands and accumulators live at a time
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -325,14 +336,14 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(ScanParams p) {
     }
     __syncthreads();                                  // weights and alphas
 
-    // 3. values: this wave's coordinates for every token of the split
-    v4f cs[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) cs[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // B: coordinate `coord`, tokens 32 ks + 8 kg + j (j < 8): 4 x their
-      // indices as the bytes of two words, then the centroid hi / lo parts
+    // 3. values: this wave's coordinates for every token of the split. Per
+    //    K step of 32 tokens: B = the decoded centroids of the lane's
+    //    coordinate for tokens 32 ks + 8 kg + j (j < 8), A = the weights of
+    //    the 4 row tiles. The next step's B is decoded after this step's
+    //    products are issued.
+    auto decode_b = [&](int ks, H8 &bh, H8 &bl) {
+      // 4 x the tokens' indices as the bytes of two words, then the
+      // centroid hi / lo parts from the table
       uint32_t ix[2] = {0u, 0u};
 #pragma unroll
       for (int q = 0; q < VW; ++q) {
@@ -341,7 +352,6 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(ScanParams p) {
         ix[0] |= e.x << q;
         ix[1] |= e.y << q;
       }
-      H8 bh, bl;
       const uint8_t *ct = reinterpret_cast<const uint8_t *>(ctab);
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
@@ -350,16 +360,26 @@ __global__ __launch_bounds__(4 * D) void prefill_kernel(ScanParams p) {
         bh.u[j / 2] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);   // hi halves of e0, e1
         bl.u[j / 2] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);   // lo halves
       }
+    };
+    v4f cs[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) cs[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+    H8 bh[2], bl[2];
+    decode_b(0, bh[0], bl[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        H8 ah, al;
+        H8 ah[1], al[1];
         const uint8_t *src = wts + ((rt * KS + ks) * 2) * 1024 + lane * 16;
-        ah.q = *reinterpret_cast<const uint4 *>(src);
-        al.q = *reinterpret_cast<const uint4 *>(src + 1024);
-        cs[rt] = mfma_f16_16x16x32(ah.h, bh.h, cs[rt]);
-        cs[rt] = mfma_f16_16x16x32(ah.h, bl.h, cs[rt]);
-        cs[rt] = mfma_f16_16x16x32(al.h, bh.h, cs[rt]);
+        ah[0].q = *reinterpret_cast<const uint4 *>(src);
+        al[0].q = *reinterpret_cast<const uint4 *>(src + 1024);
+        cs[rt] = mfma_f16_16x16x32(ah[0].h, bh[cur].h, cs[rt]);
+        cs[rt] = mfma_f16_16x16x32(ah[0].h, bl[cur].h, cs[rt]);
+        cs[rt] = mfma_f16_16x16x32(al[0].h, bh[cur].h, cs[rt]);
       }
+      if (ks + 1 < KS) decode_b(ks + 1, bh[cur ^ 1], bl[cur ^ 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     const float down = ldexpf(1.0f, -sc) * (1.0f / kCentScale);

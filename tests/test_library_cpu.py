@@ -223,7 +223,13 @@ def test_prefill_validation():
     assert _prefill(k, v, pos0=0) == tq.TQ_EINVAL
     assert _prefill(k, v, max_ctx=512) == tq.TQ_EINVAL
     # the partials of every (position, head) pair
-    assert tq.prefill_attend_workspace(2, 8, 2, 4, 256, 128) == 2 * 2 * 1 * (8 * 4) * (128 + 2) * 4
+    # up to 8 (position, head) pairs per KV head: the decode kernels' partials
+    # (1 block per group here); more: the single-pass kernel's partials (2
+    # blocks of 128-token splits per group) and one prepared query record per
+    # 8 pairs (sized for 4-bit keys: 2 row groups x 9 fragments x 2 KiB + 128)
+    assert tq.prefill_attend_workspace(2, 2, 2, 4, 256, 128) == 2 * 2 * 1 * (2 * 4) * (128 + 2) * 4
+    assert tq.prefill_attend_workspace(2, 8, 2, 4, 256, 128) == (2 * 2 * 2 * (8 * 4) * (128 + 2) * 4 +
+                                                                 2 * 2 * 4 * (2 * 9 * 2 * 1024 + 128))
     assert _prefill(k, v, ws=tq.decode_attend_workspace(2, 2, 4, 256, 128)) == tq.TQ_EINVAL
     assert _prefill(k, v, chunk=0) == tq.TQ_OK
     assert _prefill(k, v, batch=0) == tq.TQ_OK
