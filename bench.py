@@ -72,7 +72,7 @@ def parse():
                     help="time the oracle on the batched and long-context decode workloads in full (minutes) "
                          "and on the 22-layer encode's layer {0, 21} x row {0, 63} slices")
     ap.add_argument("--only", default="", help="comma list of extra sections: "
-                                               "dec3,app3,pre3,k8v4,dec5,enc4,search,ablation,single")
+                                               "dec3,app3,pre3,k8v4,dec5,enc4,search,ablation,formulations,single")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch each timed kernel a few times eagerly, after a 1 GiB calibration copy, "
                          "for hardware-counter runs; prints no JSON line")
@@ -687,6 +687,58 @@ def mse_keys_ablation(torch, tq, syn, copies, steps):
     return res
 
 
+def scan_formulations(torch, tq, syn, copies, steps):
+    """The logit scan of the decode-layer workload (8 KV / 32 Q heads, 32768
+    4-bit keys) in its two formulations, over `copies` rotated cache copies:
+    the bit planes on the matrix cores (tq_logits, each block preparing its
+    queries; and tq_prepare_queries + tq_logits_prepared, the preparation in
+    a launch of its own) and the codebook in LDS (tq_logits_table: nibble
+    tables per head, one lane per key, after a preparation launch). Times per
+    call; the counters that split them per kernel come from rocprofv3."""
+    w = syn.WORKLOADS[2]
+    dev = "cuda"
+    kc, _, _ = setup_codecs(torch, tq, syn, w, dev)
+    x = syn.keys(w, device=dev)
+    q = syn.queries(w, device=dev)
+    caches = []
+    for _ in range(copies):
+        codes, scal = tq.alloc_key_cache(w.n_seq, w.n_tok, kc)
+        tq.encode_kv(kc, x, codes, scal)
+        caches.append((codes, scal))
+    del x
+    outs = [torch.empty((w.batch, w.n_q, w.n_tok), dtype=torch.float32, device=dev) for _ in range(copies)]
+    prep = tq.prepare_queries(kc, q, n_kv_heads=w.n_kv, group=w.group)
+    tws = torch.empty(max(256, int(tq.lib.tq_logits_table_workspace(w.batch, w.n_kv, w.group, w.d))),
+                      dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    calls = {
+        "matrix_cores": lambda c: (lambda: tq.logits(kc, q, caches[c][0], caches[c][1], n_kv_heads=w.n_kv,
+                                                     group=w.group, n_keys=w.n_tok, out=outs[c])),
+        "matrix_cores_prepared": lambda c: (lambda: (tq.prepare_queries(kc, q, n_kv_heads=w.n_kv, group=w.group,
+                                                                        prepared=prep),
+                                                     tq.logits_prepared(kc, prep, w.batch, caches[c][0], caches[c][1],
+                                                                        n_kv_heads=w.n_kv, group=w.group,
+                                                                        n_keys=w.n_tok, out=outs[c]))),
+        "lds_table": lambda c: (lambda: tq.logits_table(kc, q, caches[c][0], caches[c][1], n_kv_heads=w.n_kv,
+                                                        group=w.group, n_keys=w.n_tok, out=outs[c], workspace=tws)),
+    }
+    nbytes = w.n_vec * (kc.record_bytes + 4) + w.batch * w.n_q * w.n_tok * 4
+    res = dict(workload=w.name, copies=copies, bytes_per_call=nbytes)
+    ref = None
+    for name, mk in calls.items():
+        t = time_replays(torch, [capture(torch, [mk(c) for c in range(copies)])], max(1, steps // copies)) / copies
+        mk(0)()
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = outs[0].clone()
+        err = float((outs[0] - ref).abs().max() / ref.abs().max())
+        res[name] = dict(avg_us=t * 1e6, hbm_frac=hbm(nbytes, t), frac_of_read_probe=of_probe(nbytes, t),
+                         max_rel_diff_vs_matrix_cores=err)
+    del caches
+    torch.cuda.empty_cache()
+    return res
+
+
 def single_head_workload(torch, tq, syn, reps=50):
     """The single-head workload: encode of 4096 fp32 keys (d 128, 2 Lloyd-Max
     bits + QJL) and all 16 x 4096 logits. Its 2.8 MB fit any cache and a call
@@ -888,15 +940,22 @@ def pmc_pass(torch, tq, syn):
         tq.encode_kv(kc, x, codes, scal)
     for _ in range(3):
         tq.logits(kc, q, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok, out=out)
+    # the two formulations of the scan with their preparation launches
+    prep = tq.prepare_queries(kc, q, n_kv_heads=w.n_kv, group=w.group)
+    for _ in range(3):
+        tq.prepare_queries(kc, q, n_kv_heads=w.n_kv, group=w.group, prepared=prep)
+        tq.logits_prepared(kc, prep, w.batch, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok, out=out)
+        tq.logits_table(kc, q, codes, scal, n_kv_heads=w.n_kv, group=w.group, n_keys=w.n_tok, out=out)
     torch.cuda.synchronize()
-    del x, q, codes, scal, out
+    del x, q, codes, scal, out, prep
     torch.cuda.empty_cache()
     for cfg in (3, 5):
         decode_workload(torch, tq, syn, cfg, copies=1, steps=3)
         torch.cuda.empty_cache()
     search_workload(torch, tq, syn, copies=1, steps=2)
     torch.cuda.empty_cache()
-    log("[pmc] done: copy 1 GiB x2, encode x3, logits x3, decode attention of workloads 3 and 5, search scan")
+    log("[pmc] done: copy 1 GiB x2, encode x3, logits x3, prepared and LDS-table scans x3, decode attention of "
+        "workloads 3 and 5, search scan")
 
 
 # ------------------------------------------------------------------ main
@@ -990,6 +1049,9 @@ def main():
         torch.cuda.empty_cache()
         if not only or "ablation" in only:
             extras["mse_keys_ablation"] = mse_keys_ablation(torch, tq, syn, copies=16, steps=32)
+        torch.cuda.empty_cache()
+        if not only or "formulations" in only:
+            extras["logit_scan_formulations"] = scan_formulations(torch, tq, syn, copies=16, steps=32)
         torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:

@@ -77,6 +77,8 @@ def _load():
         "tq_topk": ([P, I64, I64, I64, I32, P, P, P, SZ, P], I32),
         "tq_topk_workspace": ([I64, I64, I32], SZ),
         "tq_probe_read": ([P, SZ, P, P], I32),
+        "tq_logits_table": ([CP, P, I32, I32, I32, I32, P, P, I64, I64, P, P, SZ, P], I32),
+        "tq_logits_table_workspace": ([I32, I32, I32, I32], SZ),
         "tq_status_string": ([I32], ctypes.c_char_p),
         "tq_last_error": ([], ctypes.c_char_p),
     }
@@ -112,7 +114,8 @@ EXPORTED = ("tq_make_codebook", "tq_rate_plan", "tq_key_record_bytes", "tq_mse_k
             "tq_decode_attend_noalloc_max_workspace",
             "tq_append_decode_attend", "tq_append_decode_attend_workspace", "tq_prefill_attend",
             "tq_prefill_attend_workspace", "tq_encode_fp8_keys", "tq_decode_attend_k8",
-            "tq_topk", "tq_topk_workspace", "tq_probe_read", "tq_status_string", "tq_last_error")
+            "tq_topk", "tq_topk_workspace", "tq_probe_read", "tq_logits_table", "tq_logits_table_workspace",
+            "tq_status_string", "tq_last_error")
 
 
 def _check(status: int, what: str):
@@ -739,6 +742,38 @@ def probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
         raise ValueError("src must be a contiguous CUDA tensor and sink a CUDA tensor")
     st = lib.tq_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream))
     _check(st, "tq_probe_read")
+
+
+@_on_stream
+def logits_table(codec: Codec, q: torch.Tensor, codes: torch.Tensor, scalars: torch.Tensor, n_kv_heads: int,
+                 group: int, n_keys: int, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """Measurement path: the logits of tq_logits from the LDS-table formulation of the scan
+    (tq_logits_table); float32 [batch, n_kv_heads*group, n_keys]."""
+    dev = codec.signs.device
+    _tensor("q", q)
+    if q.dim() != 3:
+        raise ValueError("q must be [batch, n_kv_heads*group, d]")
+    batch = q.shape[0]
+    n_q = n_kv_heads * group
+    _check_queries("q", q, codec, (batch, n_q), dev)
+    q = q.contiguous()
+    cap = _check_key_cache(codec, codes, scalars, batch * n_kv_heads, dev)
+    if n_keys < 0 or n_keys > cap:
+        raise ValueError(f"n_keys={n_keys} outside [0, {cap}]")
+    if out is None:
+        out = torch.empty((batch, n_q, n_keys), dtype=torch.float32, device=dev)
+    _check_out(out, (batch, n_q, n_keys), (torch.float32,), dev)
+    need = int(lib.tq_logits_table_workspace(batch, n_kv_heads, group, codec.d))
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    _check_workspace(workspace, need, dev)
+    cs = codec.struct()
+    st = lib.tq_logits_table(ctypes.byref(cs), _ptr(q), _DTYPE[q.dtype], batch, n_kv_heads, group, _ptr(codes),
+                             _ptr(scalars), cap, n_keys, _ptr(out), _ptr(workspace), workspace.numel(),
+                             _stream(stream))
+    _check(st, "tq_logits_table")
+    return out
 
 
 @_on_stream

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/tq.h"
+#include "../../include/tq_probe.h"
 #include "tq_kernels.h"
 #include "tq_mfma.h"
 
@@ -480,6 +481,41 @@ tq_status tq_logits(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batc
                     float *logits, void *workspace, size_t ws_bytes, void *stream) {
   return logits_call("tq_logits", 1, kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys, logits,
                      workspace, ws_bytes, stream);
+}
+
+size_t tq_logits_table_workspace(int32_t batch, int32_t n_kv_heads, int32_t group, int32_t d) {
+  if (batch < 0 || n_kv_heads < 0 || group < 0 || (d != 64 && d != 128)) return 0;
+  return align_up(tq::table_workspace_bytes(batch, n_kv_heads, group, d));
+}
+
+tq_status tq_logits_table(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,
+                          int32_t group, const uint8_t *kcodes, const uint16_t *kscalars, int64_t cap,
+                          int64_t n_keys, float *logits, void *workspace, size_t ws_bytes, void *stream) {
+  const char *fn = "tq_logits_table";
+  tq_status s = check_codec(kc, 1, fn);
+  if (s != TQ_OK) return s;
+  if (kc->is_key != 1) return fail(TQ_EINVAL, "%s: full key records (is_key = 1) only", fn);
+  if (!dtype_ok(qt)) return fail(TQ_EINVAL, "%s: bad query dtype", fn);
+  if (batch < 0 || n_kv_heads < 0 || group < 0 || n_keys < 0 || cap < 0) return fail(TQ_EINVAL, "%s: negative size", fn);
+  if (n_keys > cap) return fail(TQ_EINVAL, "%s: n_keys > cap", fn);
+  if (cap % 32) return fail(TQ_EINVAL, "%s: cap must be a multiple of 32", fn);
+  if (group > 32) return fail(TQ_EUNSUPPORTED, "%s: group=%d > 32", fn, group);
+  if (!sequences_fit(batch, n_kv_heads))
+    return fail(TQ_EUNSUPPORTED, "%s: batch*n_kv_heads above %lld", fn, static_cast<long long>(kMaxSequences));
+  if (!seq_offsets_fit(cap, key_rec_bytes(kc)))
+    return fail(TQ_EUNSUPPORTED, "%s: one sequence's codes exceed 4 GiB", fn);
+  if (batch == 0 || n_kv_heads == 0 || group == 0 || n_keys == 0) return ok();
+  if (!q || !kcodes || !kscalars || !logits || !workspace) return fail(TQ_EINVAL, "%s: NULL pointer", fn);
+  const size_t need = tq_logits_table_workspace(batch, n_kv_heads, group, kc->d);
+  if (ws_bytes < need) return fail(TQ_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 || reinterpret_cast<uintptr_t>(kcodes) % 16 ||
+      reinterpret_cast<uintptr_t>(kscalars) % 16)
+    return fail(TQ_EINVAL, "%s: workspace and key cache must be 16-byte aligned", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  tq::ScanParams sp = scan_params(kc, q, qt, batch, n_kv_heads, group, kcodes, kscalars, cap, n_keys, tq::kLogitSplit);
+  sp.logits = logits;
+  hipError_t e = tq::launch_logits_table(sp, kc->d, kc->lm_bits, static_cast<float *>(workspace), st);
+  return hip_status(e, fn);
 }
 
 tq_status tq_logits_mse(const tq_codec *kc, const void *q, tq_dtype qt, int32_t batch, int32_t n_kv_heads,

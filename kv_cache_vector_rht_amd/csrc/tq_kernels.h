@@ -120,6 +120,11 @@ constexpr int kPrefillMaxHeads = 1024;
 constexpr int kPrefillBlockPairs = 64;
 constexpr int kPrefillSplitTokens = 128;
 
+// The logit scan with per-head nibble tables in LDS (measurement path):
+// workspace bytes (q' and p of every head chunk) and the launches.
+size_t table_workspace_bytes(int32_t batch, int32_t n_kv, int32_t group, int32_t d);
+hipError_t launch_logits_table(const ScanParams &p, int d, int kw, float *qp, hipStream_t st);
+
 // Row-wise top-k: columns per first-stage block, largest k.
 constexpr int kTopkChunk = 4096;
 constexpr int kTopkMaxK = 1024;
