@@ -360,7 +360,9 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(2, 
           v[i] = fmaf(v[i], rs[T], -cq);
           asm volatile("" : "+v"(v[i]));  // consume the decisions here
         }
-        __builtin_amdgcn_sched_barrier(0);
+        // two values' decisions interleave (they fill each other's wait
+        // states between a lane mask's write and its use as a carry)
+        if (i % 2 == 0) __builtin_amdgcn_sched_barrier(0);
       }
       // plane words: word b of a token = its group b of lane half 0 | that of
       // lane half 1 << 16. d = 128: lane half h keeps words 2 h, 2 h + 1 of
