@@ -920,8 +920,10 @@ def cpu_baseline(w, syn, torch, full=False):
 def pmc_pass(torch, tq, syn):
     """Launches for hardware-counter runs: a 1 GiB device copy (the
     calibration kernel: 1 GiB read, 1 GiB written), each kernel of the
-    headline step three times eagerly, then the decode-attention workloads
-    (one cache copy each) and the search scan (one database)."""
+    headline step three times eagerly, the prepared and LDS-table logit
+    scans, then the decode-attention workloads, the prefill chunk and the
+    fused append step (one cache copy each) and the search scan (one
+    database)."""
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -952,10 +954,14 @@ def pmc_pass(torch, tq, syn):
     for cfg in (3, 5):
         decode_workload(torch, tq, syn, cfg, copies=1, steps=3)
         torch.cuda.empty_cache()
+    prefill_chunk_workload(torch, tq, syn, 3, chunk=16, copies=1, steps=2)
+    torch.cuda.empty_cache()
+    append_step_workload(torch, tq, syn, 3, copies=1, steps=2)
+    torch.cuda.empty_cache()
     search_workload(torch, tq, syn, copies=1, steps=2)
     torch.cuda.empty_cache()
     log("[pmc] done: copy 1 GiB x2, encode x3, logits x3, prepared and LDS-table scans x3, decode attention of "
-        "workloads 3 and 5, search scan")
+        "workloads 3 and 5, the 16-token prefill chunk and the fused append step of workload 3, search scan")
 
 
 # ------------------------------------------------------------------ main
