@@ -1000,8 +1000,8 @@ def main():
     cp = copy_probe(torch)
     t_dom = kd["avg_us"] * 1e-6
     # the roofs of the dominant kernel: HBM (algorithmic bytes), the matrix
-    # cores (algorithmic flops of its dense products, fp16 peak) and VALU
-    # issue (wave instructions the counters saw per launch, while the
+    # cores (algorithmic flops of its dense products, fp16 peak) and vector
+    # ALU issue, "alu" (wave instructions the counters saw per launch, while the
     # committed counter summary is current); the binding roof is the one the
     # kernel comes closest to
     roofs = {"hbm": {"achieved": kd["bytes_per_launch"] / t_dom / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
@@ -1015,9 +1015,9 @@ def main():
                          "per_unit_what": "algorithmic flops per key (the d x d QJL projection)"}
     valu = profile_field(dom, "valu_instructions_per_launch")
     if valu:
-        roofs["valu"] = {"achieved": valu / t_dom / 1e9, "peak": VALU_PEAK / 1e9, "unit": "G wave-instructions/s",
-                         "frac": valu / t_dom / VALU_PEAK, "per_unit": valu / kd["units_per_launch"],
-                         "per_unit_what": "VALU wave instructions per key (counter SQ_INSTS_VALU)"}
+        roofs["alu"] = {"achieved": valu / t_dom / 1e9, "peak": VALU_PEAK / 1e9, "unit": "G wave-instructions/s",
+                        "frac": valu / t_dom / VALU_PEAK, "per_unit": valu / kd["units_per_launch"],
+                        "per_unit_what": "VALU wave instructions per key (counter SQ_INSTS_VALU)"}
     bound = max(roofs, key=lambda r: roofs[r]["frac"])
     rb = roofs[bound]
     roof = {"kernel": dom, "bound": bound, "achieved": rb["achieved"], "peak": rb["peak"], "unit": rb["unit"],
