@@ -335,9 +335,22 @@ constexpr int attend_split() {
   return ring + NRG * (512 / 64) * 1024 <= 160 * 1024 - 4096 ? 512 : 256;
 }
 
-// First head of this block's chunk of 8 heads: the chunks of a group are
-// the launch grid's z dimension.
-__device__ __forceinline__ int head_chunk0() { return 8 * static_cast<int>(blockIdx.z); }
+// A block's place in a group: its block index bx in [0, nb) and its chunk
+// of 8 heads. The chunks are the launch grid's z dimension, or (p.zin > 0,
+// nb a multiple of 8) interleaved into x: x = 8 (zin u + c) + r stands for
+// block 8 u + r of chunk c. Consecutive block ids go to the XCDs in turn,
+// so the zin blocks that scan the same splits for different chunks then
+// start together on the same XCD and its L2 serves their repeated reads.
+__device__ __forceinline__ int head_chunk0(const ScanParams &p) {
+  return 8 * (p.zin ? static_cast<int>((blockIdx.x >> 3) % static_cast<uint32_t>(p.zin)) : static_cast<int>(blockIdx.z));
+}
+__device__ __forceinline__ int scan_block_index(const ScanParams &p) {
+  return p.zin ? static_cast<int>((blockIdx.x & 7u) + 8u * (blockIdx.x / (8u * static_cast<uint32_t>(p.zin))))
+               : static_cast<int>(blockIdx.x);
+}
+__device__ __forceinline__ int scan_blocks(const ScanParams &p) {
+  return p.zin ? static_cast<int>(gridDim.x / static_cast<uint32_t>(p.zin)) : static_cast<int>(gridDim.x);
+}
 
 // Row of q holding head v of the group of (b, kv-head kvh).
 __device__ __forceinline__ int64_t query_row(const ScanParams &p, int64_t b, int64_t kvh, int v) {
@@ -364,7 +377,7 @@ __device__ __forceinline__ void issue_prep(const ScanParams &p, int64_t bh, int 
     for (int k = 0; k < PI::HPW; ++k) {
       const int h = wave + NW * k;
       if (h < GE) {
-        const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, head_chunk0() + h);
+        const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, head_chunk0(p) + h);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int64_t i = row * D + E * lane + e;
@@ -642,7 +655,7 @@ __device__ __forceinline__ void issue_q_rows(const ScanParams &p, int64_t bh, in
   const int upr = D * es / 16;
   const int unit = wave * kWave + lane_id();
   if (unit < GE * upr) {
-    const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, head_chunk0() + unit / upr);
+    const int64_t row = query_row(p, bh / p.n_kv, bh % p.n_kv, head_chunk0(p) + unit / upr);
     dma16_at(static_cast<const uint8_t *>(p.q) + row * D * es + (unit % upr) * 16, scratch + unit * 16);
   }
 }
@@ -788,7 +801,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
   if (ctx < 1) {                                   // nothing to append: an empty partial
     for (int e = tid; e < GE * (D + 2); e += 4 * D) {
       const int hl = e / (D + 2), i = e % (D + 2);
-      part[(head_chunk0() + hl) * (D + 2) + i] = (i == 0) ? -INFINITY : 0.f;
+      part[(head_chunk0(p) + hl) * (D + 2) + i] = (i == 0) ? -INFINITY : 0.f;
     }
     return;
   }
@@ -825,7 +838,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int i = lane + kWave * e;
-        x[k][e] = isq ? load_elem(p.q, (b * n_q + kvh * G + head_chunk0() + r) * D + i, p.xt)
+        x[k][e] = isq ? load_elem(p.q, (b * n_q + kvh * G + head_chunk0(p) + r) * D + i, p.xt)
                       : load_elem(r == GE ? p.k_new : p.v_new, bh * D + i, p.kv_t);
         sgn[k][e] = sg[i];
       }
@@ -936,7 +949,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
 #pragma unroll
       for (int e = 0; e < E; ++e) slm = fmaf(rot[hl * D + lane + kWave * e], ck[lane + kWave * e], slm);
       slm = wave_sum(slm);
-      float *ph = part + (head_chunk0() + hl) * (D + 2);
+      float *ph = part + (head_chunk0(p) + hl) * (D + 2);
       if (lane == 0) { ph[0] = shat[0] * slm * p.sm_scale; ph[1] = 1.0f; }
 #pragma unroll
       for (int e = 0; e < E; ++e) ph[2 + lane + kWave * e] = vh[lane + kWave * e];
@@ -1024,7 +1037,7 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
     slm = wave_sum(slm);
     sqj = wave_sum(sqj);
     const float logit = shat[0] * fmaf(kappa * shat[1], sqj, slm);
-    float *ph = part + (head_chunk0() + hl) * (D + 2);
+    float *ph = part + (head_chunk0(p) + hl) * (D + 2);
     if (lane == 0) { ph[0] = logit * p.sm_scale; ph[1] = 1.0f; }
 #pragma unroll
     for (int e = 0; e < E; ++e) ph[2 + lane + kWave * e] = vh[lane + kWave * e];
@@ -1035,8 +1048,9 @@ __device__ __forceinline__ void append_block(const ScanParams &p, int64_t bh, in
 
 // One block per (batch*kv-head, block index within the group) and the heads
 // [h0, h0 + GE) of the group, GE <= 4 NRG. The block prepares the queries of
-// those heads, then walks the splits blockIdx.x, blockIdx.x + gridDim.x, ...
-// (SH::S tokens each) through the LDS ring. Per split, each wave:
+// those heads, then walks the splits bx, bx + nb, ... (SH::S tokens each;
+// bx and nb from scan_block_index, scan_blocks) through the LDS ring. Per
+// split, each wave:
 //  1. computes the logits of its key tiles for every head (key MFMA);
 //     LOGITS: stores them and moves on; decode: scales them by sm_scale and
 //     publishes its per-head maxima and largest value norm   -- barrier
@@ -1094,7 +1108,7 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
 
   const int G = p.group;
   const int n_q = p.n_kv * G;
-  const int h0 = head_chunk0();
+  const int h0 = head_chunk0(p);
   const int GE = min(GMAX, G - h0);
   // append launches: grid (groups, nb + 1) with the append blocks at y = 0,
   // so that they are dispatched before every scan block (interleaved with
@@ -1108,8 +1122,8 @@ __device__ __forceinline__ void scan_block(const ScanParams &p) {
   ctx64 = ctx64 < 0 ? 0 : (ctx64 > p.max_ctx ? p.max_ctx : ctx64);
   // append: one block per group encodes the new token (the last slot of the
   // context) and the others scan the context before it
-  const int nb = APPEND ? static_cast<int>(gridDim.y) - 1 : static_cast<int>(gridDim.x);
-  const int bx = APPEND ? static_cast<int>(blockIdx.y) - 1 : static_cast<int>(blockIdx.x);
+  const int nb = APPEND ? static_cast<int>(gridDim.y) - 1 : scan_blocks(p);
+  const int bx = APPEND ? static_cast<int>(blockIdx.y) - 1 : scan_block_index(p);
   if constexpr (APPEND) {
     if (bx < 0) {
       append_block<D, KW, VW>(p, bh, GE, nb, ring);
@@ -1466,7 +1480,7 @@ template <int D, int KW, int NRG>
 __global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
   using PS = PrepShape<D, KW, NRG>;
   __shared__ __attribute__((aligned(1024))) uint8_t scratch[PS::BYTES];
-  const int GE = min(4 * NRG, p.group - head_chunk0());
+  const int GE = min(4 * NRG, p.group - head_chunk0(p));
   const int64_t bh = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   PrepIn<D, D / 16> pin;
@@ -1478,7 +1492,7 @@ __global__ __launch_bounds__(4 * D) void prep_kernel(ScanParams p) {
   // fragment f = rg NMF + mf (as the scan blocks hold it) is written by
   // wave f % NW from its registers; the constants from the scratch
   constexpr int64_t PSTR = prepared_stride(D, key_lm(KW));
-  uint8_t *dst = p.prepared_w + (bh * p.n_hchunks + head_chunk0() / 8) * PSTR;
+  uint8_t *dst = p.prepared_w + (bh * p.n_hchunks + head_chunk0(p) / 8) * PSTR;
   constexpr int NW = D / 16;
   const int lane = lane_id();
 #pragma unroll
@@ -1567,6 +1581,21 @@ static void launch_decode_kv(const ScanParams &p, dim3 grid, hipStream_t st) {
   }
 }
 
+// Grid of a scan launch: (blocks, groups, head chunks), or with the chunks
+// interleaved into x (INTERLEAVE, more than one chunk and nb a multiple of
+// 8: sets q.zin); APPEND: (groups, blocks + 1, chunks).
+static inline dim3 scan_grid(ScanParams &q, bool append, bool interleave) {
+  const uint32_t groups = static_cast<uint32_t>(q.batch) * q.n_kv;
+  const uint32_t chunks = static_cast<uint32_t>(q.n_hchunks);
+  q.zin = 0;
+  if (append) return dim3(groups, static_cast<uint32_t>(q.nb + 1), chunks);
+  if (interleave && chunks > 1 && q.nb % 8 == 0) {
+    q.zin = q.n_hchunks;
+    return dim3(static_cast<uint32_t>(q.nb) * chunks, groups, 1);
+  }
+  return dim3(static_cast<uint32_t>(q.nb), groups, chunks);
+}
+
 // MODE 0: the logit scan, 1: from prepared queries, 2: the preparation alone.
 template <int D, int KW, int MODE>
 static void launch_logits_k(const ScanParams &p, dim3 grid, hipStream_t st) {
@@ -1594,12 +1623,13 @@ static void launch_logits_k(const ScanParams &p, dim3 grid, hipStream_t st) {
 template <int D, int MODE, int K0>
 hipError_t launch_logits_m(const ScanParams &p, int kw, hipStream_t st) {
   if (p.batch == 0 || p.n_kv == 0 || (MODE != 2 && p.max_ctx == 0)) return hipSuccess;
-  dim3 grid(static_cast<uint32_t>(p.nb), static_cast<uint32_t>(p.batch) * p.n_kv, static_cast<uint32_t>(p.n_hchunks));
+  ScanParams q = p;
+  const dim3 grid = MODE == 2 ? scan_grid(q, false, false) : scan_grid(q, false, true);
   switch (key_lm(kw)) {
-    case 1: launch_logits_k<D, K0 + 1, MODE>(p, grid, st); break;
-    case 2: launch_logits_k<D, K0 + 2, MODE>(p, grid, st); break;
-    case 3: launch_logits_k<D, K0 + 3, MODE>(p, grid, st); break;
-    default: launch_logits_k<D, K0 + 4, MODE>(p, grid, st);
+    case 1: launch_logits_k<D, K0 + 1, MODE>(q, grid, st); break;
+    case 2: launch_logits_k<D, K0 + 2, MODE>(q, grid, st); break;
+    case 3: launch_logits_k<D, K0 + 3, MODE>(q, grid, st); break;
+    default: launch_logits_k<D, K0 + 4, MODE>(q, grid, st);
   }
   return hipGetLastError();
 }
@@ -1659,17 +1689,17 @@ hipError_t launch_decode_da(const ScanParams &p, int kw, int vw, hipStream_t st)
   if (p.batch == 0 || p.n_kv == 0) return hipSuccess;
   const uint32_t groups = static_cast<uint32_t>(p.batch) * p.n_kv;
   const uint32_t chunks = static_cast<uint32_t>(p.n_hchunks);
-  dim3 grid = APPEND ? dim3(groups, static_cast<uint32_t>(p.nb + 1), chunks)
-                     : dim3(static_cast<uint32_t>(p.nb), groups, chunks);
+  ScanParams q = p;
+  const dim3 grid = scan_grid(q, APPEND, true);
   switch (kw) {
-    case 1: launch_decode_v<D, 1, APPEND>(p, vw, grid, st); break;
-    case 2: launch_decode_v<D, 2, APPEND>(p, vw, grid, st); break;
-    case 3: launch_decode_v<D, 3, APPEND>(p, vw, grid, st); break;
-    case 4: launch_decode_v<D, 4, APPEND>(p, vw, grid, st); break;
+    case 1: launch_decode_v<D, 1, APPEND>(q, vw, grid, st); break;
+    case 2: launch_decode_v<D, 2, APPEND>(q, vw, grid, st); break;
+    case 3: launch_decode_v<D, 3, APPEND>(q, vw, grid, st); break;
+    case 4: launch_decode_v<D, 4, APPEND>(q, vw, grid, st); break;
     case kKeyFp8:
-      if constexpr (!APPEND) launch_decode_v<D, kKeyFp8, false>(p, vw, grid, st);
+      if constexpr (!APPEND) launch_decode_v<D, kKeyFp8, false>(q, vw, grid, st);
       break;
-    default: launch_decode_msek_d<D, APPEND>(p, kw, vw, grid, st);
+    default: launch_decode_msek_d<D, APPEND>(q, kw, vw, grid, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -47,6 +47,9 @@ struct ScanParams {
   int32_t h0;                           // first head of this launch's head chunk (multiple of 8)
   int32_t n_hchunks;                    // ceil(group / 8)
   int32_t nb;                           // blocks per (batch, kv-head) group
+  // > 0: the head chunks of a group are interleaved into the grid's x
+  // dimension (x = nb zin blocks, y = groups) instead of riding on z
+  int32_t zin;
   float sm_scale;
   int32_t qjl;                          // 1: full estimator; 0 (logit scan only): its first (MSE) term
   float *partials;                      // decode: [batch*n_kv][nb][group][D+2]

@@ -146,6 +146,9 @@ def test_encode_is_deterministic():
     (128, 1, 8, 1, 1, 1), (64, 3, 5, 1, 1, 200),
     # 256 (batch, kv-head) groups: one block per group walks all 4 splits
     (128, 3, 4, 4, 64, 1000),
+    # 16 blocks per group, several head chunks (the last one short): the
+    # chunks interleaved into the grid's x dimension
+    (128, 2, 24, 1, 1, 4001), (64, 3, 20, 1, 2, 4096),
 ])
 def test_logits_given_oracle_codes(d, w, group, batch, n_kv, n_keys):
     say(f"logits d={d} w={w} G={group} batch={batch} n_kv={n_kv} n_keys={n_keys}")
@@ -187,6 +190,10 @@ def test_logits_given_oracle_codes(d, w, group, batch, n_kv, n_keys):
     # 8 heads, several 512-token splits per block and a ragged last one
     (128, 3, 4, 8, 1, 1, 2100, [2100]),
     (64, 3, 4, 8, 2, 1, 1600, [1600, 1025]),
+    # 8 blocks per group and two or three head chunks (the last one short):
+    # the chunks interleaved into the grid's x dimension
+    (128, 2, 4, 16, 2, 1, 4096, [4096, 2900]),
+    (64, 3, 4, 20, 1, 2, 4096, [4096]),
 ])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_decode_attend_given_oracle_codes(d, kw, vw, group, batch, n_kv, T, lens, out_dtype):

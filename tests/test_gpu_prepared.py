@@ -19,6 +19,8 @@ pytestmark = pytest.mark.gpu
     (64, 2, 8, 3, 1, 777, torch.bfloat16),
     (64, 4, 5, 1, 3, 4096, torch.float16),
     (128, 4, 1, 4, 2, 300, torch.float32),
+    # 16 blocks per group: the three head chunks interleaved into the grid's x
+    (128, 2, 24, 1, 2, 4001, torch.bfloat16),
 ])
 def test_prepared_logits_equal_one_call_logits(d, w, group, batch, n_kv, n_keys, qdt):
     say(f"prepared logits d={d} w={w} G={group} batch={batch} n_kv={n_kv} keys={n_keys} q={qdt}")
