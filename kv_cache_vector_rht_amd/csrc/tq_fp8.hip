@@ -5,15 +5,52 @@
 // OCP e4m3fn byte of x / scale, rounded to nearest even, finite values
 // beyond +-448 saturating (NaN stays NaN). The decode kernels read these
 // records with the key width kKeyFp8.
+#include <cfloat>
+#include <cmath>
+
 #include "tq_device.h"
 #include "tq_kernels.h"
 
 namespace tq {
 namespace {
 
-// One thread per 8 consecutive coordinates of a token: 8 loads, one 8-byte store.
+// The 8 coordinates of one unit as floats. VEC: the unit's elements are
+// 16-byte aligned (one 16-byte load for 16-bit inputs, two for fp32).
+template <int XT, bool VEC>
+__device__ __forceinline__ void load8(const void *x, int64_t x0, float (&y)[8]) {
+  if constexpr (VEC) {
+    if constexpr (XT == 0) {
+      const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + x0);
+      const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + x0 + 4);
+      y[0] = a.x; y[1] = a.y; y[2] = a.z; y[3] = a.w;
+      y[4] = b.x; y[5] = b.y; y[6] = b.z; y[7] = b.w;
+    } else {
+      const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + x0);
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t lo = static_cast<uint16_t>(w[e] & 0xffffu), hi = static_cast<uint16_t>(w[e] >> 16);
+        y[2 * e] = XT == 1 ? bf16_bits_to_float(lo) : f16_bits_to_float(lo);
+        y[2 * e + 1] = XT == 1 ? bf16_bits_to_float(hi) : f16_bits_to_float(hi);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (XT == 0) y[e] = static_cast<const float *>(x)[x0 + e];
+      else if constexpr (XT == 1) y[e] = bf16_bits_to_float(static_cast<const uint16_t *>(x)[x0 + e]);
+      else y[e] = f16_bits_to_float(static_cast<const uint16_t *>(x)[x0 + e]);
+    }
+  }
+}
+
+// One thread per 8 consecutive coordinates of a token, one 8-byte store.
+// POW2: scale is a power of two, so x / scale = x * (1 / scale) exactly
+// (both are the exact quotient rounded once).
+template <int XT, bool VEC, bool POW2>
 __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeParams p, int d, float scale, int64_t n_units) {
   const int per_tok = d / 8;
+  const float inv = 1.0f / scale;
   for (int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; u < n_units;
        u += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t tok = u / per_tok;
@@ -21,13 +58,10 @@ __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeParams p, int d, 
     const int64_t s = tok / p.n_tok, t = tok % p.n_tok;
     const int64_t x0 = s * p.x_seq_stride + t * p.x_tok_stride + 8 * c8;
     float y[8];
+    load8<XT, VEC>(p.x, x0, y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v;
-      if (p.xt == 0) v = static_cast<const float *>(p.x)[x0 + e];
-      else if (p.xt == 1) v = bf16_bits_to_float(static_cast<const uint16_t *>(p.x)[x0 + e]);
-      else v = f16_bits_to_float(static_cast<const uint16_t *>(p.x)[x0 + e]);
-      v = __fdiv_rn(v, scale);
+      const float v = POW2 ? y[e] * inv : __fdiv_rn(y[e], scale);
       y[e] = (fabsf(v) > 448.0f) ? copysignf(448.0f, v) : v;
     }
     int w0 = 0, w1 = 0;
@@ -40,6 +74,25 @@ __global__ __launch_bounds__(256) void encode_fp8_kernel(EncodeParams p, int d, 
   }
 }
 
+template <int XT, bool VEC>
+void launch_fp8_x(const EncodeParams &p, int d, float scale, int64_t n_units, dim3 grid, hipStream_t st) {
+  int ex = 0;
+  const bool pow2 = std::frexp(scale, &ex) == 0.5f && scale >= FLT_MIN;   // (1 / scale finite)
+  if (pow2) hipLaunchKernelGGL((encode_fp8_kernel<XT, VEC, true>), grid, dim3(256), 0, st, p, d, scale, n_units);
+  else hipLaunchKernelGGL((encode_fp8_kernel<XT, VEC, false>), grid, dim3(256), 0, st, p, d, scale, n_units);
+}
+
+template <int XT>
+void launch_fp8_t(const EncodeParams &p, int d, float scale, int64_t n_units, dim3 grid, hipStream_t st) {
+  // every unit starts 8 elements into a row: 16-byte aligned when the base
+  // and both strides are (in bytes)
+  const int64_t esz = XT == 0 ? 4 : 2;
+  const bool vec = reinterpret_cast<uintptr_t>(p.x) % 16 == 0 && (p.x_seq_stride * esz) % 16 == 0 &&
+                   (p.x_tok_stride * esz) % 16 == 0;
+  if (vec) launch_fp8_x<XT, true>(p, d, scale, n_units, grid, st);
+  else launch_fp8_x<XT, false>(p, d, scale, n_units, grid, st);
+}
+
 }  // namespace
 
 hipError_t launch_encode_fp8(const EncodeParams &p, int d, float scale, hipStream_t st) {
@@ -47,7 +100,10 @@ hipError_t launch_encode_fp8(const EncodeParams &p, int d, float scale, hipStrea
   if (n_units == 0) return hipSuccess;
   int64_t blocks = (n_units + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(encode_fp8_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, p, d, scale, n_units);
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  if (p.xt == 0) launch_fp8_t<0>(p, d, scale, n_units, grid, st);
+  else if (p.xt == 1) launch_fp8_t<1>(p, d, scale, n_units, grid, st);
+  else launch_fp8_t<2>(p, d, scale, n_units, grid, st);
   return hipGetLastError();
 }
 

@@ -20,9 +20,13 @@ DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("scale", [1.0, 0.6])
-def test_encode_fp8_keys_bit_exact(d, dt, scale):
-    say(f"fp8 key encode d={d} dtype={dt} scale={scale}")
+@pytest.mark.parametrize("scale,layout", [(1.0, "contiguous"), (0.6, "contiguous"), (0.25, "contiguous"),
+                                          (0.6, "offset"), (4.0, "offset")])
+def test_encode_fp8_keys_bit_exact(d, dt, scale, layout):
+    """Scales 1, 0.25 and 4 take the reciprocal product (exact for powers of
+    two), 0.6 the correctly rounded quotient; rows that start one element
+    into a wider buffer take the element-wise loads."""
+    say(f"fp8 key encode d={d} dtype={dt} scale={scale} layout={layout}")
     n_seq, n_tok, t0, cap = 3, 257, 5, 300
     g = torch.Generator(device="cpu")
     g.manual_seed(d + int(10 * scale))
@@ -30,7 +34,13 @@ def test_encode_fp8_keys_bit_exact(d, dt, scale):
     x[0, 0, :4] = torch.tensor([600.0, -1e4, 1e-7, -0.0])       # saturation, subnormal range, -0
     x = x.to(DTYPES[dt])
     codes = tq.alloc_fp8_key_cache(n_seq, cap, d)
-    tq.encode_fp8_keys(x.to("cuda"), codes, scale=scale, t0=t0)
+    if layout == "offset":
+        wide = torch.zeros((n_seq, n_tok, d + 1), dtype=x.dtype, device="cuda")
+        wide[:, :, 1:] = x.to("cuda")
+        xd = wide[:, :, 1:]
+    else:
+        xd = x.to("cuda")
+    tq.encode_fp8_keys(xd, codes, scale=scale, t0=t0)
     torch.cuda.synchronize()
     ref = O.e4m3_encode(x.to(torch.float32).numpy(), scale)
     got = codes.cpu().numpy()
