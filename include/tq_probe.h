@@ -3,7 +3,7 @@
  * path: a plain read-and-reduce stream that measures how many bytes per
  * second the GPU's memory delivers to a kernel that only reads, the ceiling
  * against which the read-dominated scans (logits, decode attention) are
- * judged beside the datasheet peak; and the LDS-table formulation of the
+ * compared with the datasheet peak; and the LDS-table formulation of the
  * logit scan, measured beside the matrix-core one.
  *
  * tq_probe_read: every 16-byte chunk of src [0, bytes) is loaded once (eight

@@ -105,7 +105,7 @@ def test_exact_ties_same_cells_in_encode_and_append(d, dt):
 
     # against the oracle: the negative ties are the only index differences
     # (the oracle sends them to the upper cell), each on its threshold; the
-    # rest of each key (residual norm, sign bits) is judged with the GPU's
+    # rest of each key (residual norm, sign bits) is checked with the GPU's
     # indices
     enc_k = O.encode(to_f64(xk_t), s, C, T, S)
     enc_v = O.encode(to_f64(xv_t), sv, C, T)

@@ -4,7 +4,7 @@
       fp64 pre-decision value (y_i or z_j, unit domain) lies within 1e-6 of
       the crossed boundary. After an excused index mismatch the oracle
       recomputes r, gamma and z from the GPU's indices before the vector's
-      signs are judged.
+      signs are compared.
 (ii)  fp16 scalars may differ by one ulp only where the fp64 value lies
       within 1e-6 (relative) of an fp16 rounding midpoint.
 (iii) Excused mismatches number at most 1e-5 of the coded items.
