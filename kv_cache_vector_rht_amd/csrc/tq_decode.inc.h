@@ -1535,19 +1535,42 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(ScanParams p) {
   const int nb = p.nb + p.append;                          // partials per group
   const int64_t pstride = static_cast<int64_t>(G) * (D + 2);
   const float *ph = p.partials + bh * nb * pstride + (h0 + hl) * (D + 2);
-  float M = -INFINITY;
-  for (int j = lane; j < nb; j += kWave) M = fmaxf(M, ph[j * pstride]);
-  M = wave_max(M);
-  float L = 0.f;
+  // one pass over the partials, MB at a time: every load of a batch is
+  // issued before any is used (the partials come from other XCDs' blocks,
+  // so each round trip goes to memory), and the running sums are rescaled
+  // when a batch raises the maximum. With at most MB partials this is the
+  // plain max-then-sum merge.
+  constexpr int MB = 8;
+  float M = -INFINITY, L = 0.f;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int j = 0; j < nb; ++j) {
-    const float m = ph[j * pstride];
-    const float w = (m == -INFINITY) ? 0.f : __expf(m - M);
-    L = fmaf(ph[j * pstride + 1], w, L);
+  for (int j0 = 0; j0 < nb; j0 += MB) {
+    float mj[MB], lj[MB], aj[MB][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = fmaf(ph[j * pstride + 2 + lane + kWave * e], w, acc[e]);
+    for (int u = 0; u < MB; ++u) {
+      const float *pj = ph + min(j0 + u, nb - 1) * pstride;   // (batch tail: re-read, weight 0)
+      mj[u] = pj[0];
+      lj[u] = pj[1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) aj[u][e] = pj[2 + lane + kWave * e];
+    }
+    float mx = M;
+#pragma unroll
+    for (int u = 0; u < MB; ++u)
+      if (j0 + u < nb) mx = fmaxf(mx, mj[u]);
+    const float r = (M == -INFINITY) ? 0.f : __expf(M - mx);
+    L *= r;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= r;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const float w = (j0 + u >= nb || mj[u] == -INFINITY) ? 0.f : __expf(mj[u] - mx);
+      L = fmaf(lj[u], w, L);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(aj[u][e], w, acc[e]);
+    }
+    M = mx;
   }
   float x[E];
 #pragma unroll
