@@ -50,8 +50,12 @@ is named in the function that relies on it:
                 keeps its index planes and norm only, and its logit is the
                 estimator's first term n sum_i q'_i c[idx_i].
 
-Parity of the estimator itself (logits given codes) is unpinned beyond its
-special cases: the pages print no logit values.
+The pages print no worked logit values. The estimator is pinned instead by
+what they state about it and by independent restatements: its mean over
+fresh sketches equals <q, k> (unbiasedness over 1e5 pairs, with a negative
+control that drops the QJL term and the variance in closed form), and
+key_logits equals the formula written with scipy's Hadamard matrix and
+explicit products.
 """
 from __future__ import annotations
 
