@@ -229,14 +229,21 @@ def test_decode_attend_given_oracle_codes(d, kw, vw, group, batch, n_kv, T, lens
 # ------------------------------------------------------------------ graphs
 
 
-def test_calls_replay_in_a_hip_graph():
-    """encode + logits + decode captured in one HIP graph: every replay, with
-    eager work and synchronisations in between, reproduces the eager
-    results bit for bit (the benchmark times such replays)."""
-    say("graph capture: encode + logits + decode, 3 replays")
-    d, kw, vw, batch, n_kv, group, T = 128, 3, 4, 2, 2, 4, 600
+@pytest.mark.parametrize("group,T,chunk", [
+    (4, 600, 2),
+    # 16 logit and 8 decode blocks per group, three head chunks: the chunks
+    # interleaved into the grid's x dimension; a 96-pair single-pass prefill
+    (24, 4000, 4),
+])
+def test_calls_replay_in_a_hip_graph(group, T, chunk):
+    """encode + logits + decode + a prefill chunk captured in one HIP graph:
+    every replay, with eager work and synchronisations in between,
+    reproduces the eager results bit for bit (the benchmark times such
+    replays)."""
+    say(f"graph capture: encode + logits + decode + prefill, G={group} T={T} chunk={chunk}, 3 replays")
+    d, kw, vw, batch, n_kv = 128, 3, 4, 2, 2
     kc, vc = key_codec(801, d, kw), value_codec(802, d, vw)
-    cap = 608
+    cap = (T + 31) // 32 * 32 + 32
     k = _inputs(batch * n_kv, T, d, torch.bfloat16, seed=11, stream=1, scale_channels=True)
     v = _inputs(batch * n_kv, T, d, torch.bfloat16, seed=12, stream=2)
     q = _inputs(batch, n_kv * group, d, torch.bfloat16, seed=13, stream=3)
@@ -247,6 +254,10 @@ def test_calls_replay_in_a_hip_graph():
     out = torch.empty((batch, n_kv * group, d), dtype=torch.float32, device="cuda")
     lws = torch.empty(max(256, tq.logits_workspace(batch, n_kv, group, d)), dtype=torch.uint8, device="cuda")
     dws = torch.empty(tq.decode_attend_workspace(batch, n_kv, group, T, d), dtype=torch.uint8, device="cuda")
+    qp = _inputs(batch * chunk, n_kv * group, d, torch.bfloat16, seed=14, stream=3).view(batch, chunk, n_kv * group, d)
+    p0 = torch.tensor([T - chunk, T // 2], dtype=torch.int32, device="cuda")
+    pout = torch.empty((batch, chunk, n_kv * group, d), dtype=torch.float32, device="cuda")
+    pws = torch.empty(tq.prefill_attend_workspace(batch, chunk, n_kv, group, T, d), dtype=torch.uint8, device="cuda")
 
     def calls():
         tq.encode_kv(kc.gpu, k, kcodes, kscal)
@@ -254,10 +265,12 @@ def test_calls_replay_in_a_hip_graph():
         tq.logits(kc.gpu, q, kcodes, kscal, n_kv_heads=n_kv, group=group, n_keys=T, out=lg, workspace=lws)
         tq.decode_attend(kc.gpu, vc.gpu, q, kcodes, kscal, vcodes, vscal, ctx, n_kv_heads=n_kv, group=group,
                          max_ctx=T, out=out, workspace=dws)
+        tq.prefill_attend(kc.gpu, vc.gpu, qp, kcodes, kscal, vcodes, vscal, p0, n_kv_heads=n_kv, group=group,
+                          max_ctx=T, out=pout, workspace=pws)
 
     calls()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (kcodes, kscal, vcodes, vscal, lg, out)]
+    ref = [t.clone() for t in (kcodes, kscal, vcodes, vscal, lg, out, pout)]
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -269,13 +282,13 @@ def test_calls_replay_in_a_hip_graph():
         calls()
     scratch = tq.alloc_key_cache(batch * n_kv, cap, kc.gpu)
     for rep in range(3):
-        for t in (kcodes, kscal, vcodes, vscal, lg, out):
+        for t in (kcodes, kscal, vcodes, vscal, lg, out, pout):
             t.zero_()
         tq.encode_kv(kc.gpu, k, *scratch)            # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip((kcodes, kscal, vcodes, vscal, lg, out), ref):
+        for a, b in zip((kcodes, kscal, vcodes, vscal, lg, out, pout), ref):
             assert torch.equal(a, b), f"replay {rep} differs"
 
 
