@@ -55,6 +55,10 @@ def test_encode_fp8_keys_bit_exact(d, dt, scale, layout):
     (64, 2, 1, 1, 3, 96, [95], "f16"),
     (128, 3, 16, 1, 1, 64, [37], "bf16"),
     (128, 4, 4, 32, 8, 600, [600, 1, 300, 0, 257, 512, 599, 513] * 4, "bf16"),
+    # 8 blocks per group and two or three head chunks: the chunks
+    # interleaved into the grid's x dimension
+    (128, 4, 16, 1, 1, 4096, [4000], "bf16"),
+    (64, 2, 24, 2, 1, 4096, [4096, 1500], "f32"),
 ])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_decode_attend_k8_given_codes(d, vw, group, batch, n_kv, T, lens, qdt, out_dtype):
